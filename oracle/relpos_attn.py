@@ -1,0 +1,190 @@
+"""Plain float64 definition of the paged chunk attention path (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may use this
+module. It shares no code with the HIP path and imports nothing from it.
+
+Sources, cited by page title and section (OASR documentation):
+
+* "ASR Engine", section 4.3 "Batched paged forward": a cohort of B streams shares one block pool;
+  each stream has a block table (B, blocks_per_seq) and a cache_seqlens entry (B,); the chunk's K/V
+  are written into the stream's pages, and cache_seqlens is advanced by commit_chunk_paged only
+  after the forward, so during the forward it counts the frames cached *before* the chunk.
+  One PagedKVCache per layer shares the block table and cache_seqlens.
+* "Scheduler", section 4.3 "Heterogeneous-offset batching": the attention runs over the paged pool
+  with a per-stream length mask built from cache_seqlens, and the Conformer relative-position bias
+  matrix_bd is added to the scores scaled by 1/sqrt(d_k); the positional embedding is built per
+  stream when offsets differ and collapses to one broadcast table when they match.
+* "Model Layer", "Three optional encoder declarations" (fixed_attention_window): a Transformer-XL
+  table's distances are cache + i - j; a uniform cache_seqlens lets one shared table serve the
+  whole cohort, otherwise each row needs its own table.
+* "Model Layer", "The engine-facing surface" (forward_offline_packed) and "ASR Engine" section 4.1
+  (sequence packing): the offline forward packs utterances into one gapless varlen row and
+  attention never crosses an utterance boundary.
+
+Readings where the pages are silent (each is listed, with its reason, in the design notes):
+
+* Score: s[i, j] = ((q_i + u) . k_j + (q_i + v) . p[cache + i - j]) * scale, scale = 1/sqrt(D)
+  applied to the sum (the pages scale matrix_bd by 1/sqrt(d_k); the content term carries the same
+  scale in standard scaled dot-product attention).
+* No mask inside the window: each of the C chunk queries sees every cached frame and every chunk
+  frame (unlimited left context, no causality inside the chunk).
+* Table orientation: row r of a table with centre ``center`` holds the embedding of the signed
+  distance ``center - r`` (row 0 is the largest positive distance). A shared table is centred at
+  (P - 1) / 2; a per-row table of stream b holds 2 T_b - 1 rows centred at T_b - 1, T_b = c_b + C.
+* GQA: query head h reads kv head h * Hk // H.
+* Page layout (the pages give none): k_pool[n, g, s, d] and v_pool[n, g, d, s] (V transposed inside
+  each page); logical frame t of stream b sits in block block_tables[b, t // S], slot t % S.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+DEFAULT_LAYOUT = {"k_pool": "[num_blocks, n_kv_head, block_size, head_dim]",
+                  "v_pool": "[num_blocks, n_kv_head, head_dim, block_size]"}
+
+
+def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens):
+    """Write each stream's chunk K/V into its pages ("ASR Engine" section 4.3, steps 1 and 5).
+
+    k_new, v_new: [B, C, Hk, D]. Frame t of the chunk of stream b is logical frame
+    L = cache_seqlens[b] + t, stored in block block_tables[b, L // S] at slot L % S.
+    Returns new pools; every element that is not written is copied unchanged. Works on any dtype
+    (pass integer views of the storage to compare bit patterns).
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    n_streams, chunk = k_new.shape[0], k_new.shape[1]
+    block_size = k_pool.shape[2]
+    for b in range(n_streams):
+        for t in range(chunk):
+            frame = int(cache_seqlens[b]) + t
+            block = int(block_tables[b, frame // block_size])
+            slot = frame % block_size
+            k_out[block, :, slot, :] = k_new[b, t]
+            v_out[block, :, :, slot] = v_new[b, t]
+    return k_out, v_out
+
+
+def gather_stream(k_pool, v_pool, block_table_row, n_frames):
+    """Read logical frames [0, n_frames) of one stream through its block table.
+
+    Returns K, V as [n_frames, Hk, D] arrays in the pool's dtype ("Scheduler" section 4.3: the
+    attention reads the paged pool through each stream's table).
+    """
+    block_size = k_pool.shape[2]
+    ks, vs = [], []
+    for t in range(n_frames):
+        block = int(block_table_row[t // block_size])
+        slot = t % block_size
+        ks.append(k_pool[block, :, slot, :])
+        vs.append(v_pool[block, :, :, slot])
+    return np.stack(ks), np.stack(vs)
+
+
+def table_row(center, cache, i, j):
+    """Row of a Transformer-XL table that holds the distance cache + i - j ("Model Layer",
+    fixed_attention_window declaration), with rows in descending distance order."""
+    return center - (cache + i - j)
+
+
+def _attend(q, k, v, pos_rows, u, w, center, cache, scale):
+    """Attention of C queries at absolute positions cache + i over T = cache + C keys (one stream).
+
+    q: [C, H, D]; k, v: [T, Hk, D]; pos_rows: [P_b, H, D] table of this stream. Returns the output
+    [C, H, D] and the probabilities [H, C, T].
+    """
+    n_q, n_head, _ = q.shape
+    n_k, n_kv_head = k.shape[0], k.shape[1]
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    rows = table_row(center, cache, i, j)  # [C, T]
+    if rows.min() < 0 or rows.max() >= pos_rows.shape[0]:
+        raise ValueError("relative-position table too short for distances cache + i - j")
+    out = np.empty((n_q, n_head, v.shape[2]))
+    probs = np.empty((n_head, n_q, n_k))
+    for h in range(n_head):
+        g = h * n_kv_head // n_head
+        content = (q[:, h, :] + u[h]) @ k[:, g, :].T                       # (q + u) . k_j
+        emb = pos_rows[rows, h, :]                                            # p[cache + i - j]
+        position = np.einsum("id,ijd->ij", q[:, h, :] + w[h], emb)           # (q + v) . p
+        s = (content + position) * scale
+        s = s - s.max(axis=1, keepdims=True)
+        a = np.exp(s)
+        a = a / a.sum(axis=1, keepdims=True)
+        probs[h] = a
+        out[:, h, :] = a @ v[:, g, :]
+    return out, probs
+
+
+def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u, pos_bias_v,
+                      per_row_pos=False, scale=None, return_probs=False):
+    """Chunk attention of every stream over its cached frames plus its own chunk.
+
+    q: [B, C, H, D]. The chunk's K/V must already be in the pools (append first, then attend).
+    pos: one shared table [P, H, D] centred at (P - 1) / 2, or per-row tables [B, P_max, H, D],
+    row b centred at T_b - 1 with 2 T_b - 1 meaningful rows. pos_bias_u, pos_bias_v: [H, D].
+    Returns out [B, C, H, D] in float64 (and the per-stream probabilities when asked).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    u = np.asarray(pos_bias_u, dtype=np.float64)
+    w = np.asarray(pos_bias_v, dtype=np.float64)
+    n_streams, chunk, _, head_dim = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(head_dim)
+    out = np.empty(q.shape)
+    all_probs = []
+    for b in range(n_streams):
+        cache = int(cache_seqlens[b])
+        n_k = cache + chunk
+        k, v = gather_stream(k_pool, v_pool, block_tables[b], n_k)
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        if per_row_pos:
+            center = n_k - 1
+            rows = np.asarray(pos[b][: 2 * n_k - 1], dtype=np.float64)
+        else:
+            if pos.shape[0] % 2 != 1:
+                raise ValueError("a shared relative-position table has an odd number of rows")
+            center = (pos.shape[0] - 1) // 2
+            rows = np.asarray(pos, dtype=np.float64)
+        out[b], probs = _attend(q[b], k, v, rows, u, w, center, cache, scale)
+        all_probs.append(probs)
+    if return_probs:
+        return out, all_probs
+    return out
+
+
+def varlen_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, scale=None,
+                       return_probs=False):
+    """Full-context attention inside each packed segment ("Model Layer", forward_offline_packed).
+
+    q: [total, H, D], k, v: [total, Hk, D], packed gapless; segment s is frames
+    [cu_seqlens[s], cu_seqlens[s+1]). Its table has 2 L_s - 1 rows centred at L_s - 1 and starts at
+    row 2 cu_seqlens[s] - s of pos [2 total - S, H, D]. Each segment is the chunk case with
+    cache = 0 and C = L_s. Returns out [total, H, D] in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    u = np.asarray(pos_bias_u, dtype=np.float64)
+    w = np.asarray(pos_bias_v, dtype=np.float64)
+    head_dim = q.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(head_dim)
+    out = np.empty(q.shape)
+    all_probs = []
+    n_seg = len(cu_seqlens) - 1
+    for s in range(n_seg):
+        lo, hi = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        n = hi - lo
+        if n == 0:
+            all_probs.append(np.zeros((q.shape[1], 0, 0)))
+            continue
+        row0 = 2 * lo - s
+        rows = np.asarray(pos[row0: row0 + 2 * n - 1], dtype=np.float64)
+        out[lo:hi], probs = _attend(q[lo:hi], k[lo:hi], v[lo:hi], rows, u, w, n - 1, 0, scale)
+        all_probs.append(probs)
+    if return_probs:
+        return out, all_probs
+    return out

@@ -1,0 +1,19 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This package only draws and lays out inputs (random values, block tables, cache lengths, the
+sinusoidal positional tables that feed the attention). It contains none of the attention's
+arithmetic and imports neither the oracle nor the HIP path.
+"""
+
+from .cohorts import (  # noqa: F401
+    CONFIGS,
+    ChunkCohort,
+    VarlenCohort,
+    make_chunk_cohort,
+    make_varlen_cohort,
+    make_config,
+    sinusoidal_embedding,
+    relpos_projection,
+    embed_distances,
+    descending_table,
+)

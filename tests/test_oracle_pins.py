@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped term, a flipped distance
+sign, an off-by-one table centre, a transposed operand, a wrong page address) fails at least one
+of them; ``test_planted_mistakes_are_caught`` plants such slips in the oracle and checks that.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.relpos_attn as orc
+from synth import descending_table, embed_distances, make_chunk_cohort, make_varlen_cohort, relpos_projection
+from synth import CONFIGS, make_config
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F64 = torch.float64
+
+
+def np64(t):
+    return t.detach().cpu().to(F64).numpy()
+
+
+# --------------------------------------------------------------------------------------------
+# Append and page addressing
+# --------------------------------------------------------------------------------------------
+
+def test_append_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "append_worked_example.json")))
+    S, N, Hk, D, C = g["block_size"], g["num_blocks"], g["n_kv_head"], g["head_dim"], g["chunk_size"]
+    bt = np.array(g["block_tables"])
+    cs = np.array(g["cache_seqlens"])
+    B = bt.shape[0]
+    k_new = np.zeros((B, C, Hk, D))
+    for b in range(B):
+        for t in range(C):
+            for d in range(D):
+                k_new[b, t, :, d] = 100 * b + 10 * t + d
+    v_new = -k_new - 1000
+    kp = np.full((N, Hk, S, D), np.nan)
+    vp = np.full((N, Hk, D, S), np.nan)
+    k2, v2 = oracle.paged_kv_append(kp, vp, k_new, v_new, bt, cs)
+    expect_k = np.full_like(kp, np.nan)
+    expect_v = np.full_like(vp, np.nan)
+    for p in g["placements"]:
+        expect_k[p["block"], :, p["slot"], :] = k_new[p["stream"], p["t"]]
+        expect_v[p["block"], :, :, p["slot"]] = v_new[p["stream"], p["t"]]
+    np.testing.assert_array_equal(k2, expect_k)
+    np.testing.assert_array_equal(v2, expect_v)
+
+
+@pytest.mark.parametrize("S", [4, 8, 16])
+def test_append_then_gather_round_trip(S):
+    """Appending chunks step by step and reading back through the table returns the stream's
+    frames in order; no element outside the written slots changes (bit patterns compared)."""
+    rng = np.random.default_rng(S)
+    B, Hk, D, C, steps = 3, 2, 4, 5, 4
+    pages = (C * steps + S - 1) // S
+    N = B * pages + 3
+    ids = rng.permutation(N)
+    bt = np.full((B, pages + 2), -1)
+    for b in range(B):
+        bt[b, :pages] = ids[b * pages:(b + 1) * pages]
+    kp = np.full((N, Hk, S, D), np.nan)
+    vp = np.full((N, Hk, D, S), np.nan)
+    seq_k = rng.standard_normal((B, C * steps, Hk, D))
+    seq_v = rng.standard_normal((B, C * steps, Hk, D))
+    for step in range(steps):
+        cs = np.full(B, step * C)
+        kp, vp = oracle.paged_kv_append(kp, vp, seq_k[:, step * C:(step + 1) * C],
+                                        seq_v[:, step * C:(step + 1) * C], bt, cs)
+    for b in range(B):
+        k, v = oracle.gather_stream(kp, vp, bt[b], C * steps)
+        np.testing.assert_array_equal(k, seq_k[b])
+        np.testing.assert_array_equal(v, seq_v[b])
+    written = B * C * steps * Hk * D
+    assert np.count_nonzero(~np.isnan(kp)) == written
+    assert np.count_nonzero(~np.isnan(vp)) == written
+
+
+def test_append_is_bit_exact_on_bf16_patterns():
+    """The append is a copy: bf16 bit patterns (as int16) survive untouched, NaN payloads too."""
+    rng = np.random.default_rng(1)
+    kp = rng.integers(-2**15, 2**15, size=(6, 1, 4, 2)).astype(np.int16)
+    vp = rng.integers(-2**15, 2**15, size=(6, 1, 2, 4)).astype(np.int16)
+    k_new = rng.integers(-2**15, 2**15, size=(1, 3, 1, 2)).astype(np.int16)
+    v_new = rng.integers(-2**15, 2**15, size=(1, 3, 1, 2)).astype(np.int16)
+    bt = np.array([[4, 0]])
+    k2, v2 = oracle.paged_kv_append(kp, vp, k_new, v_new, bt, np.array([2]))
+    assert (k2[4, :, 2] == k_new[0, 0]).all() and (k2[4, :, 3] == k_new[0, 1]).all()
+    assert (k2[0, :, 0] == k_new[0, 2]).all()
+    assert (v2[4, :, :, 2] == v_new[0, 0]).all() and (v2[0, :, :, 0] == v_new[0, 2]).all()
+    changed = (k2 != kp).any(axis=(1, 3)).sum()
+    assert changed <= 3
+
+
+# --------------------------------------------------------------------------------------------
+# Attention pins
+# --------------------------------------------------------------------------------------------
+
+def _paged_from_sequences(seq_k, seq_v, caches, C, S, rng, pad_blocks=2):
+    """Page full logical sequences into a fresh NaN pool through the oracle's append (which the
+    tests above pin), frame by frame; returns pools and tables."""
+    B = len(seq_k)
+    Hk, D = seq_k[0].shape[1], seq_k[0].shape[2]
+    pages = [(c + C + S - 1) // S for c in caches]
+    N = sum(pages) + pad_blocks
+    ids = rng.permutation(N)
+    M = max(pages) + 1
+    bt = np.full((B, M), -1)
+    at = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = ids[at:at + n]
+        at += n
+    kp = np.full((N, Hk, S, D), np.nan)
+    vp = np.full((N, Hk, D, S), np.nan)
+    for b in range(B):
+        for t in range(caches[b] + C):
+            kp, vp = oracle.paged_kv_append(kp, vp, seq_k[b][None, t:t + 1], seq_v[b][None, t:t + 1],
+                                            bt[b:b + 1], np.array([t]))
+    return kp, vp, bt
+
+
+def _random_streaming_case(seed, caches, C=4, H=2, Hk=2, D=8, S=4, zero_pos=False, margin=0):
+    rng = np.random.default_rng(seed)
+    B = len(caches)
+    seq_k = [rng.standard_normal((c + C, Hk, D)) for c in caches]
+    seq_v = [rng.standard_normal((c + C, Hk, D)) for c in caches]
+    q = rng.standard_normal((B, C, H, D))
+    u = 0.3 * rng.standard_normal((H, D))
+    w = 0.3 * rng.standard_normal((H, D))
+    proj = relpos_projection(H * D, torch.Generator().manual_seed(seed))
+    if zero_pos:
+        proj = proj * 0
+        u = u * 0
+        w = w * 0
+    kp, vp, bt = _paged_from_sequences(seq_k, seq_v, caches, C, S, rng)
+    center = max(caches) + C - 1 + margin
+    table = descending_table(center, proj, H, D).numpy()
+    return dict(q=q, u=u, w=w, proj=proj, kp=kp, vp=vp, bt=bt, cs=np.array(caches), table=table,
+                seq_k=seq_k, seq_v=seq_v, C=C, H=H, Hk=Hk, D=D)
+
+
+def _brute_force(case):
+    """Scalar loops over logical sequences; the positional term takes the embedding of the
+    distance (cache + i) - j straight from the projected sinusoid, with no table at all."""
+    q, u, w = case["q"], case["u"], case["w"]
+    C, H, Hk, D = case["C"], case["H"], case["Hk"], case["D"]
+    out = np.zeros(q.shape)
+    for b, c in enumerate(case["cs"]):
+        c = int(c)
+        T = c + C
+        emb = {}
+        for i in range(C):
+            for j in range(T):
+                dist = (c + i) - j
+                if dist not in emb:
+                    emb[dist] = embed_distances([dist], case["proj"], H, D).numpy()[0]
+        for h in range(H):
+            g = (h * Hk) // H
+            for i in range(C):
+                scores = []
+                for j in range(T):
+                    a = math.fsum((q[b, i, h, d] + u[h, d]) * case["seq_k"][b][j, g, d] for d in range(D))
+                    p = math.fsum((q[b, i, h, d] + w[h, d]) * emb[(c + i) - j][h, d] for d in range(D))
+                    scores.append((a + p) / math.sqrt(D))
+                mx = max(scores)
+                ex = [math.exp(s - mx) for s in scores]
+                z = math.fsum(ex)
+                for d in range(D):
+                    out[b, i, h, d] = math.fsum(ex[j] / z * case["seq_v"][b][j, g, d] for j in range(T))
+    return out
+
+
+def _oracle(case, **kw):
+    return oracle.chunk_relpos_attn(case["q"], case["kp"], case["vp"], case["bt"], case["cs"],
+                                    case["table"], case["u"], case["w"], **kw)
+
+
+@pytest.mark.parametrize("caches,Hk", [([0, 4, 9], 2), ([3, 12], 1)])
+def test_oracle_matches_brute_force(caches, Hk):
+    case = _random_streaming_case(11, caches, Hk=Hk)
+    err = np.abs(_oracle(case) - _brute_force(case)).max()
+    assert err < 1e-12, err
+
+
+def test_reduces_to_textbook_attention_when_no_position_term():
+    """u = v = 0 and p = 0: plain softmax(Q K^T / sqrt(D)) V, from torch's float64 CPU routine."""
+    case = _random_streaming_case(5, [0, 7, 13], Hk=2, zero_pos=True)
+    out = _oracle(case)
+    for b, c in enumerate(case["cs"]):
+        qq = torch.from_numpy(case["q"][b]).permute(1, 0, 2)                    # [H, C, D]
+        kk = torch.from_numpy(case["seq_k"][b]).permute(1, 0, 2).contiguous()  # [Hk, T, D]
+        vv = torch.from_numpy(case["seq_v"][b]).permute(1, 0, 2).contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)
+        err = np.abs(out[b] - ref.permute(1, 0, 2).numpy()).max()
+        assert err < 1e-12, err
+
+
+def test_probabilities_are_a_distribution():
+    case = _random_streaming_case(6, [2, 10])
+    _, probs = _oracle(case, return_probs=True)
+    for b, p in enumerate(probs):
+        assert p.shape[-1] == case["cs"][b] + case["C"]
+        assert (p >= 0).all()
+        assert np.abs(p.sum(-1) - 1).max() < 1e-12
+
+
+@pytest.mark.parametrize("dstar", [-3, -1, 0, 2, 5, 9, 40])
+def test_one_hot_distance_closed_form(dstar):
+    """Only distance d* carries an embedding (alpha on dim 0); q = e_0, u = v = k = 0. Then
+    query i boosts exactly key j* = cache + i - d* by alpha / sqrt(D), which fixes the
+    probabilities in closed form and pins the sign and origin of the distance."""
+    C, H, D, S = 4, 1, 8, 4
+    caches = [6, 0]
+    alpha = 3.0
+    rng = np.random.default_rng(0)
+    B = len(caches)
+    seq_k = [np.zeros((c + C, 1, D)) for c in caches]
+    seq_v = [rng.standard_normal((c + C, 1, D)) for c in caches]
+    kp, vp, bt = _paged_from_sequences(seq_k, seq_v, caches, C, S, rng)
+    center = max(caches) + C - 1
+    table = np.zeros((2 * center + 1, H, D))
+    for r in range(table.shape[0]):
+        if center - r == dstar:                      # row r holds distance center - r
+            table[r, 0, 0] = alpha
+    q = np.zeros((B, C, H, D))
+    q[..., 0] = 1.0
+    zero = np.zeros((H, D))
+    out, probs = oracle.chunk_relpos_attn(q, kp, vp, bt, np.array(caches), table, zero, zero,
+                                          return_probs=True)
+    a = alpha / math.sqrt(D)
+    for b, c in enumerate(caches):
+        T = c + C
+        for i in range(C):
+            jstar = c + i - dstar
+            expect = np.full(T, 1.0 / T)
+            if 0 <= jstar < T:
+                expect = np.full(T, 1.0 / (math.exp(a) + T - 1))
+                expect[jstar] = math.exp(a) / (math.exp(a) + T - 1)
+            assert np.abs(probs[b][0, i] - expect).max() < 1e-14
+            np.testing.assert_allclose(out[b, i, 0], expect @ seq_v[b][:, 0], atol=1e-13)
+
+
+def test_block_permutation_invariance():
+    """Relabelling physical blocks (pool'[pi(n)] = pool[n], table' = pi(table)) changes nothing."""
+    case = _random_streaming_case(8, [5, 0, 11])
+    base = _oracle(case)
+    rng = np.random.default_rng(3)
+    N = case["kp"].shape[0]
+    pi = rng.permutation(N)
+    kp2 = np.empty_like(case["kp"])
+    vp2 = np.empty_like(case["vp"])
+    kp2[pi] = case["kp"]
+    vp2[pi] = case["vp"]
+    bt2 = np.where(case["bt"] >= 0, pi[np.maximum(case["bt"], 0)], -1)
+    out2 = oracle.chunk_relpos_attn(case["q"], kp2, vp2, bt2, case["cs"], case["table"],
+                                    case["u"], case["w"])
+    np.testing.assert_array_equal(base, out2)
+
+
+def _dense_blockcausal(q_all, k_all, v_all, u, w, proj, C):
+    """Whole-utterance attention with a chunk mask (key chunk <= query chunk) and the positional
+    bias (q_t + v) . emb(t - j) / sqrt(D), through torch's float64 scaled_dot_product_attention."""
+    n, H, D = q_all.shape
+    Hk = k_all.shape[1]
+    t = np.arange(n)
+    dist = t[:, None] - t[None, :]
+    emb = embed_distances(dist.reshape(-1), proj, H, D).numpy().reshape(n, n, H, D)
+    out = np.zeros((n, H, D))
+    for h in range(H):
+        g = h * Hk // H
+        bias = np.einsum("td,tjd->tj", q_all[:, h] + w[h], emb[:, :, h]) / math.sqrt(D)
+        bias = np.where((t[None, :] // C) <= (t[:, None] // C), bias, -np.inf)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q_all[:, h] + u[h])[None], torch.from_numpy(k_all[:, g])[None],
+            torch.from_numpy(v_all[:, g])[None], attn_mask=torch.from_numpy(bias)[None])
+        out[:, h] = ref[0].numpy()
+    return out
+
+
+def _streaming_vs_dense(seed, steps=5, C=4, H=2, Hk=1, D=8, S=8, margin=0):
+    """Run the chunk oracle step by step from an empty cache, each step with its own table of
+    2 (cache + C) - 1 rows, and compare with the dense block-causal reference."""
+    rng = np.random.default_rng(seed)
+    n = steps * C
+    q_all = rng.standard_normal((n, H, D))
+    k_all = rng.standard_normal((n, Hk, D))
+    v_all = rng.standard_normal((n, Hk, D))
+    u = 0.5 * rng.standard_normal((H, D))
+    w = 0.5 * rng.standard_normal((H, D))
+    proj = relpos_projection(H * D, torch.Generator().manual_seed(seed))
+    pages = (n + S - 1) // S
+    bt = rng.permutation(pages + 2)[None, :pages]
+    kp = np.full((pages + 2, Hk, S, D), np.nan)
+    vp = np.full((pages + 2, Hk, D, S), np.nan)
+    outs = []
+    for step in range(steps):
+        c = step * C
+        sl = slice(c, c + C)
+        kp, vp = oracle.paged_kv_append(kp, vp, k_all[None, sl], v_all[None, sl], bt, np.array([c]))
+        table = descending_table(c + C - 1 + margin, proj, H, D).numpy()
+        outs.append(oracle.chunk_relpos_attn(q_all[None, sl], kp, vp, bt, np.array([c]), table, u, w)[0])
+    stream = np.concatenate(outs)
+    dense = _dense_blockcausal(q_all, k_all, v_all, u, w, proj, C)
+    return np.abs(stream - dense).max()
+
+
+def test_streaming_steps_equal_dense_block_causal_attention():
+    err = _streaming_vs_dense(21)
+    assert err < 1e-12, err
+
+
+def test_shared_and_per_row_tables_agree():
+    """With tables that depend only on distance, one shared table (centred for the longest row)
+    and per-row tables (each centred at its own T_b - 1) give identical results; for a uniform
+    cache they are the same table."""
+    for caches in ([8, 8, 8], [0, 5, 12]):
+        case = _random_streaming_case(9, caches)
+        shared = _oracle(case)
+        C = case["C"]
+        P = case["table"].shape[0]
+        per_row = np.zeros((len(caches), P, case["H"], case["D"]))
+        center = (P - 1) // 2
+        for b, c in enumerate(caches):
+            T = c + C
+            per_row[b, :2 * T - 1] = descending_table(T - 1, case["proj"], case["H"], case["D"]).numpy()
+            per_row[b, 2 * T - 1:] = np.nan                     # outside row b's table: never read
+            if c == max(caches):
+                np.testing.assert_array_equal(per_row[b, :2 * T - 1], case["table"][center - T + 1:center + T])
+        out = oracle.chunk_relpos_attn(case["q"], case["kp"], case["vp"], case["bt"], case["cs"],
+                                       per_row, case["u"], case["w"], per_row_pos=True)
+        assert np.abs(out - shared).max() < 1e-13
+
+
+def test_row_locality():
+    """A stream's output depends only on its own inputs: other rows may change or vanish."""
+    case = _random_streaming_case(12, [4, 9, 2])
+    full = _oracle(case)
+    sub = dict(case)
+    sub["q"] = case["q"][1:2]
+    sub["bt"] = case["bt"][1:2]
+    sub["cs"] = case["cs"][1:2]
+    np.testing.assert_array_equal(_oracle(sub)[0], full[1])
+
+
+def test_varlen_segments_equal_chunk_case_and_dense():
+    """A packed segment of length L is the chunk case with cache 0 and C = L, and equals dense
+    full-context attention with bias (q_t + v) . emb(t - j); segments never mix."""
+    lengths = [5, 1, 9, 3]
+    H, D = 2, 8
+    co = make_varlen_cohort(lengths, H, D, dtype=F64, seed=4)
+    q, k, v = np64(co.q), np64(co.k), np64(co.v)
+    u, w = np64(co.pos_bias_u), np64(co.pos_bias_v)
+    pos = np64(co.pos)
+    out = oracle.varlen_relpos_attn(q, k, v, co.cu_seqlens.numpy(), pos, u, w)
+    cu = co.cu_seqlens.numpy()
+    for s, n in enumerate(lengths):
+        lo, hi = cu[s], cu[s + 1]
+        dense = _dense_blockcausal(q[lo:hi], k[lo:hi], v[lo:hi], u, w, co.meta["proj"], C=n)
+        assert np.abs(out[lo:hi] - dense).max() < 1e-12
+        # chunk entry, cache 0, C = L, one page holding the whole segment
+        kp = k[lo:hi].transpose(1, 0, 2)[None]                 # [1, Hk, L, D]
+        vp = v[lo:hi].transpose(1, 2, 0)[None]                 # [1, Hk, D, L]
+        table = pos[2 * lo - s: 2 * lo - s + 2 * n - 1]
+        chunk = oracle.chunk_relpos_attn(q[None, lo:hi], kp, vp, np.array([[0]]), np.array([0]),
+                                         table, u, w)[0]
+        assert np.abs(chunk - out[lo:hi]).max() < 1e-13
+
+
+def test_workload_geometry_matches_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "workload_geometry.json")))
+    co = make_config(0)
+    assert co.pos.shape[0] == g["tiny_fp32"]["table_rows"]
+    assert co.k_pool.shape[0] == 32
+    for fw in g["fixed_window"]:
+        pages = (fw["window"] + fw["chunk"] + 16 - 1) // 16
+        assert pages == fw["pages_per_stream"]
+    assert CONFIGS[1]["block_size"] == g["engine_defaults"]["block_size_frames"]
+    assert CONFIGS[1]["max_blocks_per_seq"] == g["engine_defaults"]["max_blocks_per_seq"]
+    co1 = make_chunk_cohort(2, 4, 64, 16, 16, [256, 256], dtype=torch.bfloat16)
+    assert co1.meta["pages"] == [17, 17]
+
+
+# --------------------------------------------------------------------------------------------
+# Sensitivity: plant slips in the oracle and check that the pins above notice them.
+# --------------------------------------------------------------------------------------------
+
+def _pin_errors(margin=3):
+    # tables carry a few spare rows, so a slipped row index stays inside the table and must be
+    # caught by value, not by the oracle's own bounds check
+    case = _random_streaming_case(11, [0, 4, 9], margin=margin)
+    brute = np.abs(_oracle(case) - _brute_force(case)).max()
+    dense = _streaming_vs_dense(21, steps=3, margin=margin)
+    return brute, dense
+
+
+def test_pins_hold_with_spare_table_rows():
+    brute, dense = _pin_errors()
+    assert brute < 1e-12 and dense < 1e-12
+
+
+@pytest.mark.parametrize("slip", ["sign", "centre", "no_u", "swap_uv", "no_scale_pos"])
+def test_planted_mistakes_are_caught(monkeypatch, slip):
+    if slip == "sign":
+        monkeypatch.setattr(orc, "table_row", lambda center, cache, i, j: center + (cache + i - j))
+    elif slip == "centre":
+        monkeypatch.setattr(orc, "table_row", lambda center, cache, i, j: center - (cache + i - j) - 1)
+    else:
+        real = orc._attend
+
+        def slipped(q, k, v, pos_rows, u, w, center, cache, scale):
+            if slip == "no_u":
+                u = u * 0
+            elif slip == "swap_uv":
+                u, w = w, u
+            elif slip == "no_scale_pos":
+                pos_rows = pos_rows * math.sqrt(q.shape[-1])
+            return real(q, k, v, pos_rows, u, w, center, cache, scale)
+        monkeypatch.setattr(orc, "_attend", slipped)
+    # the mirrored distance needs a table long enough on both sides to stay in range
+    brute, dense = _pin_errors(margin=30 if slip == "sign" else 3)
+    assert max(brute, dense) > 1e-6, (brute, dense)
