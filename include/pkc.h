@@ -1,0 +1,170 @@
+/*
+ * pkc.h - paged chunk attention with a Transformer-XL relative-position term, for AMD gfx950.
+ *
+ * C ABI of libpkc.so. Every entry point takes plain device pointers and sizes, validates them on
+ * the host before launching anything, enqueues its kernels on the caller's HIP stream and returns
+ * without synchronising. The library allocates no device memory and keeps no state between calls;
+ * all buffers belong to the caller. Calls on different streams are independent.
+ *
+ * Sources (OASR documentation pages, cited by title and section):
+ *   [ENG 4.3]  "ASR Engine", section 4.3 "Batched paged forward": a cohort of streams shares one
+ *              block pool; each stream has a row of block_tables (B, blocks_per_seq) and an entry
+ *              of cache_seqlens (B,); the chunk's K/V land in the stream's pages; cache_seqlens is
+ *              advanced (commit_chunk_paged) only after the forward.
+ *   [ENG 6]    "ASR Engine", section 6 "Paged KV cache" options: block_size_frames,
+ *              max_blocks_per_seq; section 8: pool exhaustion is an error, not silent.
+ *   [SCH 4.3]  "Scheduler", section 4.3 "Heterogeneous-offset batching": attention over the
+ *              paged pool with per-stream lengths from cache_seqlens and the relative-position
+ *              bias matrix_bd / sqrt(d_k) added to the scores.
+ *   [MOD fix]  "Model Layer", "Three optional encoder declarations", fixed_attention_window: a
+ *              Transformer-XL table's distances are cache + i - j; a uniform cache_seqlens lets
+ *              one shared table serve the cohort, otherwise each row needs its own table.
+ *   [MOD surf] "Model Layer", "The engine-facing surface": forward_chunk_paged (streaming chunk
+ *              entry), forward_offline_packed (gapless varlen offline forward), n_kv_head and
+ *              head_dim (paged-streaming geometry).
+ *
+ * Score of chunk query i (absolute position cache + i) against key j (0 <= j < cache + C):
+ *     s[i][j] = ((q_i + u) . k_j + (q_i + v) . p[cache + i - j]) * softmax_scale
+ * followed by a softmax over j and a weighted sum of v_j. No mask inside the window: every chunk
+ * query sees every cached frame and every frame of its own chunk.
+ *
+ * Layouts (row-major, innermost last). B = batch, C = chunk_size, H = n_head, Hk = n_kv_head,
+ * D = head_dim, S = block_size, N = num_blocks, M = max_blocks_per_seq:
+ *   q, out          [B, C, H, D]
+ *   k_new, v_new    [B, C, Hk, D]
+ *   k_pool          [N, Hk, S, D]            one pool per layer
+ *   v_pool          [N, Hk, D, S]            V is stored transposed inside each page
+ *   block_tables    int32 [B, M]             logical frame t of stream b is in block
+ *                                            block_tables[b][t / S], slot t % S
+ *   cache_seqlens   int32 [B]                frames cached before this chunk
+ *   pos_bias_u, _v  [H, D]
+ *   pos (shared)    [pos_len, H, D]          row r holds distance (pos_len - 1) / 2 - r
+ *   pos (per row)   [B, pos_len, H, D]       stream b's table: rows [0, 2 T_b - 1), centred at
+ *                                            T_b - 1 (T_b = cache_seqlens[b] + C); rows past
+ *                                            that are never read
+ * Query head h reads kv head h / (H / Hk). Element type: fp32 or bf16 for every floating-point
+ * buffer of a call; accumulation is fp32 either way; bf16 outputs are rounded to nearest even.
+ *
+ * Device-side preconditions (not checkable on the host without a synchronisation):
+ *   0 <= cache_seqlens[b] <= max_cache_seqlen; block_tables[b][t / S] in [0, N) for every
+ *   t < cache_seqlens[b] + C; no two streams own the same page. Kernels clamp cache lengths and
+ *   block IDs into range, so a violation gives unspecified values but never an out-of-bounds access.
+ *   Table entries past a stream's last page are never read.
+ */
+#ifndef PKC_H
+#define PKC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkc_status {
+  PKC_OK = 0,
+  PKC_ERR_NULL = 1,        /* a required pointer is NULL                                    */
+  PKC_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree                      */
+  PKC_ERR_DTYPE = 3,       /* unknown element type                                          */
+  PKC_ERR_UNSUPPORTED = 4, /* valid, but not built (e.g. head_dim != 64 for attention)      */
+  PKC_ERR_CAPACITY = 5,    /* max_cache_seqlen + chunk_size > max_blocks_per_seq * block_size */
+  PKC_ERR_HIP = 6,         /* the HIP runtime reported an error at launch                   */
+  PKC_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned                       */
+} pkc_status;
+
+typedef enum pkc_dtype { PKC_F32 = 0, PKC_BF16 = 1 } pkc_dtype;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pkc_version(void);
+
+/* Static description of a status code. */
+const char* pkc_status_string(int status);
+
+/*
+ * paged_kv_append - write each stream's new chunk K/V into its pages [ENG 4.3].
+ *
+ * For b < batch and t < chunk_size, with L = cache_seqlens[b] + t:
+ *     k_pool[block_tables[b][L / S]][g][L % S][:] = k_new[b][t][g][:]
+ *     v_pool[block_tables[b][L / S]][g][:][L % S] = v_new[b][t][g][:]
+ * for every kv head g. No other pool element is touched; the copy is bit-exact. The caller then
+ * runs the attention and afterwards advances cache_seqlens by chunk_size itself.
+ * Errors: NULL pointers -> PKC_ERR_NULL; non-positive sizes or head_dim not a multiple of 8 ->
+ * PKC_ERR_SHAPE; max_cache_seqlen + chunk_size > max_blocks_per_seq * block_size ->
+ * PKC_ERR_CAPACITY (the analogue of the pool/table ceiling errors of [ENG 6]).
+ */
+pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new, void* k_pool,
+                           void* v_pool, const int32_t* block_tables, const int32_t* cache_seqlens,
+                           int32_t batch, int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_cache_seqlen, hipStream_t stream);
+
+/*
+ * chunk_paged_relpos_attn - chunk attention over cached frames plus the chunk [SCH 4.3],
+ * [MOD fix], as called once per layer inside forward_chunk_paged [MOD surf].
+ *
+ * The chunk's K/V must already be in the pools (paged_kv_append first). For every stream b,
+ * head h and chunk query i < chunk_size, attends over the T_b = cache_seqlens[b] + chunk_size
+ * frames of stream b read through block_tables, and writes out[b][i][h][:].
+ * pos_per_row = 0: pos is one shared table of pos_len rows (pos_len odd and
+ *   (pos_len - 1) / 2 >= max_cache_seqlen + chunk_size - 1), indexed by distance around its centre.
+ * pos_per_row = 1: pos holds one table per stream, pos_len rows apart
+ *   (pos_len >= 2 * (max_cache_seqlen + chunk_size) - 1).
+ * softmax_scale <= 0 selects 1 / sqrt(head_dim).
+ * Errors: as paged_kv_append; n_head % n_kv_head != 0 or a table too short -> PKC_ERR_SHAPE;
+ * head_dim != 64 or block_size % 8 != 0 -> PKC_ERR_UNSUPPORTED.
+ */
+pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_tables,
+                                   const int32_t* cache_seqlens, const void* pos, int32_t pos_len,
+                                   int32_t pos_per_row, const void* pos_bias_u,
+                                   const void* pos_bias_v, void* out, int32_t batch,
+                                   int32_t chunk_size, int32_t n_head, int32_t n_kv_head,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_cache_seqlen,
+                                   float softmax_scale, hipStream_t stream);
+
+/*
+ * paged_kv_append_relpos_attn - one layer's step of the hot path in a single launch: the append
+ * of paged_kv_append followed by the attention of chunk_paged_relpos_attn [ENG 4.3], [SCH 4.3].
+ * The chunk's keys and values are taken from k_new / v_new for the attention and written into
+ * the pools in the same kernel; the results equal the two calls in sequence. Arguments and errors
+ * are those of the two calls (k_pool / v_pool are written).
+ */
+pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const void* k_new,
+                                       const void* v_new, void* k_pool, void* v_pool,
+                                       const int32_t* block_tables, const int32_t* cache_seqlens,
+                                       const void* pos, int32_t pos_len, int32_t pos_per_row,
+                                       const void* pos_bias_u, const void* pos_bias_v, void* out,
+                                       int32_t batch, int32_t chunk_size, int32_t n_head,
+                                       int32_t n_kv_head, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_cache_seqlen, float softmax_scale,
+                                       hipStream_t stream);
+
+/*
+ * varlen_packed_relpos_attn - full-context attention inside each utterance of a packed, gapless
+ * row [MOD surf] (forward_offline_packed), with one relative-position table per utterance.
+ *
+ * q, out: [total_frames, H, D]; k, v: [total_frames, Hk, D]; cu_seqlens: int32 [num_seqs + 1],
+ * cu_seqlens[0] = 0, nondecreasing, cu_seqlens[num_seqs] = total_frames; every segment length
+ * <= max_seqlen. Utterance s (frames [cu_seqlens[s], cu_seqlens[s+1]), length L) has a table of
+ * 2 L - 1 rows centred at L - 1 starting at row 2 cu_seqlens[s] of pos [2 total_frames, H, D]
+ * (2 L rows are reserved per utterance, the last unused). Frames attend only within their own
+ * utterance; empty utterances are allowed. The kernel clamps cu_seqlens into [0, total_frames],
+ * so malformed offsets give unspecified values but no out-of-bounds access; frames of an
+ * utterance longer than max_seqlen past max_seqlen are not written.
+ * Errors: as above; head_dim != 64 -> PKC_ERR_UNSUPPORTED.
+ */
+pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens, int32_t num_seqs,
+                                     int32_t total_frames, int32_t max_seqlen, const void* pos,
+                                     const void* pos_bias_u, const void* pos_bias_v, void* out,
+                                     int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                                     float softmax_scale, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKC_H */

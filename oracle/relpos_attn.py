@@ -88,43 +88,48 @@ def table_row(center, cache, i, j):
     return center - (cache + i - j)
 
 
-def _attend(q, k, v, pos_rows, u, w, center, cache, scale):
+def _attend(q, k, v, pos_rows, u, w, center, cache, scale, query_rows=None):
     """Attention of C queries at absolute positions cache + i over T = cache + C keys (one stream).
 
     q: [C, H, D]; k, v: [T, Hk, D]; pos_rows: [P_b, H, D] table of this stream. Returns the output
-    [C, H, D] and the probabilities [H, C, T].
+    and the probabilities for the queries in ``query_rows`` (default: all C), as
+    [len(query_rows), H, D] and [H, len(query_rows), T].
     """
     n_q, n_head, _ = q.shape
     n_k, n_kv_head = k.shape[0], k.shape[1]
-    i = np.arange(n_q)[:, None]
-    j = np.arange(n_k)[None, :]
-    rows = table_row(center, cache, i, j)  # [C, T]
-    if rows.min() < 0 or rows.max() >= pos_rows.shape[0]:
-        raise ValueError("relative-position table too short for distances cache + i - j")
-    out = np.empty((n_q, n_head, v.shape[2]))
-    probs = np.empty((n_head, n_q, n_k))
-    for h in range(n_head):
-        g = h * n_kv_head // n_head
-        content = (q[:, h, :] + u[h]) @ k[:, g, :].T                       # (q + u) . k_j
-        emb = pos_rows[rows, h, :]                                            # p[cache + i - j]
-        position = np.einsum("id,ijd->ij", q[:, h, :] + w[h], emb)           # (q + v) . p
-        s = (content + position) * scale
-        s = s - s.max(axis=1, keepdims=True)
-        a = np.exp(s)
-        a = a / a.sum(axis=1, keepdims=True)
-        probs[h] = a
-        out[:, h, :] = a @ v[:, g, :]
+    if query_rows is None:
+        query_rows = np.arange(n_q)
+    query_rows = np.asarray(query_rows)
+    j = np.arange(n_k)
+    out = np.empty((len(query_rows), n_head, v.shape[2]))
+    probs = np.empty((n_head, len(query_rows), n_k))
+    for x, i in enumerate(query_rows):
+        rows = table_row(center, cache, int(i), j)                            # [T]
+        if rows.min() < 0 or rows.max() >= pos_rows.shape[0]:
+            raise ValueError("relative-position table too short for distances cache + i - j")
+        emb = pos_rows[rows]                                                  # p[cache + i - j]: [T, H, D]
+        for h in range(n_head):
+            g = h * n_kv_head // n_head
+            content = k[:, g, :] @ (q[i, h, :] + u[h])                       # (q + u) . k_j
+            position = emb[:, h, :] @ (q[i, h, :] + w[h])                    # (q + v) . p
+            s = (content + position) * scale
+            s = s - s.max()
+            a = np.exp(s)
+            a = a / a.sum()
+            probs[h, x] = a
+            out[x, h, :] = a @ v[:, g, :]
     return out, probs
 
 
 def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u, pos_bias_v,
-                      per_row_pos=False, scale=None, return_probs=False):
+                      per_row_pos=False, scale=None, return_probs=False, streams=None):
     """Chunk attention of every stream over its cached frames plus its own chunk.
 
     q: [B, C, H, D]. The chunk's K/V must already be in the pools (append first, then attend).
     pos: one shared table [P, H, D] centred at (P - 1) / 2, or per-row tables [B, P_max, H, D],
     row b centred at T_b - 1 with 2 T_b - 1 meaningful rows. pos_bias_u, pos_bias_v: [H, D].
     Returns out [B, C, H, D] in float64 (and the per-stream probabilities when asked).
+    ``streams`` (default: all) restricts the work to a sample of streams; other rows are NaN.
     """
     q = np.asarray(q, dtype=np.float64)
     u = np.asarray(pos_bias_u, dtype=np.float64)
@@ -132,9 +137,9 @@ def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_b
     n_streams, chunk, _, head_dim = q.shape
     if scale is None:
         scale = 1.0 / np.sqrt(head_dim)
-    out = np.empty(q.shape)
+    out = np.full(q.shape, np.nan)
     all_probs = []
-    for b in range(n_streams):
+    for b in (range(n_streams) if streams is None else streams):
         cache = int(cache_seqlens[b])
         n_k = cache + chunk
         k, v = gather_stream(k_pool, v_pool, block_tables[b], n_k)
@@ -156,13 +161,17 @@ def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_b
 
 
 def varlen_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, scale=None,
-                       return_probs=False):
+                       return_probs=False, segments=None, query_rows=None):
     """Full-context attention inside each packed segment ("Model Layer", forward_offline_packed).
 
     q: [total, H, D], k, v: [total, Hk, D], packed gapless; segment s is frames
     [cu_seqlens[s], cu_seqlens[s+1]). Its table has 2 L_s - 1 rows centred at L_s - 1 and starts at
-    row 2 cu_seqlens[s] - s of pos [2 total - S, H, D]. Each segment is the chunk case with
+    row 2 cu_seqlens[s] of pos [2 total, H, D] (each utterance owns 2 L_s rows, the last one
+    unused, so empty utterances keep every offset consistent). Each segment is the chunk case with
     cache = 0 and C = L_s. Returns out [total, H, D] in float64.
+
+    ``segments`` (default: all) and ``query_rows`` (a callable L -> rows of the segment, default
+    all) restrict the work to a sample; rows not computed are NaN in ``out``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -172,18 +181,19 @@ def varlen_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, scale=N
     head_dim = q.shape[2]
     if scale is None:
         scale = 1.0 / np.sqrt(head_dim)
-    out = np.empty(q.shape)
+    out = np.full(q.shape, np.nan)
     all_probs = []
     n_seg = len(cu_seqlens) - 1
-    for s in range(n_seg):
+    for s in (range(n_seg) if segments is None else segments):
         lo, hi = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
         n = hi - lo
         if n == 0:
             all_probs.append(np.zeros((q.shape[1], 0, 0)))
             continue
-        row0 = 2 * lo - s
+        row0 = 2 * lo
         rows = np.asarray(pos[row0: row0 + 2 * n - 1], dtype=np.float64)
-        out[lo:hi], probs = _attend(q[lo:hi], k[lo:hi], v[lo:hi], rows, u, w, n - 1, 0, scale)
+        qr = np.arange(n) if query_rows is None else np.asarray(query_rows(n))
+        out[lo + qr], probs = _attend(q[lo:hi], k[lo:hi], v[lo:hi], rows, u, w, n - 1, 0, scale, qr)
         all_probs.append(probs)
     if return_probs:
         return out, all_probs

@@ -1,0 +1,171 @@
+"""Python binding of libpkc.so (paged chunk attention with a Transformer-XL relative-position term).
+
+Argument marshalling only: every function here turns torch tensors into device pointers and
+sizes, calls the C ABI declared in include/pkc.h on torch's current HIP stream, and raises
+PkcError on a non-zero status. All computation happens in the HIP kernels. There is no CPU
+fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkc.so")
+
+PKC_F32, PKC_BF16 = 0, 1
+_DTYPES = {torch.float32: PKC_F32, torch.bfloat16: PKC_BF16}
+
+_i32 = ctypes.c_int32
+_ptr = ctypes.c_void_p
+_f32 = ctypes.c_float
+
+# Exported entry points and their argument types (mirrors include/pkc.h).
+SIGNATURES = {
+    "pkc_version": ([], ctypes.c_int),
+    "pkc_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "paged_kv_append": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr] + [_i32] * 8 + [_ptr],
+                        ctypes.c_int),
+    "chunk_paged_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _ptr,
+                                 _ptr, _ptr] + [_i32] * 9 + [_f32, _ptr], ctypes.c_int),
+    "paged_kv_append_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                     _i32, _i32, _ptr, _ptr, _ptr] + [_i32] * 9 + [_f32, _ptr],
+                                    ctypes.c_int),
+    "varlen_packed_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _ptr,
+                                   _ptr, _ptr, _ptr, _i32, _i32, _i32, _f32, _ptr], ctypes.c_int),
+}
+
+
+class PkcError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m paged_kv_chunk_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def version():
+    return lib().pkc_version()
+
+
+def status_string(status):
+    return lib().pkc_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != 0:
+        raise PkcError(status, what)
+
+
+def _dtype(*ts):
+    dt = ts[0].dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for t in ts:
+        if t.dtype != dt:
+            raise TypeError("all floating-point tensors of a call must share one dtype")
+    return _DTYPES[dt]
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    return t.data_ptr()
+
+
+def _table(t):
+    if t.dtype != torch.int32:
+        raise TypeError("block tables, cache lengths and offsets are int32")
+    return _p(t)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, max_cache_seqlen,
+                    stream=None):
+    """Write k_new / v_new [B, C, Hk, D] into k_pool [N, Hk, S, D] / v_pool [N, Hk, D, S]."""
+    B, C, Hk, D = k_new.shape
+    N, _, S, _ = k_pool.shape
+    st = lib().paged_kv_append(_dtype(k_new, v_new, k_pool, v_pool), _p(k_new), _p(v_new),
+                               _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
+                               B, C, Hk, D, S, N, block_tables.shape[1], int(max_cache_seqlen),
+                               _stream(stream))
+    _check(st, "paged_kv_append")
+
+
+def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u,
+                            pos_bias_v, max_cache_seqlen, per_row_pos=False, out=None,
+                            softmax_scale=0.0, stream=None):
+    """Chunk attention; q [B, C, H, D]; pos shared [P, H, D] or per-row [B, P, H, D]."""
+    B, C, H, D = q.shape
+    N, Hk, S, _ = k_pool.shape
+    if out is None:
+        out = torch.empty_like(q)
+    P = pos.shape[1] if per_row_pos else pos.shape[0]
+    st = lib().chunk_paged_relpos_attn(
+        _dtype(q, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out), _p(q), _p(k_pool), _p(v_pool),
+        _table(block_tables), _table(cache_seqlens), _p(pos), P, int(bool(per_row_pos)),
+        _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk, D, S, N, block_tables.shape[1],
+        int(max_cache_seqlen), float(softmax_scale), _stream(stream))
+    _check(st, "chunk_paged_relpos_attn")
+    return out
+
+
+def paged_kv_append_relpos_attn(q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, pos,
+                                pos_bias_u, pos_bias_v, max_cache_seqlen, per_row_pos=False,
+                                out=None, softmax_scale=0.0, stream=None):
+    """Append and attention of one layer in one launch (pools are written)."""
+    B, C, H, D = q.shape
+    N, Hk, S, _ = k_pool.shape
+    if out is None:
+        out = torch.empty_like(q)
+    P = pos.shape[1] if per_row_pos else pos.shape[0]
+    st = lib().paged_kv_append_relpos_attn(
+        _dtype(q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out), _p(q),
+        _p(k_new), _p(v_new), _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
+        _p(pos), P, int(bool(per_row_pos)), _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk,
+        D, S, N, block_tables.shape[1], int(max_cache_seqlen), float(softmax_scale),
+        _stream(stream))
+    _check(st, "paged_kv_append_relpos_attn")
+    return out
+
+
+def varlen_packed_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, max_seqlen,
+                              out=None, softmax_scale=0.0, stream=None):
+    """Attention inside each packed utterance; q [total, H, D], k/v [total, Hk, D]."""
+    total, H, D = q.shape
+    Hk = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib().varlen_packed_relpos_attn(
+        _dtype(q, k, v, pos, pos_bias_u, pos_bias_v, out), _p(q), _p(k), _p(v), _table(cu_seqlens),
+        cu_seqlens.shape[0] - 1, total, int(max_seqlen), _p(pos), _p(pos_bias_u), _p(pos_bias_v),
+        _p(out), H, Hk, D, float(softmax_scale), _stream(stream))
+    _check(st, "varlen_packed_relpos_attn")
+    return out

@@ -1,0 +1,202 @@
+// C ABI of libpkc.so: host-side validation, then one launch on the caller's stream.
+// Validation never touches the GPU, so every error path returns before any HIP call.
+#include <stdint.h>
+
+#include "pkc.h"
+#include "pkc_launch.h"
+
+using namespace pkc;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pkc_status check_dtype(pkc_dtype dtype) {
+  return (dtype == PKC_F32 || dtype == PKC_BF16) ? PKC_OK : PKC_ERR_DTYPE;
+}
+
+// Checks shared by the append and the attention: pool geometry and capacity.
+pkc_status check_pool(int32_t batch, int32_t chunk, int32_t n_kv_head, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_blocks,
+                      int32_t max_cache) {
+  if (batch <= 0 || chunk <= 0 || n_kv_head <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks <= 0 || max_cache < 0)
+    return PKC_ERR_SHAPE;
+  if (head_dim % 8 != 0) return PKC_ERR_SHAPE;
+  if ((int64_t)max_cache + chunk > (int64_t)max_blocks * block_size) return PKC_ERR_CAPACITY;
+  // every index below fits in int32 arithmetic inside the kernels except the flat offsets,
+  // which the kernels form in size_t
+  if ((int64_t)max_cache + chunk >= (int64_t)1 << 30) return PKC_ERR_SHAPE;
+  return PKC_OK;
+}
+
+pkc_status check_attn(int32_t chunk, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                      int32_t block_size, int32_t max_cache, int32_t pos_len, int32_t pos_per_row) {
+  if (n_head <= 0 || n_head % n_kv_head != 0) return PKC_ERR_SHAPE;
+  if (pos_per_row != 0 && pos_per_row != 1) return PKC_ERR_SHAPE;
+  const int64_t longest = (int64_t)max_cache + chunk;
+  if (pos_per_row) {
+    if (pos_len < 2 * longest - 1) return PKC_ERR_SHAPE;
+  } else {
+    if (pos_len <= 0 || pos_len % 2 != 1) return PKC_ERR_SHAPE;
+    if ((pos_len - 1) / 2 < longest - 1) return PKC_ERR_SHAPE;
+  }
+  if (head_dim != 64) return PKC_ERR_UNSUPPORTED;
+  if (block_size % 8 != 0) return PKC_ERR_UNSUPPORTED;
+  if ((longest + block_size - 1) / block_size > kMaxStagedBlocks) return PKC_ERR_UNSUPPORTED;
+  return PKC_OK;
+}
+
+pkc_status from_hip(hipError_t e) { return e == hipSuccess ? PKC_OK : PKC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int pkc_version(void) { return kVersion; }
+
+const char* pkc_status_string(int status) {
+  switch (status) {
+    case PKC_OK: return "ok";
+    case PKC_ERR_NULL: return "a required pointer is NULL";
+    case PKC_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case PKC_ERR_DTYPE: return "unknown element type";
+    case PKC_ERR_UNSUPPORTED: return "configuration not supported by the built kernels";
+    case PKC_ERR_CAPACITY: return "max_cache_seqlen + chunk_size exceeds max_blocks_per_seq * block_size";
+    case PKC_ERR_HIP: return "HIP runtime error at launch";
+    case PKC_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new, void* k_pool,
+                           void* v_pool, const int32_t* block_tables, const int32_t* cache_seqlens,
+                           int32_t batch, int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_cache_seqlen, hipStream_t stream) {
+  pkc_status st = check_dtype(dtype);
+  if (st != PKC_OK) return st;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !cache_seqlens) return PKC_ERR_NULL;
+  st = check_pool(batch, chunk_size, n_kv_head, head_dim, block_size, num_blocks,
+                  max_blocks_per_seq, max_cache_seqlen);
+  if (st != PKC_OK) return st;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKC_ERR_ALIGN;
+  AppendParams p{k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, batch, chunk_size,
+                 n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq, max_cache_seqlen};
+  return from_hip(launch_paged_append(dtype, p, stream));
+}
+
+static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new, const void* v_new,
+                              const void* k_pool, const void* v_pool, void* k_pool_w,
+                              void* v_pool_w, const int32_t* block_tables,
+                              const int32_t* cache_seqlens, const void* pos, int32_t pos_len,
+                              int32_t pos_per_row, const void* pos_bias_u, const void* pos_bias_v,
+                              void* out, int32_t batch, int32_t chunk_size, int32_t n_head,
+                              int32_t n_kv_head, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream) {
+  pkc_status st = check_dtype(dtype);
+  if (st != PKC_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_tables || !cache_seqlens || !pos || !pos_bias_u ||
+      !pos_bias_v || !out)
+    return PKC_ERR_NULL;
+  st = check_pool(batch, chunk_size, n_kv_head, head_dim, block_size, num_blocks,
+                  max_blocks_per_seq, max_cache_seqlen);
+  if (st != PKC_OK) return st;
+  st = check_attn(chunk_size, n_head, n_kv_head, head_dim, block_size, max_cache_seqlen, pos_len,
+                  pos_per_row);
+  if (st != PKC_OK) return st;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(pos) ||
+      !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))
+    return PKC_ERR_ALIGN;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKC_ERR_ALIGN;
+  AttnParams p{};
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = block_tables;
+  p.cache_seqlens = cache_seqlens;
+  p.pos = pos;
+  p.pos_bias_u = pos_bias_u;
+  p.pos_bias_v = pos_bias_v;
+  p.out = out;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_pool_w = k_pool_w;
+  p.v_pool_w = v_pool_w;
+  p.batch = batch;
+  p.chunk = chunk_size;
+  p.n_head = n_head;
+  p.n_kv_head = n_kv_head;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_cache = max_cache_seqlen;
+  p.pos_len = pos_len;
+  p.pos_per_row = pos_per_row;
+  p.softmax_scale = softmax_scale;
+  return from_hip(launch_chunk_attn(dtype, p, stream));
+}
+
+pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_tables,
+                                   const int32_t* cache_seqlens, const void* pos, int32_t pos_len,
+                                   int32_t pos_per_row, const void* pos_bias_u,
+                                   const void* pos_bias_v, void* out, int32_t batch,
+                                   int32_t chunk_size, int32_t n_head, int32_t n_kv_head,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_cache_seqlen,
+                                   float softmax_scale, hipStream_t stream) {
+  return attn_common(dtype, q, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_tables,
+                     cache_seqlens, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
+                     chunk_size, n_head, n_kv_head, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_cache_seqlen, softmax_scale, stream);
+}
+
+pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const void* k_new,
+                                       const void* v_new, void* k_pool, void* v_pool,
+                                       const int32_t* block_tables, const int32_t* cache_seqlens,
+                                       const void* pos, int32_t pos_len, int32_t pos_per_row,
+                                       const void* pos_bias_u, const void* pos_bias_v, void* out,
+                                       int32_t batch, int32_t chunk_size, int32_t n_head,
+                                       int32_t n_kv_head, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_cache_seqlen, float softmax_scale,
+                                       hipStream_t stream) {
+  if (!k_new || !v_new) return PKC_ERR_NULL;
+  return attn_common(dtype, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, block_tables,
+                     cache_seqlens, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
+                     chunk_size, n_head, n_kv_head, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_cache_seqlen, softmax_scale, stream);
+}
+
+pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens, int32_t num_seqs,
+                                     int32_t total_frames, int32_t max_seqlen, const void* pos,
+                                     const void* pos_bias_u, const void* pos_bias_v, void* out,
+                                     int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                                     float softmax_scale, hipStream_t stream) {
+  pkc_status st = check_dtype(dtype);
+  if (st != PKC_OK) return st;
+  if (!q || !k || !v || !cu_seqlens || !pos || !pos_bias_u || !pos_bias_v || !out)
+    return PKC_ERR_NULL;
+  if (num_seqs <= 0 || total_frames < 0 || max_seqlen < 0 || n_head <= 0 || n_kv_head <= 0 ||
+      n_head % n_kv_head != 0 || head_dim <= 0 || head_dim % 8 != 0)
+    return PKC_ERR_SHAPE;
+  if ((int64_t)total_frames >= (int64_t)1 << 29 || (int64_t)max_seqlen > total_frames)
+    return PKC_ERR_SHAPE;
+  if (head_dim != 64) return PKC_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pos) ||
+      !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))
+    return PKC_ERR_ALIGN;
+  if (total_frames == 0 || max_seqlen == 0) return PKC_OK;
+  VarlenParams p{q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, out, num_seqs, total_frames,
+                 max_seqlen, n_head, n_kv_head, head_dim, softmax_scale};
+  return from_hip(launch_varlen_attn(dtype, p, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Paged K/V append: each stream's chunk K/V into the pages its block table names.
+//
+// Source: OASR docs, "ASR Engine", section 4.3 "Batched paged forward" -- one pool shared by the
+// cohort, one block-table row per stream, the chunk written at logical frames
+// [cache_seqlens[b], cache_seqlens[b] + C), cache_seqlens advanced only after the forward.
+//
+// One workgroup per (stream, kv head). K rows are copied 16 bytes per lane straight into their
+// slots (rows of the K page are contiguous). V pages are stored transposed ([head_dim][block_size])
+// so that attention can read 8 consecutive frames of one dimension with one 16-byte load; the
+// workgroup therefore stages the chunk's V rows in LDS and writes each dimension's run of frames,
+// consecutive lanes writing consecutive slots.
+#include "pkc_device.h"
+#include "pkc_launch.h"
+
+namespace pkc {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTileFrames = 64;  // frames staged per LDS round
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ k_pool,
+                    T* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
+                    const int32_t* __restrict__ cache_seqlens, int chunk, int n_kv_head, int head_dim,
+                    int block_size, int num_blocks, int max_blocks, int max_cache) {
+  extern __shared__ unsigned char smem_raw[];
+  T* sv = reinterpret_cast<T*>(smem_raw);  // [kTileFrames][head_dim + pad]
+  constexpr int VEC = 16 / sizeof(T);
+  const int pitch = head_dim + VEC;         // keeps 16-byte alignment, shifts banks per frame
+
+  const int b = blockIdx.x / n_kv_head;
+  const int g = blockIdx.x % n_kv_head;
+  const int cache = clampi(cache_seqlens[b], 0, max_cache);
+  const int32_t* bt = block_tables + (size_t)b * max_blocks;
+  const int nvec = head_dim / VEC;
+
+  for (int t0 = 0; t0 < chunk; t0 += kTileFrames) {
+    const int nt = min(kTileFrames, chunk - t0);
+    // K: direct copy; V: stage rows in LDS.
+    for (int x = threadIdx.x; x < nt * nvec; x += kThreads) {
+      const int t = t0 + x / nvec;
+      const int dv = (x % nvec) * VEC;
+      const int frame = cache + t;
+      const int blk = clampi(bt[frame / block_size], 0, num_blocks - 1);
+      const int slot = frame % block_size;
+      const size_t src = (((size_t)b * chunk + t) * n_kv_head + g) * head_dim + dv;
+      const uint4 kv = *reinterpret_cast<const uint4*>(k_new + src);
+      *reinterpret_cast<uint4*>(k_pool + (((size_t)blk * n_kv_head + g) * block_size + slot) * head_dim + dv) = kv;
+      *reinterpret_cast<uint4*>(sv + (x / nvec) * pitch + dv) = *reinterpret_cast<const uint4*>(v_new + src);
+    }
+    __syncthreads();
+    // V: for each dimension, the run of frames goes to consecutive slots of the transposed page.
+    for (int x = threadIdx.x; x < nt * head_dim; x += kThreads) {
+      const int d = x / nt;
+      const int tl = x % nt;
+      const int frame = cache + t0 + tl;
+      const int blk = clampi(bt[frame / block_size], 0, num_blocks - 1);
+      const int slot = frame % block_size;
+      v_pool[(((size_t)blk * n_kv_head + g) * head_dim + d) * block_size + slot] = sv[tl * pitch + d];
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream) {
+  const dim3 grid(p.batch * p.n_kv_head);
+  if (dtype == PKC_BF16) {
+    const size_t smem = (size_t)kTileFrames * (p.head_dim + 8) * sizeof(bf16);
+    hipLaunchKernelGGL(paged_append_kernel<bf16>, grid, dim3(kThreads), smem, stream,
+                       (const bf16*)p.k_new, (const bf16*)p.v_new, (bf16*)p.k_pool, (bf16*)p.v_pool,
+                       p.block_tables, p.cache_seqlens, p.chunk, p.n_kv_head, p.head_dim,
+                       p.block_size, p.num_blocks, p.max_blocks, p.max_cache);
+  } else {
+    const size_t smem = (size_t)kTileFrames * (p.head_dim + 4) * sizeof(float);
+    hipLaunchKernelGGL(paged_append_kernel<float>, grid, dim3(kThreads), smem, stream,
+                       (const float*)p.k_new, (const float*)p.v_new, (float*)p.k_pool,
+                       (float*)p.v_pool, p.block_tables, p.cache_seqlens, p.chunk, p.n_kv_head,
+                       p.head_dim, p.block_size, p.num_blocks, p.max_blocks, p.max_cache);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkc

@@ -1,0 +1,90 @@
+// Device helpers shared by the gfx950 kernels: element types, 8-element operand fragments and
+// the 16x16 MFMA wrappers.
+//
+// Fragment convention. Every MFMA here is a 16x16 output tile with a 32-deep contraction, and
+// every lane supplies 8 consecutive contraction elements of one operand row (A) or column (B):
+// lane l covers row/column (l % 16) and contraction elements [8 * (l / 16), 8 * (l / 16) + 8).
+// For bf16 that is exactly one v_mfma_f32_16x16x32_bf16. For fp32 the same 8 elements feed eight
+// v_mfma_f32_16x16x4_f32, the s-th taking element s of every lane, so lane group g supplies
+// contraction index 8 g + s; summing over s and g covers all 32 in both cases, and operands A and
+// B always pair the same elements. The output tile puts element (row 4 (l / 16) + e, column
+// l % 16) in register e of lane l.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkc {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+struct f32x8 {
+  floatx4 lo, hi;
+};
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+// ---- 8-element loads (16 B for bf16, 32 B for fp32; addresses are 16-byte aligned) ----------
+
+__device__ __forceinline__ bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 load8(const float* p) {
+  f32x8 r;
+  r.lo = *reinterpret_cast<const floatx4*>(p);
+  r.hi = *reinterpret_cast<const floatx4*>(p + 4);
+  return r;
+}
+
+__device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
+__device__ __forceinline__ void store8(float* p, f32x8 v) {
+  *reinterpret_cast<floatx4*>(p) = v.lo;
+  *reinterpret_cast<floatx4*>(p + 4) = v.hi;
+}
+
+__device__ __forceinline__ float get(const bf16x8& v, int e) { return (float)v[e]; }
+__device__ __forceinline__ float get(const f32x8& v, int e) { return e < 4 ? v.lo[e] : v.hi[e - 4]; }
+__device__ __forceinline__ void set(bf16x8& v, int e, float x) { v[e] = (bf16)x; }
+__device__ __forceinline__ void set(f32x8& v, int e, float x) {
+  if (e < 4) v.lo[e] = x; else v.hi[e - 4] = x;
+}
+
+template <typename T> __device__ __forceinline__ typename Frag<T>::type zero8() {
+  typename Frag<T>::type v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) set(v, e, 0.f);
+  return v;
+}
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f(float x) { return (T)x; }
+
+// ---- 16x16x32 products ------------------------------------------------------------------------
+
+__device__ __forceinline__ floatx4 mma(const bf16x8& a, const bf16x8& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma(const f32x8& a, const f32x8& b, floatx4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[s], b.lo[s], c, 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[s], b.hi[s], c, 0, 0, 0);
+  return c;
+}
+
+// ---- wave-level helpers -----------------------------------------------------------------------
+
+__device__ __forceinline__ float xor_max(float x, int mask) {
+  return fmaxf(x, __shfl_xor(x, mask, 64));
+}
+__device__ __forceinline__ float xor_sum(float x, int mask) { return x + __shfl_xor(x, mask, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace pkc

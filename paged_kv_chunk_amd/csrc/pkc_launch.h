@@ -1,0 +1,63 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernel files. Sizes have been
+// validated by the caller; launchers only pick the instantiation and grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkc.h"
+
+namespace pkc {
+
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* cache_seqlens;
+  int batch, chunk, n_kv_head, head_dim, block_size, num_blocks, max_blocks, max_cache;
+};
+
+struct AttnParams {
+  const void* q;
+  const void* k_pool;      // read
+  const void* v_pool;      // read
+  const int32_t* block_tables;
+  const int32_t* cache_seqlens;
+  const void* pos;
+  const void* pos_bias_u;
+  const void* pos_bias_v;
+  void* out;
+  // fused append: when k_new is non-null the chunk's K/V come from k_new / v_new and are also
+  // written into k_pool_w / v_pool_w (the same pools as k_pool / v_pool)
+  const void* k_new;
+  const void* v_new;
+  void* k_pool_w;
+  void* v_pool_w;
+  int batch, chunk, n_head, n_kv_head, head_dim, block_size, num_blocks, max_blocks, max_cache;
+  int pos_len, pos_per_row;
+  float softmax_scale;
+};
+
+struct VarlenParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_seqlens;
+  const void* pos;
+  const void* pos_bias_u;
+  const void* pos_bias_v;
+  void* out;
+  int num_seqs, total, max_seqlen, n_head, n_kv_head, head_dim;
+  float softmax_scale;
+};
+
+hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream);
+hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream);
+hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_t stream);
+
+// Largest number of pages per stream the attention kernel stages in LDS.
+constexpr int kMaxStagedBlocks = 4096;
+
+}  // namespace pkc

@@ -18,7 +18,7 @@ v_pool [num_blocks, n_kv_head, head_dim, block_size] (V transposed inside each p
 Table layout: row r of a table with centre ``center`` holds the embedding of distance center - r.
 A shared table has 2 (max_cache + C) - 1 rows. Per-row tables are packed as
 [B, 2 (max_cache + C) - 1, H, D]; stream b uses the first 2 T_b - 1 rows, centred at T_b - 1.
-Packed varlen tables put segment s's 2 L_s - 1 rows at row 2 cu_seqlens[s] - s.
+Packed varlen tables put segment s's 2 L_s - 1 rows at row 2 cu_seqlens[s] (2 L_s rows reserved).
 """
 
 from __future__ import annotations
@@ -166,7 +166,7 @@ class VarlenCohort:
     k: torch.Tensor            # [total, Hk, D]
     v: torch.Tensor            # [total, Hk, D]
     cu_seqlens: torch.Tensor   # [S + 1] int32
-    pos: torch.Tensor          # [2 total - S, H, D]
+    pos: torch.Tensor          # [2 total, H, D]
     pos_bias_u: torch.Tensor   # [H, D]
     pos_bias_v: torch.Tensor   # [H, D]
     lengths: list
@@ -188,14 +188,14 @@ def make_varlen_cohort(lengths, H, D, *, Hk=None, dtype=BF16, seed=0, device="cp
     u = _randn((H, D), gen, "cpu", dtype, 0.02).to(device)
     w = _randn((H, D), gen, "cpu", dtype, 0.02).to(device)
     proj = relpos_projection(H * D, gen)
-    n_rows = max(2 * total - len(lengths), 0)
+    n_rows = 2 * total
     pos = torch.zeros((n_rows, H, D), dtype=torch.float64)
     lmax = max(lengths) if lengths else 1
     full = descending_table(max(lmax - 1, 0), proj, H, D)
     for s, n in enumerate(lengths):
         if n == 0:
             continue
-        row0 = 2 * int(cu[s]) - s
+        row0 = 2 * int(cu[s])
         lo = (lmax - 1) - (n - 1)
         pos[row0: row0 + 2 * n - 1] = full[lo: lo + 2 * n - 1]
     return VarlenCohort(q=q, k=k, v=v, cu_seqlens=cu.to(device), pos=pos.to(dtype).to(device),

@@ -1,0 +1,146 @@
+"""Host-only checks of the C ABI: the library loads, exports every function include/pkc.h
+declares, and every validation error returns its status before anything is launched.
+
+No call here passes validation: the pointers are fake (never dereferenced), so each case is built
+to fail a host-side check.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_chunk_amd as pkc
+from paged_kv_chunk_amd import build as pkc_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkc.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, CAP, HIP, ALIGN = range(8)
+P = 0x10000          # a fake, 16-byte aligned "device" address
+BAD = 0x10008        # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkc.LIB_PATH):
+        pkc_build.build()
+    return pkc.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:pkc_status|int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["paged_kv_append", "chunk_paged_relpos_attn", "paged_kv_append_relpos_attn",
+              "varlen_packed_relpos_attn", "pkc_version", "pkc_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(pkc.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+        assert name in pkc.SIGNATURES, name
+
+
+def test_version_and_status_strings(lib):
+    assert pkc.version() >= 100
+    for s in range(8):
+        assert pkc.status_string(s) and pkc.status_string(s) != "unknown status"
+    assert pkc.status_string(99) == "unknown status"
+
+
+def append(lib, dtype=1, k_new=P, v_new=P, k_pool=P, v_pool=P, bt=P, cs=P, B=2, C=16, Hk=4, D=64,
+           S=16, N=32, M=8, max_cache=64):
+    return lib.paged_kv_append(dtype, k_new, v_new, k_pool, v_pool, bt, cs, B, C, Hk, D, S, N, M,
+                               max_cache, None)
+
+
+def attn(lib, dtype=1, q=P, k_pool=P, v_pool=P, bt=P, cs=P, pos=P, pos_len=159, per_row=0, u=P,
+         w=P, out=P, B=2, C=16, H=4, Hk=4, D=64, S=16, N=32, M=8, max_cache=64, scale=0.0):
+    return lib.chunk_paged_relpos_attn(dtype, q, k_pool, v_pool, bt, cs, pos, pos_len, per_row, u,
+                                       w, out, B, C, H, Hk, D, S, N, M, max_cache, scale, None)
+
+
+def fused(lib, k_new=P, v_new=P, **kw):
+    a = dict(dtype=1, q=P, k_pool=P, v_pool=P, bt=P, cs=P, pos=P, pos_len=159, per_row=0, u=P,
+             w=P, out=P, B=2, C=16, H=4, Hk=4, D=64, S=16, N=32, M=8, max_cache=64, scale=0.0)
+    a.update(kw)
+    return lib.paged_kv_append_relpos_attn(a["dtype"], a["q"], k_new, v_new, a["k_pool"],
+                                           a["v_pool"], a["bt"], a["cs"], a["pos"], a["pos_len"],
+                                           a["per_row"], a["u"], a["w"], a["out"], a["B"], a["C"],
+                                           a["H"], a["Hk"], a["D"], a["S"], a["N"], a["M"],
+                                           a["max_cache"], a["scale"], None)
+
+
+def varlen(lib, dtype=1, q=P, k=P, v=P, cu=P, S=4, total=100, max_len=40, pos=P, u=P, w=P, out=P,
+           H=8, Hk=8, D=64):
+    return lib.varlen_packed_relpos_attn(dtype, q, k, v, cu, S, total, max_len, pos, u, w, out, H,
+                                         Hk, D, 0.0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), DTYPE),
+    (dict(k_new=None), NULL), (dict(v_pool=None), NULL), (dict(bt=None), NULL), (dict(cs=None), NULL),
+    (dict(B=0), SHAPE), (dict(C=0), SHAPE), (dict(D=60), SHAPE), (dict(S=0), SHAPE),
+    (dict(max_cache=-1), SHAPE), (dict(N=0), SHAPE),
+    (dict(max_cache=113), CAP),                      # 113 + 16 > 8 * 16
+    (dict(M=4, max_cache=64), CAP),
+    (dict(k_pool=BAD), ALIGN), (dict(k_new=BAD), ALIGN),
+])
+def test_append_validation(lib, kw, status):
+    assert append(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=-1), DTYPE),
+    (dict(q=None), NULL), (dict(pos=None), NULL), (dict(u=None), NULL), (dict(out=None), NULL),
+    (dict(H=6, Hk=4), SHAPE), (dict(H=0), SHAPE),
+    (dict(pos_len=158), SHAPE),                      # even shared table
+    (dict(pos_len=157), SHAPE),                      # (157 - 1) / 2 < 64 + 16 - 1
+    (dict(per_row=1, pos_len=158), SHAPE),           # per-row needs 2 * 80 - 1
+    (dict(per_row=2), SHAPE),
+    (dict(D=128), UNSUP), (dict(S=12, M=12), UNSUP),
+    (dict(max_cache=120), CAP),
+    (dict(q=BAD), ALIGN), (dict(pos=BAD), ALIGN), (dict(out=BAD), ALIGN),
+])
+def test_attention_validation(lib, kw, status):
+    assert attn(lib, **kw) == status
+
+
+def test_fused_validation(lib):
+    assert fused(lib, k_new=None) == NULL
+    assert fused(lib, v_new=None) == NULL
+    assert fused(lib, k_new=BAD) == ALIGN
+    assert fused(lib, max_cache=200) == CAP
+    assert fused(lib, pos_len=100) == SHAPE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), DTYPE), (dict(cu=None), NULL), (dict(k=None), NULL),
+    (dict(S=0), SHAPE), (dict(H=6, Hk=4), SHAPE), (dict(max_len=101), SHAPE), (dict(D=12), SHAPE),
+    (dict(D=128), UNSUP), (dict(v=BAD), ALIGN),
+])
+def test_varlen_validation(lib, kw, status):
+    assert varlen(lib, **kw) == status
+
+
+def test_varlen_empty_batch_is_a_no_op(lib):
+    assert varlen(lib, total=0, max_len=0) == OK
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    x = torch.zeros(2, 16, 4, 64)
+    with pytest.raises(ValueError):
+        pkc.chunk_paged_relpos_attn(x, torch.zeros(4, 4, 16, 64), torch.zeros(4, 4, 64, 16),
+                                    torch.zeros(2, 2, dtype=torch.int32),
+                                    torch.zeros(2, dtype=torch.int32), torch.zeros(31, 4, 64),
+                                    torch.zeros(4, 64), torch.zeros(4, 64), max_cache_seqlen=0,
+                                    out=torch.zeros_like(x))

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Tolerances (max-abs over every compared output): 2e-2 for bf16 storage, 1e-4 for fp32; the
+append and the block indexing are compared bit for bit. Every input is seeded and synthetic.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_chunk_amd as pkc
+from synth import make_chunk_cohort, make_config, make_varlen_cohort
+from gpu_helpers import TOL, bits, compact, host64, max_err, oracle_chunk, poison
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    print(f"\n[gpu] {request.node.nodeid}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_chunk(co, fused=False):
+    """Run one layer on the GPU (append then attention, or the fused entry). Pools are updated."""
+    if fused:
+        return pkc.paged_kv_append_relpos_attn(co.q, co.k_new, co.v_new, co.k_pool, co.v_pool,
+                                               co.block_tables, co.cache_seqlens, co.pos,
+                                               co.pos_bias_u, co.pos_bias_v, co.max_cache_seqlen,
+                                               per_row_pos=co.per_row_pos)
+    pkc.paged_kv_append(co.k_new, co.v_new, co.k_pool, co.v_pool, co.block_tables,
+                        co.cache_seqlens, co.max_cache_seqlen)
+    return pkc.chunk_paged_relpos_attn(co.q, co.k_pool, co.v_pool, co.block_tables,
+                                       co.cache_seqlens, co.pos, co.pos_bias_u, co.pos_bias_v,
+                                       co.max_cache_seqlen, per_row_pos=co.per_row_pos)
+
+
+def clone(co):
+    import copy
+    c2 = copy.copy(co)
+    c2.k_pool = co.k_pool.clone()
+    c2.v_pool = co.v_pool.clone()
+    return c2
+
+
+# --------------------------------------------------------------------------------------------
+# Paged append: bit-exact on the whole pool
+# --------------------------------------------------------------------------------------------
+
+SMALL = {
+    "fp32_ragged": dict(B=3, H=2, D=64, C=16, block_size=16, cache_seqlens=[0, 37, 100], dtype=F32),
+    "bf16_ragged": dict(B=3, H=2, D=64, C=16, block_size=16, cache_seqlens=[0, 37, 100], dtype=BF16),
+    "partial_tile_S8": dict(B=3, H=2, D=64, C=5, block_size=8, cache_seqlens=[3, 0, 64], dtype=BF16),
+    "two_tiles_per_row": dict(B=2, H=2, D=64, C=20, block_size=32, cache_seqlens=[7, 50],
+                              dtype=BF16, per_row_pos=True, pos_noise=0.5),
+    "gqa_h4_k2": dict(B=3, H=4, Hk=2, D=64, C=16, block_size=16, cache_seqlens=[31, 8, 129],
+                      dtype=BF16),
+    "gqa_h4_k1_fp32": dict(B=2, H=4, Hk=1, D=64, C=16, block_size=16, cache_seqlens=[31, 8],
+                           dtype=F32),
+    "single_query": dict(B=3, H=2, D=64, C=1, block_size=16, cache_seqlens=[0, 1, 255], dtype=BF16),
+    "long_cache": dict(B=1, H=2, D=64, C=16, block_size=64, cache_seqlens=[1000], dtype=BF16),
+    "per_row_ragged_fp32": dict(B=4, H=2, D=64, C=16, block_size=32, cache_seqlens=[0, 16, 48, 272],
+                                dtype=F32, per_row_pos=True, pos_noise=0.5),
+    "odd_lengths": dict(B=4, H=2, D=64, C=13, block_size=8, cache_seqlens=[5, 11, 1, 90],
+                        dtype=BF16),
+}
+
+
+def small_cohort(name, seed=0):
+    return make_chunk_cohort(seed=seed, device=DEV, **SMALL[name])
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_append_bit_exact_small(name):
+    co = small_cohort(name)
+    kb, vb = bits(co.k_pool), bits(co.v_pool)
+    ek, ev = oracle.paged_kv_append(kb, vb, bits(co.k_new), bits(co.v_new),
+                                    co.block_tables.cpu().numpy(), co.cache_seqlens.cpu().numpy())
+    pkc.paged_kv_append(co.k_new, co.v_new, co.k_pool, co.v_pool, co.block_tables,
+                        co.cache_seqlens, co.max_cache_seqlen)
+    np.testing.assert_array_equal(bits(co.k_pool), ek)
+    np.testing.assert_array_equal(bits(co.v_pool), ev)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_append_bit_exact_workloads(cfg):
+    co = make_config(cfg, device=DEV)
+    kb, vb = bits(co.k_pool), bits(co.v_pool)
+    ek, ev = oracle.paged_kv_append(kb, vb, bits(co.k_new), bits(co.v_new),
+                                    co.block_tables.cpu().numpy(), co.cache_seqlens.cpu().numpy())
+    pkc.paged_kv_append(co.k_new, co.v_new, co.k_pool, co.v_pool, co.block_tables,
+                        co.cache_seqlens, co.max_cache_seqlen)
+    assert (bits(co.k_pool) == ek).all()
+    assert (bits(co.v_pool) == ev).all()
+
+
+# --------------------------------------------------------------------------------------------
+# Attention parity
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_attention_parity_small(name):
+    co = poison(small_cohort(name, seed=3))
+    ref = oracle_chunk(co)
+    out = gpu_chunk(co)
+    err = max_err(out, ref)
+    assert err <= TOL[co.q.dtype], (name, err)
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "two_tiles_per_row", "gqa_h4_k2", "odd_lengths",
+                                  "per_row_ragged_fp32"])
+def test_fused_equals_append_then_attend(name):
+    """The fused entry writes the same pool bits and produces the same output bits."""
+    co = small_cohort(name, seed=4)
+    co2 = clone(co)
+    out_a = gpu_chunk(co)
+    out_f = gpu_chunk(co2, fused=True)
+    np.testing.assert_array_equal(bits(co.k_pool), bits(co2.k_pool))
+    np.testing.assert_array_equal(bits(co.v_pool), bits(co2.v_pool))
+    np.testing.assert_array_equal(bits(out_a), bits(out_f))
+
+
+@pytest.mark.parametrize("cfg,streams", [(0, None), (1, None), (2, "sample"), (3, None)])
+def test_attention_parity_workloads(cfg, streams):
+    co = make_config(cfg, device=DEV)
+    B = co.q.shape[0]
+    if streams == "sample":
+        rng = np.random.default_rng(cfg)
+        streams = sorted(rng.choice(B, size=16, replace=False).tolist())
+    ref = oracle_chunk(co, streams)
+    co_f = clone(co)
+    out = gpu_chunk(co)
+    sel = slice(None) if streams is None else torch.as_tensor(streams, device=DEV)
+    err = max_err(out[sel], ref)
+    assert err <= TOL[co.q.dtype], (cfg, err)
+    out_f = gpu_chunk(co_f, fused=True)
+    np.testing.assert_array_equal(bits(out), bits(out_f))
+
+
+def test_block_relabelling_is_bitwise_invariant():
+    co = small_cohort("bf16_ragged", seed=5)
+    N = co.k_pool.shape[0]
+    pi = torch.randperm(N, generator=torch.Generator().manual_seed(1)).to(DEV)
+    co2 = clone(co)
+    co2.k_pool[pi] = co.k_pool
+    co2.v_pool[pi] = co.v_pool
+    bt = co.block_tables.long()
+    co2.block_tables = torch.where(bt >= 0, pi[bt.clamp(min=0)], bt).to(torch.int32)
+    np.testing.assert_array_equal(bits(gpu_chunk(co)), bits(gpu_chunk(co2)))
+
+
+def test_row_results_do_not_depend_on_the_cohort():
+    """Row-locality: a stream's output bits are the same alone, in a cohort, and after the
+    cohort's rows are permuted."""
+    co = small_cohort("bf16_ragged", seed=6)
+    full = gpu_chunk(clone(co))
+    for b in range(co.q.shape[0]):
+        one = clone(co)
+        one.q = co.q[b:b + 1].contiguous()
+        one.k_new = co.k_new[b:b + 1].contiguous()
+        one.v_new = co.v_new[b:b + 1].contiguous()
+        one.block_tables = co.block_tables[b:b + 1].contiguous()
+        one.cache_seqlens = co.cache_seqlens[b:b + 1].contiguous()
+        np.testing.assert_array_equal(bits(gpu_chunk(one))[0], bits(full)[b])
+    perm = torch.tensor([2, 0, 1], device=DEV)
+    pc = clone(co)
+    pc.q = co.q[perm].contiguous()
+    pc.k_new = co.k_new[perm].contiguous()
+    pc.v_new = co.v_new[perm].contiguous()
+    pc.block_tables = co.block_tables[perm].contiguous()
+    pc.cache_seqlens = co.cache_seqlens[perm].contiguous()
+    np.testing.assert_array_equal(bits(gpu_chunk(pc)), bits(full)[perm.cpu().numpy()])
+
+
+def test_uniform_cache_shared_and_per_row_tables_agree():
+    co = make_chunk_cohort(3, 2, 64, 16, 16, [48, 48, 48], dtype=BF16, seed=9, device=DEV)
+    per = clone(co)
+    per.pos = co.pos[None].expand(3, *co.pos.shape).contiguous()
+    per.per_row_pos = True
+    np.testing.assert_array_equal(bits(gpu_chunk(co)), bits(gpu_chunk(per)))
+
+
+# --------------------------------------------------------------------------------------------
+# Packed varlen
+# --------------------------------------------------------------------------------------------
+
+def gpu_varlen(co):
+    return pkc.varlen_packed_relpos_attn(co.q, co.k, co.v, co.cu_seqlens, co.pos, co.pos_bias_u,
+                                         co.pos_bias_v, max(co.lengths))
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_varlen_parity_small(dtype):
+    co = make_varlen_cohort([1, 5, 0, 16, 17, 40, 100], 2, 64, dtype=dtype, seed=2, device=DEV)
+    ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
+                                    co.cu_seqlens.cpu().numpy(), host64(co.pos),
+                                    host64(co.pos_bias_u), host64(co.pos_bias_v))
+    err = max_err(gpu_varlen(co), ref)
+    assert err <= TOL[dtype], err
+
+
+def test_varlen_gqa_parity():
+    co = make_varlen_cohort([33, 64, 7], 4, 64, Hk=2, dtype=BF16, seed=3, device=DEV)
+    ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
+                                    co.cu_seqlens.cpu().numpy(), host64(co.pos),
+                                    host64(co.pos_bias_u), host64(co.pos_bias_v))
+    assert max_err(gpu_varlen(co), ref) <= TOL[BF16]
+
+
+def test_varlen_workload_sampled():
+    co = make_config(4, device=DEV)
+    out = gpu_varlen(co)
+    lengths = co.lengths
+    segs = sorted({int(np.argmax(lengths)), int(np.argmin(lengths)), 0, len(lengths) - 1})
+    rng = np.random.default_rng(4)
+
+    def rows(n):
+        pick = set(range(min(16, n))) | set(range(max(0, n - 16), n))
+        pick |= set(rng.choice(n, size=min(16, n), replace=False).tolist())
+        return sorted(pick)
+    ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
+                                    co.cu_seqlens.cpu().numpy(), host64(co.pos),
+                                    host64(co.pos_bias_u), host64(co.pos_bias_v),
+                                    segments=segs, query_rows=rows)
+    have = ~np.isnan(ref[:, 0, 0])
+    assert have.sum() > 0
+    g = out.detach().cpu().double().numpy()
+    assert np.isfinite(g).all()
+    err = float(np.abs(g[have] - ref[have]).max())
+    assert err <= TOL[BF16], err
+
+
+def test_varlen_segment_equals_chunk_at_zero_cache():
+    """A packed utterance of 16 frames is the chunk case with cache 0 and C = 16."""
+    vc = make_varlen_cohort([16], 2, 64, dtype=BF16, seed=5, device=DEV)
+    ch = make_chunk_cohort(1, 2, 64, 16, 16, [0], dtype=BF16, seed=5, device=DEV)
+    ch.q = vc.q[None].contiguous()
+    ch.k_new = vc.k[None].contiguous()
+    ch.v_new = vc.v[None].contiguous()
+    ch.pos = vc.pos[:31].contiguous()
+    ch.pos_bias_u = vc.pos_bias_u
+    ch.pos_bias_v = vc.pos_bias_v
+    a = gpu_varlen(vc)
+    b = gpu_chunk(ch)[0]
+    assert float((a.double() - b.double()).abs().max()) <= 1e-6

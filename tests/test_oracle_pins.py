@@ -367,7 +367,7 @@ def test_varlen_segments_equal_chunk_case_and_dense():
         # chunk entry, cache 0, C = L, one page holding the whole segment
         kp = k[lo:hi].transpose(1, 0, 2)[None]                 # [1, Hk, L, D]
         vp = v[lo:hi].transpose(1, 2, 0)[None]                 # [1, Hk, D, L]
-        table = pos[2 * lo - s: 2 * lo - s + 2 * n - 1]
+        table = pos[2 * lo: 2 * lo + 2 * n - 1]
         chunk = oracle.chunk_relpos_attn(q[None, lo:hi], kp, vp, np.array([[0]]), np.array([0]),
                                          table, u, w)[0]
         assert np.abs(chunk - out[lo:hi]).max() < 1e-13
