@@ -1,0 +1,297 @@
+"""Benchmark of the paged chunk attention hot path on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic cohort: for each of the 12 encoder
+layers, the paged append of the chunk's K/V and the chunk attention with the Transformer-XL term,
+launched as one fused kernel per layer on one HIP stream. The default workload is the d_model 256
+streaming cohort (B = 64 streams, 4 heads, head_dim 64, chunk 16, uniform cache 256 frames,
+block size 16, one shared relative-position table, 12 layers, bf16 storage, fp32 accumulation).
+
+Inputs are resident in HBM before timing starts. To measure HBM rather than the 256 MB
+Infinity Cache, the step rotates over --rotate independent cohorts (each with its own pools,
+queries and tables); with 3 sets the working set is ~720 MB.
+
+Each cohort's 12-layer chain is captured once as a HIP graph and a step replays it, as a
+streaming engine replays its captured encoder step; launching kernels one by one from Python
+would time the host, not the GPU (--eager does that, with HIP events around every launch).
+
+Prints one JSON line. `value` is chunk*heads per second per layer: B * H * layers / step time.
+`roofline` prices the fused kernel's algorithmic bytes per launch against 8 TB/s; the kernel's
+average launch duration is the graph-replay time of the timed region, measured with HIP events on
+the replay stream, divided by the number of kernel launches in it (gaps between the graph's
+kernels count against the kernel). `cpu_baseline` times the float64 oracle on a bounded sample on
+the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged chunk-attention chunk·heads/sec per layer + % of HBM roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_chunk_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(co):
+    """Bytes the fused append + attention must move for one layer of a cohort: read q, k_new,
+    v_new, the cached K/V and the positional band rows in use, u and v, the block-table entries
+    and cache lengths; write the new K/V into the pool and the output."""
+    B, C, H, D = co.q.shape
+    Hk = co.k_new.shape[2]
+    eb = co.q.element_size()
+    cache = co.cache_seqlens.cpu().tolist()
+    S = co.block_size
+    qo = 2 * B * C * H * D * eb
+    new = 4 * B * C * Hk * D * eb
+    cached = 2 * sum(cache) * Hk * D * eb
+    if co.per_row_pos:
+        band = sum(c + 2 * C - 1 for c in cache) * H * D * eb
+    else:
+        band = (max(cache) + 2 * C - 1) * H * D * eb
+    uv = 2 * H * D * eb
+    tables = sum((c + C + S - 1) // S for c in cache) * 4 + B * 4
+    return qo + new + cached + band + uv + tables
+
+
+def build_sets(cfg_index, n_sets, n_layers, device):
+    """n_sets independent cohorts, each of n_layers layers sharing one block table and cache
+    lengths (one block ID addresses every layer's pool)."""
+    from synth import make_config
+    sets = []
+    for r in range(n_sets):
+        layers = []
+        base = make_config(cfg_index, layer=0, seed=r, device=device)
+        for l in range(n_layers):
+            co = base if l == 0 else make_config(cfg_index, layer=l, seed=r, device=device)
+            co.block_tables = base.block_tables
+            co.cache_seqlens = base.cache_seqlens
+            co.out = torch.empty_like(co.q)
+            layers.append(co)
+        sets.append(layers)
+    return sets
+
+
+def launch_layer(pkc, co, stream):
+    pkc.paged_kv_append_relpos_attn(co.q, co.k_new, co.v_new, co.k_pool, co.v_pool,
+                                    co.block_tables, co.cache_seqlens, co.pos, co.pos_bias_u,
+                                    co.pos_bias_v, co.max_cache_seqlen,
+                                    per_row_pos=co.per_row_pos, out=co.out, stream=stream)
+
+
+def cpu_baseline(co, min_seconds):
+    """The float64 oracle (append + attention) on one layer of the cohort, repeated until
+    min_seconds of host time have passed; BLAS held to one thread."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    host = lambda t: t.detach().cpu().double().numpy()
+    B, C, H, D = co.q.shape
+    bt = co.block_tables.cpu().numpy()
+    cs = co.cache_seqlens.cpu().numpy()
+    args = [host(co.k_pool), host(co.v_pool), host(co.k_new), host(co.v_new)]
+    q, pos, u, w = host(co.q), host(co.pos), host(co.pos_bias_u), host(co.pos_bias_v)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        kp, vp = oracle.paged_kv_append(*args, bt, cs)
+        oracle.chunk_relpos_attn(q, kp, vp, bt, cs, pos, u, w, per_row_pos=co.per_row_pos)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return dict(value=B * H * reps / el, unit="chunk·heads/s", cores=1, kind="oracle",
+                sample=f"{reps} x one layer of the timed cohort (B={B}, H={H}, all streams), "
+                       f"append + attention in float64 numpy, {el:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="cohort workload index (1, 2 or 3)")
+    ap.add_argument("--rotate", type=int, default=3, help="independent cohort sets cycled per step")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch layer by layer from Python with HIP events around each launch "
+                         "instead of replaying captured graphs")
+    ap.add_argument("--no-events", action="store_true", help="eager mode without per-launch events")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the workload, time a plain device copy of this many MiB "
+                         "(reference for HBM counters and achievable bandwidth)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the path has "
+              "no cross-GPU exchange and this build measures one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+
+    global torch
+    import torch
+    import paged_kv_chunk_amd as pkc
+    from synth import CONFIGS
+
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": ms,
+                          "read_plus_write_GBps": 2 * n / (ms / 1e3) / 1e9}), flush=True)
+        return
+
+    cfg = CONFIGS[args.config]
+    if cfg["kind"] != "chunk":
+        raise SystemExit("bench.py times the streaming cohort workloads (1, 2 or 3)")
+    n_layers = cfg["n_layers"]
+    dev = "cuda"
+    sets = build_sets(args.config, args.rotate, n_layers, dev)
+    stream = torch.cuda.current_stream()
+    co0 = sets[0][0]
+    B, C, H, D = co0.q.shape
+
+    def step(i, events=None):
+        for li, co in enumerate(sets[i % len(sets)]):
+            if events is not None:
+                events[2 * li].record(stream)
+            launch_layer(pkc, co, stream)
+            if events is not None:
+                events[2 * li + 1].record(stream)
+
+    for i in range(max(args.warmup, len(sets))):
+        step(i)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    if args.eager:
+        use_events = not args.no_events
+        ev = ([[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)]
+               for _ in range(args.steps)] if use_events else None)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            step(i, ev[i] if use_events else None)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(end) / args.steps
+        if use_events:
+            durs = [ev[i][2 * l].elapsed_time(ev[i][2 * l + 1]) for i in range(args.steps)
+                    for l in range(n_layers)]
+            kernel_ms = sum(durs) / len(durs)
+            kernel_src = "eager launches, HIP events around each launch"
+        else:
+            kernel_ms = ms_step / n_layers
+            kernel_src = "eager launches, step time / launches"
+        mode = "eager"
+    else:
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for r in range(len(sets)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for co in sets[r]:
+                        launch_layer(pkc, co, cap)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(end) / args.steps
+        kernel_ms = ms_step / n_layers
+        kernel_src = "graph replay, timed-region time / kernel launches"
+        mode = "graph"
+
+    units = B * H * n_layers
+    value = units / (ms_step / 1e3)
+    bytes_per_launch = algorithmic_bytes(co0)
+    achieved = bytes_per_launch / (kernel_ms / 1e3) / 1e9
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        rec = json.load(open(tpath)).get(f"fused_cfg{args.config}")
+        if rec and rec.get("source_hash") == kernel_source_hash():
+            traffic = rec.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "chunk·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg['name']}: B={B} streams, H={H}, head_dim={D}, chunk={C}, "
+                        f"cache={co0.max_cache_seqlen} frames, block_size={co0.block_size}, "
+                        f"{n_layers} layers, fused append+attention per layer",
+            "streams": B, "heads": H, "head_dim": D, "chunk": C,
+            "cache_frames": co0.max_cache_seqlen, "block_size": co0.block_size,
+            "layers": n_layers, "rotated_cohorts": len(sets), "launch": mode,
+            "shared_pos_table": not co0.per_row_pos,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "chunk_attn_kernel<bf16, fused>",
+            "kernel_us": kernel_ms * 1e3,
+            "kernel_time_from": kernel_src,
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(co0, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

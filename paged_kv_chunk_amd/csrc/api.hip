@@ -44,7 +44,7 @@ pkc_status check_attn(int32_t chunk, int32_t n_head, int32_t n_kv_head, int32_t 
     if ((pos_len - 1) / 2 < longest - 1) return PKC_ERR_SHAPE;
   }
   if (head_dim != 64) return PKC_ERR_UNSUPPORTED;
-  if (block_size % 8 != 0) return PKC_ERR_UNSUPPORTED;
+  if (block_size < 8 || (block_size & (block_size - 1)) != 0) return PKC_ERR_UNSUPPORTED;
   if ((longest + block_size - 1) / block_size > kMaxStagedBlocks) return PKC_ERR_UNSUPPORTED;
   return PKC_OK;
 }
@@ -113,6 +113,9 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
       !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))
     return PKC_ERR_ALIGN;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKC_ERR_ALIGN;
+  if (chunk_attn_lds_bytes(dtype == PKC_BF16 ? 2 : 4, chunk_size, max_cache_seqlen, block_size,
+                           k_new != nullptr) > kMaxDynamicLds)
+    return PKC_ERR_UNSUPPORTED;
   AttnParams p{};
   p.q = q;
   p.k_pool = k_pool;

@@ -1,30 +1,48 @@
-// Relative-position attention for gfx950: the paged chunk path and the packed varlen path.
+// Chunk attention over a paged K/V pool with a Transformer-XL relative-position term (gfx950).
 //
 // Sources: OASR docs, "Scheduler", section 4.3 "Heterogeneous-offset batching" (attention over the
 // paged pool, per-stream lengths from cache_seqlens, matrix_bd / sqrt(d_k) added to the scores);
 // "Model Layer", fixed_attention_window declaration (distances cache + i - j; one shared table for
-// a uniform cache, one table per row otherwise); "ASR Engine", section 4.3 (the append that
-// precedes it, fused here when k_new is given); "Model Layer", "The engine-facing surface"
-// (forward_offline_packed: gapless varlen rows, attention inside each utterance).
+// a uniform cache, one table per row otherwise); "ASR Engine", section 4.3 (the append of the
+// chunk's K/V that precedes the attention, fused into this kernel when k_new is given).
 //
-// Work decomposition. One workgroup of kWaves wavefronts per (stream or utterance, head, 16-query
-// tile). The T keys are cut into 32-key steps; wave w takes steps w, w + kWaves, ... and keeps its
-// own online-softmax state; the waves merge through LDS at the end in a fixed order, so a row's
-// result depends only on its own length (never on the cohort or the batch width).
+// Work decomposition. One workgroup of kWaves wavefronts per (stream b, head h, 16-query tile).
+// The T = cache + C keys split into
+//   * the body, keys [0, body_end) with body_end = cache rounded down to a multiple of 32: whole
+//     32-key steps read straight from the pool pages, no masking;
+//   * the tail, keys [body_end, T) (at most 31 + C keys): staged once into LDS at kernel start -
+//     K rows and V transposed, the chunk's own frames taken from k_new / v_new when fused and from
+//     the pool otherwise, zero past T - and processed as masked steps.
+// The split and the step-to-wave assignment depend only on the cache length, so the fused and the
+// unfused entries do identical arithmetic on identical values.
+// Each wave takes a contiguous range of body steps (so one band tile carries over from step to
+// step) and every kWaves-th tail step, keeps its own online-softmax state, and the waves merge
+// through LDS in a fixed order: a stream's result depends only on its own cache length.
 //
-// Per step the wave computes, with 16x16 MFMA tiles whose columns are the 16 queries:
-//   S^T = K . (q + u)^T          two tiles (32 keys x 16 queries), contraction over head_dim
-//   G^T = P_band . (q + v)^T     three tiles: the 47 table rows this step can touch
+// Latency. Everything a wave needs is requested before it first waits: the block IDs of the
+// stream's first 128 pages (into a wave-private LDS window, no workgroup barrier), the queries,
+// the band rows and the first two body steps; later steps are fetched two steps ahead into
+// alternating register sets. The chunk's K/V are written into the pool only at the very end: on
+// CDNA global stores share the in-order vector-memory counter with loads, so a store issued
+// early would hold up every later load wait. The softmax scale (and log2 e) is folded into
+// q + u and q + v, and the running max moves only when a score exceeds it by 2^8 (the
+// probabilities stay <= 256, exact after the final division), which keeps the rescale of the
+// accumulator out of most steps.
+//
+// Per 32-key step, with 16x16 MFMA tiles whose columns are the 16 queries:
+//   S^T = K . (q + u)^T          two tiles (32 keys), contraction over head_dim
+//   G^T = P_band . (q + v)^T     three tiles: the 47 table rows the step touches (tile 0 is the
+//                                previous step's tile 2 inside a body range)
 //   O^T += V^T . softmax(S + Bd)^T
-// Key order inside a step is permuted so that the 8 scores a lane holds after the S^T tiles are
-// exactly the 8 consecutive keys it must feed to the PV product (tile 0 row 4a + e is key 8a + e,
-// tile 1 row 4a + e is key 8a + 4 + e). V pages are stored transposed, so the V^T operand is one
-// 16-byte load of 8 consecutive frames per lane. The relative shift Bd[i][j] = G[i][j + 15 - i']
-// (i' = query inside the tile) moves data between lanes of the same query column; it goes through
-// a per-wave LDS tile.
+// Key order inside a step is permuted so that the 8 scores a lane holds after the S^T tiles are the
+// 8 consecutive keys it feeds to the PV product (tile 0 row 4a + e is key 8a + e, tile 1 row
+// 4a + e is key 8a + 4 + e). V pages are stored transposed ([head_dim][block_size]), so the V^T
+// operand is one 16-byte load of 8 consecutive frames per lane. The relative shift
+// Bd[i][j] = G[i][j + 15 - i'] (i' = query inside the tile) moves data between lanes of one query
+// column; it goes through a per-wave LDS tile.
 //
-// Table geometry: the row for (query i, key j) is R0 + j - i, where R0 = centre - cache. Only rows
-// [R0 - (C - 1), R0 + T - 1] are ever read.
+// Table geometry: the row for (query i, key j) is R0 + j - i with R0 = centre - cache; only rows
+// [R0 - (C - 1), R0 + T - 1] are read.
 #include <math.h>
 
 #include "pkc_device.h"
@@ -34,236 +52,367 @@ namespace pkc {
 
 namespace {
 
-constexpr int kD = 64;          // head_dim of these kernels
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kWaveLds = kD * 16 + 32;  // floats per wave: O^T tile + m + l (band tile aliases it)
+constexpr int kD = 64;                  // head_dim of this kernel
+constexpr int kWaveLds = kD * 16 + 32;  // floats per wave: O^T tile + m + l (skew tile aliases it)
+constexpr int kSkewPitch = 48;          // floats per query column of the skew tile (47 rows used)
+constexpr int kBtWindow = 128;          // block IDs each wave keeps in its LDS window
+constexpr float kRescaleLog2 = 8.f;     // headroom before the running max moves
 
-// ------------------------------------------------------------------------------------------------
-// Key/value sources
-// ------------------------------------------------------------------------------------------------
-
-// Keys of one stream read through its block table (LDS copy s_bt); with kFused, keys at or past
-// `cache` come from the chunk's own k_new / v_new rows.
-template <typename T, bool kFused>
-struct PagedSource {
+template <typename T>
+struct ChunkArgs {
+  const T* q;
   const T* k_pool;
   const T* v_pool;
-  const T* k_new;   // [C, Hk, D] rows of this stream (fused only)
+  const int32_t* bt;
+  const int32_t* cs;
+  const T* pos;
+  const T* u;
+  const T* w;
+  T* out;
+  const T* k_new;   // fused only
   const T* v_new;
-  const int* s_bt;
-  int Hk, hk, S, cache, T_len;
-
-  __device__ __forceinline__ const T* k_row(int key) const {
-    if (kFused && key >= cache) return k_new + ((size_t)(key - cache) * Hk + hk) * kD;
-    return k_pool + (((size_t)s_bt[key / S] * Hk + hk) * S + key % S) * kD;
-  }
-  // 8 consecutive keys [kg, kg + 8) of dimension d in one load when possible.
-  __device__ __forceinline__ bool v_whole(int kg) const {
-    return kg + 8 <= T_len && (!kFused || kg + 8 <= cache);
-  }
-  __device__ __forceinline__ const T* v_group(int kg) const {
-    return v_pool + ((size_t)s_bt[kg / S] * Hk + hk) * kD * S + (kg % S);
-  }
-  __device__ __forceinline__ size_t v_dim_stride() const { return (size_t)S; }
-  __device__ __forceinline__ float v_elem(int key, int d) const {
-    if (kFused && key >= cache) return to_f(v_new[((size_t)(key - cache) * Hk + hk) * kD + d]);
-    return to_f(v_pool[(((size_t)s_bt[key / S] * Hk + hk) * kD + d) * S + key % S]);
-  }
+  T* k_pool_w;
+  T* v_pool_w;
+  int C, H, Hk, S, logS, N, M, max_cache, pos_len, per_row, qtiles;
+  int tail_cap, vt_pitch;            // LDS tail geometry (keys, elements per V^T row)
+  int off_bt, off_kt, off_vt;        // byte offsets of the LDS regions
+  float scale_log2;
 };
 
-// Keys of one packed utterance, rows [0, T_len) starting at k / v (stride Hk * D per frame).
 template <typename T>
-struct PackedSource {
-  const T* k;
-  const T* v;
-  int Hk, hk, T_len;
-
-  __device__ __forceinline__ const T* k_row(int key) const {
-    return k + ((size_t)key * Hk + hk) * kD;
-  }
-  __device__ __forceinline__ bool v_whole(int) const { return false; }
-  __device__ __forceinline__ const T* v_group(int) const { return v; }
-  __device__ __forceinline__ size_t v_dim_stride() const { return 1; }
-  __device__ __forceinline__ float v_elem(int key, int d) const {
-    return to_f(v[((size_t)key * Hk + hk) * kD + d]);
-  }
-};
-
-// ------------------------------------------------------------------------------------------------
-// One 32-key step
-// ------------------------------------------------------------------------------------------------
-
-template <typename T>
-struct StepData {
+struct StepRegs {
   typedef typename Frag<T>::type F;
   F k[2][2];   // [key tile][head_dim half]
   F v[4];      // [16-dim tile]
-  F p[3][2];   // [band tile][head_dim half]
+  F p[2][2];   // band tiles 1 and 2 [tile][head_dim half]
 };
 
-template <typename T, typename Src>
-__device__ __forceinline__ void load_step(StepData<T>& sd, const Src& src, int j0, const T* ptab,
-                                          size_t prow_stride, int band0, int rlo, int rhi,
-                                          int lane) {
-  const int m16 = lane & 15;
-  const int grp = lane >> 4;
-  const int T_len = src.T_len;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int key = min(j0 + 8 * (m16 >> 2) + 4 * tt + (m16 & 3), T_len - 1);
-    const T* row = src.k_row(key);
-    sd.k[tt][0] = load8(row + 8 * grp);
-    sd.k[tt][1] = load8(row + 32 + 8 * grp);
-  }
-  const int kg = j0 + 8 * grp;
-  if (src.v_whole(kg)) {
-    const T* base = src.v_group(kg);
-    const size_t ds = src.v_dim_stride();
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) sd.v[dt] = load8(base + (size_t)(16 * dt + m16) * ds);
-  } else {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kg + e;
-        set(sd.v[dt], e, key < T_len ? src.v_elem(key, 16 * dt + m16) : 0.f);
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    const int r = clampi(band0 + 16 * t + m16, rlo, rhi);
-    const T* row = ptab + (size_t)r * prow_stride;
-    sd.p[t][0] = load8(row + 8 * grp);
-    sd.p[t][1] = load8(row + 32 + 8 * grp);
-  }
-}
+template <typename T> constexpr int kt_pitch() { return kD + 16 / (int)sizeof(T); }
 
-// Attention of one 16-query tile (queries q0 .. q0 + 15 of C) over the T keys of `src`, written
-// to out_row0 + i * out_stride. q_row0 + i * q_stride is query row i.
-template <typename T, typename Src>
-__device__ __forceinline__ void attend_tile(const Src& src, const T* q_row0, size_t q_stride,
-                                            const T* u_h, const T* w_h, const T* ptab,
-                                            size_t prow_stride, int R0, int C, int q0,
-                                            float scale_log2, T* out_row0, size_t out_stride,
-                                            float* s_wave) {
+// Running softmax state of one lane (one query column, 8 keys of each step).
+struct Softmax {
+  float m, l;
+  floatx4 o[4];
+};
+
+// One 32-key step given its operand fragments and the three band product tiles (scores already
+// in log2 units). kMask: keys at or past valid_keys are excluded.
+template <typename T, bool kMask>
+__device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>::type (&kf)[2][2],
+                                             const typename Frag<T>::type (&vf)[4],
+                                             const typename Frag<T>::type (&qu)[2],
+                                             const floatx4& g0, const floatx4& g1,
+                                             const floatx4& g2, float* s_g, int valid_keys) {
   typedef typename Frag<T>::type F;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int m16 = lane & 15;
   const int grp = lane >> 4;
-  const int T_len = src.T_len;
+  floatx4 sc[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    sc[tt] = mma(kf[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
+    sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
+  }
+  // Relative shift through LDS: G^T[row][query] -> s_g[query * kSkewPitch + row]; the lane then
+  // reads its 8 keys' values from its own query column, shifted by 15 - query.
+  float* colw = s_g + m16 * kSkewPitch + 4 * grp;
+  *reinterpret_cast<floatx4*>(colw) = g0;
+  *reinterpret_cast<floatx4*>(colw + 16) = g1;
+  *reinterpret_cast<floatx4*>(colw + 32) = g2;
+  __builtin_amdgcn_wave_barrier();
+  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * grp;
+  float x[2][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = sc[tt][e] + colr[4 * tt + e];
+      if (kMask) v = (8 * grp + 4 * tt + e < valid_keys) ? v : -INFINITY;
+      x[tt][e] = v;
+      mx = fmaxf(mx, v);
+    }
+  __builtin_amdgcn_wave_barrier();
+  mx = column_max(mx);
+  const bool move = mx > st.m + kRescaleLog2;
+  if (__ballot(move) != 0) {
+    const float m_new = move ? mx : st.m;
+    const float alpha = fast_exp2(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
+    st.m = m_new;
+  }
+  F pf;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = fast_exp2(x[tt][e] - st.m);
+      st.l += pe;
+      set(pf, 4 * tt + e, pe);
+    }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
+}
 
-  F qu[2], qv[2];
+template <typename T, bool kFused, int kWaves, int kS>
+__global__ void __launch_bounds__(kWaves * 64)
+chunk_attn_kernel(ChunkArgs<T> a) {
+  typedef typename Frag<T>::type F;
+  constexpr int kThreads = kWaves * 64;
+  constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte vector
+  constexpr int NV = kD / VEC;          // vectors per row
+  constexpr int KTP = kt_pitch<T>();
+  const int S = kS ? kS : a.S;
+  const int logS = kS == 16 ? 4 : (kS == 32 ? 5 : a.logS);
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* s_wave = reinterpret_cast<float*>(smem);
+  int* s_win = reinterpret_cast<int*>(smem + a.off_bt) + (threadIdx.x >> 6) * kBtWindow;
+  T* s_kt = reinterpret_cast<T*>(smem + a.off_kt);
+  T* s_vt = reinterpret_cast<T*>(smem + a.off_vt);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m16 = lane & 15;
+  const int grp = lane >> 4;
+
+  // Grid order (b, h, query tile), tile fastest: consecutive workgroups go round-robin to the
+  // XCDs, so for H a multiple of 8 each XCD serves one head and a shared table's band for that
+  // head stays in that XCD's L2.
+  int id = blockIdx.x;
+  const int qt = id % a.qtiles;
+  id /= a.qtiles;
+  const int h = id % a.H;
+  const int b = id / a.H;
+  const int hk = h / (a.H / a.Hk);
+  const int32_t* bt = a.bt + (size_t)b * a.M;
+
+  // ---- 1. requests that need nothing: block IDs of pages [0, 128), queries, u, v, cache ------
+  const int nwin = min(a.M, kBtWindow);
+  const int bt_lo = lane < nwin ? bt[lane] : 0;
+  const int bt_hi = lane + 64 < nwin ? bt[lane + 64] : 0;
+  F qq[2], uu[2], ww[2];
   {
-    const T* qrow = q_row0 + (size_t)min(q0 + m16, C - 1) * q_stride;
+    const int iq = min(qt * 16 + m16, a.C - 1);
+    const T* qrow = a.q + (((size_t)b * a.C + iq) * a.H + h) * kD;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int d0 = 32 * half + 8 * grp;
-      const F qq = load8(qrow + d0);
-      const F uu = load8(u_h + d0);
-      const F ww = load8(w_h + d0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        set(qu[half], e, get(qq, e) + get(uu, e));
-        set(qv[half], e, get(qq, e) + get(ww, e));
-      }
+      qq[half] = load8(qrow + d0);
+      uu[half] = load8(a.u + h * kD + d0);
+      ww[half] = load8(a.w + h * kD + d0);
     }
   }
-  const int rlo = R0 - (C - 1);
+  const int cache = clampi(a.cs[b], 0, a.max_cache);
+  const int T_len = cache + a.C;
+  const int body_end = (cache >> 5) << 5;
+  const int pool_end = kFused ? cache : T_len;  // tail keys below this come from the pool
+  const int tail_pad = (T_len - body_end + 31) & ~31;
+  const size_t page = (size_t)S * kD;            // elements of one (block, kv head) page
+  const uint32_t blk_stride = (uint32_t)(a.Hk * S * kD);
+  const T* kp = a.k_pool + (size_t)hk * page;
+  const T* vp = a.v_pool + (size_t)hk * page;
+  const int nbody = body_end >> 5;
+  const int s_begin = (wave * nbody) / kWaves;
+  const int s_end = ((wave + 1) * nbody) / kWaves;
+
+  const int center = a.per_row ? (T_len - 1) : (a.pos_len - 1) / 2;
+  const int R0 = center - cache;
+  const int rlo = R0 - (a.C - 1);
   const int rhi = R0 + T_len - 1;
-  const int qlast = q0 + 15;
+  const int qlast = qt * 16 + 15;
+  const size_t prow = (size_t)a.H * kD;
+  const T* ptab = a.pos + (a.per_row ? (size_t)b * a.pos_len * prow : 0) + (size_t)h * kD;
+  auto band_row = [&](int r) { return ptab + (size_t)(uint32_t)clampi(r, rlo, rhi) * prow; };
 
-  float* s_g = s_wave + wave * kWaveLds;
-  const int nsteps = (T_len + 31) / 32;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  floatx4 o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // the window, and a page's block ID from it (pages past it: straight from the table)
+  s_win[lane] = clampi(bt_lo, 0, a.N - 1);
+  s_win[64 + lane] = clampi(bt_hi, 0, a.N - 1);
+  auto block_of = [&](int pg) -> uint32_t {
+    return (uint32_t)(pg < kBtWindow ? s_win[pg] : clampi(bt[pg], 0, a.N - 1));
+  };
 
-  StepData<T> cur, nxt;
-  int s = wave;
-  if (s < nsteps) load_step(cur, src, 32 * s, ptab, prow_stride, R0 + 32 * s - qlast, rlo, rhi, lane);
-  for (; s < nsteps; s += kWaves) {
+  // ---- 2. body loads of the first two steps (band tile 0 of the first step too) ----------------
+  auto load_step = [&](StepRegs<T>& r, int s) {
     const int j0 = 32 * s;
-    const int sn = s + kWaves;
-    if (sn < nsteps)
-      load_step(nxt, src, 32 * sn, ptab, prow_stride, R0 + 32 * sn - qlast, rlo, rhi, lane);
-    floatx4 sc[2];
+    const int key = j0 + 8 * (m16 >> 2) + (m16 & 3);          // key of tile 0; tile 1 is key + 4
+    const T* krow = kp + (uint64_t)block_of(key >> logS) * blk_stride +
+                    (uint32_t)((key & (S - 1)) * kD + 8 * grp);
+    r.k[0][0] = load8(krow);
+    r.k[0][1] = load8(krow + 32);
+    r.k[1][0] = load8(krow + 4 * kD);
+    r.k[1][1] = load8(krow + 4 * kD + 32);
+    const int kg = j0 + 8 * grp;
+    const T* vb = vp + (uint64_t)block_of(kg >> logS) * blk_stride +
+                  (uint32_t)(m16 * S + (kg & (S - 1)));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) r.v[dt] = load8(vb + 16 * dt * S);
+    const int rb = R0 + j0 - qlast;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const T* row = band_row(rb + 16 * (t + 1) + m16) + 8 * grp;
+      r.p[t][0] = load8(row);
+      r.p[t][1] = load8(row + 32);
+    }
+  };
+  StepRegs<T> ra, rb2;
+  F p0[2];
+  if (s_begin < s_end) {
+    const T* row = band_row(R0 + 32 * s_begin - qlast + m16) + 8 * grp;
+    p0[0] = load8(row);
+    p0[1] = load8(row + 32);
+    load_step(ra, s_begin);
+    if (s_begin + 1 < s_end) load_step(rb2, s_begin + 1);
+  }
+
+  // ---- 3. tail keys [body_end, T) into LDS: K rows and V transposed, zero V past T ------------
+  for (int x = tid; x < tail_pad * NV; x += kThreads) {
+    const int r = x / NV;
+    const int dv = (x % NV) * VEC;
+    const int key = body_end + r;
+    if (key < T_len) {
+      const T* src;
+      if (key < pool_end) {
+        src = kp + (uint64_t)block_of(key >> logS) * blk_stride + (uint32_t)((key & (S - 1)) * kD + dv);
+      } else {
+        src = a.k_new + ((size_t)(b * a.C + key - cache) * a.Hk + hk) * kD + dv;
+      }
+      *reinterpret_cast<uint4*>(s_kt + r * KTP + dv) = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+  for (int x = tid; x < tail_pad * NV; x += kThreads) {
+    const int r = x / NV;
+    const int dv = (x % NV) * VEC;
+    const int key = body_end + r;
+    if (key >= pool_end && key < T_len) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(
+          a.v_new + ((size_t)(b * a.C + key - cache) * a.Hk + hk) * kD + dv);
+      const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) s_vt[(dv + k) * a.vt_pitch + r] = e[k];
+    } else if (key >= T_len) {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) s_vt[(dv + k) * a.vt_pitch + r] = from_f<T>(0.f);
+    }
+  }
+  // pool keys of the tail element by element from the transposed pages (thread column
+  // r = tid % 32 of every 32-key group, dimensions d = tid / 32 + 8 n)
+  for (int c0 = 0; c0 < pool_end - body_end; c0 += 32) {
+    const int r = c0 + (tid & 31);
+    const int key = body_end + r;
+    if (key < pool_end) {
+      const T* src = vp + (uint64_t)block_of(key >> logS) * blk_stride + (uint32_t)(key & (S - 1));
+      for (int d = tid >> 5; d < kD; d += kThreads / 32) s_vt[d * a.vt_pitch + r] = src[d * S];
+    }
+  }
+
+  // queries with the biases, pre-scaled into log2 units
+  F qu[2], qv[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      set(qu[half], e, (get(qq[half], e) + get(uu[half], e)) * a.scale_log2);
+      set(qv[half], e, (get(qq[half], e) + get(ww[half], e)) * a.scale_log2);
+    }
+
+  // ---- 4. body steps, two register sets in turn ------------------------------------------------
+  float* s_g = s_wave + wave * kWaveLds;
+  Softmax st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (s_begin < s_end) {
+    floatx4 g_prev = mma(p0[0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+    g_prev = mma(p0[1], qv[1], g_prev);
+    auto run = [&](StepRegs<T>& r, int s) {
+      floatx4 g1 = mma(r.p[0][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      g1 = mma(r.p[0][1], qv[1], g1);
+      floatx4 g2 = mma(r.p[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      g2 = mma(r.p[1][1], qv[1], g2);
+      step_compute<T, false>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, 32);
+      g_prev = g2;
+      if (s + 2 < s_end) load_step(r, s + 2);
+    };
+    for (int s = s_begin; s < s_end; s += 2) {
+      run(ra, s);
+      if (s + 1 < s_end) run(rb2, s + 1);
+    }
+  }
+
+  // ---- 5. tail steps from LDS (the one workgroup barrier: the tail was staged by all threads;
+  // body steps above use only the wave's own registers and LDS) ---------------------------------
+  __syncthreads();
+  for (int k = wave; k < (tail_pad >> 5); k += kWaves) {
+    const int j0 = body_end + 32 * k;
+    F kf[2][2], vf[4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      sc[tt] = mma(cur.k[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
-      sc[tt] = mma(cur.k[tt][1], qu[1], sc[tt]);
+      const T* row = s_kt + (32 * k + 8 * (m16 >> 2) + 4 * tt + (m16 & 3)) * KTP + 8 * grp;
+      kf[tt][0] = load8(row);
+      kf[tt][1] = load8(row + 32);
     }
-    floatx4 gb[3];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(s_vt + (16 * dt + m16) * a.vt_pitch + 32 * k + 8 * grp);
+    const int rb = R0 + j0 - qlast;
+    floatx4 g[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      gb[t] = mma(cur.p[t][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-      gb[t] = mma(cur.p[t][1], qv[1], gb[t]);
+      const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
+      const F p_lo = load8(row);
+      const F p_hi = load8(row + 32);
+      g[t] = mma(p_lo, qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      g[t] = mma(p_hi, qv[1], g[t]);
     }
-    // Relative shift through LDS: G^T[row][query] -> s_g[row * 16 + query].
-#pragma unroll
-    for (int t = 0; t < 3; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_g[(16 * t + 4 * grp + e) * 16 + m16] = gb[t][e];
-    __builtin_amdgcn_wave_barrier();
-    float sv[2][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int koff = 8 * grp + 4 * tt + e;
-        const float bd = s_g[(koff + 15 - m16) * 16 + m16];
-        float x = (sc[tt][e] + bd) * scale_log2;
-        x = (j0 + koff < T_len) ? x : -INFINITY;
-        sv[tt][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    __builtin_amdgcn_wave_barrier();
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    F pf;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pe = fast_exp2(sv[tt][e] - m_new);
-        l_run += pe;
-        set(pf, 4 * tt + e, pe);
-      }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] = mma(cur.v[dt], pf, o[dt]);
-    m_run = m_new;
-    cur = nxt;
+    step_compute<T, true>(st, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
   }
 
-  // Merge the waves' partial states in a fixed order.
-  l_run = xor_sum(l_run, 16);
-  l_run = xor_sum(l_run, 32);
+  // ---- 6. fused append: this tile's chunk frames from LDS into the pool ---------------------
+  // (issued after the wave's last load, so no load wait queues behind these stores, and they
+  // drain while the waves merge)
+  if (kFused && h % (a.H / a.Hk) == 0) {
+    const int t_lo = qt * 16;
+    const int t_hi = min(a.C, t_lo + 16);
+    for (int x = tid; x < (t_hi - t_lo) * NV; x += kThreads) {
+      const int t = t_lo + x / NV;
+      const int dv = (x % NV) * VEC;
+      const int key = cache + t;
+      T* dst = a.k_pool_w + (size_t)hk * page + (uint64_t)block_of(key >> logS) * blk_stride +
+               (uint32_t)((key & (S - 1)) * kD + dv);
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s_kt + (key - body_end) * KTP + dv);
+    }
+    for (int x = tid; x < 16 * kD; x += kThreads) {
+      const int t = t_lo + (x & 15);
+      const int d = x >> 4;
+      if (t < t_hi) {
+        const int key = cache + t;
+        a.v_pool_w[(size_t)hk * page + (uint64_t)block_of(key >> logS) * blk_stride +
+                   (uint32_t)(d * S + (key & (S - 1)))] = s_vt[d * a.vt_pitch + (key - body_end)];
+      }
+    }
+  }
+  // ---- 7. merge the waves' partial states in a fixed order -------------------------------------
+  st.l = column_sum(st.l);
   float* s_o = s_wave + wave * kWaveLds;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[(16 * dt + 4 * grp + e) * 16 + m16] = o[dt][e];
+    for (int e = 0; e < 4; ++e) s_o[(16 * dt + 4 * grp + e) * 16 + m16] = st.o[dt][e];
   if (grp == 0) {
-    s_o[kD * 16 + m16] = m_run;
-    s_o[kD * 16 + 16 + m16] = l_run;
+    s_o[kD * 16 + m16] = st.m;
+    s_o[kD * 16 + 16 + m16] = st.l;
   }
   __syncthreads();
-  for (int x = threadIdx.x; x < 16 * (kD / 4); x += kThreads) {
+  for (int x = tid; x < 16 * (kD / 4); x += kThreads) {
     const int il = x & 15;
     const int d0 = (x >> 4) * 4;
-    const int i = q0 + il;
-    if (i >= C) continue;
+    const int i = qt * 16 + il;
+    if (i >= a.C) continue;
     float mmax = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mmax = fmaxf(mmax, s_wave[w * kWaveLds + kD * 16 + il]);
@@ -278,141 +427,32 @@ __device__ __forceinline__ void attend_tile(const Src& src, const T* q_row0, siz
       for (int k = 0; k < 4; ++k) acc[k] += f * so[(d0 + k) * 16 + il];
     }
     const float inv = 1.f / lsum;
-    T* dst = out_row0 + (size_t)i * out_stride + d0;
+    T* dst = a.out + (((size_t)b * a.C + i) * a.H + h) * kD + d0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) dst[k] = from_f<T>(acc[k] * inv);
   }
+
 }
 
-// ------------------------------------------------------------------------------------------------
-// Paged chunk kernel
-// ------------------------------------------------------------------------------------------------
+// Wavefronts per workgroup. Fixed (never chosen from the cohort size), so a stream's step-to-wave
+// assignment and merge order, and with them its result bits, depend on its own length only.
+template <typename T> constexpr int waves_of() { return 4; }
 
-template <typename T>
-struct ChunkArgs {
-  const T* q;
-  const T* k_pool;
-  const T* v_pool;
-  const int32_t* bt;
-  const int32_t* cs;
-  const T* pos;
-  const T* u;
-  const T* w;
-  T* out;
-  const T* k_new;   // non-null: fused append
-  const T* v_new;
-  T* k_pool_w;
-  T* v_pool_w;
-  int C, H, Hk, S, N, M, max_cache, pos_len, per_row, qtiles;
-  float scale_log2;
-};
+template <typename T, bool kFused, int kS>
+void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_attn_kernel<T, kFused, waves_of<T>(), kS>), grid,
+                     dim3(waves_of<T>() * 64), smem, stream, a);
+}
 
 template <typename T, bool kFused>
-__global__ void __launch_bounds__(kThreads)
-chunk_attn_kernel(ChunkArgs<T> a) {
-  extern __shared__ float smem[];
-  float* s_wave = smem;                                          // [kWaves][kWaveLds]
-  int* s_bt = reinterpret_cast<int*>(smem + kWaves * kWaveLds);  // pages of this stream
-
-  // Grid order (b, h, query tile) with the tile fastest: consecutive workgroups go to different
-  // XCDs round-robin, and for H a multiple of 8 each XCD sees one head, so a shared table's band
-  // for that head stays in that XCD's L2.
-  int id = blockIdx.x;
-  const int qt = id % a.qtiles;
-  id /= a.qtiles;
-  const int h = id % a.H;
-  const int b = id / a.H;
-  const int hk = h / (a.H / a.Hk);
-  const int cache = clampi(a.cs[b], 0, a.max_cache);
-  const int T_len = cache + a.C;
-  const int npages = (T_len + a.S - 1) / a.S;
-  const int32_t* bt = a.bt + (size_t)b * a.M;
-
-  for (int x = threadIdx.x; x < npages; x += kThreads) s_bt[x] = clampi(bt[x], 0, a.N - 1);
-
-  if (kFused && h % (a.H / a.Hk) == 0) {
-    // Append this tile's chunk frames; the first query head of each kv head writes. The attention
-    // below takes the chunk from k_new / v_new, never from these freshly written slots.
-    const int t_lo = qt * 16;
-    const int t_hi = min(a.C, t_lo + 16);
-    for (int x = threadIdx.x; x < (t_hi - t_lo) * (kD / 8); x += kThreads) {
-      const int t = t_lo + x / (kD / 8);
-      const int dv = (x % (kD / 8)) * 8;
-      const int frame = cache + t;
-      const int blk = clampi(bt[frame / a.S], 0, a.N - 1);
-      const int slot = frame % a.S;
-      const size_t src = (((size_t)b * a.C + t) * a.Hk + hk) * kD + dv;
-      store8(a.k_pool_w + (((size_t)blk * a.Hk + hk) * a.S + slot) * kD + dv, load8(a.k_new + src));
-      const typename Frag<T>::type vv = load8(a.v_new + src);
-      T* vdst = a.v_pool_w + (((size_t)blk * a.Hk + hk) * kD + dv) * a.S + slot;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vdst[(size_t)e * a.S] = from_f<T>(get(vv, e));
-    }
+void launch_s(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
+  // the block sizes of the streaming workloads get constant page geometry; fp32 (used for
+  // checking) always takes the general instantiation
+  if constexpr (sizeof(T) == 2) {
+    if (a.S == 16) return launch_inst<T, kFused, 16>(a, grid, smem, stream);
+    if (a.S == 32) return launch_inst<T, kFused, 32>(a, grid, smem, stream);
   }
-  __syncthreads();  // s_bt ready
-
-  PagedSource<T, kFused> src;
-  src.k_pool = a.k_pool;
-  src.v_pool = a.v_pool;
-  src.k_new = kFused ? a.k_new + (size_t)b * a.C * a.Hk * kD : nullptr;
-  src.v_new = kFused ? a.v_new + (size_t)b * a.C * a.Hk * kD : nullptr;
-  src.s_bt = s_bt;
-  src.Hk = a.Hk;
-  src.hk = hk;
-  src.S = a.S;
-  src.cache = cache;
-  src.T_len = T_len;
-
-  const int center = a.per_row ? (T_len - 1) : (a.pos_len - 1) / 2;
-  const T* ptab = a.pos + (a.per_row ? (size_t)b * a.pos_len * a.H * kD : 0) + (size_t)h * kD;
-  const size_t qstride = (size_t)a.H * kD;
-  attend_tile<T>(src, a.q + ((size_t)b * a.C * a.H + h) * kD, qstride, a.u + h * kD, a.w + h * kD,
-                 ptab, (size_t)a.H * kD, center - cache, a.C, qt * 16, a.scale_log2,
-                 a.out + ((size_t)b * a.C * a.H + h) * kD, qstride, s_wave);
-}
-
-// ------------------------------------------------------------------------------------------------
-// Packed varlen kernel: each utterance is the chunk case with cache 0 and C = L.
-// ------------------------------------------------------------------------------------------------
-
-template <typename T>
-struct VarlenArgs {
-  const T* q;
-  const T* k;
-  const T* v;
-  const int32_t* cu;
-  const T* pos;
-  const T* u;
-  const T* w;
-  T* out;
-  int H, Hk, qtiles, total;
-  float scale_log2;
-};
-
-template <typename T>
-__global__ void __launch_bounds__(kThreads)
-varlen_attn_kernel(VarlenArgs<T> a) {
-  extern __shared__ float smem[];
-  int id = blockIdx.x;
-  const int qt = id % a.qtiles;
-  id /= a.qtiles;
-  const int h = id % a.H;
-  const int s = id / a.H;
-  const int lo = clampi(a.cu[s], 0, a.total);
-  const int L = clampi(a.cu[s + 1], lo, a.total) - lo;
-  if (qt * 16 >= L) return;  // uniform over the workgroup
-  const int hk = h / (a.H / a.Hk);
-  PackedSource<T> src;
-  src.k = a.k + (size_t)lo * a.Hk * kD;
-  src.v = a.v + (size_t)lo * a.Hk * kD;
-  src.Hk = a.Hk;
-  src.hk = hk;
-  src.T_len = L;
-  const T* ptab = a.pos + (size_t)(2 * lo) * a.H * kD + (size_t)h * kD;
-  const size_t stride = (size_t)a.H * kD;
-  attend_tile<T>(src, a.q + ((size_t)lo * a.H + h) * kD, stride, a.u + h * kD, a.w + h * kD, ptab,
-                 stride, L - 1, L, qt * 16, a.scale_log2, a.out + ((size_t)lo * a.H + h) * kD,
-                 stride, smem);
+  launch_inst<T, kFused, 0>(a, grid, smem, stream);
 }
 
 template <typename T>
@@ -435,56 +475,44 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   a.H = p.n_head;
   a.Hk = p.n_kv_head;
   a.S = p.block_size;
+  a.logS = 0;
+  while ((1 << a.logS) < p.block_size) ++a.logS;
   a.N = p.num_blocks;
   a.M = p.max_blocks;
   a.max_cache = p.max_cache;
   a.pos_len = p.pos_len;
   a.per_row = p.pos_per_row;
   a.qtiles = (p.chunk + 15) / 16;
+  a.tail_cap = ((31 + p.chunk + 31) / 32) * 32;
+  a.vt_pitch = a.tail_cap + 16 / (int)sizeof(T);
+  constexpr int kWaves = waves_of<T>();
+  size_t off = (size_t)kWaves * kWaveLds * sizeof(float);
+  a.off_bt = (int)off;
+  off += (size_t)kWaves * kBtWindow * sizeof(int);
+  a.off_kt = (int)off;
+  off += (size_t)a.tail_cap * kt_pitch<T>() * sizeof(T);
+  a.off_vt = (int)off;
+  off += (size_t)kD * a.vt_pitch * sizeof(T);
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int pages = (p.max_cache + p.chunk + p.block_size - 1) / p.block_size;
-  const size_t smem = (size_t)kWaves * kWaveLds * sizeof(float) + (size_t)pages * sizeof(int);
   const dim3 grid((unsigned)p.batch * p.n_head * a.qtiles);
-  if (p.k_new) {
-    hipLaunchKernelGGL((chunk_attn_kernel<T, true>), grid, dim3(kThreads), smem, stream, a);
-  } else {
-    hipLaunchKernelGGL((chunk_attn_kernel<T, false>), grid, dim3(kThreads), smem, stream, a);
-  }
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
-  VarlenArgs<T> a;
-  a.q = (const T*)p.q;
-  a.k = (const T*)p.k;
-  a.v = (const T*)p.v;
-  a.cu = p.cu_seqlens;
-  a.pos = (const T*)p.pos;
-  a.u = (const T*)p.pos_bias_u;
-  a.w = (const T*)p.pos_bias_v;
-  a.out = (T*)p.out;
-  a.H = p.n_head;
-  a.Hk = p.n_kv_head;
-  a.qtiles = (p.max_seqlen + 15) / 16;
-  a.total = p.total;
-  const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
-  a.scale_log2 = scale * 1.4426950408889634f;
-  const size_t smem = (size_t)kWaves * kWaveLds * sizeof(float);
-  const dim3 grid((unsigned)p.num_seqs * p.n_head * a.qtiles);
-  hipLaunchKernelGGL(varlen_attn_kernel<T>, grid, dim3(kThreads), smem, stream, a);
+  if (p.k_new) launch_s<T, true>(a, grid, off, stream);
+  else launch_s<T, false>(a, grid, off, stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream) {
-  return dtype == PKC_BF16 ? launch_chunk_t<bf16>(p, stream) : launch_chunk_t<float>(p, stream);
+size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int, int, bool) {
+  const int tail_cap = ((31 + chunk + 31) / 32) * 32;
+  const int vec = 16 / dtype_bytes;
+  const int waves = dtype_bytes == 2 ? waves_of<bf16>() : waves_of<float>();
+  return (size_t)waves * kWaveLds * 4 + (size_t)waves * kBtWindow * 4 +
+         (size_t)tail_cap * (kD + vec) * dtype_bytes + (size_t)kD * (tail_cap + vec) * dtype_bytes;
 }
 
-hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_t stream) {
-  return dtype == PKC_BF16 ? launch_varlen_t<bf16>(p, stream) : launch_varlen_t<float>(p, stream);
+hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream) {
+  return dtype == PKC_BF16 ? launch_chunk_t<bf16>(p, stream) : launch_chunk_t<float>(p, stream);
 }
 
 }  // namespace pkc

@@ -83,6 +83,29 @@ __device__ __forceinline__ float xor_max(float x, int mask) {
 }
 __device__ __forceinline__ float xor_sum(float x, int mask) { return x + __shfl_xor(x, mask, 64); }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column of a 16x16 MFMA tile) with
+// the gfx950 row-swap instructions: v_permlane16_swap / v_permlane32_swap with both operands the
+// same register leave, in every lane, the two values of its pair (lower row first), so all four
+// lanes combine the same operands in the same order and end with identical results.
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float column_max(float x) { return pair32_max(pair16_max(x)); }
+__device__ __forceinline__ float column_sum(float x) { return pair32_sum(pair16_sum(x)); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }

@@ -60,4 +60,8 @@ hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_
 // Largest number of pages per stream the attention kernel stages in LDS.
 constexpr int kMaxStagedBlocks = 4096;
 
+// Dynamic LDS of one chunk-attention workgroup, and the budget it must fit.
+size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int max_cache, int block_size, bool fused);
+constexpr size_t kMaxDynamicLds = 64 * 1024;
+
 }  // namespace pkc

@@ -106,7 +106,8 @@ def test_append_validation(lib, kw, status):
     (dict(pos_len=157), SHAPE),                      # (157 - 1) / 2 < 64 + 16 - 1
     (dict(per_row=1, pos_len=158), SHAPE),           # per-row needs 2 * 80 - 1
     (dict(per_row=2), SHAPE),
-    (dict(D=128), UNSUP), (dict(S=12, M=12), UNSUP),
+    (dict(D=128), UNSUP), (dict(S=12, M=12), UNSUP), (dict(S=24, M=12), UNSUP),
+    (dict(S=4, M=40), UNSUP),
     (dict(max_cache=120), CAP),
     (dict(q=BAD), ALIGN), (dict(pos=BAD), ALIGN), (dict(out=BAD), ALIGN),
 ])
@@ -120,6 +121,10 @@ def test_fused_validation(lib):
     assert fused(lib, k_new=BAD) == ALIGN
     assert fused(lib, max_cache=200) == CAP
     assert fused(lib, pos_len=100) == SHAPE
+    # the fused entry stages the chunk in LDS: long chunks are refused, not launched
+    assert fused(lib, dtype=0, C=40, M=16, pos_len=2 * (64 + 40) - 1) == UNSUP
+    assert fused(lib, C=160, M=16, pos_len=2 * (64 + 160) - 1) == UNSUP
+    assert attn(lib, C=160, M=16, pos_len=2 * (64 + 160) - 1) == UNSUP
 
 
 @pytest.mark.parametrize("kw,status", [
