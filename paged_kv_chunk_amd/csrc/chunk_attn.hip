@@ -386,13 +386,22 @@ chunk_attn_kernel(ChunkArgs<T> a) {
                (uint32_t)((key & (S - 1)) * kD + dv);
       *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s_kt + (key - body_end) * KTP + dv);
     }
-    for (int x = tid; x < 16 * kD; x += kThreads) {
-      const int t = t_lo + (x & 15);
-      const int d = x >> 4;
-      if (t < t_hi) {
-        const int key = cache + t;
-        a.v_pool_w[(size_t)hk * page + (uint64_t)block_of(key >> logS) * blk_stride +
-                   (uint32_t)(d * S + (key & (S - 1)))] = s_vt[d * a.vt_pitch + (key - body_end)];
+    // V: 8-frame groups of one dimension, aligned to the page slots (never across a page: block
+    // sizes are powers of two >= 8); a 16-byte store when all 8 frames belong to this tile
+    const int f_lo = cache + t_lo, f_hi = cache + t_hi;
+    const int g0 = (f_lo >> 3) << 3;
+    const int ngroups = (f_hi - g0 + 7) >> 3;
+    for (int x = tid; x < ngroups * kD; x += kThreads) {
+      const int d = x & (kD - 1);
+      const int kg = g0 + 8 * (x >> 6);
+      T* dst = a.v_pool_w + (size_t)hk * page + (uint64_t)block_of(kg >> logS) * blk_stride +
+               (uint32_t)(d * S + (kg & (S - 1)));
+      const T* src = s_vt + d * a.vt_pitch + (kg - body_end);
+      if (kg >= f_lo && kg + 8 <= f_hi) {
+        store8(dst, load8(src));
+      } else {
+        for (int c = 0; c < 8; ++c)
+          if (kg + c >= f_lo && kg + c < f_hi) dst[c] = src[c];
       }
     }
   }
@@ -440,8 +449,18 @@ template <typename T> constexpr int waves_of() { return 4; }
 
 template <typename T, bool kFused, int kS>
 void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_attn_kernel<T, kFused, waves_of<T>(), kS>), grid,
-                     dim3(waves_of<T>() * 64), smem, stream, a);
+  auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS>;
+  if (smem > 64 * 1024) {
+    // beyond the default dynamic LDS size (long chunks): opt in once; MI355X allows 160 KB per
+    // workgroup
+    static bool opted = false;
+    if (!opted) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynamicLds);
+      opted = true;
+    }
+  }
+  hipLaunchKernelGGL(fn, grid, dim3(waves_of<T>() * 64), smem, stream, a);
 }
 
 template <typename T, bool kFused>

@@ -62,6 +62,6 @@ constexpr int kMaxStagedBlocks = 4096;
 
 // Dynamic LDS of one chunk-attention workgroup, and the budget it must fit.
 size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int max_cache, int block_size, bool fused);
-constexpr size_t kMaxDynamicLds = 64 * 1024;
+constexpr size_t kMaxDynamicLds = 160 * 1024;
 
 }  // namespace pkc

@@ -122,9 +122,9 @@ def test_fused_validation(lib):
     assert fused(lib, max_cache=200) == CAP
     assert fused(lib, pos_len=100) == SHAPE
     # the fused entry stages the chunk in LDS: long chunks are refused, not launched
-    assert fused(lib, dtype=0, C=40, M=16, pos_len=2 * (64 + 40) - 1) == UNSUP
-    assert fused(lib, C=160, M=16, pos_len=2 * (64 + 160) - 1) == UNSUP
-    assert attn(lib, C=160, M=16, pos_len=2 * (64 + 160) - 1) == UNSUP
+    assert fused(lib, dtype=0, C=300, M=32, pos_len=2 * (64 + 300) - 1) == UNSUP
+    assert fused(lib, C=490, M=40, pos_len=2 * (64 + 490) - 1) == UNSUP
+    assert attn(lib, C=490, M=40, pos_len=2 * (64 + 490) - 1) == UNSUP
 
 
 @pytest.mark.parametrize("kw,status", [
