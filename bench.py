@@ -124,6 +124,84 @@ def cpu_baseline(co, min_seconds):
                        f"append + attention in float64 numpy, {el:.1f} s")
 
 
+def varlen_flops(co):
+    """Algorithmic FLOPs of the packed offline attention: per utterance and head, L^2 dot products
+    of length D for each of the content term, the position term and the PV product."""
+    H, D = co.q.shape[1], co.q.shape[2]
+    return sum(6 * L * L * D * H for L in co.lengths)
+
+
+def varlen_bytes(co):
+    """Algorithmic bytes: read q, k, v and each utterance's 2L - 1 table rows, write out."""
+    total, H, D = co.q.shape
+    Hk = co.k.shape[1]
+    eb = co.q.element_size()
+    rows = sum(2 * L - 1 for L in co.lengths if L > 0)
+    return (2 * total * H + 2 * total * Hk) * D * eb + rows * H * D * eb + 2 * H * D * eb
+
+
+def bench_varlen(args, cfg, pkc):
+    """Packed offline attention: time whole calls replayed from HIP graphs over rotated batches."""
+    from synth import make_config
+    sets = [make_config(4, seed=r, device="cuda") for r in range(args.rotate)]
+    for co in sets:
+        co.out = torch.empty_like(co.q)
+    stream = torch.cuda.current_stream()
+
+    def call(co, st):
+        pkc.varlen_packed_relpos_attn(co.q, co.k, co.v, co.cu_seqlens, co.pos, co.pos_bias_u,
+                                      co.pos_bias_v, max(co.lengths), out=co.out, stream=st)
+
+    for co in sets:
+        call(co, stream)
+    torch.cuda.synchronize()
+    graphs = []
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for co in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                call(co, cap)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = sum(varlen_flops(co) for co in sets) / len(sets)
+    nbytes = sum(varlen_bytes(co) for co in sets) / len(sets)
+    units = sum(len(co.lengths) * co.q.shape[1] for co in sets) / len(sets)
+    tflops = flops / (ms / 1e3) / 1e12
+    result = {
+        "metric": "packed offline rel-pos attention utterance·heads/sec + % of bf16 MFMA roofline, 1 GPU",
+        "value": units / (ms / 1e3),
+        "unit": "utterance·heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: {cfg['n_seqs']} utterances, lengths uniform in "
+                               f"[{cfg['len_lo']}, {cfg['len_hi']}], H={cfg['H']}, head_dim={cfg['D']}, "
+                               "per-utterance tables, no cache", "rotated_batches": len(sets),
+                   "launch": "graph"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tflops / 2500.0, "traffic": None,
+                     "kernel": "varlen_attn_kernel<bf16>", "kernel_us": ms * 1e3,
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,8 +250,8 @@ def main():
         return
 
     cfg = CONFIGS[args.config]
-    if cfg["kind"] != "chunk":
-        raise SystemExit("bench.py times the streaming cohort workloads (1, 2 or 3)")
+    if cfg["kind"] == "varlen":
+        return bench_varlen(args, cfg, pkc)
     n_layers = cfg["n_layers"]
     dev = "cuda"
     sets = build_sets(args.config, args.rotate, n_layers, dev)
