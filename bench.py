@@ -40,11 +40,30 @@ METRIC = "paged chunk-attention chunk·heads/sec per layer + % of HBM roofline, 
 HBM_PEAK_GBS = 8000.0
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {
+    "chunk": ["chunk_attn.hip", "pkc_step.h", "pkc_device.h", "pkc_launch.h"],
+    "varlen": ["varlen_attn.hip", "pkc_step.h", "pkc_device.h", "pkc_launch.h"],
+}
+
+
+def kernel_source_hash(kernel="chunk"):
+    """Hash of the sources one kernel is compiled from: stored counter readings are used only
+    while it matches."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_chunk_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, "paged_kv_chunk_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
+
+
+def stored_traffic(key, kernel):
+    """HBM bytes per launch from the committed counter summary, or None once the kernel changed."""
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(tpath):
+        return None
+    rec = json.load(open(tpath)).get(key)
+    if rec and rec.get("source_hash") == kernel_source_hash(kernel):
+        return rec.get("bytes_per_launch")
+    return None
 
 
 def algorithmic_bytes(co):
@@ -193,7 +212,7 @@ def bench_varlen(args, cfg, pkc):
                                "per-utterance tables, no cache", "rotated_batches": len(sets),
                    "launch": "graph"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": tflops / 2500.0, "traffic": None,
+                     "frac": tflops / 2500.0, "traffic": stored_traffic("varlen_cfg4", "varlen"),
                      "kernel": "varlen_attn_kernel<bf16>", "kernel_us": ms * 1e3,
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes,
@@ -324,12 +343,7 @@ def main():
     bytes_per_launch = algorithmic_bytes(co0)
     achieved = bytes_per_launch / (kernel_ms / 1e3) / 1e9
 
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tpath):
-        rec = json.load(open(tpath)).get(f"fused_cfg{args.config}")
-        if rec and rec.get("source_hash") == kernel_source_hash():
-            traffic = rec.get("bytes_per_launch")
+    traffic = stored_traffic(f"fused_cfg{args.config}", "chunk")
 
     result = {
         "metric": METRIC,
