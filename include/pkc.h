@@ -113,8 +113,9 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  * softmax_scale <= 0 selects 1 / sqrt(head_dim).
  * Errors: as paged_kv_append; n_head % n_kv_head != 0 or a table too short -> PKC_ERR_SHAPE;
  * head_dim != 64, block_size not a power of two >= 8, or a chunk too long for the kernel's LDS
- * staging -> PKC_ERR_UNSUPPORTED. The kernel stages up to 31 + chunk_size frames in LDS, which
- * allows chunk_size <= 481 in bf16 and <= 225 in fp32.
+ * staging -> PKC_ERR_UNSUPPORTED. The kernel stages the chunk's chunk_size frames in LDS (the
+ * cached frames stream from the pages), which allows chunk_size <= 512 in bf16 and <= 256 in
+ * fp32.
  */
 pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_tables,

@@ -8,11 +8,11 @@
 //
 // Work decomposition. One workgroup of kWaves wavefronts per (stream b, head h, 16-query tile).
 // The T = cache + C keys split into
-//   * the body, keys [0, body_end) with body_end = cache rounded down to a multiple of 32: whole
-//     32-key steps read straight from the pool pages, no masking;
-//   * the tail, keys [body_end, T) (at most 31 + C keys): staged once into LDS at kernel start -
-//     K rows and V transposed, the chunk's own frames taken from k_new / v_new when fused and from
-//     the pool otherwise, zero past T - and processed as masked steps.
+//   * the body, the cached keys [0, cache): 32-key steps read straight from the pool pages; the
+//     last one is masked when cache is not a multiple of 32 (its V past cache zeroed);
+//   * the tail, the chunk's own frames [cache, T): staged into LDS - K rows and V transposed,
+//     taken from k_new / v_new when fused and from the pool otherwise, zero past T - and
+//     processed as masked steps.
 // The split and the step-to-wave assignment depend only on the cache length, so the fused and the
 // unfused entries do identical arithmetic on identical values.
 // Each wave takes a contiguous range of body steps (so one band tile carries over from step to
@@ -21,13 +21,14 @@
 //
 // Latency. Everything a wave needs is requested before it first waits: the block IDs of the
 // stream's first 128 pages (into a wave-private LDS window, no workgroup barrier), the queries,
-// the band rows and the first two body steps; later steps are fetched two steps ahead into
-// alternating register sets. The chunk's K/V are written into the pool only at the very end: on
-// CDNA global stores share the in-order vector-memory counter with loads, so a store issued
-// early would hold up every later load wait. The softmax scale (and log2 e) is folded into
-// q + u and q + v, and the running max moves only when a score exceeds it by 2^8 (the
-// probabilities stay <= 256, exact after the final division), which keeps the rescale of the
-// accumulator out of most steps.
+// the chunk's frames (short fused chunks), the band rows and the first two body steps; later
+// steps are fetched two steps ahead into alternating register sets, and the band rows of the
+// wave's tail step into the set the body frees last. The chunk's K/V are written into the pool
+// only at the very end: on CDNA global stores share the in-order vector-memory counter with
+// loads, so a store issued early would hold up every later load wait. The softmax scale (and
+// log2 e) is folded into q + u and q + v, and the running max moves only when a score exceeds it
+// by 2^8 (the probabilities stay <= 256, exact after the final division), which keeps the
+// rescale of the accumulator out of most steps.
 //
 // Per 32-key step, with 16x16 MFMA tiles whose columns are the 16 queries:
 //   S^T = K . (q + u)^T          two tiles (32 keys), contraction over head_dim
@@ -87,7 +88,7 @@ struct StepRegs {
 
 template <typename T> constexpr int kt_pitch() { return kD + 16 / (int)sizeof(T); }
 
-template <typename T, bool kFused, int kWaves, int kS>
+template <typename T, bool kFused, int kWaves, int kS, bool kRegTail>
 __global__ void __launch_bounds__(kWaves * 64)
 chunk_attn_kernel(ChunkArgs<T> a) {
   typedef typename Frag<T>::type F;
@@ -121,7 +122,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const int hk = h / (a.H / a.Hk);
   const int32_t* bt = a.bt + (size_t)b * a.M;
 
-  // ---- 1. requests that need nothing: block IDs of pages [0, 128), queries, u, v, cache ------
+  // ---- 1. requests that need nothing: block IDs of pages [0, 128), queries, u, v, chunk -------
   const int nwin = min(a.M, kBtWindow);
   const int bt_lo = lane < nwin ? bt[lane] : 0;
   const int bt_hi = lane + 64 < nwin ? bt[lane + 64] : 0;
@@ -137,18 +138,27 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       ww[half] = load8(a.w + h * kD + d0);
     }
   }
+  // the chunk's own frames (fused, short chunks: one 16-byte vector of K and of V per thread)
+  uint4 nk, nv;
+  if constexpr (kRegTail) {
+    if (tid < a.C * NV) {
+      const size_t row = ((size_t)(b * a.C + tid / NV) * a.Hk + hk) * kD + (tid % NV) * VEC;
+      nk = *reinterpret_cast<const uint4*>(a.k_new + row);
+      nv = *reinterpret_cast<const uint4*>(a.v_new + row);
+    }
+  }
   const int cache = clampi(a.cs[b], 0, a.max_cache);
   const int T_len = cache + a.C;
-  const int body_end = (cache >> 5) << 5;
-  const int pool_end = kFused ? cache : T_len;  // tail keys below this come from the pool
-  const int tail_pad = (T_len - body_end + 31) & ~31;
-  const size_t page = (size_t)S * kD;            // elements of one (block, kv head) page
+  const int nbody = (cache + 31) >> 5;                 // body steps over the cached keys
+  const int s_part = (cache & 31) ? nbody - 1 : -1;    // the partial one, if any
+  const int ntail = (a.C + 31) >> 5;                   // tail steps over the chunk's frames
+  const size_t page = (size_t)S * kD;                  // elements of one (block, kv head) page
   const uint32_t blk_stride = (uint32_t)(a.Hk * S * kD);
   const T* kp = a.k_pool + (size_t)hk * page;
   const T* vp = a.v_pool + (size_t)hk * page;
-  const int nbody = body_end >> 5;
   const int s_begin = (wave * nbody) / kWaves;
   const int s_end = ((wave + 1) * nbody) / kWaves;
+  const int nmine = s_end - s_begin;
 
   const int center = a.per_row ? (T_len - 1) : (a.pos_len - 1) / 2;
   const int R0 = center - cache;
@@ -159,14 +169,30 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const T* ptab = a.pos + (a.per_row ? (size_t)b * a.pos_len * prow : 0) + (size_t)h * kD;
   auto band_row = [&](int r) { return ptab + (size_t)(uint32_t)clampi(r, rlo, rhi) * prow; };
 
-  // the window, and a page's block ID from it (pages past it: straight from the table)
+  // the window, and a page's block ID from it (pages past it: straight from the table). The
+  // masked last body step can reach one page past the stream's table row: such pages read as
+  // block 0 in the window and as the row's last entry past it (their frames are masked).
   s_win[lane] = clampi(bt_lo, 0, a.N - 1);
   s_win[64 + lane] = clampi(bt_hi, 0, a.N - 1);
   auto block_of = [&](int pg) -> uint32_t {
-    return (uint32_t)(pg < kBtWindow ? s_win[pg] : clampi(bt[pg], 0, a.N - 1));
+    return (uint32_t)(pg < kBtWindow ? s_win[pg] : clampi(bt[min(pg, a.M - 1)], 0, a.N - 1));
   };
+  // the chunk's frames into the LDS tail (row t = frame t; V transposed, zero past the chunk)
+  if constexpr (kRegTail) {
+    if (tid < a.C * NV) {
+      const int t = tid / NV;
+      const int dv = (tid % NV) * VEC;
+      *reinterpret_cast<uint4*>(s_kt + t * KTP + dv) = nk;
+      const uint32_t wd[4] = {nv.x, nv.y, nv.z, nv.w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        reinterpret_cast<uint16_t*>(s_vt)[(dv + c) * a.vt_pitch + t] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
+    }
+    for (int x = tid; x < (32 * ntail - a.C) * kD; x += kThreads)
+      s_vt[(x % kD) * a.vt_pitch + a.C + x / kD] = from_f<T>(0.f);
+  }
 
-  // ---- 2. body loads of the first two steps (band tile 0 of the first step too) ----------------
+  // ---- 2. loads of the first two body steps (band tile 0 of the first one too) ----------------
   auto load_step = [&](StepRegs<T>& r, int s) {
     const int j0 = 32 * s;
     const int key = j0 + 8 * (m16 >> 2) + (m16 & 3);          // key of tile 0; tile 1 is key + 4
@@ -189,54 +215,72 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       r.p[t][1] = load8(row + 32);
     }
   };
+  // band tiles of this wave's first tail step, into a register set the body no longer needs
+  // (tiles 0, 1, 2 in k[0], p[0], p[1]): the tail step then waits on nothing
+  auto load_tail_band = [&](StepRegs<T>& r) {
+    if (wave < ntail) {
+      const int rb = R0 + cache + 32 * wave - qlast;
+      F* dst[3] = {r.k[0], r.p[0], r.p[1]};
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
+        dst[t][0] = load8(row);
+        dst[t][1] = load8(row + 32);
+      }
+    }
+  };
   StepRegs<T> ra, rb2;
   F p0[2];
-  if (s_begin < s_end) {
+  if (nmine > 0) {
     const T* row = band_row(R0 + 32 * s_begin - qlast + m16) + 8 * grp;
     p0[0] = load8(row);
     p0[1] = load8(row + 32);
     load_step(ra, s_begin);
-    if (s_begin + 1 < s_end) load_step(rb2, s_begin + 1);
+    if (nmine > 1) load_step(rb2, s_begin + 1);
+    else load_tail_band(rb2);
+  } else {
+    load_tail_band(ra);
   }
 
-  // ---- 3. tail keys [body_end, T) into LDS: K rows and V transposed, zero V past T ------------
-  for (int x = tid; x < tail_pad * NV; x += kThreads) {
-    const int r = x / NV;
-    const int dv = (x % NV) * VEC;
-    const int key = body_end + r;
-    if (key < T_len) {
-      const T* src;
-      if (key < pool_end) {
-        src = kp + (uint64_t)block_of(key >> logS) * blk_stride + (uint32_t)((key & (S - 1)) * kD + dv);
-      } else {
-        src = a.k_new + ((size_t)(b * a.C + key - cache) * a.Hk + hk) * kD + dv;
+  // ---- 3. long chunks: the chunk's frames into the LDS tail with a loop ------------------------
+  // (from k_new / v_new when fused, else from the pool, where an earlier append put them)
+  if constexpr (!kRegTail) {
+    for (int x = tid; x < 32 * ntail * NV; x += kThreads) {
+      const int t = x / NV;
+      const int dv = (x % NV) * VEC;
+      if (t < a.C) {
+        const int key = cache + t;
+        const T* src = kFused ? a.k_new + ((size_t)(b * a.C + t) * a.Hk + hk) * kD + dv
+                              : kp + (uint64_t)block_of(key >> logS) * blk_stride +
+                                    (uint32_t)((key & (S - 1)) * kD + dv);
+        *reinterpret_cast<uint4*>(s_kt + t * KTP + dv) = *reinterpret_cast<const uint4*>(src);
       }
-      *reinterpret_cast<uint4*>(s_kt + r * KTP + dv) = *reinterpret_cast<const uint4*>(src);
     }
-  }
-  for (int x = tid; x < tail_pad * NV; x += kThreads) {
-    const int r = x / NV;
-    const int dv = (x % NV) * VEC;
-    const int key = body_end + r;
-    if (key >= pool_end && key < T_len) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(
-          a.v_new + ((size_t)(b * a.C + key - cache) * a.Hk + hk) * kD + dv);
-      const T* e = reinterpret_cast<const T*>(&raw);
+    for (int x = tid; x < 32 * ntail * NV; x += kThreads) {
+      const int t = x / NV;
+      const int dv = (x % NV) * VEC;
+      if (kFused && t < a.C) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(
+            a.v_new + ((size_t)(b * a.C + t) * a.Hk + hk) * kD + dv);
+        const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) s_vt[(dv + k) * a.vt_pitch + r] = e[k];
-    } else if (key >= T_len) {
+        for (int k = 0; k < VEC; ++k) s_vt[(dv + k) * a.vt_pitch + t] = e[k];
+      } else if (t >= a.C) {
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) s_vt[(dv + k) * a.vt_pitch + r] = from_f<T>(0.f);
+        for (int k = 0; k < VEC; ++k) s_vt[(dv + k) * a.vt_pitch + t] = from_f<T>(0.f);
+      }
     }
-  }
-  // pool keys of the tail element by element from the transposed pages (thread column
-  // r = tid % 32 of every 32-key group, dimensions d = tid / 32 + 8 n)
-  for (int c0 = 0; c0 < pool_end - body_end; c0 += 32) {
-    const int r = c0 + (tid & 31);
-    const int key = body_end + r;
-    if (key < pool_end) {
-      const T* src = vp + (uint64_t)block_of(key >> logS) * blk_stride + (uint32_t)(key & (S - 1));
-      for (int d = tid >> 5; d < kD; d += kThreads / 32) s_vt[d * a.vt_pitch + r] = src[d * S];
+    if (!kFused) {
+      // frames from the transposed pages, element by element (thread column t = tid % 32 of
+      // every 32-frame group, dimensions d = tid / 32 + 8 n)
+      for (int c0 = 0; c0 < a.C; c0 += 32) {
+        const int t = c0 + (tid & 31);
+        if (t < a.C) {
+          const int key = cache + t;
+          const T* src = vp + (uint64_t)block_of(key >> logS) * blk_stride + (uint32_t)(key & (S - 1));
+          for (int d = tid >> 5; d < kD; d += kThreads / 32) s_vt[d * a.vt_pitch + t] = src[d * S];
+        }
+      }
     }
   }
 
@@ -258,7 +302,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (s_begin < s_end) {
+  if (nmine > 0) {
     floatx4 g_prev = mma(p0[0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
     g_prev = mma(p0[1], qv[1], g_prev);
     auto run = [&](StepRegs<T>& r, int s) {
@@ -266,9 +310,17 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       g1 = mma(r.p[0][1], qv[1], g1);
       floatx4 g2 = mma(r.p[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
       g2 = mma(r.p[1][1], qv[1], g2);
-      step_compute<T, false>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, 32);
+      if (s == s_part) {
+        // the last cached page is partly filled: frames at or past cache are excluded, and
+        // their V is zeroed (the slots may hold anything)
+        zero_from(r.v, cache - (32 * s + 8 * grp));
+        step_compute<T, true>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, cache - 32 * s);
+      } else {
+        step_compute<T, false>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, 32);
+      }
       g_prev = g2;
       if (s + 2 < s_end) load_step(r, s + 2);
+      else if (s + 2 == s_end) load_tail_band(r);
     };
     for (int s = s_begin; s < s_end; s += 2) {
       run(ra, s);
@@ -276,11 +328,11 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     }
   }
 
-  // ---- 5. tail steps from LDS (the one workgroup barrier: the tail was staged by all threads;
-  // body steps above use only the wave's own registers and LDS) ---------------------------------
+  // ---- 5. tail steps over the chunk's frames, from LDS (the one workgroup barrier: the tail was
+  // staged by all threads; body steps above use only the wave's own registers and LDS) ---------
   __syncthreads();
-  for (int k = wave; k < (tail_pad >> 5); k += kWaves) {
-    const int j0 = body_end + 32 * k;
+  for (int k = wave; k < ntail; k += kWaves) {
+    const int j0 = cache + 32 * k;
     F kf[2][2], vf[4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -290,15 +342,31 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(s_vt + (16 * dt + m16) * a.vt_pitch + 32 * k + 8 * grp);
-    const int rb = R0 + j0 - qlast;
+    F pb[3][2];
+    if (k == wave) {
+      // prefetched: in the register set the body left free (ra after an even number of body
+      // steps, rb2 after an odd one)
+      const StepRegs<T>& r = (nmine & 1) ? rb2 : ra;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        pb[0][half] = r.k[0][half];
+        pb[1][half] = r.p[0][half];
+        pb[2][half] = r.p[1][half];
+      }
+    } else {
+      const int rb = R0 + j0 - qlast;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
+        pb[t][0] = load8(row);
+        pb[t][1] = load8(row + 32);
+      }
+    }
     floatx4 g[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
-      const F p_lo = load8(row);
-      const F p_hi = load8(row + 32);
-      g[t] = mma(p_lo, qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-      g[t] = mma(p_hi, qv[1], g[t]);
+      g[t] = mma(pb[t][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      g[t] = mma(pb[t][1], qv[1], g[t]);
     }
     step_compute<T, true>(st, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
   }
@@ -315,10 +383,10 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       const int key = cache + t;
       T* dst = a.k_pool_w + (size_t)hk * page + (uint64_t)block_of(key >> logS) * blk_stride +
                (uint32_t)((key & (S - 1)) * kD + dv);
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s_kt + (key - body_end) * KTP + dv);
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s_kt + t * KTP + dv);
     }
     // V: 8-frame groups of one dimension, aligned to the page slots (never across a page: block
-    // sizes are powers of two >= 8); a 16-byte store when all 8 frames belong to this tile
+    // sizes are powers of two >= 8); one 16-byte store when all 8 frames belong to this tile
     const int f_lo = cache + t_lo, f_hi = cache + t_hi;
     const int g0 = (f_lo >> 3) << 3;
     const int ngroups = (f_hi - g0 + 7) >> 3;
@@ -327,12 +395,15 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       const int kg = g0 + 8 * (x >> 6);
       T* dst = a.v_pool_w + (size_t)hk * page + (uint64_t)block_of(kg >> logS) * blk_stride +
                (uint32_t)(d * S + (kg & (S - 1)));
-      const T* src = s_vt + d * a.vt_pitch + (kg - body_end);
+      const T* row = s_vt + d * a.vt_pitch;
       if (kg >= f_lo && kg + 8 <= f_hi) {
-        store8(dst, load8(src));
+        F v8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) set(v8, c, to_f(row[kg + c - cache]));
+        store8(dst, v8);
       } else {
         for (int c = 0; c < 8; ++c)
-          if (kg + c >= f_lo && kg + c < f_hi) dst[c] = src[c];
+          if (kg + c >= f_lo && kg + c < f_hi) dst[c] = row[kg + c - cache];
       }
     }
   }
@@ -378,9 +449,9 @@ chunk_attn_kernel(ChunkArgs<T> a) {
 // assignment and merge order, and with them its result bits, depend on its own length only.
 template <typename T> constexpr int waves_of() { return 4; }
 
-template <typename T, bool kFused, int kS>
+template <typename T, bool kFused, int kS, bool kRegTail>
 void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
-  auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS>;
+  auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail>;
   if (smem > 64 * 1024) {
     // beyond the default dynamic LDS size (long chunks): opt in once; MI355X allows 160 KB per
     // workgroup
@@ -398,11 +469,20 @@ template <typename T, bool kFused>
 void launch_s(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
   // the block sizes of the streaming workloads get constant page geometry; fp32 (used for
   // checking) always takes the general instantiation
-  if constexpr (sizeof(T) == 2) {
-    if (a.S == 16) return launch_inst<T, kFused, 16>(a, grid, smem, stream);
-    if (a.S == 32) return launch_inst<T, kFused, 32>(a, grid, smem, stream);
+  // fused bf16 chunks of at most 32 frames: the chunk's K and V are one 16-byte vector each per
+  // thread, requested at kernel start and held in registers
+  if constexpr (sizeof(T) == 2 && kFused) {
+    if (a.C <= 32) {
+      if (a.S == 16) return launch_inst<T, kFused, 16, true>(a, grid, smem, stream);
+      if (a.S == 32) return launch_inst<T, kFused, 32, true>(a, grid, smem, stream);
+      return launch_inst<T, kFused, 0, true>(a, grid, smem, stream);
+    }
   }
-  launch_inst<T, kFused, 0>(a, grid, smem, stream);
+  if constexpr (sizeof(T) == 2) {
+    if (a.S == 16) return launch_inst<T, kFused, 16, false>(a, grid, smem, stream);
+    if (a.S == 32) return launch_inst<T, kFused, 32, false>(a, grid, smem, stream);
+  }
+  launch_inst<T, kFused, 0, false>(a, grid, smem, stream);
 }
 
 template <typename T>
@@ -433,7 +513,7 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   a.pos_len = p.pos_len;
   a.per_row = p.pos_per_row;
   a.qtiles = (p.chunk + 15) / 16;
-  a.tail_cap = ((31 + p.chunk + 31) / 32) * 32;
+  a.tail_cap = ((p.chunk + 31) / 32) * 32;
   a.vt_pitch = a.tail_cap + 16 / (int)sizeof(T);
   constexpr int kWaves = waves_of<T>();
   size_t off = (size_t)kWaves * kWaveLds * sizeof(float);
@@ -454,7 +534,7 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
 }  // namespace
 
 size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int, int, bool) {
-  const int tail_cap = ((31 + chunk + 31) / 32) * 32;
+  const int tail_cap = ((chunk + 31) / 32) * 32;
   const int vec = 16 / dtype_bytes;
   const int waves = dtype_bytes == 2 ? waves_of<bf16>() : waves_of<float>();
   return (size_t)waves * kWaveLds * 4 + (size_t)waves * kBtWindow * 4 +

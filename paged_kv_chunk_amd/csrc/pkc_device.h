@@ -59,6 +59,25 @@ template <typename T> __device__ __forceinline__ typename Frag<T>::type zero8() 
   return v;
 }
 
+// Zero the elements at positions >= n (any n; <= 0 clears all, >= 8 keeps all) of four
+// fragments. bf16 works on whole 32-bit words, so nothing is unpacked.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void zero_from(bf16x8 (&v)[4], int n) {
+  u32x4 keep;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    keep[w] = (2 * w < n ? 0x0000ffffu : 0u) | (2 * w + 1 < n ? 0xffff0000u : 0u);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    v[dt] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v[dt]) & keep);
+}
+__device__ __forceinline__ void zero_from(f32x8 (&v)[4], int n) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) set(v[dt], e, e < n ? get(v[dt], e) : 0.f);
+}
+
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return (T)x; }

@@ -121,10 +121,11 @@ def test_fused_validation(lib):
     assert fused(lib, k_new=BAD) == ALIGN
     assert fused(lib, max_cache=200) == CAP
     assert fused(lib, pos_len=100) == SHAPE
-    # the fused entry stages the chunk in LDS: long chunks are refused, not launched
-    assert fused(lib, dtype=0, C=300, M=32, pos_len=2 * (64 + 300) - 1) == UNSUP
-    assert fused(lib, C=490, M=40, pos_len=2 * (64 + 490) - 1) == UNSUP
-    assert attn(lib, C=490, M=40, pos_len=2 * (64 + 490) - 1) == UNSUP
+    # the chunk is staged in LDS: chunks past 512 frames (bf16) / 256 (fp32) are refused, not
+    # launched
+    assert fused(lib, dtype=0, C=257, M=32, pos_len=2 * (64 + 257) - 1) == UNSUP
+    assert fused(lib, C=513, M=40, pos_len=2 * (64 + 513) - 1) == UNSUP
+    assert attn(lib, C=513, M=40, pos_len=2 * (64 + 513) - 1) == UNSUP
 
 
 @pytest.mark.parametrize("kw,status", [

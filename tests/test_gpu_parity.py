@@ -67,6 +67,16 @@ SMALL = {
                                 dtype=F32, per_row_pos=True, pos_noise=0.5),
     "odd_lengths": dict(B=4, H=2, D=64, C=13, block_size=8, cache_seqlens=[5, 11, 1, 90],
                         dtype=BF16),
+    # the largest tail the register-held staging takes (31 pool keys + 32 chunk frames) ...
+    "chunk32_full_tail": dict(B=3, H=2, D=64, C=32, block_size=16, cache_seqlens=[31, 63, 0],
+                              dtype=BF16),
+    # ... and bf16 chunks past it, staged by the loop
+    "long_chunk_bf16": dict(B=3, H=2, D=64, C=80, block_size=16, cache_seqlens=[45, 128, 0],
+                            dtype=BF16),
+    # the longest chunks the LDS staging takes (dynamic LDS past 64 KB)
+    "max_chunk_bf16": dict(B=2, H=2, D=64, C=512, block_size=32, cache_seqlens=[40, 0],
+                           dtype=BF16),
+    "max_chunk_fp32": dict(B=1, H=2, D=64, C=256, block_size=16, cache_seqlens=[77], dtype=F32),
 }
 
 
@@ -112,7 +122,8 @@ def test_attention_parity_small(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_ragged", "two_tiles_per_row", "gqa_h4_k2", "odd_lengths",
-                                  "per_row_ragged_fp32"])
+                                  "per_row_ragged_fp32", "chunk32_full_tail", "long_chunk_bf16",
+                                  "max_chunk_bf16"])
 def test_fused_equals_append_then_attend(name):
     """The fused entry writes the same pool bits and produces the same output bits (both entries
     split the keys and assign them to waves by the cache length alone)."""
