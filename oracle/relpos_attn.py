@@ -44,11 +44,14 @@ DEFAULT_LAYOUT = {"k_pool": "[num_blocks, n_kv_head, block_size, head_dim]",
                   "v_pool": "[num_blocks, n_kv_head, head_dim, block_size]"}
 
 
-def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens):
+def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens, chunk_lens=None):
     """Write each stream's chunk K/V into its pages ("ASR Engine" section 4.3, steps 1 and 5).
 
     k_new, v_new: [B, C, Hk, D]. Frame t of the chunk of stream b is logical frame
     L = cache_seqlens[b] + t, stored in block block_tables[b, L // S] at slot L % S.
+    ``chunk_lens`` (default: C for every stream) gives each stream's real frames n_b <= C: only
+    frames t < n_b are written ("ASR Engine" section 4.3 step 6: a stream commits its actual
+    frames; the final window is short). A stream with n_b = 0 (the padding lane) writes nothing.
     Returns new pools; every element that is not written is copied unchanged. Works on any dtype
     (pass integer views of the storage to compare bit patterns).
     """
@@ -57,7 +60,8 @@ def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens):
     n_streams, chunk = k_new.shape[0], k_new.shape[1]
     block_size = k_pool.shape[2]
     for b in range(n_streams):
-        for t in range(chunk):
+        n_real = chunk if chunk_lens is None else int(chunk_lens[b])
+        for t in range(n_real):
             frame = int(cache_seqlens[b]) + t
             block = int(block_tables[b, frame // block_size])
             slot = frame % block_size
@@ -122,14 +126,22 @@ def _attend(q, k, v, pos_rows, u, w, center, cache, scale, query_rows=None):
 
 
 def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u, pos_bias_v,
-                      per_row_pos=False, scale=None, return_probs=False, streams=None):
+                      per_row_pos=False, scale=None, return_probs=False, streams=None,
+                      chunk_lens=None):
     """Chunk attention of every stream over its cached frames plus its own chunk.
 
     q: [B, C, H, D]. The chunk's K/V must already be in the pools (append first, then attend).
     pos: one shared table [P, H, D] centred at (P - 1) / 2, or per-row tables [B, P_max, H, D],
-    row b centred at T_b - 1 with 2 T_b - 1 meaningful rows. pos_bias_u, pos_bias_v: [H, D].
-    Returns out [B, C, H, D] in float64 (and the per-stream probabilities when asked).
-    ``streams`` (default: all) restricts the work to a sample of streams; other rows are NaN.
+    row b centred at T_b - 1 with 2 T_b - 1 meaningful rows, T_b = c_b + C. pos_bias_u,
+    pos_bias_v: [H, D]. Returns out [B, C, H, D] in float64 (and the per-stream probabilities
+    when asked). ``streams`` (default: all) restricts the work to a sample of streams; other rows
+    are NaN.
+
+    ``chunk_lens`` (default: C for every stream) gives each stream's real frames n_b <= C (a short
+    final window, "ASR Engine" section 4.3 step 6 and section 8; a padding lane has n_b = 0,
+    "ASR Engine" section 9). Reading: frames t >= n_b do not exist, so query i < n_b attends over
+    keys j < c_b + n_b, and output rows i >= n_b are zero. Tables keep the geometry of the full
+    chunk width (a per-row table stays centred at c_b + C - 1).
     """
     q = np.asarray(q, dtype=np.float64)
     u = np.asarray(pos_bias_u, dtype=np.float64)
@@ -141,19 +153,24 @@ def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_b
     all_probs = []
     for b in (range(n_streams) if streams is None else streams):
         cache = int(cache_seqlens[b])
-        n_k = cache + chunk
+        n_real = chunk if chunk_lens is None else int(chunk_lens[b])
+        out[b] = 0.0
+        if n_real == 0:
+            all_probs.append(np.zeros((q.shape[2], 0, cache)))
+            continue
+        n_k = cache + n_real
         k, v = gather_stream(k_pool, v_pool, block_tables[b], n_k)
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
         if per_row_pos:
-            center = n_k - 1
-            rows = np.asarray(pos[b][: 2 * n_k - 1], dtype=np.float64)
+            center = cache + chunk - 1
+            rows = np.asarray(pos[b][: 2 * (cache + chunk) - 1], dtype=np.float64)
         else:
             if pos.shape[0] % 2 != 1:
                 raise ValueError("a shared relative-position table has an odd number of rows")
             center = (pos.shape[0] - 1) // 2
             rows = np.asarray(pos, dtype=np.float64)
-        out[b], probs = _attend(q[b], k, v, rows, u, w, center, cache, scale)
+        out[b, :n_real], probs = _attend(q[b, :n_real], k, v, rows, u, w, center, cache, scale)
         all_probs.append(probs)
     if return_probs:
         return out, all_probs

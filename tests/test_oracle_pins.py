@@ -426,3 +426,105 @@ def test_planted_mistakes_are_caught(monkeypatch, slip):
     # the mirrored distance needs a table long enough on both sides to stay in range
     brute, dense = _pin_errors(margin=30 if slip == "sign" else 3)
     assert max(brute, dense) > 1e-6, (brute, dense)
+
+
+# --------------------------------------------------------------------------------------------
+# Per-row chunk lengths (a short final window) and the padding lane
+# --------------------------------------------------------------------------------------------
+
+def _short_final_window(seed, lens, C=4, H=2, Hk=1, D=8, S=4, per_row=False):
+    """Stream one utterance chunk by chunk; step k carries lens[k] <= C real frames, padded to C
+    with NaN (in q, k_new and v_new alike, so any use of a padded frame shows). Returns the real
+    frames' outputs, the padded rows' outputs, the final pools and the dense reference."""
+    rng = np.random.default_rng(seed)
+    n = sum(lens)
+    q_all = rng.standard_normal((n, H, D))
+    k_all = rng.standard_normal((n, Hk, D))
+    v_all = rng.standard_normal((n, Hk, D))
+    u = 0.5 * rng.standard_normal((H, D))
+    w = 0.5 * rng.standard_normal((H, D))
+    proj = relpos_projection(H * D, torch.Generator().manual_seed(seed))
+    pages = (len(lens) * C + S - 1) // S
+    bt = rng.permutation(pages + 2)[None, :pages]
+    kp = np.full((pages + 2, Hk, S, D), np.nan)
+    vp = np.full((pages + 2, Hk, D, S), np.nan)
+    real, pad = [], []
+    c = 0
+    for m in lens:
+        def padded(x):
+            y = np.full((C,) + x.shape[1:], np.nan)
+            y[:m] = x[c:c + m]
+            return y[None]
+        cl = np.array([m])
+        kp, vp = oracle.paged_kv_append(kp, vp, padded(k_all), padded(v_all), bt, np.array([c]), cl)
+        table = descending_table(c + C - 1, proj, H, D).numpy()       # built for the full width
+        pos = table[None] if per_row else table
+        o = oracle.chunk_relpos_attn(padded(q_all), kp, vp, bt, np.array([c]), pos, u, w,
+                                     per_row_pos=per_row, chunk_lens=cl)[0]
+        real.append(o[:m])
+        pad.append(o[m:])
+        c += m
+    # dense reference over the real frames only: chunk k holds frames [k C, k C + lens[k]), so
+    # the block-causal mask is by step index, not by frame // C
+    step_of = np.concatenate([np.full(m, k) for k, m in enumerate(lens)])
+    t = np.arange(n)
+    dist = t[:, None] - t[None, :]
+    emb = embed_distances(dist.reshape(-1), proj, H, D).numpy().reshape(n, n, H, D)
+    dense = np.zeros((n, H, D))
+    for h in range(H):
+        g = h * Hk // H
+        bias = np.einsum("td,tjd->tj", q_all[:, h] + w[h], emb[:, :, h]) / math.sqrt(D)
+        bias = np.where(step_of[None, :] <= step_of[:, None], bias, -np.inf)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q_all[:, h] + u[h])[None], torch.from_numpy(k_all[:, g])[None],
+            torch.from_numpy(v_all[:, g])[None], attn_mask=torch.from_numpy(bias)[None])
+        dense[:, h] = ref[0].numpy()
+    return np.concatenate(real), pad, kp, vp, bt, dense
+
+
+@pytest.mark.parametrize("per_row", [False, True])
+def test_short_final_window_equals_dense_attention_over_real_frames(per_row):
+    """Full chunks then a short final window (and a short middle one): the real frames' outputs
+    equal dense block-causal attention over the frames that exist, padded frames are never read
+    (they are NaN), padded output rows are zero, and nothing is written past the real frames."""
+    lens = [4, 4, 2, 4, 3]
+    real, pad, kp, vp, bt, dense = _short_final_window(31, lens, per_row=per_row)
+    assert np.abs(real - dense).max() < 1e-12
+    for p in pad:
+        assert (p == 0).all()
+    # the pool holds exactly the sum(lens) real frames; every other slot is still NaN
+    S = kp.shape[2]
+    n = sum(lens)
+    written = np.zeros(kp.shape[0] * S, dtype=bool)
+    for t in range(n):
+        written[bt[0, t // S] * S + t % S] = True
+    slots_k = ~np.isnan(kp).all(axis=(1, 3)).reshape(-1)
+    assert (slots_k == written).all()
+
+
+def test_padding_lane_is_inert():
+    """A row with chunk length 0 (the padding lane, its table pointing only at a scratch block)
+    appends nothing, outputs zeros, and leaves every other row's output unchanged."""
+    case = _random_streaming_case(41, [4, 9, 2])
+    base = _oracle(case)
+    B = len(case["cs"])
+    scratch = case["kp"].shape[0]
+    kp = np.concatenate([case["kp"], np.full((1,) + case["kp"].shape[1:], np.nan)])
+    vp = np.concatenate([case["vp"], np.full((1,) + case["vp"].shape[1:], np.nan)])
+    bt = np.concatenate([case["bt"], np.full((1, case["bt"].shape[1]), scratch)])
+    cs = np.concatenate([case["cs"], [5]])
+    q = np.concatenate([case["q"], np.full((1,) + case["q"].shape[1:], np.nan)])
+    lens = np.array([case["C"]] * B + [0])
+    junk = np.full((B + 1, case["C"], case["Hk"], case["D"]), np.nan)
+    kp2, vp2 = oracle.paged_kv_append(kp, vp, junk, junk, bt, cs, np.array([0] * (B + 1)))
+    np.testing.assert_array_equal(kp2, kp)
+    out = oracle.chunk_relpos_attn(q, kp, vp, bt, cs, case["table"], case["u"], case["w"],
+                                   chunk_lens=lens)
+    np.testing.assert_array_equal(out[:B], base)
+    assert (out[B] == 0).all()
+
+
+def test_chunk_lens_of_full_width_change_nothing():
+    case = _random_streaming_case(43, [0, 5, 11])
+    lens = np.full(len(case["cs"]), case["C"])
+    np.testing.assert_array_equal(_oracle(case, chunk_lens=lens), _oracle(case))
