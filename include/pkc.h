@@ -22,6 +22,9 @@
  *   [MOD surf] "Model Layer", "The engine-facing surface": forward_chunk_paged (streaming chunk
  *              entry), forward_offline_packed (gapless varlen offline forward), n_kv_head and
  *              head_dim (paged-streaming geometry).
+ *   [ENG 9]    "ASR Engine", section 4.3 step 6 and sections 8-9: each stream commits its actual
+ *              frames (a final window may be short); a cohort is padded to a wider graph shape
+ *              through a padding lane whose rows compute only for themselves.
  *
  * Score of chunk query i (absolute position cache + i) against key j (0 <= j < cache + C):
  *     s[i][j] = ((q_i + u) . k_j + (q_i + v) . p[cache + i - j]) * softmax_scale
@@ -37,19 +40,27 @@
  *   block_tables    int32 [B, M]             logical frame t of stream b is in block
  *                                            block_tables[b][t / S], slot t % S
  *   cache_seqlens   int32 [B]                frames cached before this chunk
+ *   chunk_lens      int32 [B] or NULL        real frames n_b <= C of each stream's chunk (NULL:
+ *                                            every stream has C). Reading of [ENG 9]: frames
+ *                                            t >= n_b do not exist - they are not appended, are
+ *                                            not keys, and their output rows are zero. n_b = 0
+ *                                            is a padding lane: nothing of it is read or written
+ *                                            but its zero output rows
  *   pos_bias_u, _v  [H, D]
  *   pos (shared)    [pos_len, H, D]          row r holds distance (pos_len - 1) / 2 - r
  *   pos (per row)   [B, pos_len, H, D]       stream b's table: rows [0, 2 T_b - 1), centred at
- *                                            T_b - 1 (T_b = cache_seqlens[b] + C); rows past
+ *                                            T_b - 1 (T_b = cache_seqlens[b] + C, the full
+ *                                            chunk width whatever chunk_lens says); rows past
  *                                            that are never read
  * Query head h reads kv head h / (H / Hk). Element type: fp32 or bf16 for every floating-point
  * buffer of a call; accumulation is fp32 either way; bf16 outputs are rounded to nearest even.
  *
  * Device-side preconditions (not checkable on the host without a synchronisation):
  *   0 <= cache_seqlens[b] <= max_cache_seqlen; block_tables[b][t / S] in [0, N) for every
- *   t < cache_seqlens[b] + C; no two streams own the same page. Kernels clamp cache lengths and
- *   block IDs into range, so a violation gives unspecified values but never an out-of-bounds access.
- *   Table entries past a stream's last page are never read.
+ *   t < cache_seqlens[b] + n_b; no two streams own the same page. Kernels clamp cache lengths,
+ *   chunk lengths and block IDs into range, so a violation gives unspecified values but never an
+ *   out-of-bounds access. Table entries past a stream's last page may be read (up to 32 frames
+ *   past its cached frames, inside its table row); their frames are masked, never used.
  */
 #ifndef PKC_H
 #define PKC_H
@@ -84,18 +95,19 @@ const char* pkc_status_string(int status);
 /*
  * paged_kv_append - write each stream's new chunk K/V into its pages [ENG 4.3].
  *
- * For b < batch and t < chunk_size, with L = cache_seqlens[b] + t:
+ * For b < batch and t < n_b (chunk_lens[b], or chunk_size when chunk_lens is NULL), with
+ * L = cache_seqlens[b] + t:
  *     k_pool[block_tables[b][L / S]][g][L % S][:] = k_new[b][t][g][:]
  *     v_pool[block_tables[b][L / S]][g][:][L % S] = v_new[b][t][g][:]
  * for every kv head g. No other pool element is touched; the copy is bit-exact. The caller then
- * runs the attention and afterwards advances cache_seqlens by chunk_size itself.
+ * runs the attention and afterwards advances cache_seqlens by n_b itself.
  * Errors: NULL pointers -> PKC_ERR_NULL; non-positive sizes or head_dim not a multiple of 8 ->
  * PKC_ERR_SHAPE; max_cache_seqlen + chunk_size > max_blocks_per_seq * block_size ->
  * PKC_ERR_CAPACITY (the analogue of the pool/table ceiling errors of [ENG 6]).
  */
 pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new, void* k_pool,
                            void* v_pool, const int32_t* block_tables, const int32_t* cache_seqlens,
-                           int32_t batch, int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
+                           const int32_t* chunk_lens, int32_t batch, int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_cache_seqlen, hipStream_t stream);
 
@@ -104,8 +116,9 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  * [MOD fix], as called once per layer inside forward_chunk_paged [MOD surf].
  *
  * The chunk's K/V must already be in the pools (paged_kv_append first). For every stream b,
- * head h and chunk query i < chunk_size, attends over the T_b = cache_seqlens[b] + chunk_size
- * frames of stream b read through block_tables, and writes out[b][i][h][:].
+ * head h and chunk query i < n_b, attends over the cache_seqlens[b] + n_b frames of stream b
+ * read through block_tables, and writes out[b][i][h][:]; rows i >= n_b are written as zero
+ * (n_b = chunk_lens[b], or chunk_size when chunk_lens is NULL).
  * pos_per_row = 0: pos is one shared table of pos_len rows (pos_len odd and
  *   (pos_len - 1) / 2 >= max_cache_seqlen + chunk_size - 1), indexed by distance around its centre.
  * pos_per_row = 1: pos holds one table per stream, pos_len rows apart
@@ -119,7 +132,8 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  */
 pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_tables,
-                                   const int32_t* cache_seqlens, const void* pos, int32_t pos_len,
+                                   const int32_t* cache_seqlens, const int32_t* chunk_lens,
+                                   const void* pos, int32_t pos_len,
                                    int32_t pos_per_row, const void* pos_bias_u,
                                    const void* pos_bias_v, void* out, int32_t batch,
                                    int32_t chunk_size, int32_t n_head, int32_t n_kv_head,
@@ -137,7 +151,8 @@ pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k
 pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const void* k_new,
                                        const void* v_new, void* k_pool, void* v_pool,
                                        const int32_t* block_tables, const int32_t* cache_seqlens,
-                                       const void* pos, int32_t pos_len, int32_t pos_per_row,
+                                       const int32_t* chunk_lens, const void* pos, int32_t pos_len,
+                                       int32_t pos_per_row,
                                        const void* pos_bias_u, const void* pos_bias_v, void* out,
                                        int32_t batch, int32_t chunk_size, int32_t n_head,
                                        int32_t n_kv_head, int32_t head_dim, int32_t block_size,

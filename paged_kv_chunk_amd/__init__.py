@@ -27,13 +27,13 @@ _f32 = ctypes.c_float
 SIGNATURES = {
     "pkc_version": ([], ctypes.c_int),
     "pkc_status_string": ([ctypes.c_int], ctypes.c_char_p),
-    "paged_kv_append": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr] + [_i32] * 8 + [_ptr],
-                        ctypes.c_int),
-    "chunk_paged_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _ptr,
-                                 _ptr, _ptr] + [_i32] * 9 + [_f32, _ptr], ctypes.c_int),
+    "paged_kv_append": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr] + [_i32] * 8
+                        + [_ptr], ctypes.c_int),
+    "chunk_paged_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _i32, _i32,
+                                 _ptr, _ptr, _ptr] + [_i32] * 9 + [_f32, _ptr], ctypes.c_int),
     "paged_kv_append_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
-                                     _i32, _i32, _ptr, _ptr, _ptr] + [_i32] * 9 + [_f32, _ptr],
-                                    ctypes.c_int),
+                                     _ptr, _i32, _i32, _ptr, _ptr, _ptr] + [_i32] * 9
+                                    + [_f32, _ptr], ctypes.c_int),
     "varlen_packed_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _ptr,
                                    _ptr, _ptr, _ptr, _i32, _i32, _i32, _f32, _ptr], ctypes.c_int),
 }
@@ -97,8 +97,10 @@ def _p(t):
 
 
 def _table(t):
+    if t is None:
+        return None
     if t.dtype != torch.int32:
-        raise TypeError("block tables, cache lengths and offsets are int32")
+        raise TypeError("block tables, cache lengths, chunk lengths and offsets are int32")
     return _p(t)
 
 
@@ -108,21 +110,23 @@ def _stream(stream):
 
 
 def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, max_cache_seqlen,
-                    stream=None):
-    """Write k_new / v_new [B, C, Hk, D] into k_pool [N, Hk, S, D] / v_pool [N, Hk, D, S]."""
+                    chunk_lens=None, stream=None):
+    """Write k_new / v_new [B, C, Hk, D] into k_pool [N, Hk, S, D] / v_pool [N, Hk, D, S]
+    (only the first chunk_lens[b] frames of stream b when chunk_lens is given)."""
     B, C, Hk, D = k_new.shape
     N, _, S, _ = k_pool.shape
     st = lib().paged_kv_append(_dtype(k_new, v_new, k_pool, v_pool), _p(k_new), _p(v_new),
                                _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
-                               B, C, Hk, D, S, N, block_tables.shape[1], int(max_cache_seqlen),
-                               _stream(stream))
+                               _table(chunk_lens), B, C, Hk, D, S, N, block_tables.shape[1],
+                               int(max_cache_seqlen), _stream(stream))
     _check(st, "paged_kv_append")
 
 
 def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u,
                             pos_bias_v, max_cache_seqlen, per_row_pos=False, out=None,
-                            softmax_scale=0.0, stream=None):
-    """Chunk attention; q [B, C, H, D]; pos shared [P, H, D] or per-row [B, P, H, D]."""
+                            softmax_scale=0.0, chunk_lens=None, stream=None):
+    """Chunk attention; q [B, C, H, D]; pos shared [P, H, D] or per-row [B, P, H, D];
+    chunk_lens int32 [B] (optional): real frames per stream."""
     B, C, H, D = q.shape
     N, Hk, S, _ = k_pool.shape
     if out is None:
@@ -130,8 +134,9 @@ def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos,
     P = pos.shape[1] if per_row_pos else pos.shape[0]
     st = lib().chunk_paged_relpos_attn(
         _dtype(q, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out), _p(q), _p(k_pool), _p(v_pool),
-        _table(block_tables), _table(cache_seqlens), _p(pos), P, int(bool(per_row_pos)),
-        _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk, D, S, N, block_tables.shape[1],
+        _table(block_tables), _table(cache_seqlens), _table(chunk_lens), _p(pos), P,
+        int(bool(per_row_pos)), _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk, D, S, N,
+        block_tables.shape[1],
         int(max_cache_seqlen), float(softmax_scale), _stream(stream))
     _check(st, "chunk_paged_relpos_attn")
     return out
@@ -139,8 +144,9 @@ def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos,
 
 def paged_kv_append_relpos_attn(q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, pos,
                                 pos_bias_u, pos_bias_v, max_cache_seqlen, per_row_pos=False,
-                                out=None, softmax_scale=0.0, stream=None):
-    """Append and attention of one layer in one launch (pools are written)."""
+                                out=None, softmax_scale=0.0, chunk_lens=None, stream=None):
+    """Append and attention of one layer in one launch (pools are written); chunk_lens int32 [B]
+    (optional): real frames per stream."""
     B, C, H, D = q.shape
     N, Hk, S, _ = k_pool.shape
     if out is None:
@@ -149,7 +155,8 @@ def paged_kv_append_relpos_attn(q, k_new, v_new, k_pool, v_pool, block_tables, c
     st = lib().paged_kv_append_relpos_attn(
         _dtype(q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out), _p(q),
         _p(k_new), _p(v_new), _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
-        _p(pos), P, int(bool(per_row_pos)), _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk,
+        _table(chunk_lens), _p(pos), P, int(bool(per_row_pos)), _p(pos_bias_u), _p(pos_bias_v),
+        _p(out), B, C, H, Hk,
         D, S, N, block_tables.shape[1], int(max_cache_seqlen), float(softmax_scale),
         _stream(stream))
     _check(st, "paged_kv_append_relpos_attn")

@@ -64,6 +64,7 @@ struct ChunkArgs {
   const T* v_pool;
   const int32_t* bt;
   const int32_t* cs;
+  const int32_t* lens;   // real frames per stream, or null
   const T* pos;
   const T* u;
   const T* w;
@@ -148,10 +149,22 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     }
   }
   const int cache = clampi(a.cs[b], 0, a.max_cache);
-  const int T_len = cache + a.C;
+  // real frames of this stream's chunk: frames past them do not exist (not appended, not keys;
+  // their output rows are zero); a stream with none is a padding lane and reads nothing
+  const int n_real = a.lens ? clampi(a.lens[b], 0, a.C) : a.C;
+  if (qt * 16 >= n_real) {
+    for (int x = tid; x < 16 * NV; x += kThreads) {
+      const int i = qt * 16 + x / NV;
+      if (i < a.C)
+        *reinterpret_cast<uint4*>(a.out + (((size_t)b * a.C + i) * a.H + h) * kD + (x % NV) * VEC) =
+            uint4{0u, 0u, 0u, 0u};
+    }
+    return;   // uniform over the workgroup
+  }
+  const int T_len = cache + n_real;   // keys
   const int nbody = (cache + 31) >> 5;                 // body steps over the cached keys
   const int s_part = (cache & 31) ? nbody - 1 : -1;    // the partial one, if any
-  const int ntail = (a.C + 31) >> 5;                   // tail steps over the chunk's frames
+  const int ntail = (n_real + 31) >> 5;                // tail steps over the chunk's frames
   const size_t page = (size_t)S * kD;                  // elements of one (block, kv head) page
   const uint32_t blk_stride = (uint32_t)(a.Hk * S * kD);
   const T* kp = a.k_pool + (size_t)hk * page;
@@ -160,7 +173,8 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const int s_end = ((wave + 1) * nbody) / kWaves;
   const int nmine = s_end - s_begin;
 
-  const int center = a.per_row ? (T_len - 1) : (a.pos_len - 1) / 2;
+  // a per-row table is built for the full chunk width: centred at cache + C - 1
+  const int center = a.per_row ? (cache + a.C - 1) : (a.pos_len - 1) / 2;
   const int R0 = center - cache;
   const int rlo = R0 - (a.C - 1);
   const int rhi = R0 + T_len - 1;
@@ -179,7 +193,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   };
   // the chunk's frames into the LDS tail (row t = frame t; V transposed, zero past the chunk)
   if constexpr (kRegTail) {
-    if (tid < a.C * NV) {
+    if (tid < n_real * NV) {
       const int t = tid / NV;
       const int dv = (tid % NV) * VEC;
       *reinterpret_cast<uint4*>(s_kt + t * KTP + dv) = nk;
@@ -188,8 +202,8 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       for (int c = 0; c < 8; ++c)
         reinterpret_cast<uint16_t*>(s_vt)[(dv + c) * a.vt_pitch + t] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
     }
-    for (int x = tid; x < (32 * ntail - a.C) * kD; x += kThreads)
-      s_vt[(x % kD) * a.vt_pitch + a.C + x / kD] = from_f<T>(0.f);
+    for (int x = tid; x < (32 * ntail - n_real) * kD; x += kThreads)
+      s_vt[(x % kD) * a.vt_pitch + n_real + x / kD] = from_f<T>(0.f);
   }
 
   // ---- 2. loads of the first two body steps (band tile 0 of the first one too) ----------------
@@ -248,7 +262,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     for (int x = tid; x < 32 * ntail * NV; x += kThreads) {
       const int t = x / NV;
       const int dv = (x % NV) * VEC;
-      if (t < a.C) {
+      if (t < n_real) {
         const int key = cache + t;
         const T* src = kFused ? a.k_new + ((size_t)(b * a.C + t) * a.Hk + hk) * kD + dv
                               : kp + (uint64_t)block_of(key >> logS) * blk_stride +
@@ -259,13 +273,13 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     for (int x = tid; x < 32 * ntail * NV; x += kThreads) {
       const int t = x / NV;
       const int dv = (x % NV) * VEC;
-      if (kFused && t < a.C) {
+      if (kFused && t < n_real) {
         const uint4 raw = *reinterpret_cast<const uint4*>(
             a.v_new + ((size_t)(b * a.C + t) * a.Hk + hk) * kD + dv);
         const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
         for (int k = 0; k < VEC; ++k) s_vt[(dv + k) * a.vt_pitch + t] = e[k];
-      } else if (t >= a.C) {
+      } else if (t >= n_real) {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) s_vt[(dv + k) * a.vt_pitch + t] = from_f<T>(0.f);
       }
@@ -273,9 +287,9 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     if (!kFused) {
       // frames from the transposed pages, element by element (thread column t = tid % 32 of
       // every 32-frame group, dimensions d = tid / 32 + 8 n)
-      for (int c0 = 0; c0 < a.C; c0 += 32) {
+      for (int c0 = 0; c0 < n_real; c0 += 32) {
         const int t = c0 + (tid & 31);
-        if (t < a.C) {
+        if (t < n_real) {
           const int key = cache + t;
           const T* src = vp + (uint64_t)block_of(key >> logS) * blk_stride + (uint32_t)(key & (S - 1));
           for (int d = tid >> 5; d < kD; d += kThreads / 32) s_vt[d * a.vt_pitch + t] = src[d * S];
@@ -376,7 +390,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   // drain while the waves merge)
   if (kFused && h % (a.H / a.Hk) == 0) {
     const int t_lo = qt * 16;
-    const int t_hi = min(a.C, t_lo + 16);
+    const int t_hi = min(n_real, t_lo + 16);
     for (int x = tid; x < (t_hi - t_lo) * NV; x += kThreads) {
       const int t = t_lo + x / NV;
       const int dv = (x % NV) * VEC;
@@ -424,6 +438,12 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     const int d0 = (x >> 4) * 4;
     const int i = qt * 16 + il;
     if (i >= a.C) continue;
+    T* dst = a.out + (((size_t)b * a.C + i) * a.H + h) * kD + d0;
+    if (i >= n_real) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[k] = from_f<T>(0.f);
+      continue;
+    }
     float mmax = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mmax = fmaxf(mmax, s_wave[w * kWaveLds + kD * 16 + il]);
@@ -438,7 +458,6 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       for (int k = 0; k < 4; ++k) acc[k] += f * so[(d0 + k) * 16 + il];
     }
     const float inv = 1.f / lsum;
-    T* dst = a.out + (((size_t)b * a.C + i) * a.H + h) * kD + d0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) dst[k] = from_f<T>(acc[k] * inv);
   }
@@ -493,6 +512,7 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   a.v_pool = (const T*)p.v_pool;
   a.bt = p.block_tables;
   a.cs = p.cache_seqlens;
+  a.lens = p.chunk_lens;
   a.pos = (const T*)p.pos;
   a.u = (const T*)p.pos_bias_u;
   a.w = (const T*)p.pos_bias_v;

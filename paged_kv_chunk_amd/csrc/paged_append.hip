@@ -2,7 +2,9 @@
 //
 // Source: OASR docs, "ASR Engine", section 4.3 "Batched paged forward" -- one pool shared by the
 // cohort, one block-table row per stream, the chunk written at logical frames
-// [cache_seqlens[b], cache_seqlens[b] + C), cache_seqlens advanced only after the forward.
+// [cache_seqlens[b], cache_seqlens[b] + C), cache_seqlens advanced only after the forward; step 6
+// commits each stream's actual frames, so with per-stream chunk lengths n_b only the first n_b
+// frames are written (a padding lane, n_b = 0, writes nothing; section 9).
 //
 // One workgroup per (stream, kv head). K rows are copied 16 bytes per lane straight into their
 // slots (rows of the K page are contiguous). V pages are stored transposed ([head_dim][block_size])
@@ -23,7 +25,8 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ k_pool,
                     T* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
-                    const int32_t* __restrict__ cache_seqlens, int chunk, int n_kv_head, int head_dim,
+                    const int32_t* __restrict__ cache_seqlens, const int32_t* __restrict__ chunk_lens,
+                    int chunk, int n_kv_head, int head_dim,
                     int block_size, int num_blocks, int max_blocks, int max_cache) {
   extern __shared__ unsigned char smem_raw[];
   T* sv = reinterpret_cast<T*>(smem_raw);  // [kTileFrames][head_dim + pad]
@@ -35,9 +38,10 @@ paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T*
   const int cache = clampi(cache_seqlens[b], 0, max_cache);
   const int32_t* bt = block_tables + (size_t)b * max_blocks;
   const int nvec = head_dim / VEC;
+  const int n_real = chunk_lens ? clampi(chunk_lens[b], 0, chunk) : chunk;
 
-  for (int t0 = 0; t0 < chunk; t0 += kTileFrames) {
-    const int nt = min(kTileFrames, chunk - t0);
+  for (int t0 = 0; t0 < n_real; t0 += kTileFrames) {
+    const int nt = min(kTileFrames, n_real - t0);
     // K: direct copy; V: stage rows in LDS.
     for (int x = threadIdx.x; x < nt * nvec; x += kThreads) {
       const int t = t0 + x / nvec;
@@ -72,14 +76,14 @@ hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream
     const size_t smem = (size_t)kTileFrames * (p.head_dim + 8) * sizeof(bf16);
     hipLaunchKernelGGL(paged_append_kernel<bf16>, grid, dim3(kThreads), smem, stream,
                        (const bf16*)p.k_new, (const bf16*)p.v_new, (bf16*)p.k_pool, (bf16*)p.v_pool,
-                       p.block_tables, p.cache_seqlens, p.chunk, p.n_kv_head, p.head_dim,
+                       p.block_tables, p.cache_seqlens, p.chunk_lens, p.chunk, p.n_kv_head, p.head_dim,
                        p.block_size, p.num_blocks, p.max_blocks, p.max_cache);
   } else {
     const size_t smem = (size_t)kTileFrames * (p.head_dim + 4) * sizeof(float);
     hipLaunchKernelGGL(paged_append_kernel<float>, grid, dim3(kThreads), smem, stream,
                        (const float*)p.k_new, (const float*)p.v_new, (float*)p.k_pool,
-                       (float*)p.v_pool, p.block_tables, p.cache_seqlens, p.chunk, p.n_kv_head,
-                       p.head_dim, p.block_size, p.num_blocks, p.max_blocks, p.max_cache);
+                       (float*)p.v_pool, p.block_tables, p.cache_seqlens, p.chunk_lens, p.chunk,
+                       p.n_kv_head, p.head_dim, p.block_size, p.num_blocks, p.max_blocks, p.max_cache);
   }
   return hipGetLastError();
 }

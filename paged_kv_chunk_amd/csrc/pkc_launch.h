@@ -16,6 +16,7 @@ struct AppendParams {
   void* v_pool;
   const int32_t* block_tables;
   const int32_t* cache_seqlens;
+  const int32_t* chunk_lens;   // real frames per stream, or null: all chunk frames
   int batch, chunk, n_kv_head, head_dim, block_size, num_blocks, max_blocks, max_cache;
 };
 
@@ -25,6 +26,7 @@ struct AttnParams {
   const void* v_pool;      // read
   const int32_t* block_tables;
   const int32_t* cache_seqlens;
+  const int32_t* chunk_lens;   // real frames per stream, or null: all chunk frames
   const void* pos;
   const void* pos_bias_u;
   const void* pos_bias_v;

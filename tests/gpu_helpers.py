@@ -73,15 +73,38 @@ def compact(co, streams):
         u=host64(co.pos_bias_u), w=host64(co.pos_bias_v), per_row=co.per_row_pos)
 
 
-def oracle_chunk(co, streams=None):
+def oracle_chunk(co, streams=None, chunk_lens=None):
     """Oracle append + attention for `streams` (default all) of a cohort whose pools have not been
-    appended to yet. Returns float64 [len(streams), C, H, D]."""
+    appended to yet (chunk_lens: optional real frames per stream of the whole cohort). Returns
+    float64 [len(streams), C, H, D]."""
     if streams is None:
         streams = list(range(co.q.shape[0]))
     h = compact(co, streams)
-    kp, vp = oracle.paged_kv_append(h["k_pool"], h["v_pool"], h["k_new"], h["v_new"], h["bt"], h["cs"])
+    lens = None if chunk_lens is None else np.asarray(chunk_lens)[streams]
+    kp, vp = oracle.paged_kv_append(h["k_pool"], h["v_pool"], h["k_new"], h["v_new"], h["bt"], h["cs"],
+                                    lens)
     return oracle.chunk_relpos_attn(h["q"], kp, vp, h["bt"], h["cs"], h["pos"], h["u"], h["w"],
-                                    per_row_pos=h["per_row"])
+                                    per_row_pos=h["per_row"], chunk_lens=lens)
+
+
+def poison_padding(co, chunk_lens):
+    """NaN the frames a stream's chunk does not have: its padded rows of q, k_new and v_new, and
+    the pool slots they would have been appended to."""
+    C = co.q.shape[1]
+    S = co.block_size
+    bt = co.block_tables.cpu().numpy()
+    cs = co.cache_seqlens.cpu().numpy()
+    nan = float("nan")
+    for b, n in enumerate(chunk_lens):
+        n = int(n)
+        co.q[b, n:] = nan
+        co.k_new[b, n:] = nan
+        co.v_new[b, n:] = nan
+        for t in range(int(cs[b]) + n, int(cs[b]) + C):
+            blk, slot = int(bt[b, t // S]), t % S
+            co.k_pool[blk, :, slot, :] = nan
+            co.v_pool[blk, :, :, slot] = nan
+    return co
 
 
 def max_err(gpu, ref):

@@ -58,14 +58,14 @@ def test_version_and_status_strings(lib):
 
 def append(lib, dtype=1, k_new=P, v_new=P, k_pool=P, v_pool=P, bt=P, cs=P, B=2, C=16, Hk=4, D=64,
            S=16, N=32, M=8, max_cache=64):
-    return lib.paged_kv_append(dtype, k_new, v_new, k_pool, v_pool, bt, cs, B, C, Hk, D, S, N, M,
-                               max_cache, None)
+    return lib.paged_kv_append(dtype, k_new, v_new, k_pool, v_pool, bt, cs, None, B, C, Hk, D, S,
+                               N, M, max_cache, None)
 
 
 def attn(lib, dtype=1, q=P, k_pool=P, v_pool=P, bt=P, cs=P, pos=P, pos_len=159, per_row=0, u=P,
          w=P, out=P, B=2, C=16, H=4, Hk=4, D=64, S=16, N=32, M=8, max_cache=64, scale=0.0):
-    return lib.chunk_paged_relpos_attn(dtype, q, k_pool, v_pool, bt, cs, pos, pos_len, per_row, u,
-                                       w, out, B, C, H, Hk, D, S, N, M, max_cache, scale, None)
+    return lib.chunk_paged_relpos_attn(dtype, q, k_pool, v_pool, bt, cs, None, pos, pos_len, per_row,
+                                       u, w, out, B, C, H, Hk, D, S, N, M, max_cache, scale, None)
 
 
 def fused(lib, k_new=P, v_new=P, **kw):
@@ -73,7 +73,8 @@ def fused(lib, k_new=P, v_new=P, **kw):
              w=P, out=P, B=2, C=16, H=4, Hk=4, D=64, S=16, N=32, M=8, max_cache=64, scale=0.0)
     a.update(kw)
     return lib.paged_kv_append_relpos_attn(a["dtype"], a["q"], k_new, v_new, a["k_pool"],
-                                           a["v_pool"], a["bt"], a["cs"], a["pos"], a["pos_len"],
+                                           a["v_pool"], a["bt"], a["cs"], None, a["pos"],
+                                           a["pos_len"],
                                            a["per_row"], a["u"], a["w"], a["out"], a["B"], a["C"],
                                            a["H"], a["Hk"], a["D"], a["S"], a["N"], a["M"],
                                            a["max_cache"], a["scale"], None)

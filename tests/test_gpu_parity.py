@@ -11,7 +11,7 @@ import torch
 import oracle
 import paged_kv_chunk_amd as pkc
 from synth import make_chunk_cohort, make_config, make_varlen_cohort
-from gpu_helpers import TOL, bits, compact, host64, max_err, oracle_chunk, poison
+from gpu_helpers import TOL, bits, compact, host64, max_err, oracle_chunk, poison, poison_padding
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -25,18 +25,19 @@ def announce(request):
     torch.cuda.synchronize()
 
 
-def gpu_chunk(co, fused=False):
+def gpu_chunk(co, fused=False, chunk_lens=None):
     """Run one layer on the GPU (append then attention, or the fused entry). Pools are updated."""
     if fused:
         return pkc.paged_kv_append_relpos_attn(co.q, co.k_new, co.v_new, co.k_pool, co.v_pool,
                                                co.block_tables, co.cache_seqlens, co.pos,
                                                co.pos_bias_u, co.pos_bias_v, co.max_cache_seqlen,
-                                               per_row_pos=co.per_row_pos)
+                                               per_row_pos=co.per_row_pos, chunk_lens=chunk_lens)
     pkc.paged_kv_append(co.k_new, co.v_new, co.k_pool, co.v_pool, co.block_tables,
-                        co.cache_seqlens, co.max_cache_seqlen)
+                        co.cache_seqlens, co.max_cache_seqlen, chunk_lens=chunk_lens)
     return pkc.chunk_paged_relpos_attn(co.q, co.k_pool, co.v_pool, co.block_tables,
                                        co.cache_seqlens, co.pos, co.pos_bias_u, co.pos_bias_v,
-                                       co.max_cache_seqlen, per_row_pos=co.per_row_pos)
+                                       co.max_cache_seqlen, per_row_pos=co.per_row_pos,
+                                       chunk_lens=chunk_lens)
 
 
 def clone(co):
@@ -290,3 +291,90 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits(out), bits(eager), err_msg=f"replay {r}")
         _ = (co.q.float() * 2).sum().item()   # unrelated eager work between replays
+
+
+# --------------------------------------------------------------------------------------------
+# Per-row chunk lengths (short final windows) and padding lanes
+# --------------------------------------------------------------------------------------------
+
+def _lens_for(co, seed):
+    """Seeded real-frame counts covering 0 (padding lane), 1, C and values in between."""
+    B, C = co.q.shape[0], co.q.shape[1]
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, C + 1, size=B)
+    for x, v in enumerate([0, C, 1]):
+        if x < B:
+            lens[x] = v
+    return lens.astype(np.int32)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("name", ["bf16_ragged", "gqa_h4_k2", "odd_lengths", "per_row_ragged_fp32",
+                                  "chunk32_full_tail", "long_chunk_bf16"])
+def test_chunk_lens_parity(name, fused):
+    """Streams with fewer real frames than the chunk width: the GPU writes exactly the oracle's
+    pool bits (nothing past the real frames) and matches its output; padded rows are exactly
+    zero. Padded frames are NaN everywhere, so any read of one shows."""
+    co = poison(small_cohort(name, seed=6))
+    lens = _lens_for(co, 7)
+    poison_padding(co, lens)
+    ref = oracle_chunk(co, chunk_lens=lens)
+    kb, vb = bits(co.k_pool), bits(co.v_pool)
+    ek, ev = oracle.paged_kv_append(kb, vb, bits(co.k_new), bits(co.v_new),
+                                    co.block_tables.cpu().numpy(), co.cache_seqlens.cpu().numpy(), lens)
+    out = gpu_chunk(co, fused=fused, chunk_lens=torch.from_numpy(lens).to(DEV))
+    np.testing.assert_array_equal(bits(co.k_pool), ek)
+    np.testing.assert_array_equal(bits(co.v_pool), ev)
+    o = out.detach().cpu().double().numpy()
+    C = co.q.shape[1]
+    for b, n in enumerate(lens):
+        assert (o[b, n:] == 0).all(), b
+    assert np.abs(o - ref).max() <= TOL[co.q.dtype], (name, np.abs(o - ref).max())
+
+
+def test_chunk_lens_fused_equals_unfused_bitwise():
+    co = small_cohort("odd_lengths", seed=8)
+    lens = _lens_for(co, 9)
+    co2 = clone(co)
+    t = torch.from_numpy(lens).to(DEV)
+    a = gpu_chunk(co, chunk_lens=t)
+    f = gpu_chunk(co2, fused=True, chunk_lens=t)
+    np.testing.assert_array_equal(bits(a), bits(f))
+    np.testing.assert_array_equal(bits(co.k_pool), bits(co2.k_pool))
+
+
+def test_full_chunk_lens_equal_no_lens_bitwise():
+    co = small_cohort("bf16_ragged", seed=10)
+    co2 = clone(co)
+    full = torch.full((co.q.shape[0],), co.q.shape[1], dtype=torch.int32, device=DEV)
+    np.testing.assert_array_equal(bits(gpu_chunk(co, fused=True)),
+                                  bits(gpu_chunk(co2, fused=True, chunk_lens=full)))
+
+
+def test_padding_lanes_are_inert_and_leave_other_rows_bitwise_unchanged():
+    """A cohort padded with lanes of chunk length 0, whose tables point only at a NaN scratch
+    block: the real rows' outputs and pool bits are those of the unpadded cohort, the padding
+    rows' outputs are zero and the scratch block is untouched."""
+    co = make_config(0, device=DEV)
+    base = clone(co)
+    out_base = gpu_chunk(base, fused=True).clone()
+    B, C, H, D = co.q.shape
+    P = 3
+    N = co.k_pool.shape[0]
+    nan = float("nan")
+    kp = torch.cat([co.k_pool, torch.full_like(co.k_pool[:1], nan)])
+    vp = torch.cat([co.v_pool, torch.full_like(co.v_pool[:1], nan)])
+    bt = torch.cat([co.block_tables, torch.full((P, co.block_tables.shape[1]), N, dtype=torch.int32,
+                                                device=DEV)])
+    cs = torch.cat([co.cache_seqlens, torch.tensor([0, 7, int(co.max_cache_seqlen)], dtype=torch.int32,
+                                                   device=DEV)])
+    pad = lambda x: torch.cat([x, torch.full((P,) + tuple(x.shape[1:]), nan, dtype=x.dtype, device=DEV)])
+    q, k_new, v_new = pad(co.q), pad(co.k_new), pad(co.v_new)
+    lens = torch.tensor([C] * B + [0] * P, dtype=torch.int32, device=DEV)
+    out = pkc.paged_kv_append_relpos_attn(q, k_new, v_new, kp, vp, bt, cs, co.pos, co.pos_bias_u,
+                                          co.pos_bias_v, co.max_cache_seqlen, chunk_lens=lens)
+    np.testing.assert_array_equal(bits(out[:B]), bits(out_base))
+    assert (out[B:] == 0).all()
+    np.testing.assert_array_equal(bits(kp[:N]), bits(base.k_pool))
+    np.testing.assert_array_equal(bits(vp[:N]), bits(base.v_pool))
+    assert torch.isnan(kp[N:]).all() and torch.isnan(vp[N:]).all()
