@@ -33,6 +33,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -69,21 +71,25 @@ def stored_traffic(key, kernel):
 def algorithmic_bytes(co):
     """Bytes the fused append + attention must move for one layer of a cohort: read q, k_new,
     v_new, the cached K/V and the positional band rows in use, u and v, the block-table entries
-    and cache lengths; write the new K/V into the pool and the output."""
+    and cache lengths; write the new K/V into the pool and the output. With per-stream chunk
+    lengths n_b (``co.chunk_lens``) only real frames are read and appended (every output row is
+    still written; a padding lane, n_b = 0, reads nothing)."""
     B, C, H, D = co.q.shape
     Hk = co.k_new.shape[2]
     eb = co.q.element_size()
     cache = co.cache_seqlens.cpu().tolist()
+    lens = co.chunk_lens.cpu().tolist() if getattr(co, "chunk_lens", None) is not None else [C] * B
+    live = [(c, n) for c, n in zip(cache, lens) if n > 0]
     S = co.block_size
-    qo = 2 * B * C * H * D * eb
-    new = 4 * B * C * Hk * D * eb
-    cached = 2 * sum(cache) * Hk * D * eb
+    qo = sum(lens) * H * D * eb + B * C * H * D * eb
+    new = 4 * sum(lens) * Hk * D * eb
+    cached = 2 * sum(c for c, _ in live) * Hk * D * eb
     if co.per_row_pos:
-        band = sum(c + 2 * C - 1 for c in cache) * H * D * eb
+        band = sum(c + C + n - 1 for c, n in live) * H * D * eb
     else:
-        band = (max(cache) + 2 * C - 1) * H * D * eb
+        band = max((c + C + n - 1 for c, n in live), default=0) * H * D * eb
     uv = 2 * H * D * eb
-    tables = sum((c + C + S - 1) // S for c in cache) * 4 + B * 4
+    tables = sum((c + n + S - 1) // S for c, n in live) * 4 + B * 4 * (2 if lens != [C] * B else 1)
     return qo + new + cached + band + uv + tables
 
 
@@ -109,7 +115,26 @@ def launch_layer(pkc, co, stream):
     pkc.paged_kv_append_relpos_attn(co.q, co.k_new, co.v_new, co.k_pool, co.v_pool,
                                     co.block_tables, co.cache_seqlens, co.pos, co.pos_bias_u,
                                     co.pos_bias_v, co.max_cache_seqlen,
-                                    per_row_pos=co.per_row_pos, out=co.out, stream=stream)
+                                    per_row_pos=co.per_row_pos, out=co.out,
+                                    chunk_lens=getattr(co, "chunk_lens", None), stream=stream)
+
+
+def set_chunk_lens(sets, pad_lanes, short_frac, seed=0):
+    """Production cohort shapes: the last ``pad_lanes`` streams become padding lanes (chunk
+    length 0) and a seeded fraction ``short_frac`` of the real streams carry a short final window
+    (1..C-1 real frames). One lengths vector per cohort, shared by its layers."""
+    for r, layers in enumerate(sets):
+        co = layers[0]
+        B, C = co.q.shape[0], co.q.shape[1]
+        rng = np.random.default_rng(1000 + 17 * seed + r)
+        lens = np.full(B, C, dtype=np.int32)
+        real = B - pad_lanes
+        short = rng.choice(real, size=int(round(short_frac * real)), replace=False)
+        lens[short] = rng.integers(1, C, size=len(short))
+        lens[real:] = 0
+        t = torch.from_numpy(lens).to(co.q.device)
+        for co in layers:
+            co.chunk_lens = t
 
 
 def cpu_baseline(co, min_seconds):
@@ -128,17 +153,20 @@ def cpu_baseline(co, min_seconds):
     cs = co.cache_seqlens.cpu().numpy()
     args = [host(co.k_pool), host(co.v_pool), host(co.k_new), host(co.v_new)]
     q, pos, u, w = host(co.q), host(co.pos), host(co.pos_bias_u), host(co.pos_bias_v)
+    lens = co.chunk_lens.cpu().numpy() if getattr(co, "chunk_lens", None) is not None else None
+    real = B if lens is None else int((lens > 0).sum())
     reps, t0 = 0, time.perf_counter()
     while True:
-        kp, vp = oracle.paged_kv_append(*args, bt, cs)
-        oracle.chunk_relpos_attn(q, kp, vp, bt, cs, pos, u, w, per_row_pos=co.per_row_pos)
+        kp, vp = oracle.paged_kv_append(*args, bt, cs, lens)
+        oracle.chunk_relpos_attn(q, kp, vp, bt, cs, pos, u, w, per_row_pos=co.per_row_pos,
+                                 chunk_lens=lens)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
     if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    return dict(value=B * H * reps / el, unit="chunk·heads/s", cores=1, kind="oracle",
+        limiter.restore_original_limits()
+    return dict(value=real * H * reps / el, unit="chunk·heads/s", cores=1, kind="oracle",
                 sample=f"{reps} x one layer of the timed cohort (B={B}, H={H}, all streams), "
                        f"append + attention in float64 numpy, {el:.1f} s")
 
@@ -234,6 +262,10 @@ def main():
     ap.add_argument("--no-events", action="store_true", help="eager mode without per-launch events")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pad-lanes", type=int, default=0,
+                    help="the last N streams of the cohort are padding lanes (chunk length 0)")
+    ap.add_argument("--short-frac", type=float, default=0.0,
+                    help="fraction of the real streams in a short final window (1..C-1 frames)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the workload, time a plain device copy of this many MiB "
                          "(reference for HBM counters and achievable bandwidth)")
@@ -274,6 +306,9 @@ def main():
     n_layers = cfg["n_layers"]
     dev = "cuda"
     sets = build_sets(args.config, args.rotate, n_layers, dev)
+    lens_mode = bool(args.pad_lanes or args.short_frac)
+    if lens_mode:
+        set_chunk_lens(sets, args.pad_lanes, args.short_frac)
     stream = torch.cuda.current_stream()
     co0 = sets[0][0]
     B, C, H, D = co0.q.shape
@@ -338,12 +373,12 @@ def main():
         kernel_src = "graph replay, timed-region time / kernel launches"
         mode = "graph"
 
-    units = B * H * n_layers
+    units = (B - args.pad_lanes) * H * n_layers          # real streams' chunk·heads
     value = units / (ms_step / 1e3)
     bytes_per_launch = algorithmic_bytes(co0)
     achieved = bytes_per_launch / (kernel_ms / 1e3) / 1e9
 
-    traffic = stored_traffic(f"fused_cfg{args.config}", "chunk")
+    traffic = None if lens_mode else stored_traffic(f"fused_cfg{args.config}", "chunk")
 
     result = {
         "metric": METRIC,
@@ -380,6 +415,13 @@ def main():
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
     }
+    if lens_mode:
+        lens0 = co0.chunk_lens.cpu().numpy()
+        result["config"]["workload"] += (f"; {args.pad_lanes} padding lanes, "
+                                          f"{int(((lens0 > 0) & (lens0 < C)).sum())} streams in a "
+                                          "short final window")
+        result["config"].update(real_streams=B - args.pad_lanes, padding_lanes=args.pad_lanes,
+                                short_windows=int(((lens0 > 0) & (lens0 < C)).sum()))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(co0, args.cpu_seconds)
     print(json.dumps(result), flush=True)
