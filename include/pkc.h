@@ -161,6 +161,43 @@ pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const voi
                                        hipStream_t stream);
 
 /*
+ * paged_kv_append_relpos_attn_layers - the fused append + attention of n_layers layers in one call
+ * [ENG 4.3] (one PagedKVCache per layer sharing the block table and cache lengths; the streaming
+ * step runs them in sequence), so that one host call enqueues a whole step and a caller can
+ * capture it in a HIP graph.
+ *
+ * q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out: HOST arrays of n_layers
+ * device pointers, entry l being layer l's buffer of the layout above (entries may repeat, e.g.
+ * one positional table for every layer). block_tables, cache_seqlens, chunk_lens and every size
+ * are shared by the layers. Layer l's kernel is enqueued after layer l - 1's on the stream; the
+ * results equal n_layers calls of paged_kv_append_relpos_attn. The pointer arrays are read during
+ * the call only.
+ * Errors: those of paged_kv_append_relpos_attn for any layer, n_layers <= 0 -> PKC_ERR_SHAPE.
+ * Every layer is validated before any kernel is enqueued, so an error enqueues nothing.
+ */
+pkc_status paged_kv_append_relpos_attn_layers(
+    pkc_dtype dtype, int32_t n_layers, const void* const* q, const void* const* k_new,
+    const void* const* v_new, void* const* k_pool, void* const* v_pool,
+    const int32_t* block_tables, const int32_t* cache_seqlens, const int32_t* chunk_lens,
+    const void* const* pos, int32_t pos_len, int32_t pos_per_row, const void* const* pos_bias_u,
+    const void* const* pos_bias_v, void* const* out, int32_t batch, int32_t chunk_size,
+    int32_t n_head, int32_t n_kv_head, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream);
+
+/*
+ * paged_kv_commit - after a step's layers: cache_seqlens[b] += n_b for every stream (n_b =
+ * chunk_lens[b] clamped into [0, chunk_size], or chunk_size when chunk_lens is NULL) [ENG 4.3]
+ * step 6 (commit_chunk_paged). It runs on the device, on the caller's stream, so a captured step
+ * (layers + commit) can be replayed step after step with no host round trip: the attention reads
+ * the cache lengths from device memory and sizes nothing by them, so one graph serves every
+ * cache length up to the max_cache_seqlen it was captured with. Keeping cache_seqlens within
+ * max_cache_seqlen is the caller's business (the next attention call clamps, it does not fail).
+ * Errors: NULL cache_seqlens -> PKC_ERR_NULL; batch or chunk_size <= 0 -> PKC_ERR_SHAPE.
+ */
+pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int32_t batch,
+                           int32_t chunk_size, hipStream_t stream);
+
+/*
  * varlen_packed_relpos_attn - full-context attention inside each utterance of a packed, gapless
  * row [MOD surf] (forward_offline_packed), with one relative-position table per utterance.
  *

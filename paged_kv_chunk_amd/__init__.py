@@ -34,6 +34,10 @@ SIGNATURES = {
     "paged_kv_append_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
                                      _ptr, _i32, _i32, _ptr, _ptr, _ptr] + [_i32] * 9
                                     + [_f32, _ptr], ctypes.c_int),
+    "paged_kv_append_relpos_attn_layers": ([ctypes.c_int, _i32] + [_ptr] * 5 + [_ptr] * 3 + [_ptr]
+                                           + [_i32, _i32] + [_ptr] * 3 + [_i32] * 9 + [_f32, _ptr],
+                                           ctypes.c_int),
+    "paged_kv_commit": ([_ptr, _ptr, _i32, _i32, _ptr], ctypes.c_int),
     "varlen_packed_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _ptr,
                                    _ptr, _ptr, _ptr, _i32, _i32, _i32, _f32, _ptr], ctypes.c_int),
 }
@@ -161,6 +165,47 @@ def paged_kv_append_relpos_attn(q, k_new, v_new, k_pool, v_pool, block_tables, c
         _stream(stream))
     _check(st, "paged_kv_append_relpos_attn")
     return out
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _p(t)
+    return arr
+
+
+def paged_kv_append_relpos_attn_layers(layers, block_tables, cache_seqlens, max_cache_seqlen,
+                                       per_row_pos=False, chunk_lens=None, softmax_scale=0.0,
+                                       stream=None):
+    """Fused append + attention of several layers in one call. ``layers``: a sequence of objects
+    with attributes q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out (one per
+    layer, same shapes); block tables, cache and chunk lengths are shared."""
+    l0 = layers[0]
+    B, C, H, D = l0.q.shape
+    N, Hk, S, _ = l0.k_pool.shape
+    P = l0.pos.shape[1] if per_row_pos else l0.pos.shape[0]
+    names = ["q", "k_new", "v_new", "k_pool", "v_pool", "pos", "pos_bias_u", "pos_bias_v", "out"]
+    for x in layers:
+        for n in names:
+            t = getattr(x, n)
+            if getattr(l0, n).shape != t.shape:
+                raise ValueError(f"layer buffers of {n} differ in shape")
+    dt = _dtype(*[getattr(x, n) for x in layers for n in names])
+    arrs = {n: _ptr_array([getattr(x, n) for x in layers]) for n in names}
+    st = lib().paged_kv_append_relpos_attn_layers(
+        dt, len(layers), arrs["q"], arrs["k_new"], arrs["v_new"], arrs["k_pool"], arrs["v_pool"],
+        _table(block_tables), _table(cache_seqlens), _table(chunk_lens), arrs["pos"], P,
+        int(bool(per_row_pos)), arrs["pos_bias_u"], arrs["pos_bias_v"], arrs["out"], B, C, H, Hk,
+        D, S, N, block_tables.shape[1], int(max_cache_seqlen), float(softmax_scale),
+        _stream(stream))
+    _check(st, "paged_kv_append_relpos_attn_layers")
+
+
+def paged_kv_commit(cache_seqlens, chunk, chunk_lens=None, stream=None):
+    """cache_seqlens[b] += chunk_lens[b] (or chunk) on the device."""
+    st = lib().paged_kv_commit(_table(cache_seqlens), _table(chunk_lens), cache_seqlens.shape[0],
+                               int(chunk), _stream(stream))
+    _check(st, "paged_kv_commit")
 
 
 def varlen_packed_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, max_seqlen,

@@ -98,7 +98,8 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
                               void* out, int32_t batch, int32_t chunk_size, int32_t n_head,
                               int32_t n_kv_head, int32_t head_dim, int32_t block_size,
                               int32_t num_blocks, int32_t max_blocks_per_seq,
-                              int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream) {
+                              int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream,
+                              bool launch = true) {
   pkc_status st = check_dtype(dtype);
   if (st != PKC_OK) return st;
   if (!q || !k_pool || !v_pool || !block_tables || !cache_seqlens || !pos || !pos_bias_u ||
@@ -144,6 +145,7 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
   p.pos_len = pos_len;
   p.pos_per_row = pos_per_row;
   p.softmax_scale = softmax_scale;
+  if (!launch) return PKC_OK;
   return from_hip(launch_chunk_attn(dtype, p, stream));
 }
 
@@ -179,6 +181,41 @@ pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const voi
                      cache_seqlens, chunk_lens, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
                      chunk_size, n_head, n_kv_head, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_cache_seqlen, softmax_scale, stream);
+}
+
+pkc_status paged_kv_append_relpos_attn_layers(
+    pkc_dtype dtype, int32_t n_layers, const void* const* q, const void* const* k_new,
+    const void* const* v_new, void* const* k_pool, void* const* v_pool,
+    const int32_t* block_tables, const int32_t* cache_seqlens, const int32_t* chunk_lens,
+    const void* const* pos, int32_t pos_len, int32_t pos_per_row, const void* const* pos_bias_u,
+    const void* const* pos_bias_v, void* const* out, int32_t batch, int32_t chunk_size,
+    int32_t n_head, int32_t n_kv_head, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream) {
+  pkc_status st = check_dtype(dtype);
+  if (st != PKC_OK) return st;
+  if (n_layers <= 0) return PKC_ERR_SHAPE;
+  if (!q || !k_new || !v_new || !k_pool || !v_pool || !pos || !pos_bias_u || !pos_bias_v || !out)
+    return PKC_ERR_NULL;
+  // every layer is validated before any is launched, so an error launches nothing
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int l = 0; l < n_layers; ++l) {
+      if (!k_new[l] || !v_new[l]) return PKC_ERR_NULL;
+      st = attn_common(dtype, q[l], k_new[l], v_new[l], k_pool[l], v_pool[l], k_pool[l],
+                       v_pool[l], block_tables, cache_seqlens, chunk_lens, pos[l], pos_len,
+                       pos_per_row, pos_bias_u[l], pos_bias_v[l], out[l], batch, chunk_size,
+                       n_head, n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_cache_seqlen, softmax_scale, stream, pass == 1);
+      if (st != PKC_OK) return st;
+    }
+  }
+  return PKC_OK;
+}
+
+pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int32_t batch,
+                           int32_t chunk_size, hipStream_t stream) {
+  if (!cache_seqlens) return PKC_ERR_NULL;
+  if (batch <= 0 || chunk_size <= 0) return PKC_ERR_SHAPE;
+  return from_hip(launch_commit(cache_seqlens, chunk_lens, batch, chunk_size, stream));
 }
 
 pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,

@@ -68,7 +68,23 @@ paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T*
   }
 }
 
+// cache_seqlens[b] += real frames of stream b ("ASR Engine", section 4.3 step 6,
+// commit_chunk_paged), on the device so that a captured step needs no host round trip.
+__global__ void __launch_bounds__(kThreads)
+commit_kernel(int32_t* __restrict__ cache_seqlens, const int32_t* __restrict__ chunk_lens, int batch,
+              int chunk) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b < batch) cache_seqlens[b] += chunk_lens ? clampi(chunk_lens[b], 0, chunk) : chunk;
+}
+
 }  // namespace
+
+hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int batch, int chunk,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL(commit_kernel, dim3((batch + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, cache_seqlens, chunk_lens, batch, chunk);
+  return hipGetLastError();
+}
 
 hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream) {
   const dim3 grid(p.batch * p.n_kv_head);

@@ -56,6 +56,8 @@ struct VarlenParams {
 };
 
 hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream);
+hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int batch, int chunk,
+                         hipStream_t stream);
 hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream);
 hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_t stream);
 

@@ -38,6 +38,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["paged_kv_append", "chunk_paged_relpos_attn", "paged_kv_append_relpos_attn",
+              "paged_kv_append_relpos_attn_layers", "paged_kv_commit",
               "varlen_packed_relpos_attn", "pkc_version", "pkc_status_string"]:
         assert n in names
 
@@ -151,3 +152,34 @@ def test_binding_refuses_host_tensors(lib):
                                     torch.zeros(2, dtype=torch.int32), torch.zeros(31, 4, 64),
                                     torch.zeros(4, 64), torch.zeros(4, 64), max_cache_seqlen=0,
                                     out=torch.zeros_like(x))
+
+
+def layers_call(lib, n_layers=3, hole=None, dtype=1, C=16, max_cache=64):
+    """The multi-layer entry with fake pointers; ``hole`` = (array name, layer) set to NULL."""
+    names = ["q", "k_new", "v_new", "k_pool", "v_pool", "pos", "u", "w", "out"]
+    arrs = {}
+    for n in names:
+        a = (ctypes.c_void_p * max(n_layers, 1))(*([P] * max(n_layers, 1)))
+        if hole and hole[0] == n:
+            a[hole[1]] = None
+        arrs[n] = a
+    return lib.paged_kv_append_relpos_attn_layers(
+        dtype, n_layers, arrs["q"], arrs["k_new"], arrs["v_new"], arrs["k_pool"], arrs["v_pool"],
+        P, P, None, arrs["pos"], 159, 0, arrs["u"], arrs["w"], arrs["out"], 2, C, 4, 4, 64, 16, 32,
+        8, max_cache, 0.0, None)
+
+
+def test_layers_validation_launches_nothing_on_error(lib):
+    assert layers_call(lib, n_layers=0) == SHAPE
+    assert layers_call(lib, dtype=5) == DTYPE
+    # a hole in the last layer is reported as such; had layer 0 been launched first (no GPU
+    # here), the call would have failed with a HIP error instead
+    assert layers_call(lib, hole=("out", 2)) == NULL
+    assert layers_call(lib, hole=("k_new", 1)) == NULL
+    assert layers_call(lib, max_cache=113) == CAP
+
+
+def test_commit_validation(lib):
+    assert lib.paged_kv_commit(None, None, 4, 16, None) == NULL
+    assert lib.paged_kv_commit(P, None, 0, 16, None) == SHAPE
+    assert lib.paged_kv_commit(P, None, 4, 0, None) == SHAPE
