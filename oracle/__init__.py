@@ -15,6 +15,7 @@ Parity status: every function here is pinned by ``tests/test_oracle_pins.py``.
 from .relpos_attn import (  # noqa: F401
     DEFAULT_LAYOUT,
     paged_kv_append,
+    commit_chunk,
     gather_stream,
     table_row,
     chunk_relpos_attn,

@@ -34,6 +34,14 @@ Readings where the pages are silent (each is listed, with its reason, in the des
 * GQA: query head h reads kv head h * Hk // H.
 * Page layout (the pages give none): k_pool[n, g, s, d] and v_pool[n, g, d, s] (V transposed inside
   each page); logical frame t of stream b sits in block block_tables[b, t // S], slot t % S.
+* Bounded history ("ASR Engine", section 6, num_left_chunks and recycle_streaming_history;
+  section 9, cached_frames held at max_logical_blocks - 1 blocks, positions unaffected): a stream
+  may carry a window start w_b, the absolute position of its first cached frame, a multiple of S.
+  Absolute position p then sits in block block_tables[b, (p // S) % M], slot p % S (the table row
+  is a ring of M pages, so a recycled page is reused without rewriting the table); the cached
+  frames are p in [w_b, w_b + cache_b) and the chunk follows them. Distances are taken inside the
+  window (cache + i - j with j the key's index in the window), which a table by distance makes
+  independent of w_b.
 """
 
 from __future__ import annotations
@@ -44,7 +52,14 @@ DEFAULT_LAYOUT = {"k_pool": "[num_blocks, n_kv_head, block_size, head_dim]",
                   "v_pool": "[num_blocks, n_kv_head, head_dim, block_size]"}
 
 
-def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens, chunk_lens=None):
+def _slot(block_table_row, p, block_size):
+    """Block and slot of absolute position p in a stream's ring of pages."""
+    n_entries = len(block_table_row)
+    return int(block_table_row[(p // block_size) % n_entries]), p % block_size
+
+
+def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens, chunk_lens=None,
+                    window_start=None):
     """Write each stream's chunk K/V into its pages ("ASR Engine" section 4.3, steps 1 and 5).
 
     k_new, v_new: [B, C, Hk, D]. Frame t of the chunk of stream b is logical frame
@@ -52,6 +67,8 @@ def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens, c
     ``chunk_lens`` (default: C for every stream) gives each stream's real frames n_b <= C: only
     frames t < n_b are written ("ASR Engine" section 4.3 step 6: a stream commits its actual
     frames; the final window is short). A stream with n_b = 0 (the padding lane) writes nothing.
+    ``window_start`` (default 0): frame t goes to absolute position w_b + cache_b + t, addressed
+    through the ring of the stream's table row (see the module notes).
     Returns new pools; every element that is not written is copied unchanged. Works on any dtype
     (pass integer views of the storage to compare bit patterns).
     """
@@ -61,26 +78,46 @@ def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens, c
     block_size = k_pool.shape[2]
     for b in range(n_streams):
         n_real = chunk if chunk_lens is None else int(chunk_lens[b])
+        start = 0 if window_start is None else int(window_start[b])
         for t in range(n_real):
-            frame = int(cache_seqlens[b]) + t
-            block = int(block_tables[b, frame // block_size])
-            slot = frame % block_size
+            frame = start + int(cache_seqlens[b]) + t
+            block, slot = _slot(block_tables[b], frame, block_size)
             k_out[block, :, slot, :] = k_new[b, t]
             v_out[block, :, :, slot] = v_new[b, t]
     return k_out, v_out
 
 
-def gather_stream(k_pool, v_pool, block_table_row, n_frames):
-    """Read logical frames [0, n_frames) of one stream through its block table.
+def commit_chunk(cache_seqlens, chunk, chunk_lens=None, window_start=None, max_cached_frames=None,
+                 block_size=None):
+    """After a step: cache_b += n_b ("ASR Engine" section 4.3 step 6, commit_chunk_paged). With a
+    window start and a cap (bounded history, "ASR Engine" sections 6 and 9), the oldest whole
+    blocks are then dropped while cache_b exceeds the cap: w_b += S, cache_b -= S. Returns the new
+    (cache_seqlens, window_start) as int64 arrays (window_start None when not given)."""
+    cache = np.array(cache_seqlens, dtype=np.int64, copy=True)
+    lens = np.full(cache.shape, chunk) if chunk_lens is None else np.asarray(chunk_lens)
+    cache += lens
+    if window_start is None:
+        return cache, None
+    start = np.array(window_start, dtype=np.int64, copy=True)
+    if max_cached_frames is not None:
+        for b in range(len(cache)):
+            while cache[b] > max_cached_frames:
+                start[b] += block_size
+                cache[b] -= block_size
+    return cache, start
+
+
+def gather_stream(k_pool, v_pool, block_table_row, n_frames, start=0):
+    """Read the frames at absolute positions [start, start + n_frames) of one stream through its
+    block table (a ring of pages when start > 0).
 
     Returns K, V as [n_frames, Hk, D] arrays in the pool's dtype ("Scheduler" section 4.3: the
     attention reads the paged pool through each stream's table).
     """
     block_size = k_pool.shape[2]
     ks, vs = [], []
-    for t in range(n_frames):
-        block = int(block_table_row[t // block_size])
-        slot = t % block_size
+    for t in range(start, start + n_frames):
+        block, slot = _slot(block_table_row, t, block_size)
         ks.append(k_pool[block, :, slot, :])
         vs.append(v_pool[block, :, :, slot])
     return np.stack(ks), np.stack(vs)
@@ -127,7 +164,7 @@ def _attend(q, k, v, pos_rows, u, w, center, cache, scale, query_rows=None):
 
 def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u, pos_bias_v,
                       per_row_pos=False, scale=None, return_probs=False, streams=None,
-                      chunk_lens=None):
+                      chunk_lens=None, window_start=None):
     """Chunk attention of every stream over its cached frames plus its own chunk.
 
     q: [B, C, H, D]. The chunk's K/V must already be in the pools (append first, then attend).
@@ -142,6 +179,11 @@ def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_b
     "ASR Engine" section 9). Reading: frames t >= n_b do not exist, so query i < n_b attends over
     keys j < c_b + n_b, and output rows i >= n_b are zero. Tables keep the geometry of the full
     chunk width (a per-row table stays centred at c_b + C - 1).
+
+    ``window_start`` (default 0): stream b's cached frames are the absolute positions
+    [w_b, w_b + c_b) of its ring of pages (bounded history); the keys are those frames and the
+    chunk's, and distances are counted inside the window, so the result depends on w_b only
+    through which pages are read.
     """
     q = np.asarray(q, dtype=np.float64)
     u = np.asarray(pos_bias_u, dtype=np.float64)
@@ -159,7 +201,8 @@ def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_b
             all_probs.append(np.zeros((q.shape[2], 0, cache)))
             continue
         n_k = cache + n_real
-        k, v = gather_stream(k_pool, v_pool, block_tables[b], n_k)
+        start = 0 if window_start is None else int(window_start[b])
+        k, v = gather_stream(k_pool, v_pool, block_tables[b], n_k, start)
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
         if per_row_pos:

@@ -528,3 +528,78 @@ def test_chunk_lens_of_full_width_change_nothing():
     case = _random_streaming_case(43, [0, 5, 11])
     lens = np.full(len(case["cs"]), case["C"])
     np.testing.assert_array_equal(_oracle(case, chunk_lens=lens), _oracle(case))
+
+
+# --------------------------------------------------------------------------------------------
+# Bounded history: a left-context cap with pages recycled through a ring
+# --------------------------------------------------------------------------------------------
+
+def _bounded_stream(seed, steps, K, C=4, S=4, M=None, H=2, Hk=1, D=8):
+    """Stream one utterance with at most K chunks of cached history: after each step the commit
+    drops whole oldest blocks past the cap, and the table row is a ring of M pages, so pages are
+    reused (old frames overwritten) many times over the stream's life. Returns the streamed
+    outputs, the dense reference with the limited chunk mask, and the pool's final state."""
+    rng = np.random.default_rng(seed)
+    n = steps * C
+    q_all = rng.standard_normal((n, H, D))
+    k_all = rng.standard_normal((n, Hk, D))
+    v_all = rng.standard_normal((n, Hk, D))
+    u = 0.5 * rng.standard_normal((H, D))
+    w = 0.5 * rng.standard_normal((H, D))
+    proj = relpos_projection(H * D, torch.Generator().manual_seed(seed))
+    cap = K * C
+    if M is None:
+        M = (cap + C + S - 1) // S + 1
+    N = M + 3
+    bt = rng.permutation(N)[None, :M]
+    kp = np.full((N, Hk, S, D), np.nan)
+    vp = np.full((N, Hk, D, S), np.nan)
+    cache, start = np.array([0]), np.array([0])
+    table = descending_table(cap + C - 1, proj, H, D).numpy()
+    outs = []
+    for step in range(steps):
+        sl = slice(step * C, (step + 1) * C)
+        assert start[0] + cache[0] == step * C            # the window ends at the stream's end
+        kp, vp = oracle.paged_kv_append(kp, vp, k_all[None, sl], v_all[None, sl], bt, cache,
+                                        window_start=start)
+        outs.append(oracle.chunk_relpos_attn(q_all[None, sl], kp, vp, bt, cache, table, u, w,
+                                             window_start=start)[0])
+        cache, start = oracle.commit_chunk(cache, C, window_start=start, max_cached_frames=cap,
+                                           block_size=S)
+        assert cache[0] <= cap and start[0] % S == 0
+    stream = np.concatenate(outs)
+    # dense: query chunk a sees key chunks [a - K, a], distances i - j
+    t = np.arange(n)
+    qa, ka = t[:, None] // C, t[None, :] // C
+    dist = t[:, None] - t[None, :]
+    emb = embed_distances(dist.reshape(-1), proj, H, D).numpy().reshape(n, n, H, D)
+    dense = np.zeros((n, H, D))
+    for h in range(H):
+        g = h * Hk // H
+        bias = np.einsum("td,tjd->tj", q_all[:, h] + w[h], emb[:, :, h]) / math.sqrt(D)
+        bias = np.where((ka <= qa) & (ka >= qa - K), bias, -np.inf)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q_all[:, h] + u[h])[None], torch.from_numpy(k_all[:, g])[None],
+            torch.from_numpy(v_all[:, g])[None], attn_mask=torch.from_numpy(bias)[None])
+        dense[:, h] = ref[0].numpy()
+    return stream, dense
+
+
+@pytest.mark.parametrize("K,S", [(2, 4), (3, 2), (0, 4), (1, 4)])
+def test_bounded_history_equals_dense_attention_with_limited_left_context(K, S):
+    """num_left_chunks = K with ring-recycled pages: streaming over many more chunks than the
+    ring holds equals dense attention where a query chunk sees only its own and the K previous
+    chunks, with absolute distances (the window-relative distances of the oracle are the same).
+    The block size divides the chunk here, so whole-block eviction keeps exactly K chunks."""
+    stream, dense = _bounded_stream(61, steps=9, K=K, C=4, S=S)
+    assert np.abs(stream - dense).max() < 1e-12
+
+
+def test_commit_keeps_the_window_at_the_cap_by_whole_blocks():
+    cache, start = oracle.commit_chunk(np.array([0, 30, 60]), 16, chunk_lens=np.array([16, 5, 0]),
+                                       window_start=np.array([0, 32, 64]), max_cached_frames=40,
+                                       block_size=8)
+    # stream 2: 60 frames > 40, so three 8-frame blocks go: 36 frames from position 88
+    assert cache.tolist() == [16, 35, 36] and start.tolist() == [0, 32, 88]
+    cache, start = oracle.commit_chunk(np.array([3]), 16)
+    assert cache.tolist() == [19] and start is None
