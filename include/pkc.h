@@ -40,6 +40,16 @@
  *   block_tables    int32 [B, M]             logical frame t of stream b is in block
  *                                            block_tables[b][t / S], slot t % S
  *   cache_seqlens   int32 [B]                frames cached before this chunk
+ *   window_start    int32 [B] or NULL        bounded history [ENG 6, 9]: absolute position of
+ *                                            stream b's first cached frame, a multiple of S
+ *                                            (rounded down otherwise). Absolute position p is in
+ *                                            block block_tables[b][(p / S) % M], slot p % S:
+ *                                            the row is a ring of M pages, and a recycled page
+ *                                            is reused without rewriting the table. The cached
+ *                                            frames are [w_b, w_b + cache_seqlens[b]), the chunk
+ *                                            follows them; distances count inside the window
+ *                                            (key index j below), so positions are unaffected.
+ *                                            NULL: every window starts at 0 (no ring)
  *   chunk_lens      int32 [B] or NULL        real frames n_b <= C of each stream's chunk (NULL:
  *                                            every stream has C). Reading of [ENG 9]: frames
  *                                            t >= n_b do not exist - they are not appended, are
@@ -107,7 +117,8 @@ const char* pkc_status_string(int status);
  */
 pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new, void* k_pool,
                            void* v_pool, const int32_t* block_tables, const int32_t* cache_seqlens,
-                           const int32_t* chunk_lens, int32_t batch, int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
+                           const int32_t* chunk_lens, const int32_t* window_start, int32_t batch,
+                           int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_cache_seqlen, hipStream_t stream);
 
@@ -133,7 +144,7 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
 pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_tables,
                                    const int32_t* cache_seqlens, const int32_t* chunk_lens,
-                                   const void* pos, int32_t pos_len,
+                                   const int32_t* window_start, const void* pos, int32_t pos_len,
                                    int32_t pos_per_row, const void* pos_bias_u,
                                    const void* pos_bias_v, void* out, int32_t batch,
                                    int32_t chunk_size, int32_t n_head, int32_t n_kv_head,
@@ -151,8 +162,8 @@ pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k
 pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const void* k_new,
                                        const void* v_new, void* k_pool, void* v_pool,
                                        const int32_t* block_tables, const int32_t* cache_seqlens,
-                                       const int32_t* chunk_lens, const void* pos, int32_t pos_len,
-                                       int32_t pos_per_row,
+                                       const int32_t* chunk_lens, const int32_t* window_start,
+                                       const void* pos, int32_t pos_len, int32_t pos_per_row,
                                        const void* pos_bias_u, const void* pos_bias_v, void* out,
                                        int32_t batch, int32_t chunk_size, int32_t n_head,
                                        int32_t n_kv_head, int32_t head_dim, int32_t block_size,
@@ -169,7 +180,7 @@ pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const voi
  * q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out: HOST arrays of n_layers
  * device pointers, entry l being layer l's buffer of the layout above (entries may repeat, e.g.
  * one positional table for every layer). block_tables, cache_seqlens, chunk_lens and every size
- * are shared by the layers. Layer l's kernel is enqueued after layer l - 1's on the stream; the
+ * window_start and every size are shared by the layers. Layer l's kernel is enqueued after layer l - 1's on the stream; the
  * results equal n_layers calls of paged_kv_append_relpos_attn. The pointer arrays are read during
  * the call only.
  * Errors: those of paged_kv_append_relpos_attn for any layer, n_layers <= 0 -> PKC_ERR_SHAPE.
@@ -179,7 +190,7 @@ pkc_status paged_kv_append_relpos_attn_layers(
     pkc_dtype dtype, int32_t n_layers, const void* const* q, const void* const* k_new,
     const void* const* v_new, void* const* k_pool, void* const* v_pool,
     const int32_t* block_tables, const int32_t* cache_seqlens, const int32_t* chunk_lens,
-    const void* const* pos, int32_t pos_len, int32_t pos_per_row, const void* const* pos_bias_u,
+    const int32_t* window_start, const void* const* pos, int32_t pos_len, int32_t pos_per_row, const void* const* pos_bias_u,
     const void* const* pos_bias_v, void* const* out, int32_t batch, int32_t chunk_size,
     int32_t n_head, int32_t n_kv_head, int32_t head_dim, int32_t block_size, int32_t num_blocks,
     int32_t max_blocks_per_seq, int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream);
@@ -190,12 +201,19 @@ pkc_status paged_kv_append_relpos_attn_layers(
  * step 6 (commit_chunk_paged). It runs on the device, on the caller's stream, so a captured step
  * (layers + commit) can be replayed step after step with no host round trip: the attention reads
  * the cache lengths from device memory and sizes nothing by them, so one graph serves every
- * cache length up to the max_cache_seqlen it was captured with. Keeping cache_seqlens within
+ * cache length up to the max_cache_seqlen it was captured with.
+ * Bounded history [ENG 6, 9]: with window_start non-NULL, whole oldest blocks are then dropped
+ * while cache_seqlens[b] > max_cached_frames: window_start[b] += block_size and cache_seqlens[b]
+ * -= block_size (num_left_chunks = K is max_cached_frames = K * chunk_size with block_size
+ * dividing chunk_size; recycle_streaming_history is the ring's own capacity, at most
+ * max_blocks_per_seq * block_size - chunk_size). Without it, keeping cache_seqlens within
  * max_cache_seqlen is the caller's business (the next attention call clamps, it does not fail).
- * Errors: NULL cache_seqlens -> PKC_ERR_NULL; batch or chunk_size <= 0 -> PKC_ERR_SHAPE.
+ * Errors: NULL cache_seqlens -> PKC_ERR_NULL; batch or chunk_size <= 0, or with window_start a
+ * block_size <= 0 or a negative cap -> PKC_ERR_SHAPE.
  */
-pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int32_t batch,
-                           int32_t chunk_size, hipStream_t stream);
+pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,
+                           int32_t* window_start, int32_t max_cached_frames, int32_t batch,
+                           int32_t chunk_size, int32_t block_size, hipStream_t stream);
 
 /*
  * varlen_packed_relpos_attn - full-context attention inside each utterance of a packed, gapless

@@ -27,17 +27,14 @@ _f32 = ctypes.c_float
 SIGNATURES = {
     "pkc_version": ([], ctypes.c_int),
     "pkc_status_string": ([ctypes.c_int], ctypes.c_char_p),
-    "paged_kv_append": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr] + [_i32] * 8
-                        + [_ptr], ctypes.c_int),
-    "chunk_paged_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _i32, _i32,
-                                 _ptr, _ptr, _ptr] + [_i32] * 9 + [_f32, _ptr], ctypes.c_int),
-    "paged_kv_append_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
-                                     _ptr, _i32, _i32, _ptr, _ptr, _ptr] + [_i32] * 9
-                                    + [_f32, _ptr], ctypes.c_int),
-    "paged_kv_append_relpos_attn_layers": ([ctypes.c_int, _i32] + [_ptr] * 5 + [_ptr] * 3 + [_ptr]
-                                           + [_i32, _i32] + [_ptr] * 3 + [_i32] * 9 + [_f32, _ptr],
-                                           ctypes.c_int),
-    "paged_kv_commit": ([_ptr, _ptr, _i32, _i32, _ptr], ctypes.c_int),
+    "paged_kv_append": ([ctypes.c_int] + [_ptr] * 8 + [_i32] * 8 + [_ptr], ctypes.c_int),
+    "chunk_paged_relpos_attn": ([ctypes.c_int] + [_ptr] * 8 + [_i32, _i32] + [_ptr] * 3
+                                + [_i32] * 9 + [_f32, _ptr], ctypes.c_int),
+    "paged_kv_append_relpos_attn": ([ctypes.c_int] + [_ptr] * 10 + [_i32, _i32] + [_ptr] * 3
+                                    + [_i32] * 9 + [_f32, _ptr], ctypes.c_int),
+    "paged_kv_append_relpos_attn_layers": ([ctypes.c_int, _i32] + [_ptr] * 10 + [_i32, _i32]
+                                           + [_ptr] * 3 + [_i32] * 9 + [_f32, _ptr], ctypes.c_int),
+    "paged_kv_commit": ([_ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _ptr], ctypes.c_int),
     "varlen_packed_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _ptr,
                                    _ptr, _ptr, _ptr, _i32, _i32, _i32, _f32, _ptr], ctypes.c_int),
 }
@@ -114,21 +111,22 @@ def _stream(stream):
 
 
 def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, max_cache_seqlen,
-                    chunk_lens=None, stream=None):
+                    chunk_lens=None, window_start=None, stream=None):
     """Write k_new / v_new [B, C, Hk, D] into k_pool [N, Hk, S, D] / v_pool [N, Hk, D, S]
     (only the first chunk_lens[b] frames of stream b when chunk_lens is given)."""
     B, C, Hk, D = k_new.shape
     N, _, S, _ = k_pool.shape
     st = lib().paged_kv_append(_dtype(k_new, v_new, k_pool, v_pool), _p(k_new), _p(v_new),
                                _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
-                               _table(chunk_lens), B, C, Hk, D, S, N, block_tables.shape[1],
+                               _table(chunk_lens), _table(window_start), B, C, Hk, D, S, N,
+                               block_tables.shape[1],
                                int(max_cache_seqlen), _stream(stream))
     _check(st, "paged_kv_append")
 
 
 def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u,
                             pos_bias_v, max_cache_seqlen, per_row_pos=False, out=None,
-                            softmax_scale=0.0, chunk_lens=None, stream=None):
+                            softmax_scale=0.0, chunk_lens=None, window_start=None, stream=None):
     """Chunk attention; q [B, C, H, D]; pos shared [P, H, D] or per-row [B, P, H, D];
     chunk_lens int32 [B] (optional): real frames per stream."""
     B, C, H, D = q.shape
@@ -138,8 +136,8 @@ def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos,
     P = pos.shape[1] if per_row_pos else pos.shape[0]
     st = lib().chunk_paged_relpos_attn(
         _dtype(q, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out), _p(q), _p(k_pool), _p(v_pool),
-        _table(block_tables), _table(cache_seqlens), _table(chunk_lens), _p(pos), P,
-        int(bool(per_row_pos)), _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk, D, S, N,
+        _table(block_tables), _table(cache_seqlens), _table(chunk_lens), _table(window_start),
+        _p(pos), P, int(bool(per_row_pos)), _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk, D, S, N,
         block_tables.shape[1],
         int(max_cache_seqlen), float(softmax_scale), _stream(stream))
     _check(st, "chunk_paged_relpos_attn")
@@ -148,7 +146,8 @@ def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos,
 
 def paged_kv_append_relpos_attn(q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, pos,
                                 pos_bias_u, pos_bias_v, max_cache_seqlen, per_row_pos=False,
-                                out=None, softmax_scale=0.0, chunk_lens=None, stream=None):
+                                out=None, softmax_scale=0.0, chunk_lens=None, window_start=None,
+                                stream=None):
     """Append and attention of one layer in one launch (pools are written); chunk_lens int32 [B]
     (optional): real frames per stream."""
     B, C, H, D = q.shape
@@ -159,8 +158,8 @@ def paged_kv_append_relpos_attn(q, k_new, v_new, k_pool, v_pool, block_tables, c
     st = lib().paged_kv_append_relpos_attn(
         _dtype(q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out), _p(q),
         _p(k_new), _p(v_new), _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
-        _table(chunk_lens), _p(pos), P, int(bool(per_row_pos)), _p(pos_bias_u), _p(pos_bias_v),
-        _p(out), B, C, H, Hk,
+        _table(chunk_lens), _table(window_start), _p(pos), P, int(bool(per_row_pos)),
+        _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk,
         D, S, N, block_tables.shape[1], int(max_cache_seqlen), float(softmax_scale),
         _stream(stream))
     _check(st, "paged_kv_append_relpos_attn")
@@ -175,8 +174,8 @@ def _ptr_array(ts):
 
 
 def paged_kv_append_relpos_attn_layers(layers, block_tables, cache_seqlens, max_cache_seqlen,
-                                       per_row_pos=False, chunk_lens=None, softmax_scale=0.0,
-                                       stream=None):
+                                       per_row_pos=False, chunk_lens=None, window_start=None,
+                                       softmax_scale=0.0, stream=None):
     """Fused append + attention of several layers in one call. ``layers``: a sequence of objects
     with attributes q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out (one per
     layer, same shapes); block tables, cache and chunk lengths are shared."""
@@ -194,17 +193,21 @@ def paged_kv_append_relpos_attn_layers(layers, block_tables, cache_seqlens, max_
     arrs = {n: _ptr_array([getattr(x, n) for x in layers]) for n in names}
     st = lib().paged_kv_append_relpos_attn_layers(
         dt, len(layers), arrs["q"], arrs["k_new"], arrs["v_new"], arrs["k_pool"], arrs["v_pool"],
-        _table(block_tables), _table(cache_seqlens), _table(chunk_lens), arrs["pos"], P,
+        _table(block_tables), _table(cache_seqlens), _table(chunk_lens), _table(window_start),
+        arrs["pos"], P,
         int(bool(per_row_pos)), arrs["pos_bias_u"], arrs["pos_bias_v"], arrs["out"], B, C, H, Hk,
         D, S, N, block_tables.shape[1], int(max_cache_seqlen), float(softmax_scale),
         _stream(stream))
     _check(st, "paged_kv_append_relpos_attn_layers")
 
 
-def paged_kv_commit(cache_seqlens, chunk, chunk_lens=None, stream=None):
-    """cache_seqlens[b] += chunk_lens[b] (or chunk) on the device."""
-    st = lib().paged_kv_commit(_table(cache_seqlens), _table(chunk_lens), cache_seqlens.shape[0],
-                               int(chunk), _stream(stream))
+def paged_kv_commit(cache_seqlens, chunk, chunk_lens=None, window_start=None,
+                    max_cached_frames=0, block_size=0, stream=None):
+    """cache_seqlens[b] += chunk_lens[b] (or chunk) on the device; with window_start, whole
+    oldest blocks are then dropped while a cache exceeds max_cached_frames."""
+    st = lib().paged_kv_commit(_table(cache_seqlens), _table(chunk_lens), _table(window_start),
+                               int(max_cached_frames), cache_seqlens.shape[0], int(chunk),
+                               int(block_size), _stream(stream))
     _check(st, "paged_kv_commit")
 
 

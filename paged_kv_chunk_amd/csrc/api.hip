@@ -9,7 +9,7 @@ using namespace pkc;
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: per-stream chunk lengths
+constexpr int kVersion = 300;  // 0.3.0: chunk lengths, bounded history, multi-layer step
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -73,7 +73,7 @@ const char* pkc_status_string(int status) {
 
 pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new, void* k_pool,
                            void* v_pool, const int32_t* block_tables, const int32_t* cache_seqlens,
-                           const int32_t* chunk_lens, int32_t batch, int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
+                           const int32_t* chunk_lens, const int32_t* window_start, int32_t batch, int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_cache_seqlen, hipStream_t stream) {
   pkc_status st = check_dtype(dtype);
@@ -84,7 +84,8 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
   if (st != PKC_OK) return st;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
     return PKC_ERR_ALIGN;
-  AppendParams p{k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, chunk_lens, batch, chunk_size,
+  AppendParams p{k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, chunk_lens,
+                 window_start, batch, chunk_size,
                  n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq, max_cache_seqlen};
   return from_hip(launch_paged_append(dtype, p, stream));
 }
@@ -93,7 +94,7 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
                               const void* k_pool, const void* v_pool, void* k_pool_w,
                               void* v_pool_w, const int32_t* block_tables,
                               const int32_t* cache_seqlens, const int32_t* chunk_lens,
-                              const void* pos, int32_t pos_len,
+                              const int32_t* window_start, const void* pos, int32_t pos_len,
                               int32_t pos_per_row, const void* pos_bias_u, const void* pos_bias_v,
                               void* out, int32_t batch, int32_t chunk_size, int32_t n_head,
                               int32_t n_kv_head, int32_t head_dim, int32_t block_size,
@@ -125,6 +126,7 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
   p.block_tables = block_tables;
   p.cache_seqlens = cache_seqlens;
   p.chunk_lens = chunk_lens;
+  p.window_start = window_start;
   p.pos = pos;
   p.pos_bias_u = pos_bias_u;
   p.pos_bias_v = pos_bias_v;
@@ -152,7 +154,7 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
 pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_tables,
                                    const int32_t* cache_seqlens, const int32_t* chunk_lens,
-                                   const void* pos, int32_t pos_len,
+                                   const int32_t* window_start, const void* pos, int32_t pos_len,
                                    int32_t pos_per_row, const void* pos_bias_u,
                                    const void* pos_bias_v, void* out, int32_t batch,
                                    int32_t chunk_size, int32_t n_head, int32_t n_kv_head,
@@ -160,7 +162,7 @@ pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k
                                    int32_t max_blocks_per_seq, int32_t max_cache_seqlen,
                                    float softmax_scale, hipStream_t stream) {
   return attn_common(dtype, q, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_tables,
-                     cache_seqlens, chunk_lens, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
+                     cache_seqlens, chunk_lens, window_start, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
                      chunk_size, n_head, n_kv_head, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_cache_seqlen, softmax_scale, stream);
 }
@@ -168,8 +170,8 @@ pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k
 pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const void* k_new,
                                        const void* v_new, void* k_pool, void* v_pool,
                                        const int32_t* block_tables, const int32_t* cache_seqlens,
-                                       const int32_t* chunk_lens, const void* pos, int32_t pos_len,
-                                       int32_t pos_per_row,
+                                       const int32_t* chunk_lens, const int32_t* window_start,
+                                       const void* pos, int32_t pos_len, int32_t pos_per_row,
                                        const void* pos_bias_u, const void* pos_bias_v, void* out,
                                        int32_t batch, int32_t chunk_size, int32_t n_head,
                                        int32_t n_kv_head, int32_t head_dim, int32_t block_size,
@@ -178,7 +180,7 @@ pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const voi
                                        hipStream_t stream) {
   if (!k_new || !v_new) return PKC_ERR_NULL;
   return attn_common(dtype, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, block_tables,
-                     cache_seqlens, chunk_lens, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
+                     cache_seqlens, chunk_lens, window_start, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
                      chunk_size, n_head, n_kv_head, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_cache_seqlen, softmax_scale, stream);
 }
@@ -187,7 +189,7 @@ pkc_status paged_kv_append_relpos_attn_layers(
     pkc_dtype dtype, int32_t n_layers, const void* const* q, const void* const* k_new,
     const void* const* v_new, void* const* k_pool, void* const* v_pool,
     const int32_t* block_tables, const int32_t* cache_seqlens, const int32_t* chunk_lens,
-    const void* const* pos, int32_t pos_len, int32_t pos_per_row, const void* const* pos_bias_u,
+    const int32_t* window_start, const void* const* pos, int32_t pos_len, int32_t pos_per_row, const void* const* pos_bias_u,
     const void* const* pos_bias_v, void* const* out, int32_t batch, int32_t chunk_size,
     int32_t n_head, int32_t n_kv_head, int32_t head_dim, int32_t block_size, int32_t num_blocks,
     int32_t max_blocks_per_seq, int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream) {
@@ -201,7 +203,8 @@ pkc_status paged_kv_append_relpos_attn_layers(
     for (int l = 0; l < n_layers; ++l) {
       if (!k_new[l] || !v_new[l]) return PKC_ERR_NULL;
       st = attn_common(dtype, q[l], k_new[l], v_new[l], k_pool[l], v_pool[l], k_pool[l],
-                       v_pool[l], block_tables, cache_seqlens, chunk_lens, pos[l], pos_len,
+                       v_pool[l], block_tables, cache_seqlens, chunk_lens, window_start, pos[l],
+                       pos_len,
                        pos_per_row, pos_bias_u[l], pos_bias_v[l], out[l], batch, chunk_size,
                        n_head, n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_cache_seqlen, softmax_scale, stream, pass == 1);
@@ -211,11 +214,14 @@ pkc_status paged_kv_append_relpos_attn_layers(
   return PKC_OK;
 }
 
-pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int32_t batch,
-                           int32_t chunk_size, hipStream_t stream) {
+pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,
+                           int32_t* window_start, int32_t max_cached_frames, int32_t batch,
+                           int32_t chunk_size, int32_t block_size, hipStream_t stream) {
   if (!cache_seqlens) return PKC_ERR_NULL;
   if (batch <= 0 || chunk_size <= 0) return PKC_ERR_SHAPE;
-  return from_hip(launch_commit(cache_seqlens, chunk_lens, batch, chunk_size, stream));
+  if (window_start && (block_size <= 0 || max_cached_frames < 0)) return PKC_ERR_SHAPE;
+  return from_hip(launch_commit(cache_seqlens, chunk_lens, window_start, max_cached_frames,
+                                block_size, batch, chunk_size, stream));
 }
 
 pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,

@@ -65,6 +65,7 @@ struct ChunkArgs {
   const int32_t* bt;
   const int32_t* cs;
   const int32_t* lens;   // real frames per stream, or null
+  const int32_t* ws;     // window start per stream (bounded history), or null
   const T* pos;
   const T* u;
   const T* w;
@@ -124,9 +125,13 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const int32_t* bt = a.bt + (size_t)b * a.M;
 
   // ---- 1. requests that need nothing: block IDs of pages [0, 128), queries, u, v, chunk -------
+  // With bounded history the table row is a ring: the window's page pg sits at entry
+  // (pb + pg) mod M, pb = window start / S (whole blocks), so the window follows the start.
   const int nwin = min(a.M, kBtWindow);
-  const int bt_lo = lane < nwin ? bt[lane] : 0;
-  const int bt_hi = lane + 64 < nwin ? bt[lane + 64] : 0;
+  const int pb = a.ws ? (max(a.ws[b], 0) >> logS) % a.M : 0;
+  auto ring = [&](int pg) { const int e = pg + pb; return e >= a.M ? e - a.M : e; };
+  const int bt_lo = lane < nwin ? bt[ring(lane)] : 0;
+  const int bt_hi = lane + 64 < nwin ? bt[ring(lane + 64)] : 0;
   F qq[2], uu[2], ww[2];
   {
     const int iq = min(qt * 16 + m16, a.C - 1);
@@ -184,12 +189,12 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   auto band_row = [&](int r) { return ptab + (size_t)(uint32_t)clampi(r, rlo, rhi) * prow; };
 
   // the window, and a page's block ID from it (pages past it: straight from the table). The
-  // masked last body step can reach one page past the stream's table row: such pages read as
-  // block 0 in the window and as the row's last entry past it (their frames are masked).
+  // masked last body step can reach one page past the stream's pages: such pages read as block 0
+  // in the window and as another entry of the row past it (their frames are masked).
   s_win[lane] = clampi(bt_lo, 0, a.N - 1);
   s_win[64 + lane] = clampi(bt_hi, 0, a.N - 1);
   auto block_of = [&](int pg) -> uint32_t {
-    return (uint32_t)(pg < kBtWindow ? s_win[pg] : clampi(bt[min(pg, a.M - 1)], 0, a.N - 1));
+    return (uint32_t)(pg < kBtWindow ? s_win[pg] : clampi(bt[ring(min(pg, a.M - 1))], 0, a.N - 1));
   };
   // the chunk's frames into the LDS tail (row t = frame t; V transposed, zero past the chunk)
   if constexpr (kRegTail) {
@@ -513,6 +518,7 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   a.bt = p.block_tables;
   a.cs = p.cache_seqlens;
   a.lens = p.chunk_lens;
+  a.ws = p.window_start;
   a.pos = (const T*)p.pos;
   a.u = (const T*)p.pos_bias_u;
   a.w = (const T*)p.pos_bias_v;

@@ -4,7 +4,9 @@
 // cohort, one block-table row per stream, the chunk written at logical frames
 // [cache_seqlens[b], cache_seqlens[b] + C), cache_seqlens advanced only after the forward; step 6
 // commits each stream's actual frames, so with per-stream chunk lengths n_b only the first n_b
-// frames are written (a padding lane, n_b = 0, writes nothing; section 9).
+// frames are written (a padding lane, n_b = 0, writes nothing; section 9). With bounded history
+// (sections 6 and 9) a stream's frames are addressed by absolute position p = window_start + t
+// through its table row used as a ring: block block_tables[b][(p / S) % M], slot p % S.
 //
 // One workgroup per (stream, kv head). K rows are copied 16 bytes per lane straight into their
 // slots (rows of the K page are contiguous). V pages are stored transposed ([head_dim][block_size])
@@ -26,7 +28,7 @@ __global__ void __launch_bounds__(kThreads)
 paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ k_pool,
                     T* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
                     const int32_t* __restrict__ cache_seqlens, const int32_t* __restrict__ chunk_lens,
-                    int chunk, int n_kv_head, int head_dim,
+                    const int32_t* __restrict__ window_start, int chunk, int n_kv_head, int head_dim,
                     int block_size, int num_blocks, int max_blocks, int max_cache) {
   extern __shared__ unsigned char smem_raw[];
   T* sv = reinterpret_cast<T*>(smem_raw);  // [kTileFrames][head_dim + pad]
@@ -35,7 +37,9 @@ paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T*
 
   const int b = blockIdx.x / n_kv_head;
   const int g = blockIdx.x % n_kv_head;
-  const int cache = clampi(cache_seqlens[b], 0, max_cache);
+  // absolute position of the chunk's first frame; the window start is a whole number of blocks
+  const int start = window_start ? max(window_start[b], 0) / block_size * block_size : 0;
+  const int cache = start + clampi(cache_seqlens[b], 0, max_cache);
   const int32_t* bt = block_tables + (size_t)b * max_blocks;
   const int nvec = head_dim / VEC;
   const int n_real = chunk_lens ? clampi(chunk_lens[b], 0, chunk) : chunk;
@@ -47,7 +51,7 @@ paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T*
       const int t = t0 + x / nvec;
       const int dv = (x % nvec) * VEC;
       const int frame = cache + t;
-      const int blk = clampi(bt[frame / block_size], 0, num_blocks - 1);
+      const int blk = clampi(bt[(frame / block_size) % max_blocks], 0, num_blocks - 1);
       const int slot = frame % block_size;
       const size_t src = (((size_t)b * chunk + t) * n_kv_head + g) * head_dim + dv;
       const uint4 kv = *reinterpret_cast<const uint4*>(k_new + src);
@@ -60,7 +64,7 @@ paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T*
       const int d = x / nt;
       const int tl = x % nt;
       const int frame = cache + t0 + tl;
-      const int blk = clampi(bt[frame / block_size], 0, num_blocks - 1);
+      const int blk = clampi(bt[(frame / block_size) % max_blocks], 0, num_blocks - 1);
       const int slot = frame % block_size;
       v_pool[(((size_t)blk * n_kv_head + g) * head_dim + d) * block_size + slot] = sv[tl * pitch + d];
     }
@@ -69,20 +73,31 @@ paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T*
 }
 
 // cache_seqlens[b] += real frames of stream b ("ASR Engine", section 4.3 step 6,
-// commit_chunk_paged), on the device so that a captured step needs no host round trip.
+// commit_chunk_paged), on the device so that a captured step needs no host round trip. With a
+// window start and a cap (bounded history, sections 6 and 9), whole oldest blocks are then
+// dropped while the cache exceeds the cap.
 __global__ void __launch_bounds__(kThreads)
-commit_kernel(int32_t* __restrict__ cache_seqlens, const int32_t* __restrict__ chunk_lens, int batch,
+commit_kernel(int32_t* __restrict__ cache_seqlens, const int32_t* __restrict__ chunk_lens,
+              int32_t* __restrict__ window_start, int max_cached, int block_size, int batch,
               int chunk) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b < batch) cache_seqlens[b] += chunk_lens ? clampi(chunk_lens[b], 0, chunk) : chunk;
+  if (b >= batch) return;
+  int cache = cache_seqlens[b] + (chunk_lens ? clampi(chunk_lens[b], 0, chunk) : chunk);
+  if (window_start && cache > max_cached) {
+    const int drop = (cache - max_cached + block_size - 1) / block_size;
+    window_start[b] += drop * block_size;
+    cache -= drop * block_size;
+  }
+  cache_seqlens[b] = cache;
 }
 
 }  // namespace
 
-hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int batch, int chunk,
-                         hipStream_t stream) {
+hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int32_t* window_start,
+                         int max_cached, int block_size, int batch, int chunk, hipStream_t stream) {
   hipLaunchKernelGGL(commit_kernel, dim3((batch + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, cache_seqlens, chunk_lens, batch, chunk);
+                     stream, cache_seqlens, chunk_lens, window_start, max_cached, block_size, batch,
+                     chunk);
   return hipGetLastError();
 }
 
@@ -92,13 +107,15 @@ hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream
     const size_t smem = (size_t)kTileFrames * (p.head_dim + 8) * sizeof(bf16);
     hipLaunchKernelGGL(paged_append_kernel<bf16>, grid, dim3(kThreads), smem, stream,
                        (const bf16*)p.k_new, (const bf16*)p.v_new, (bf16*)p.k_pool, (bf16*)p.v_pool,
-                       p.block_tables, p.cache_seqlens, p.chunk_lens, p.chunk, p.n_kv_head, p.head_dim,
+                       p.block_tables, p.cache_seqlens, p.chunk_lens, p.window_start, p.chunk,
+                       p.n_kv_head, p.head_dim,
                        p.block_size, p.num_blocks, p.max_blocks, p.max_cache);
   } else {
     const size_t smem = (size_t)kTileFrames * (p.head_dim + 4) * sizeof(float);
     hipLaunchKernelGGL(paged_append_kernel<float>, grid, dim3(kThreads), smem, stream,
                        (const float*)p.k_new, (const float*)p.v_new, (float*)p.k_pool,
-                       (float*)p.v_pool, p.block_tables, p.cache_seqlens, p.chunk_lens, p.chunk,
+                       (float*)p.v_pool, p.block_tables, p.cache_seqlens, p.chunk_lens,
+                       p.window_start, p.chunk,
                        p.n_kv_head, p.head_dim, p.block_size, p.num_blocks, p.max_blocks, p.max_cache);
   }
   return hipGetLastError();

@@ -17,6 +17,7 @@ struct AppendParams {
   const int32_t* block_tables;
   const int32_t* cache_seqlens;
   const int32_t* chunk_lens;   // real frames per stream, or null: all chunk frames
+  const int32_t* window_start; // absolute position of each stream's first cached frame, or null
   int batch, chunk, n_kv_head, head_dim, block_size, num_blocks, max_blocks, max_cache;
 };
 
@@ -27,6 +28,7 @@ struct AttnParams {
   const int32_t* block_tables;
   const int32_t* cache_seqlens;
   const int32_t* chunk_lens;   // real frames per stream, or null: all chunk frames
+  const int32_t* window_start; // absolute position of each stream's first cached frame, or null
   const void* pos;
   const void* pos_bias_u;
   const void* pos_bias_v;
@@ -56,8 +58,8 @@ struct VarlenParams {
 };
 
 hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream);
-hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int batch, int chunk,
-                         hipStream_t stream);
+hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int32_t* window_start,
+                         int max_cached, int block_size, int batch, int chunk, hipStream_t stream);
 hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream);
 hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_t stream);
 

@@ -59,14 +59,15 @@ def test_version_and_status_strings(lib):
 
 def append(lib, dtype=1, k_new=P, v_new=P, k_pool=P, v_pool=P, bt=P, cs=P, B=2, C=16, Hk=4, D=64,
            S=16, N=32, M=8, max_cache=64):
-    return lib.paged_kv_append(dtype, k_new, v_new, k_pool, v_pool, bt, cs, None, B, C, Hk, D, S,
-                               N, M, max_cache, None)
+    return lib.paged_kv_append(dtype, k_new, v_new, k_pool, v_pool, bt, cs, None, None, B, C, Hk,
+                               D, S, N, M, max_cache, None)
 
 
 def attn(lib, dtype=1, q=P, k_pool=P, v_pool=P, bt=P, cs=P, pos=P, pos_len=159, per_row=0, u=P,
          w=P, out=P, B=2, C=16, H=4, Hk=4, D=64, S=16, N=32, M=8, max_cache=64, scale=0.0):
-    return lib.chunk_paged_relpos_attn(dtype, q, k_pool, v_pool, bt, cs, None, pos, pos_len, per_row,
-                                       u, w, out, B, C, H, Hk, D, S, N, M, max_cache, scale, None)
+    return lib.chunk_paged_relpos_attn(dtype, q, k_pool, v_pool, bt, cs, None, None, pos, pos_len,
+                                       per_row, u, w, out, B, C, H, Hk, D, S, N, M, max_cache,
+                                       scale, None)
 
 
 def fused(lib, k_new=P, v_new=P, **kw):
@@ -74,7 +75,7 @@ def fused(lib, k_new=P, v_new=P, **kw):
              w=P, out=P, B=2, C=16, H=4, Hk=4, D=64, S=16, N=32, M=8, max_cache=64, scale=0.0)
     a.update(kw)
     return lib.paged_kv_append_relpos_attn(a["dtype"], a["q"], k_new, v_new, a["k_pool"],
-                                           a["v_pool"], a["bt"], a["cs"], None, a["pos"],
+                                           a["v_pool"], a["bt"], a["cs"], None, None, a["pos"],
                                            a["pos_len"],
                                            a["per_row"], a["u"], a["w"], a["out"], a["B"], a["C"],
                                            a["H"], a["Hk"], a["D"], a["S"], a["N"], a["M"],
@@ -165,7 +166,7 @@ def layers_call(lib, n_layers=3, hole=None, dtype=1, C=16, max_cache=64):
         arrs[n] = a
     return lib.paged_kv_append_relpos_attn_layers(
         dtype, n_layers, arrs["q"], arrs["k_new"], arrs["v_new"], arrs["k_pool"], arrs["v_pool"],
-        P, P, None, arrs["pos"], 159, 0, arrs["u"], arrs["w"], arrs["out"], 2, C, 4, 4, 64, 16, 32,
+        P, P, None, None, arrs["pos"], 159, 0, arrs["u"], arrs["w"], arrs["out"], 2, C, 4, 4, 64, 16, 32,
         8, max_cache, 0.0, None)
 
 
@@ -180,6 +181,8 @@ def test_layers_validation_launches_nothing_on_error(lib):
 
 
 def test_commit_validation(lib):
-    assert lib.paged_kv_commit(None, None, 4, 16, None) == NULL
-    assert lib.paged_kv_commit(P, None, 0, 16, None) == SHAPE
-    assert lib.paged_kv_commit(P, None, 4, 0, None) == SHAPE
+    assert lib.paged_kv_commit(None, None, None, 0, 4, 16, 16, None) == NULL
+    assert lib.paged_kv_commit(P, None, None, 0, 0, 16, 16, None) == SHAPE
+    assert lib.paged_kv_commit(P, None, None, 0, 4, 0, 16, None) == SHAPE
+    assert lib.paged_kv_commit(P, None, P, 64, 4, 16, 0, None) == SHAPE
+    assert lib.paged_kv_commit(P, None, P, -1, 4, 16, 16, None) == SHAPE

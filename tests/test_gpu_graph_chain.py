@@ -143,3 +143,85 @@ def test_layers_entry_equals_per_layer_calls_bitwise():
     for co, r in zip(layers, twin):
         np.testing.assert_array_equal(bits(co.out), bits(r.out))
         np.testing.assert_array_equal(bits(co.k_pool), bits(r.k_pool))
+
+
+def test_bounded_history_stream_from_one_graph():
+    """num_left_chunks = 3 over a ring of 4 pages: eight steps (the ring wraps twice) replayed
+    from one captured step - layers plus the evicting commit - equal the eager sequence bitwise
+    and, on the last step, the oracle's bounded-history streaming."""
+    Bq, Lq, K, steps = 2, 2, 3, 8
+    cap = K * C
+    M = (cap + C) // S
+    layers = []
+    base = None
+    for l in range(Lq):
+        co = make_chunk_cohort(Bq, H, D, C, S, [cap] * Bq, dtype=torch.bfloat16, seed=70 + l,
+                               device=DEV, max_blocks_per_seq=M)
+        if base is None:
+            base = co
+        co.block_tables = base.block_tables
+        co.out = torch.empty_like(co.q)
+        layers.append(co)
+    bt = base.block_tables
+    assert (bt >= 0).all()                                  # every ring entry is a page
+    cs = torch.zeros(Bq, dtype=torch.int32, device=DEV)
+    ws = torch.tensor([0, 5 * S], dtype=torch.int32, device=DEV)    # stream 1 starts mid-ring
+    ref = [copy.copy(co) for co in layers]
+    for co, r in zip(layers, ref):
+        for n in ["q", "k_new", "v_new", "k_pool", "v_pool", "out"]:
+            setattr(r, n, getattr(co, n).clone())
+    ref_cs, ref_ws = cs.clone(), ws.clone()
+
+    def inputs(step):
+        g = torch.Generator().manual_seed(2000 + step)
+        return [[torch.randn((Bq, C, H, D), generator=g).to(torch.bfloat16) for _ in range(3)]
+                for _ in range(Lq)]
+
+    def load(ls, step):
+        for co, (q, k, v) in zip(ls, inputs(step)):
+            co.q.copy_(q)
+            co.k_new.copy_(k)
+            co.v_new.copy_(v)
+
+    ref_out, snap = [], None
+    for step in range(steps):
+        load(ref, step)
+        if step == steps - 1:
+            snap = (host64(ref[0].k_pool), host64(ref[0].v_pool), ref_cs.cpu().numpy().copy(),
+                    ref_ws.cpu().numpy().copy())
+        pkc.paged_kv_append_relpos_attn_layers(ref, bt, ref_cs, cap, window_start=ref_ws)
+        pkc.paged_kv_commit(ref_cs, C, window_start=ref_ws, max_cached_frames=cap, block_size=S)
+        torch.cuda.synchronize()
+        ref_out.append([bits(co.out) for co in ref])
+        assert int(ref_cs.max()) <= cap
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            pkc.paged_kv_append_relpos_attn_layers(layers, bt, cs, cap, window_start=ws,
+                                                   stream=side)
+            pkc.paged_kv_commit(cs, C, window_start=ws, max_cached_frames=cap, block_size=S,
+                                stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for step in range(steps):
+        load(layers, step)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for l, co in enumerate(layers):
+            np.testing.assert_array_equal(bits(co.out), ref_out[step][l], err_msg=f"step {step}")
+    assert cs.cpu().tolist() == ref_cs.cpu().tolist() == [cap] * Bq
+    assert ws.cpu().tolist() == ref_ws.cpu().tolist() == [steps * C - cap, 5 * S + steps * C - cap]
+
+    kp, vp, c_last, w_last = snap
+    q, k, v = [host64(x) for x in inputs(steps - 1)[0]]
+    btn = bt.cpu().numpy()
+    kp2, vp2 = oracle.paged_kv_append(kp, vp, k, v, btn, c_last, window_start=w_last)
+    co = layers[0]
+    expect = oracle.chunk_relpos_attn(q, kp2, vp2, btn, c_last, host64(co.pos),
+                                      host64(co.pos_bias_u), host64(co.pos_bias_v),
+                                      window_start=w_last)
+    assert np.abs(co.out.detach().cpu().double().numpy() - expect).max() <= TOL[torch.bfloat16]

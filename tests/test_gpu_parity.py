@@ -378,3 +378,93 @@ def test_padding_lanes_are_inert_and_leave_other_rows_bitwise_unchanged():
     np.testing.assert_array_equal(bits(kp[:N]), bits(base.k_pool))
     np.testing.assert_array_equal(bits(vp[:N]), bits(base.v_pool))
     assert torch.isnan(kp[N:]).all() and torch.isnan(vp[N:]).all()
+
+
+# --------------------------------------------------------------------------------------------
+# Bounded history: window starts and ring-addressed tables
+# --------------------------------------------------------------------------------------------
+
+def _as_ring(co, seed, wraps=3):
+    """The same cohort addressed through rings: stream b gets a window start w_b (a whole number
+    of blocks, several times round the ring) and its table row rotated so that the window's
+    pages land on the same physical blocks. Returns (window_start tensor, ring tables)."""
+    rng = np.random.default_rng(seed)
+    bt = co.block_tables.cpu().numpy()
+    M = bt.shape[1]
+    S = co.block_size
+    ring = np.full_like(bt, -1)
+    starts = []
+    for b in range(bt.shape[0]):
+        k = int(rng.integers(0, wraps * M))
+        starts.append(k * S)
+        for i in range(M):
+            ring[b, (k + i) % M] = bt[b, i]
+    return (torch.tensor(starts, dtype=torch.int32, device=DEV),
+            torch.from_numpy(ring).to(DEV))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("name", ["bf16_ragged", "odd_lengths", "per_row_ragged_fp32",
+                                  "long_chunk_bf16"])
+def test_ring_tables_with_window_starts_equal_plain_tables_bitwise(name, fused):
+    """A window start that moves the stream's pages round its ring, with the table row rotated to
+    match, addresses the same frames: outputs and pools are bitwise those of the plain table, and
+    match the oracle's ring addressing."""
+    co = poison(small_cohort(name, seed=12))
+    co2 = clone(co)
+    ws, ring = _as_ring(co, 13)
+    lens = _lens_for(co, 14)
+    t = torch.from_numpy(lens).to(DEV)
+    plain = gpu_chunk(co, fused=fused, chunk_lens=t)
+    co2.block_tables = ring
+    if fused:
+        out = pkc.paged_kv_append_relpos_attn(co2.q, co2.k_new, co2.v_new, co2.k_pool, co2.v_pool,
+                                              ring, co2.cache_seqlens, co2.pos, co2.pos_bias_u,
+                                              co2.pos_bias_v, co2.max_cache_seqlen,
+                                              per_row_pos=co2.per_row_pos, chunk_lens=t,
+                                              window_start=ws)
+    else:
+        pkc.paged_kv_append(co2.k_new, co2.v_new, co2.k_pool, co2.v_pool, ring, co2.cache_seqlens,
+                            co2.max_cache_seqlen, chunk_lens=t, window_start=ws)
+        out = pkc.chunk_paged_relpos_attn(co2.q, co2.k_pool, co2.v_pool, ring, co2.cache_seqlens,
+                                          co2.pos, co2.pos_bias_u, co2.pos_bias_v,
+                                          co2.max_cache_seqlen, per_row_pos=co2.per_row_pos,
+                                          chunk_lens=t, window_start=ws)
+    np.testing.assert_array_equal(bits(out), bits(plain))
+    np.testing.assert_array_equal(bits(co2.k_pool), bits(co.k_pool))
+    np.testing.assert_array_equal(bits(co2.v_pool), bits(co.v_pool))
+
+
+def test_ring_addressing_matches_the_oracle():
+    co = poison(small_cohort("gqa_h4_k2", seed=15))
+    ws, ring = _as_ring(co, 16)
+    co.block_tables = ring
+    h = {k: host64(getattr(co, k)) for k in ["q", "k_new", "v_new", "k_pool", "v_pool", "pos",
+                                             "pos_bias_u", "pos_bias_v"]}
+    bt, cs, w = ring.cpu().numpy(), co.cache_seqlens.cpu().numpy(), ws.cpu().numpy()
+    kp, vp = oracle.paged_kv_append(h["k_pool"], h["v_pool"], h["k_new"], h["v_new"], bt, cs,
+                                    window_start=w)
+    ref = oracle.chunk_relpos_attn(h["q"], kp, vp, bt, cs, h["pos"], h["pos_bias_u"],
+                                   h["pos_bias_v"], window_start=w)
+    out = pkc.paged_kv_append_relpos_attn(co.q, co.k_new, co.v_new, co.k_pool, co.v_pool, ring,
+                                          co.cache_seqlens, co.pos, co.pos_bias_u, co.pos_bias_v,
+                                          co.max_cache_seqlen, window_start=ws)
+    assert max_err(out, ref) <= TOL[co.q.dtype]
+
+
+def test_commit_with_eviction_matches_the_oracle():
+    rng = np.random.default_rng(17)
+    B, C, S, cap = 257, 16, 8, 40
+    cache = rng.integers(0, cap + 1, size=B).astype(np.int32)
+    start = (rng.integers(0, 1000, size=B) * S).astype(np.int32)
+    lens = rng.integers(0, C + 1, size=B).astype(np.int32)
+    ec, es = oracle.commit_chunk(cache, C, chunk_lens=lens, window_start=start,
+                                 max_cached_frames=cap, block_size=S)
+    c_t, s_t = torch.from_numpy(cache).to(DEV), torch.from_numpy(start).to(DEV)
+    pkc.paged_kv_commit(c_t, C, chunk_lens=torch.from_numpy(lens).to(DEV), window_start=s_t,
+                        max_cached_frames=cap, block_size=S)
+    assert c_t.cpu().numpy().tolist() == ec.tolist()
+    assert s_t.cpu().numpy().tolist() == es.tolist()
+    c2 = torch.from_numpy(cache).to(DEV)
+    pkc.paged_kv_commit(c2, C)
+    assert c2.cpu().numpy().tolist() == (cache + C).tolist()
