@@ -19,5 +19,6 @@ from .relpos_attn import (  # noqa: F401
     gather_stream,
     table_row,
     chunk_relpos_attn,
+    chunked_limited_keep,
     varlen_relpos_attn,
 )

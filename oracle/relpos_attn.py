@@ -42,6 +42,10 @@ Readings where the pages are silent (each is listed, with its reason, in the des
   frames are p in [w_b, w_b + cache_b) and the chunk follows them. Distances are taken inside the
   window (cache + i - j with j the key's index in the window), which a table by distance makes
   independent of w_b.
+* Other conventions ("Model Layer", the Nemotron encoder notes): WeNet's relative position needs no
+  shift - its table has one row per key, the embedding of the key's absolute position, and the
+  position term is (q_i + v) . p[j]. The chunked_limited mask lets a query see its own chunk and
+  a fixed number of earlier chunks, offline too.
 """
 
 from __future__ import annotations
@@ -129,12 +133,16 @@ def table_row(center, cache, i, j):
     return center - (cache + i - j)
 
 
-def _attend(q, k, v, pos_rows, u, w, center, cache, scale, query_rows=None):
+def _attend(q, k, v, pos_rows, u, w, center, cache, scale, query_rows=None, per_key=False,
+            keep=None):
     """Attention of C queries at absolute positions cache + i over T = cache + C keys (one stream).
 
     q: [C, H, D]; k, v: [T, Hk, D]; pos_rows: [P_b, H, D] table of this stream. Returns the output
     and the probabilities for the queries in ``query_rows`` (default: all C), as
     [len(query_rows), H, D] and [H, len(query_rows), T].
+    per_key: WeNet's convention - row j of the table is key j's own embedding (no shift), the
+    position term is (q_i + v) . p[j]. keep: optional callable (i, j array) -> bool array, the
+    keys query i may see (the others get no weight).
     """
     n_q, n_head, _ = q.shape
     n_k, n_kv_head = k.shape[0], k.shape[1]
@@ -145,15 +153,22 @@ def _attend(q, k, v, pos_rows, u, w, center, cache, scale, query_rows=None):
     out = np.empty((len(query_rows), n_head, v.shape[2]))
     probs = np.empty((n_head, len(query_rows), n_k))
     for x, i in enumerate(query_rows):
-        rows = table_row(center, cache, int(i), j)                            # [T]
-        if rows.min() < 0 or rows.max() >= pos_rows.shape[0]:
-            raise ValueError("relative-position table too short for distances cache + i - j")
-        emb = pos_rows[rows]                                                  # p[cache + i - j]: [T, H, D]
+        if per_key:
+            if pos_rows.shape[0] < n_k:
+                raise ValueError("per-key table shorter than the keys")
+            emb = pos_rows[:n_k]                                              # p[j]: [T, H, D]
+        else:
+            rows = table_row(center, cache, int(i), j)                        # [T]
+            if rows.min() < 0 or rows.max() >= pos_rows.shape[0]:
+                raise ValueError("relative-position table too short for distances cache + i - j")
+            emb = pos_rows[rows]                                              # p[cache + i - j]: [T, H, D]
+        seen = np.ones(n_k, dtype=bool) if keep is None else keep(int(i), j)
         for h in range(n_head):
             g = h * n_kv_head // n_head
             content = k[:, g, :] @ (q[i, h, :] + u[h])                       # (q + u) . k_j
             position = emb[:, h, :] @ (q[i, h, :] + w[h])                    # (q + v) . p
             s = (content + position) * scale
+            s = np.where(seen, s, -np.inf)
             s = s - s.max()
             a = np.exp(s)
             a = a / a.sum()
@@ -164,7 +179,7 @@ def _attend(q, k, v, pos_rows, u, w, center, cache, scale, query_rows=None):
 
 def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u, pos_bias_v,
                       per_row_pos=False, scale=None, return_probs=False, streams=None,
-                      chunk_lens=None, window_start=None):
+                      chunk_lens=None, window_start=None, per_key_pos=False):
     """Chunk attention of every stream over its cached frames plus its own chunk.
 
     q: [B, C, H, D]. The chunk's K/V must already be in the pools (append first, then attend).
@@ -184,6 +199,11 @@ def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_b
     [w_b, w_b + c_b) of its ring of pages (bounded history); the keys are those frames and the
     chunk's, and distances are counted inside the window, so the result depends on w_b only
     through which pages are read.
+
+    ``per_key_pos`` (WeNet's convention): the table holds one row per key instead of one per
+    distance - shared [P, H, D] or per-row [B, P_max, H, D], row j the embedding of key j's absolute
+    position (the caller builds it from positions starting at offset - cache_b) - and the position
+    term is (q_i + v) . p[j].
     """
     q = np.asarray(q, dtype=np.float64)
     u = np.asarray(pos_bias_u, dtype=np.float64)
@@ -205,7 +225,10 @@ def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_b
         k, v = gather_stream(k_pool, v_pool, block_tables[b], n_k, start)
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
-        if per_row_pos:
+        if per_key_pos:
+            center = 0
+            rows = np.asarray(pos[b] if per_row_pos else pos, dtype=np.float64)
+        elif per_row_pos:
             center = cache + chunk - 1
             rows = np.asarray(pos[b][: 2 * (cache + chunk) - 1], dtype=np.float64)
         else:
@@ -213,15 +236,27 @@ def chunk_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_b
                 raise ValueError("a shared relative-position table has an odd number of rows")
             center = (pos.shape[0] - 1) // 2
             rows = np.asarray(pos, dtype=np.float64)
-        out[b, :n_real], probs = _attend(q[b, :n_real], k, v, rows, u, w, center, cache, scale)
+        out[b, :n_real], probs = _attend(q[b, :n_real], k, v, rows, u, w, center, cache, scale,
+                                         per_key=per_key_pos)
         all_probs.append(probs)
     if return_probs:
         return out, all_probs
     return out
 
 
+def chunked_limited_keep(chunk, left_chunks):
+    """The chunked_limited mask ("Model Layer", Nemotron encoder notes): query i sees the keys of
+    its own chunk and of the ``left_chunks`` chunks before it (chunks of ``chunk`` frames counted
+    from the utterance's first frame)."""
+    def keep(i, j):
+        a, kc = i // chunk, np.asarray(j) // chunk
+        return (kc <= a) & (kc >= a - left_chunks)
+    return keep
+
+
 def varlen_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, scale=None,
-                       return_probs=False, segments=None, query_rows=None):
+                       return_probs=False, segments=None, query_rows=None, chunk=None,
+                       left_chunks=None):
     """Full-context attention inside each packed segment ("Model Layer", forward_offline_packed).
 
     q: [total, H, D], k, v: [total, Hk, D], packed gapless; segment s is frames
@@ -232,6 +267,8 @@ def varlen_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, scale=N
 
     ``segments`` (default: all) and ``query_rows`` (a callable L -> rows of the segment, default
     all) restrict the work to a sample; rows not computed are NaN in ``out``.
+    ``chunk`` and ``left_chunks`` (both or neither): apply the chunked_limited mask inside each
+    segment (see chunked_limited_keep); the table is still the segment's 2 L - 1 rows.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -253,7 +290,9 @@ def varlen_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, scale=N
         row0 = 2 * lo
         rows = np.asarray(pos[row0: row0 + 2 * n - 1], dtype=np.float64)
         qr = np.arange(n) if query_rows is None else np.asarray(query_rows(n))
-        out[lo + qr], probs = _attend(q[lo:hi], k[lo:hi], v[lo:hi], rows, u, w, n - 1, 0, scale, qr)
+        keep = None if chunk is None else chunked_limited_keep(chunk, left_chunks)
+        out[lo + qr], probs = _attend(q[lo:hi], k[lo:hi], v[lo:hi], rows, u, w, n - 1, 0, scale, qr,
+                                      keep=keep)
         all_probs.append(probs)
     if return_probs:
         return out, all_probs

@@ -414,14 +414,14 @@ def test_planted_mistakes_are_caught(monkeypatch, slip):
     else:
         real = orc._attend
 
-        def slipped(q, k, v, pos_rows, u, w, center, cache, scale):
+        def slipped(q, k, v, pos_rows, u, w, center, cache, scale, *a, **kw):
             if slip == "no_u":
                 u = u * 0
             elif slip == "swap_uv":
                 u, w = w, u
             elif slip == "no_scale_pos":
                 pos_rows = pos_rows * math.sqrt(q.shape[-1])
-            return real(q, k, v, pos_rows, u, w, center, cache, scale)
+            return real(q, k, v, pos_rows, u, w, center, cache, scale, *a, **kw)
         monkeypatch.setattr(orc, "_attend", slipped)
     # the mirrored distance needs a table long enough on both sides to stay in range
     brute, dense = _pin_errors(margin=30 if slip == "sign" else 3)
@@ -603,3 +603,127 @@ def test_commit_keeps_the_window_at_the_cap_by_whole_blocks():
     assert cache.tolist() == [16, 35, 36] and start.tolist() == [0, 32, 88]
     cache, start = oracle.commit_chunk(np.array([3]), 16)
     assert cache.tolist() == [19] and start is None
+
+
+# --------------------------------------------------------------------------------------------
+# Other conventions: WeNet's per-key table (no shift) and the chunked_limited mask
+# --------------------------------------------------------------------------------------------
+
+def _per_key_tables(case, starts, width):
+    """Per-row WeNet tables: row j of stream b is the projected sinusoid of absolute position
+    starts[b] + j (positions start at offset - cache_seqlens)."""
+    H, D = case["H"], case["D"]
+    return np.stack([embed_distances(np.arange(s, s + width), case["proj"], H, D).numpy()
+                     for s in starts])
+
+
+def test_per_key_positions_match_brute_force():
+    """(q_i + v) . emb(start_b + j), computed with scalar loops and the projected sinusoid of each
+    key's absolute position directly (no table)."""
+    case = _random_streaming_case(71, [0, 5, 9])
+    starts = [3, 17, 40]
+    C, H, Hk, D = case["C"], case["H"], case["Hk"], case["D"]
+    width = max(case["cs"]) + C
+    tables = _per_key_tables(case, starts, width)
+    out = oracle.chunk_relpos_attn(case["q"], case["kp"], case["vp"], case["bt"], case["cs"], tables,
+                                   case["u"], case["w"], per_row_pos=True, per_key_pos=True)
+    q, u, w = case["q"], case["u"], case["w"]
+    brute = np.zeros(q.shape)
+    for b, c in enumerate(case["cs"]):
+        T = int(c) + C
+        emb = embed_distances(np.arange(starts[b], starts[b] + T), case["proj"], H, D).numpy()
+        for h in range(H):
+            g = h * Hk // H
+            for i in range(C):
+                sc = [(math.fsum((q[b, i, h, d] + u[h, d]) * case["seq_k"][b][j, g, d] for d in range(D))
+                       + math.fsum((q[b, i, h, d] + w[h, d]) * emb[j, h, d] for d in range(D)))
+                      / math.sqrt(D) for j in range(T)]
+                mx = max(sc)
+                ex = [math.exp(x - mx) for x in sc]
+                z = math.fsum(ex)
+                for d in range(D):
+                    brute[b, i, h, d] = math.fsum(ex[j] / z * case["seq_v"][b][j, g, d] for j in range(T))
+    assert np.abs(out - brute).max() < 1e-12
+
+
+def test_per_key_streaming_equals_dense_absolute_position_bias():
+    """WeNet streaming from an empty cache: each step's table holds the keys' absolute positions
+    [0, c + C); the concatenated chunks equal dense block-causal attention with the bias
+    (q_t + v) . emb(j) of the key's absolute position, through float64 SDPA. A shared per-key
+    table (every stream at the same offset) gives the same result as a per-row one."""
+    rng = np.random.default_rng(73)
+    steps, C, H, Hk, D, S = 4, 4, 2, 1, 8, 4
+    n = steps * C
+    q_all = rng.standard_normal((n, H, D))
+    k_all = rng.standard_normal((n, Hk, D))
+    v_all = rng.standard_normal((n, Hk, D))
+    u = 0.5 * rng.standard_normal((H, D))
+    w = 0.5 * rng.standard_normal((H, D))
+    proj = relpos_projection(H * D, torch.Generator().manual_seed(73))
+    emb_all = embed_distances(np.arange(n), proj, H, D).numpy()
+    pages = n // S
+    bt = rng.permutation(pages + 2)[None, :pages]
+    kp = np.full((pages + 2, Hk, S, D), np.nan)
+    vp = np.full((pages + 2, Hk, D, S), np.nan)
+    outs = []
+    for step in range(steps):
+        c = step * C
+        sl = slice(c, c + C)
+        kp, vp = oracle.paged_kv_append(kp, vp, k_all[None, sl], v_all[None, sl], bt, np.array([c]))
+        shared = emb_all[:c + C]
+        o1 = oracle.chunk_relpos_attn(q_all[None, sl], kp, vp, bt, np.array([c]), shared, u, w,
+                                      per_key_pos=True)[0]
+        o2 = oracle.chunk_relpos_attn(q_all[None, sl], kp, vp, bt, np.array([c]), shared[None], u, w,
+                                      per_row_pos=True, per_key_pos=True)[0]
+        np.testing.assert_array_equal(o1, o2)
+        outs.append(o1)
+    stream = np.concatenate(outs)
+    t = np.arange(n)
+    dense = np.zeros((n, H, D))
+    for h in range(H):
+        bias = np.einsum("td,jd->tj", q_all[:, h] + w[h], emb_all[:, h]) / math.sqrt(D)
+        bias = np.where((t[None, :] // C) <= (t[:, None] // C), bias, -np.inf)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q_all[:, h] + u[h])[None], torch.from_numpy(k_all[:, 0])[None],
+            torch.from_numpy(v_all[:, 0])[None], attn_mask=torch.from_numpy(bias)[None])
+        dense[:, h] = ref[0].numpy()
+    assert np.abs(stream - dense).max() < 1e-12
+
+
+@pytest.mark.parametrize("chunk,left", [(4, 2), (3, 0), (5, 10)])
+def test_chunked_limited_offline_equals_streaming_with_the_trained_window(chunk, left):
+    """The chunked_limited mask offline equals running each chunk as one streaming step whose
+    cache is the chunk's allowed history (cache = min(a, left) chunks), and dense attention with
+    the explicit chunk mask and distance bias."""
+    lengths = [17, 9, 4]
+    H, D = 2, 8
+    co = make_varlen_cohort(lengths, H, D, dtype=F64, seed=75)
+    q, k, v = np64(co.q), np64(co.k), np64(co.v)
+    u, w = np64(co.pos_bias_u), np64(co.pos_bias_v)
+    pos = np64(co.pos)
+    cu = co.cu_seqlens.numpy()
+    out = oracle.varlen_relpos_attn(q, k, v, cu, pos, u, w, chunk=chunk, left_chunks=left)
+    for s, n in enumerate(lengths):
+        lo = cu[s]
+        for a in range(0, (n + chunk - 1) // chunk):
+            f0, f1 = a * chunk, min(n, (a + 1) * chunk)
+            h0 = max(0, a - left) * chunk                          # first key of the history
+            c = f0 - h0
+            kp = k[lo + h0: lo + f1].transpose(1, 0, 2)[None]      # one page holds the window
+            vp = v[lo + h0: lo + f1].transpose(1, 2, 0)[None]
+            table = descending_table(c + (f1 - f0) - 1, co.meta["proj"], H, D).numpy()
+            step = oracle.chunk_relpos_attn(q[None, lo + f0: lo + f1], kp, vp, np.array([[0]]),
+                                            np.array([c]), table, u, w)[0]
+            assert np.abs(step - out[lo + f0: lo + f1]).max() < 1e-12, (s, a)
+        t = np.arange(n)
+        dist = t[:, None] - t[None, :]
+        emb = embed_distances(dist.reshape(-1), co.meta["proj"], H, D).numpy().reshape(n, n, H, D)
+        keep = oracle.chunked_limited_keep(chunk, left)
+        mask = np.stack([keep(i, t) for i in range(n)])
+        for h in range(H):
+            bias = np.einsum("td,tjd->tj", q[lo:lo + n, h] + w[h], emb[:, :, h]) / math.sqrt(D)
+            bias = np.where(mask, bias, -np.inf)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[lo:lo + n, h] + u[h])[None], torch.from_numpy(k[lo:lo + n, h])[None],
+                torch.from_numpy(v[lo:lo + n, h])[None], attn_mask=torch.from_numpy(bias)[None])
+            assert np.abs(ref[0].numpy() - out[lo:lo + n, h]).max() < 1e-12
