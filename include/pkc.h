@@ -22,6 +22,9 @@
  *   [MOD surf] "Model Layer", "The engine-facing surface": forward_chunk_paged (streaming chunk
  *              entry), forward_offline_packed (gapless varlen offline forward), n_kv_head and
  *              head_dim (paged-streaming geometry).
+ *   [MOD nem]  "Model Layer", the Nemotron encoder notes: Transformer-XL relative position uses
+ *              rel_shift while WeNet's convention needs no shift; the chunked_limited mask lets
+ *              a query see its own chunk and a fixed number of earlier chunks, offline too.
  *   [ENG 9]    "ASR Engine", section 4.3 step 6 and sections 8-9: each stream commits its actual
  *              frames (a final window may be short); a cohort is padded to a wider graph shape
  *              through a padding lane whose rows compute only for themselves.
@@ -96,6 +99,13 @@ typedef enum pkc_status {
 
 typedef enum pkc_dtype { PKC_F32 = 0, PKC_BF16 = 1 } pkc_dtype;
 
+/* Layout of the positional tables (flags of the pos_layout argument). */
+typedef enum pkc_pos_layout {
+  PKC_POS_SHARED = 0,   /* one table by distance for the cohort                         */
+  PKC_POS_PER_ROW = 1,  /* one table per stream                                          */
+  PKC_POS_PER_KEY = 2   /* rows are keys, not distances (WeNet's convention, no shift)   */
+} pkc_pos_layout;
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int pkc_version(void);
 
@@ -130,10 +140,17 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  * head h and chunk query i < n_b, attends over the cache_seqlens[b] + n_b frames of stream b
  * read through block_tables, and writes out[b][i][h][:]; rows i >= n_b are written as zero
  * (n_b = chunk_lens[b], or chunk_size when chunk_lens is NULL).
- * pos_per_row = 0: pos is one shared table of pos_len rows (pos_len odd and
- *   (pos_len - 1) / 2 >= max_cache_seqlen + chunk_size - 1), indexed by distance around its centre.
- * pos_per_row = 1: pos holds one table per stream, pos_len rows apart
- *   (pos_len >= 2 * (max_cache_seqlen + chunk_size) - 1).
+ * pos_layout (pkc_pos_layout flags):
+ *   0: pos is one shared table of pos_len rows (pos_len odd and
+ *      (pos_len - 1) / 2 >= max_cache_seqlen + chunk_size - 1), indexed by distance around its
+ *      centre (Transformer-XL, [MOD fix]).
+ *   PKC_POS_PER_ROW: pos holds one such table per stream, pos_len rows apart
+ *      (pos_len >= 2 * (max_cache_seqlen + chunk_size) - 1), centred at T_b - 1.
+ *   PKC_POS_PER_KEY (WeNet's convention, [MOD nem]): no shift - row j of the table is the
+ *      embedding of key j itself (the caller builds it from the keys' absolute positions, which
+ *      start at offset - cache_seqlens), and the position term is (q_i + v) . p[j]. Shared, or
+ *      with PKC_POS_PER_ROW one table per stream pos_len rows apart; pos_len >= max_cache_seqlen
+ *      + chunk_size either way.
  * softmax_scale <= 0 selects 1 / sqrt(head_dim).
  * Errors: as paged_kv_append; n_head % n_kv_head != 0 or a table too short -> PKC_ERR_SHAPE;
  * head_dim != 64, block_size not a power of two >= 8, or a chunk too long for the kernel's LDS
@@ -145,7 +162,7 @@ pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k
                                    const void* v_pool, const int32_t* block_tables,
                                    const int32_t* cache_seqlens, const int32_t* chunk_lens,
                                    const int32_t* window_start, const void* pos, int32_t pos_len,
-                                   int32_t pos_per_row, const void* pos_bias_u,
+                                   int32_t pos_layout, const void* pos_bias_u,
                                    const void* pos_bias_v, void* out, int32_t batch,
                                    int32_t chunk_size, int32_t n_head, int32_t n_kv_head,
                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
@@ -163,7 +180,7 @@ pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const voi
                                        const void* v_new, void* k_pool, void* v_pool,
                                        const int32_t* block_tables, const int32_t* cache_seqlens,
                                        const int32_t* chunk_lens, const int32_t* window_start,
-                                       const void* pos, int32_t pos_len, int32_t pos_per_row,
+                                       const void* pos, int32_t pos_len, int32_t pos_layout,
                                        const void* pos_bias_u, const void* pos_bias_v, void* out,
                                        int32_t batch, int32_t chunk_size, int32_t n_head,
                                        int32_t n_kv_head, int32_t head_dim, int32_t block_size,
@@ -190,7 +207,8 @@ pkc_status paged_kv_append_relpos_attn_layers(
     pkc_dtype dtype, int32_t n_layers, const void* const* q, const void* const* k_new,
     const void* const* v_new, void* const* k_pool, void* const* v_pool,
     const int32_t* block_tables, const int32_t* cache_seqlens, const int32_t* chunk_lens,
-    const int32_t* window_start, const void* const* pos, int32_t pos_len, int32_t pos_per_row, const void* const* pos_bias_u,
+    const int32_t* window_start, const void* const* pos, int32_t pos_len, int32_t pos_layout,
+    const void* const* pos_bias_u,
     const void* const* pos_bias_v, void* const* out, int32_t batch, int32_t chunk_size,
     int32_t n_head, int32_t n_kv_head, int32_t head_dim, int32_t block_size, int32_t num_blocks,
     int32_t max_blocks_per_seq, int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream);

@@ -105,6 +105,11 @@ def _table(t):
     return _p(t)
 
 
+def _layout(per_row, per_key):
+    """pos_layout flags: 1 = one table per stream, 2 = rows are keys (WeNet, no shift)."""
+    return (1 if per_row else 0) | (2 if per_key else 0)
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -113,32 +118,37 @@ def _stream(stream):
 def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, max_cache_seqlen,
                     chunk_lens=None, window_start=None, stream=None):
     """Write k_new / v_new [B, C, Hk, D] into k_pool [N, Hk, S, D] / v_pool [N, Hk, D, S]
-    (only the first chunk_lens[b] frames of stream b when chunk_lens is given)."""
+    (only the first chunk_lens[b] frames of stream b when chunk_lens is given; window_start
+    int32 [B] addresses the table rows as rings)."""
     B, C, Hk, D = k_new.shape
     N, _, S, _ = k_pool.shape
     st = lib().paged_kv_append(_dtype(k_new, v_new, k_pool, v_pool), _p(k_new), _p(v_new),
                                _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
                                _table(chunk_lens), _table(window_start), B, C, Hk, D, S, N,
-                               block_tables.shape[1],
-                               int(max_cache_seqlen), _stream(stream))
+                               block_tables.shape[1], int(max_cache_seqlen), _stream(stream))
     _check(st, "paged_kv_append")
 
 
+def _table_rows(pos, per_row_pos):
+    return pos.shape[1] if per_row_pos else pos.shape[0]
+
+
 def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u,
-                            pos_bias_v, max_cache_seqlen, per_row_pos=False, out=None,
-                            softmax_scale=0.0, chunk_lens=None, window_start=None, stream=None):
-    """Chunk attention; q [B, C, H, D]; pos shared [P, H, D] or per-row [B, P, H, D];
-    chunk_lens int32 [B] (optional): real frames per stream."""
+                            pos_bias_v, max_cache_seqlen, per_row_pos=False, per_key_pos=False,
+                            out=None, softmax_scale=0.0, chunk_lens=None, window_start=None,
+                            stream=None):
+    """Chunk attention; q [B, C, H, D]; pos shared [P, H, D] or per-row [B, P, H, D], rows by
+    distance (Transformer-XL) or, with per_key_pos, by key (WeNet); chunk_lens int32 [B]
+    (optional): real frames per stream; window_start int32 [B] (optional): bounded history."""
     B, C, H, D = q.shape
     N, Hk, S, _ = k_pool.shape
     if out is None:
         out = torch.empty_like(q)
-    P = pos.shape[1] if per_row_pos else pos.shape[0]
     st = lib().chunk_paged_relpos_attn(
         _dtype(q, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out), _p(q), _p(k_pool), _p(v_pool),
         _table(block_tables), _table(cache_seqlens), _table(chunk_lens), _table(window_start),
-        _p(pos), P, int(bool(per_row_pos)), _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk, D, S, N,
-        block_tables.shape[1],
+        _p(pos), _table_rows(pos, per_row_pos), _layout(per_row_pos, per_key_pos), _p(pos_bias_u),
+        _p(pos_bias_v), _p(out), B, C, H, Hk, D, S, N, block_tables.shape[1],
         int(max_cache_seqlen), float(softmax_scale), _stream(stream))
     _check(st, "chunk_paged_relpos_attn")
     return out
@@ -146,20 +156,19 @@ def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos,
 
 def paged_kv_append_relpos_attn(q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, pos,
                                 pos_bias_u, pos_bias_v, max_cache_seqlen, per_row_pos=False,
-                                out=None, softmax_scale=0.0, chunk_lens=None, window_start=None,
-                                stream=None):
-    """Append and attention of one layer in one launch (pools are written); chunk_lens int32 [B]
-    (optional): real frames per stream."""
+                                per_key_pos=False, out=None, softmax_scale=0.0, chunk_lens=None,
+                                window_start=None, stream=None):
+    """Append and attention of one layer in one launch (pools are written); arguments as
+    chunk_paged_relpos_attn plus k_new / v_new [B, C, Hk, D]."""
     B, C, H, D = q.shape
     N, Hk, S, _ = k_pool.shape
     if out is None:
         out = torch.empty_like(q)
-    P = pos.shape[1] if per_row_pos else pos.shape[0]
     st = lib().paged_kv_append_relpos_attn(
         _dtype(q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out), _p(q),
         _p(k_new), _p(v_new), _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
-        _table(chunk_lens), _table(window_start), _p(pos), P, int(bool(per_row_pos)),
-        _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk,
+        _table(chunk_lens), _table(window_start), _p(pos), _table_rows(pos, per_row_pos),
+        _layout(per_row_pos, per_key_pos), _p(pos_bias_u), _p(pos_bias_v), _p(out), B, C, H, Hk,
         D, S, N, block_tables.shape[1], int(max_cache_seqlen), float(softmax_scale),
         _stream(stream))
     _check(st, "paged_kv_append_relpos_attn")
@@ -174,30 +183,27 @@ def _ptr_array(ts):
 
 
 def paged_kv_append_relpos_attn_layers(layers, block_tables, cache_seqlens, max_cache_seqlen,
-                                       per_row_pos=False, chunk_lens=None, window_start=None,
-                                       softmax_scale=0.0, stream=None):
+                                       per_row_pos=False, per_key_pos=False, chunk_lens=None,
+                                       window_start=None, softmax_scale=0.0, stream=None):
     """Fused append + attention of several layers in one call. ``layers``: a sequence of objects
     with attributes q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out (one per
-    layer, same shapes); block tables, cache and chunk lengths are shared."""
+    layer, same shapes); block tables, cache and chunk lengths and window starts are shared."""
     l0 = layers[0]
     B, C, H, D = l0.q.shape
     N, Hk, S, _ = l0.k_pool.shape
-    P = l0.pos.shape[1] if per_row_pos else l0.pos.shape[0]
     names = ["q", "k_new", "v_new", "k_pool", "v_pool", "pos", "pos_bias_u", "pos_bias_v", "out"]
     for x in layers:
         for n in names:
-            t = getattr(x, n)
-            if getattr(l0, n).shape != t.shape:
+            if getattr(l0, n).shape != getattr(x, n).shape:
                 raise ValueError(f"layer buffers of {n} differ in shape")
     dt = _dtype(*[getattr(x, n) for x in layers for n in names])
     arrs = {n: _ptr_array([getattr(x, n) for x in layers]) for n in names}
     st = lib().paged_kv_append_relpos_attn_layers(
         dt, len(layers), arrs["q"], arrs["k_new"], arrs["v_new"], arrs["k_pool"], arrs["v_pool"],
         _table(block_tables), _table(cache_seqlens), _table(chunk_lens), _table(window_start),
-        arrs["pos"], P,
-        int(bool(per_row_pos)), arrs["pos_bias_u"], arrs["pos_bias_v"], arrs["out"], B, C, H, Hk,
-        D, S, N, block_tables.shape[1], int(max_cache_seqlen), float(softmax_scale),
-        _stream(stream))
+        arrs["pos"], _table_rows(l0.pos, per_row_pos), _layout(per_row_pos, per_key_pos),
+        arrs["pos_bias_u"], arrs["pos_bias_v"], arrs["out"], B, C, H, Hk, D, S, N,
+        block_tables.shape[1], int(max_cache_seqlen), float(softmax_scale), _stream(stream))
     _check(st, "paged_kv_append_relpos_attn_layers")
 
 

@@ -33,11 +33,14 @@ pkc_status check_pool(int32_t batch, int32_t chunk, int32_t n_kv_head, int32_t h
 }
 
 pkc_status check_attn(int32_t chunk, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
-                      int32_t block_size, int32_t max_cache, int32_t pos_len, int32_t pos_per_row) {
+                      int32_t block_size, int32_t max_cache, int32_t pos_len, int32_t pos_layout) {
   if (n_head <= 0 || n_head % n_kv_head != 0) return PKC_ERR_SHAPE;
-  if (pos_per_row != 0 && pos_per_row != 1) return PKC_ERR_SHAPE;
+  if (pos_layout < 0 || pos_layout > (PKC_POS_PER_ROW | PKC_POS_PER_KEY)) return PKC_ERR_SHAPE;
   const int64_t longest = (int64_t)max_cache + chunk;
-  if (pos_per_row) {
+  if (pos_layout & PKC_POS_PER_KEY) {
+    // one row per key, shared or per stream
+    if (pos_len < longest) return PKC_ERR_SHAPE;
+  } else if (pos_layout & PKC_POS_PER_ROW) {
     if (pos_len < 2 * longest - 1) return PKC_ERR_SHAPE;
   } else {
     if (pos_len <= 0 || pos_len % 2 != 1) return PKC_ERR_SHAPE;
@@ -73,7 +76,8 @@ const char* pkc_status_string(int status) {
 
 pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new, void* k_pool,
                            void* v_pool, const int32_t* block_tables, const int32_t* cache_seqlens,
-                           const int32_t* chunk_lens, const int32_t* window_start, int32_t batch, int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
+                           const int32_t* chunk_lens, const int32_t* window_start, int32_t batch,
+                           int32_t chunk_size, int32_t n_kv_head, int32_t head_dim,
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_cache_seqlen, hipStream_t stream) {
   pkc_status st = check_dtype(dtype);
@@ -95,7 +99,7 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
                               void* v_pool_w, const int32_t* block_tables,
                               const int32_t* cache_seqlens, const int32_t* chunk_lens,
                               const int32_t* window_start, const void* pos, int32_t pos_len,
-                              int32_t pos_per_row, const void* pos_bias_u, const void* pos_bias_v,
+                              int32_t pos_layout, const void* pos_bias_u, const void* pos_bias_v,
                               void* out, int32_t batch, int32_t chunk_size, int32_t n_head,
                               int32_t n_kv_head, int32_t head_dim, int32_t block_size,
                               int32_t num_blocks, int32_t max_blocks_per_seq,
@@ -110,7 +114,7 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
                   max_blocks_per_seq, max_cache_seqlen);
   if (st != PKC_OK) return st;
   st = check_attn(chunk_size, n_head, n_kv_head, head_dim, block_size, max_cache_seqlen, pos_len,
-                  pos_per_row);
+                  pos_layout);
   if (st != PKC_OK) return st;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(pos) ||
       !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))
@@ -145,7 +149,7 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
   p.max_blocks = max_blocks_per_seq;
   p.max_cache = max_cache_seqlen;
   p.pos_len = pos_len;
-  p.pos_per_row = pos_per_row;
+  p.pos_layout = pos_layout;
   p.softmax_scale = softmax_scale;
   if (!launch) return PKC_OK;
   return from_hip(launch_chunk_attn(dtype, p, stream));
@@ -155,14 +159,15 @@ pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k
                                    const void* v_pool, const int32_t* block_tables,
                                    const int32_t* cache_seqlens, const int32_t* chunk_lens,
                                    const int32_t* window_start, const void* pos, int32_t pos_len,
-                                   int32_t pos_per_row, const void* pos_bias_u,
+                                   int32_t pos_layout, const void* pos_bias_u,
                                    const void* pos_bias_v, void* out, int32_t batch,
                                    int32_t chunk_size, int32_t n_head, int32_t n_kv_head,
                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                    int32_t max_blocks_per_seq, int32_t max_cache_seqlen,
                                    float softmax_scale, hipStream_t stream) {
   return attn_common(dtype, q, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_tables,
-                     cache_seqlens, chunk_lens, window_start, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
+                     cache_seqlens, chunk_lens, window_start, pos, pos_len, pos_layout, pos_bias_u,
+                     pos_bias_v, out, batch,
                      chunk_size, n_head, n_kv_head, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_cache_seqlen, softmax_scale, stream);
 }
@@ -171,7 +176,7 @@ pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const voi
                                        const void* v_new, void* k_pool, void* v_pool,
                                        const int32_t* block_tables, const int32_t* cache_seqlens,
                                        const int32_t* chunk_lens, const int32_t* window_start,
-                                       const void* pos, int32_t pos_len, int32_t pos_per_row,
+                                       const void* pos, int32_t pos_len, int32_t pos_layout,
                                        const void* pos_bias_u, const void* pos_bias_v, void* out,
                                        int32_t batch, int32_t chunk_size, int32_t n_head,
                                        int32_t n_kv_head, int32_t head_dim, int32_t block_size,
@@ -180,7 +185,8 @@ pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const voi
                                        hipStream_t stream) {
   if (!k_new || !v_new) return PKC_ERR_NULL;
   return attn_common(dtype, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, block_tables,
-                     cache_seqlens, chunk_lens, window_start, pos, pos_len, pos_per_row, pos_bias_u, pos_bias_v, out, batch,
+                     cache_seqlens, chunk_lens, window_start, pos, pos_len, pos_layout, pos_bias_u,
+                     pos_bias_v, out, batch,
                      chunk_size, n_head, n_kv_head, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_cache_seqlen, softmax_scale, stream);
 }
@@ -189,7 +195,8 @@ pkc_status paged_kv_append_relpos_attn_layers(
     pkc_dtype dtype, int32_t n_layers, const void* const* q, const void* const* k_new,
     const void* const* v_new, void* const* k_pool, void* const* v_pool,
     const int32_t* block_tables, const int32_t* cache_seqlens, const int32_t* chunk_lens,
-    const int32_t* window_start, const void* const* pos, int32_t pos_len, int32_t pos_per_row, const void* const* pos_bias_u,
+    const int32_t* window_start, const void* const* pos, int32_t pos_len, int32_t pos_layout,
+    const void* const* pos_bias_u,
     const void* const* pos_bias_v, void* const* out, int32_t batch, int32_t chunk_size,
     int32_t n_head, int32_t n_kv_head, int32_t head_dim, int32_t block_size, int32_t num_blocks,
     int32_t max_blocks_per_seq, int32_t max_cache_seqlen, float softmax_scale, hipStream_t stream) {
@@ -205,7 +212,7 @@ pkc_status paged_kv_append_relpos_attn_layers(
       st = attn_common(dtype, q[l], k_new[l], v_new[l], k_pool[l], v_pool[l], k_pool[l],
                        v_pool[l], block_tables, cache_seqlens, chunk_lens, window_start, pos[l],
                        pos_len,
-                       pos_per_row, pos_bias_u[l], pos_bias_v[l], out[l], batch, chunk_size,
+                       pos_layout, pos_bias_u[l], pos_bias_v[l], out[l], batch, chunk_size,
                        n_head, n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_cache_seqlen, softmax_scale, stream, pass == 1);
       if (st != PKC_OK) return st;

@@ -74,7 +74,7 @@ struct ChunkArgs {
   const T* v_new;
   T* k_pool_w;
   T* v_pool_w;
-  int C, H, Hk, S, logS, N, M, max_cache, pos_len, per_row, qtiles;
+  int C, H, Hk, S, logS, N, M, max_cache, pos_len, per_row, per_key, qtiles;
   int tail_cap, vt_pitch;            // LDS tail geometry (keys, elements per V^T row)
   int off_bt, off_kt, off_vt;        // byte offsets of the LDS regions
   float scale_log2;
@@ -90,7 +90,7 @@ struct StepRegs {
 
 template <typename T> constexpr int kt_pitch() { return kD + 16 / (int)sizeof(T); }
 
-template <typename T, bool kFused, int kWaves, int kS, bool kRegTail>
+template <typename T, bool kFused, int kWaves, int kS, bool kRegTail, bool kPerKey>
 __global__ void __launch_bounds__(kWaves * 64)
 chunk_attn_kernel(ChunkArgs<T> a) {
   typedef typename Frag<T>::type F;
@@ -187,6 +187,19 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const size_t prow = (size_t)a.H * kD;
   const T* ptab = a.pos + (a.per_row ? (size_t)b * a.pos_len * prow : 0) + (size_t)h * kD;
   auto band_row = [&](int r) { return ptab + (size_t)(uint32_t)clampi(r, rlo, rhi) * prow; };
+  // per-key tables (WeNet's convention, no shift): row j is key j's own embedding; keys past the
+  // last one read its row (they are masked)
+  auto key_row = [&](int j) { return ptab + (size_t)(uint32_t)min(j, T_len - 1) * prow; };
+  // P rows of a step's 32 keys in the key tiles' permuted order (tile tt row 4a + e is key
+  // j0 + 8a + 4tt + e), into p[tt][half]
+  auto load_key_rows = [&](F (&p)[2][2], int j0) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const T* row = key_row(j0 + 8 * (m16 >> 2) + 4 * tt + (m16 & 3)) + 8 * grp;
+      p[tt][0] = load8(row);
+      p[tt][1] = load8(row + 32);
+    }
+  };
 
   // the window, and a page's block ID from it (pages past it: straight from the table). The
   // masked last body step can reach one page past the stream's pages: such pages read as block 0
@@ -226,18 +239,24 @@ chunk_attn_kernel(ChunkArgs<T> a) {
                   (uint32_t)(m16 * S + (kg & (S - 1)));
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) r.v[dt] = load8(vb + 16 * dt * S);
-    const int rb = R0 + j0 - qlast;
+    if constexpr (kPerKey) {
+      load_key_rows(r.p, j0);
+    } else {
+      const int rb = R0 + j0 - qlast;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const T* row = band_row(rb + 16 * (t + 1) + m16) + 8 * grp;
-      r.p[t][0] = load8(row);
-      r.p[t][1] = load8(row + 32);
+      for (int t = 0; t < 2; ++t) {
+        const T* row = band_row(rb + 16 * (t + 1) + m16) + 8 * grp;
+        r.p[t][0] = load8(row);
+        r.p[t][1] = load8(row + 32);
+      }
     }
   };
   // band tiles of this wave's first tail step, into a register set the body no longer needs
   // (tiles 0, 1, 2 in k[0], p[0], p[1]): the tail step then waits on nothing
   auto load_tail_band = [&](StepRegs<T>& r) {
-    if (wave < ntail) {
+    if (kPerKey) {
+      if (wave < ntail) load_key_rows(r.p, cache + 32 * wave);
+    } else if (wave < ntail) {
       const int rb = R0 + cache + 32 * wave - qlast;
       F* dst[3] = {r.k[0], r.p[0], r.p[1]};
 #pragma unroll
@@ -251,9 +270,11 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   StepRegs<T> ra, rb2;
   F p0[2];
   if (nmine > 0) {
-    const T* row = band_row(R0 + 32 * s_begin - qlast + m16) + 8 * grp;
-    p0[0] = load8(row);
-    p0[1] = load8(row + 32);
+    if (!kPerKey) {
+      const T* row = band_row(R0 + 32 * s_begin - qlast + m16) + 8 * grp;
+      p0[0] = load8(row);
+      p0[1] = load8(row + 32);
+    }
     load_step(ra, s_begin);
     if (nmine > 1) load_step(rb2, s_begin + 1);
     else load_tail_band(rb2);
@@ -322,22 +343,32 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if (nmine > 0) {
-    floatx4 g_prev = mma(p0[0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-    g_prev = mma(p0[1], qv[1], g_prev);
+    floatx4 g_prev;
+    if (!kPerKey) {
+      g_prev = mma(p0[0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      g_prev = mma(p0[1], qv[1], g_prev);
+    }
     auto run = [&](StepRegs<T>& r, int s) {
-      floatx4 g1 = mma(r.p[0][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-      g1 = mma(r.p[0][1], qv[1], g1);
-      floatx4 g2 = mma(r.p[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-      g2 = mma(r.p[1][1], qv[1], g2);
+      float x[2][4];
+      floatx4 g2;
+      if constexpr (kPerKey) {
+        per_key_scores<T>(r.k, r.p, qu, qv, x);
+      } else {
+        floatx4 g1 = mma(r.p[0][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        g1 = mma(r.p[0][1], qv[1], g1);
+        g2 = mma(r.p[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        g2 = mma(r.p[1][1], qv[1], g2);
+        skew_scores<T>(r.k, qu, g_prev, g1, g2, s_g, x);
+      }
       if (s == s_part) {
         // the last cached page is partly filled: frames at or past cache are excluded, and
         // their V is zeroed (the slots may hold anything)
         zero_from(r.v, cache - (32 * s + 8 * grp));
-        step_compute<T, true>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, cache - 32 * s);
+        softmax_pv<T, true>(st, x, r.v, 0, cache - 32 * s);
       } else {
-        step_compute<T, false>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, 32);
+        softmax_pv<T, false>(st, x, r.v, 0, 32);
       }
-      g_prev = g2;
+      if (!kPerKey) g_prev = g2;
       if (s + 2 < s_end) load_step(r, s + 2);
       else if (s + 2 == s_end) load_tail_band(r);
     };
@@ -361,33 +392,51 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(s_vt + (16 * dt + m16) * a.vt_pitch + 32 * k + 8 * grp);
-    F pb[3][2];
-    if (k == wave) {
-      // prefetched: in the register set the body left free (ra after an even number of body
-      // steps, rb2 after an odd one)
-      const StepRegs<T>& r = (nmine & 1) ? rb2 : ra;
+    float x[2][4];
+    if constexpr (kPerKey) {
+      F pk[2][2];
+      if (k == wave) {
+        // prefetched into the register set the body left free (ra after an even number of
+        // body steps, rb2 after an odd one)
+        const StepRegs<T>& r = (nmine & 1) ? rb2 : ra;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        pb[0][half] = r.k[0][half];
-        pb[1][half] = r.p[0][half];
-        pb[2][half] = r.p[1][half];
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) pk[tt][half] = r.p[tt][half];
+      } else {
+        load_key_rows(pk, j0);
       }
+      per_key_scores<T>(kf, pk, qu, qv, x);
     } else {
-      const int rb = R0 + j0 - qlast;
+      F pb[3][2];
+      if (k == wave) {
+        // prefetched: in the register set the body left free (ra after an even number of body
+        // steps, rb2 after an odd one)
+        const StepRegs<T>& r = (nmine & 1) ? rb2 : ra;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          pb[0][half] = r.k[0][half];
+          pb[1][half] = r.p[0][half];
+          pb[2][half] = r.p[1][half];
+        }
+      } else {
+        const int rb = R0 + j0 - qlast;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
+          pb[t][0] = load8(row);
+          pb[t][1] = load8(row + 32);
+        }
+      }
+      floatx4 g[3];
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
-        const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
-        pb[t][0] = load8(row);
-        pb[t][1] = load8(row + 32);
+        g[t] = mma(pb[t][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        g[t] = mma(pb[t][1], qv[1], g[t]);
       }
+      skew_scores<T>(kf, qu, g[0], g[1], g[2], s_g, x);
     }
-    floatx4 g[3];
-#pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      g[t] = mma(pb[t][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-      g[t] = mma(pb[t][1], qv[1], g[t]);
-    }
-    step_compute<T, true>(st, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
+    softmax_pv<T, true>(st, x, vf, 0, T_len - j0);
   }
 
   // ---- 6. fused append: this tile's chunk frames from LDS into the pool ---------------------
@@ -473,9 +522,9 @@ chunk_attn_kernel(ChunkArgs<T> a) {
 // assignment and merge order, and with them its result bits, depend on its own length only.
 template <typename T> constexpr int waves_of() { return 4; }
 
-template <typename T, bool kFused, int kS, bool kRegTail>
+template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false>
 void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
-  auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail>;
+  auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey>;
   if (smem > 64 * 1024) {
     // beyond the default dynamic LDS size (long chunks): opt in once; MI355X allows 160 KB per
     // workgroup
@@ -493,6 +542,13 @@ template <typename T, bool kFused>
 void launch_s(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
   // the block sizes of the streaming workloads get constant page geometry; fp32 (used for
   // checking) always takes the general instantiation
+  // WeNet's per-key tables: the general block-size instantiation
+  if (a.per_key) {
+    if constexpr (sizeof(T) == 2 && kFused) {
+      if (a.C <= 32) return launch_inst<T, kFused, 0, true, true>(a, grid, smem, stream);
+    }
+    return launch_inst<T, kFused, 0, false, true>(a, grid, smem, stream);
+  }
   // fused bf16 chunks of at most 32 frames: the chunk's K and V are one 16-byte vector each per
   // thread, requested at kernel start and held in registers
   if constexpr (sizeof(T) == 2 && kFused) {
@@ -537,7 +593,8 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   a.M = p.max_blocks;
   a.max_cache = p.max_cache;
   a.pos_len = p.pos_len;
-  a.per_row = p.pos_per_row;
+  a.per_row = p.pos_layout & PKC_POS_PER_ROW;
+  a.per_key = (p.pos_layout & PKC_POS_PER_KEY) != 0;
   a.qtiles = (p.chunk + 15) / 16;
   a.tail_cap = ((p.chunk + 31) / 32) * 32;
   a.vt_pitch = a.tail_cap + 16 / (int)sizeof(T);

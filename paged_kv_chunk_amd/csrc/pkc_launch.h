@@ -40,7 +40,7 @@ struct AttnParams {
   void* k_pool_w;
   void* v_pool_w;
   int batch, chunk, n_head, n_kv_head, head_dim, block_size, num_blocks, max_blocks, max_cache;
-  int pos_len, pos_per_row;
+  int pos_len, pos_layout;
   float softmax_scale;
 };
 

@@ -29,15 +29,14 @@ struct Softmax {
   floatx4 o[4];
 };
 
-// One 32-key step given its operand fragments and the three band product tiles (scores already
-// in log2 units). kMask: keys at or past valid_keys are excluded.
-template <typename T, bool kMask>
-__device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>::type (&kf)[2][2],
-                                             const typename Frag<T>::type (&vf)[4],
-                                             const typename Frag<T>::type (&qu)[2],
-                                             const floatx4& g0, const floatx4& g1,
-                                             const floatx4& g2, float* s_g, int valid_keys) {
-  typedef typename Frag<T>::type F;
+// Scores of one 32-key step, Transformer-XL convention: S^T = K (q+u)^T from the two key tiles,
+// plus the band product shifted into place through the per-wave LDS tile (scores already in log2
+// units). x[tt][e] is key 8 grp + 4 tt + e of the step for this lane's query column.
+template <typename T>
+__device__ __forceinline__ void skew_scores(const typename Frag<T>::type (&kf)[2][2],
+                                            const typename Frag<T>::type (&qu)[2],
+                                            const floatx4& g0, const floatx4& g1, const floatx4& g2,
+                                            float* s_g, float (&x)[2][4]) {
   const int lane = threadIdx.x & 63;
   const int m16 = lane & 15;
   const int grp = lane >> 4;
@@ -55,18 +54,50 @@ __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>
   *reinterpret_cast<floatx4*>(colw + 32) = g2;
   __builtin_amdgcn_wave_barrier();
   const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * grp;
-  float x[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[tt][e] = sc[tt][e] + colr[4 * tt + e];
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Scores of one 32-key step, WeNet convention (no shift): the table has one row per key, in the
+// same permuted order as the key tiles, and S^T = K (q+u)^T + P (q+v)^T.
+template <typename T>
+__device__ __forceinline__ void per_key_scores(const typename Frag<T>::type (&kf)[2][2],
+                                               const typename Frag<T>::type (&pf)[2][2],
+                                               const typename Frag<T>::type (&qu)[2],
+                                               const typename Frag<T>::type (&qv)[2],
+                                               float (&x)[2][4]) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    floatx4 sc = mma(kf[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
+    sc = mma(kf[tt][1], qu[1], sc);
+    sc = mma(pf[tt][0], qv[0], sc);
+    sc = mma(pf[tt][1], qv[1], sc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[tt][e] = sc[e];
+  }
+}
+
+// Online softmax and PV of one step from its scores. kMask: only keys k_lo <= key < k_hi of the
+// step count for this lane's query column (bounds may differ between columns); a column with no
+// key seen yet contributes nothing.
+template <typename T, bool kMask>
+__device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
+                                           const typename Frag<T>::type (&vf)[4], int k_lo,
+                                           int k_hi) {
+  typedef typename Frag<T>::type F;
+  const int grp = (threadIdx.x & 63) >> 4;
   float mx = -INFINITY;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float v = sc[tt][e] + colr[4 * tt + e];
-      if (kMask) v = (8 * grp + 4 * tt + e < valid_keys) ? v : -INFINITY;
-      x[tt][e] = v;
-      mx = fmaxf(mx, v);
+      const int key = 8 * grp + 4 * tt + e;
+      if (kMask) x[tt][e] = (key >= k_lo && key < k_hi) ? x[tt][e] : -INFINITY;
+      mx = fmaxf(mx, x[tt][e]);
     }
-  __builtin_amdgcn_wave_barrier();
   mx = column_max(mx);
   const bool move = mx > st.m + kRescaleLog2;
   if (__ballot(move) != 0) {
@@ -77,17 +108,33 @@ __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>
     for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
     st.m = m_new;
   }
+  // (with a mask, a column may still have seen nothing: its max is -inf, and every probability
+  // of it must be 0, not exp2(-inf - -inf))
+  const float m_ref = (kMask && st.m == -INFINITY) ? 0.f : st.m;
   F pf;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float pe = fast_exp2(x[tt][e] - st.m);
+      const float pe = fast_exp2(x[tt][e] - m_ref);
       st.l += pe;
       set(pf, 4 * tt + e, pe);
     }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
+}
+
+// One 32-key Transformer-XL step given its operand fragments and the three band product tiles.
+// kMask: keys at or past valid_keys are excluded.
+template <typename T, bool kMask>
+__device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>::type (&kf)[2][2],
+                                             const typename Frag<T>::type (&vf)[4],
+                                             const typename Frag<T>::type (&qu)[2],
+                                             const floatx4& g0, const floatx4& g1,
+                                             const floatx4& g2, float* s_g, int valid_keys) {
+  float x[2][4];
+  skew_scores<T>(kf, qu, g0, g1, g2, s_g, x);
+  softmax_pv<T, kMask>(st, x, vf, 0, valid_keys);
 }
 
 }  // namespace pkc

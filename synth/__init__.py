@@ -16,4 +16,6 @@ from .cohorts import (  # noqa: F401
     relpos_projection,
     embed_distances,
     descending_table,
+    key_position_tables,
+    use_key_position_tables,
 )

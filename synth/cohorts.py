@@ -63,6 +63,26 @@ def descending_table(center, proj, n_head, head_dim):
     return embed_distances(dist, proj, n_head, head_dim)
 
 
+def key_position_tables(proj, starts, width, n_head, head_dim):
+    """Per-key tables (WeNet's convention): row j of table b is the projected sinusoid of the
+    absolute position starts[b] + j; float64 [len(starts), width, n_head, head_dim]."""
+    return torch.stack([embed_distances(torch.arange(s0, s0 + width), proj, n_head, head_dim)
+                        for s0 in starts])
+
+
+def use_key_position_tables(co, starts, per_row=True):
+    """Replace a chunk cohort's tables by per-key tables whose keys start at absolute positions
+    ``starts`` (one per stream; ``per_row=False`` takes starts[0] for one shared table), each of
+    max_cache_seqlen + C rows."""
+    B, C, H, D = co.q.shape
+    width = co.max_cache_seqlen + C
+    tabs = key_position_tables(co.meta["proj"], starts if per_row else starts[:1], width, H, D)
+    co.pos = (tabs if per_row else tabs[0]).to(co.q.dtype).to(co.q.device)
+    co.per_row_pos = per_row
+    co.per_key_pos = True
+    return co
+
+
 def _randn(shape, gen, device, dtype, std=1.0):
     x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
     if std != 1.0:
@@ -88,6 +108,7 @@ class ChunkCohort:
     block_size: int
     max_cache_seqlen: int
     meta: dict = field(default_factory=dict)
+    per_key_pos: bool = False     # pos rows are keys (WeNet), not distances
 
     @property
     def shape(self):

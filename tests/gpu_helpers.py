@@ -70,7 +70,8 @@ def compact(co, streams):
         q=host64(co.q[sel]), k_new=host64(co.k_new[sel]), v_new=host64(co.v_new[sel]),
         k_pool=host64(co.k_pool.index_select(0, idx)), v_pool=host64(co.v_pool.index_select(0, idx)),
         bt=bt2, cs=cs, pos=host64(co.pos[sel] if co.per_row_pos else co.pos),
-        u=host64(co.pos_bias_u), w=host64(co.pos_bias_v), per_row=co.per_row_pos)
+        u=host64(co.pos_bias_u), w=host64(co.pos_bias_v), per_row=co.per_row_pos,
+        per_key=getattr(co, "per_key_pos", False))
 
 
 def oracle_chunk(co, streams=None, chunk_lens=None):
@@ -84,7 +85,8 @@ def oracle_chunk(co, streams=None, chunk_lens=None):
     kp, vp = oracle.paged_kv_append(h["k_pool"], h["v_pool"], h["k_new"], h["v_new"], h["bt"], h["cs"],
                                     lens)
     return oracle.chunk_relpos_attn(h["q"], kp, vp, h["bt"], h["cs"], h["pos"], h["u"], h["w"],
-                                    per_row_pos=h["per_row"], chunk_lens=lens)
+                                    per_row_pos=h["per_row"], chunk_lens=lens,
+                                    per_key_pos=h["per_key"])
 
 
 def poison_padding(co, chunk_lens):

@@ -108,7 +108,9 @@ def test_append_validation(lib, kw, status):
     (dict(pos_len=158), SHAPE),                      # even shared table
     (dict(pos_len=157), SHAPE),                      # (157 - 1) / 2 < 64 + 16 - 1
     (dict(per_row=1, pos_len=158), SHAPE),           # per-row needs 2 * 80 - 1
-    (dict(per_row=2), SHAPE),
+    (dict(per_row=4), SHAPE), (dict(per_row=-1), SHAPE),
+    (dict(per_row=2, pos_len=79), SHAPE),            # per-key table needs 64 + 16 rows
+    (dict(per_row=3, pos_len=79), SHAPE),
     (dict(D=128), UNSUP), (dict(S=12, M=12), UNSUP), (dict(S=24, M=12), UNSUP),
     (dict(S=4, M=40), UNSUP),
     (dict(max_cache=120), CAP),

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import paged_kv_chunk_amd as pkc
-from synth import make_chunk_cohort, make_config, make_varlen_cohort
+from synth import make_chunk_cohort, make_config, make_varlen_cohort, use_key_position_tables
 from gpu_helpers import TOL, bits, compact, host64, max_err, oracle_chunk, poison, poison_padding
 
 pytestmark = pytest.mark.gpu
@@ -31,13 +31,14 @@ def gpu_chunk(co, fused=False, chunk_lens=None):
         return pkc.paged_kv_append_relpos_attn(co.q, co.k_new, co.v_new, co.k_pool, co.v_pool,
                                                co.block_tables, co.cache_seqlens, co.pos,
                                                co.pos_bias_u, co.pos_bias_v, co.max_cache_seqlen,
-                                               per_row_pos=co.per_row_pos, chunk_lens=chunk_lens)
+                                               per_row_pos=co.per_row_pos, chunk_lens=chunk_lens,
+                                               per_key_pos=co.per_key_pos)
     pkc.paged_kv_append(co.k_new, co.v_new, co.k_pool, co.v_pool, co.block_tables,
                         co.cache_seqlens, co.max_cache_seqlen, chunk_lens=chunk_lens)
     return pkc.chunk_paged_relpos_attn(co.q, co.k_pool, co.v_pool, co.block_tables,
                                        co.cache_seqlens, co.pos, co.pos_bias_u, co.pos_bias_v,
                                        co.max_cache_seqlen, per_row_pos=co.per_row_pos,
-                                       chunk_lens=chunk_lens)
+                                       chunk_lens=chunk_lens, per_key_pos=co.per_key_pos)
 
 
 def clone(co):
@@ -468,3 +469,37 @@ def test_commit_with_eviction_matches_the_oracle():
     c2 = torch.from_numpy(cache).to(DEV)
     pkc.paged_kv_commit(c2, C)
     assert c2.cpu().numpy().tolist() == (cache + C).tolist()
+
+
+# --------------------------------------------------------------------------------------------
+# WeNet's convention: per-key tables, no shift
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("name,per_row", [("bf16_ragged", True), ("bf16_ragged", False),
+                                          ("gqa_h4_k2", True), ("odd_lengths", True),
+                                          ("per_row_ragged_fp32", True), ("long_chunk_bf16", True),
+                                          ("chunk32_full_tail", False)])
+def test_per_key_tables_parity(name, per_row, fused):
+    """Tables with one row per key (the keys' absolute positions start at offset - cache per
+    stream): the GPU matches the oracle, with short windows and padding lanes mixed in."""
+    co = poison(small_cohort(name, seed=20))
+    B = co.q.shape[0]
+    starts = np.random.default_rng(21).integers(0, 500, size=B).tolist()
+    use_key_position_tables(co, starts, per_row=per_row)
+    if per_row:
+        C = co.q.shape[1]
+        for b, c in enumerate(co.cache_seqlens.cpu().tolist()):
+            co.pos[b, c + C:] = float("nan")              # rows past the stream's keys
+    lens = _lens_for(co, 22)
+    poison_padding(co, lens)
+    ref = oracle_chunk(co, chunk_lens=lens)
+    out = gpu_chunk(co, fused=fused, chunk_lens=torch.from_numpy(lens).to(DEV))
+    assert max_err(out, ref) <= TOL[co.q.dtype], (name, max_err(out, ref))
+
+
+def test_per_key_fused_equals_unfused_bitwise():
+    co = small_cohort("odd_lengths", seed=23)
+    use_key_position_tables(co, [5, 0, 100, 7], per_row=True)
+    co2 = clone(co)
+    np.testing.assert_array_equal(bits(gpu_chunk(co)), bits(gpu_chunk(co2, fused=True)))
