@@ -90,7 +90,9 @@ struct StepRegs {
 
 template <typename T> constexpr int kt_pitch() { return kD + 16 / (int)sizeof(T); }
 
-template <typename T, bool kFused, int kWaves, int kS, bool kRegTail, bool kPerKey>
+// kGen: per-stream chunk lengths or window starts may be given. Without them (the common case)
+// both are compile-time constants, which keeps the prologue's instruction count down.
+template <typename T, bool kFused, int kWaves, int kS, bool kRegTail, bool kPerKey, bool kGen>
 __global__ void __launch_bounds__(kWaves * 64)
 chunk_attn_kernel(ChunkArgs<T> a) {
   typedef typename Frag<T>::type F;
@@ -128,8 +130,12 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   // With bounded history the table row is a ring: the window's page pg sits at entry
   // (pb + pg) mod M, pb = window start / S (whole blocks), so the window follows the start.
   const int nwin = min(a.M, kBtWindow);
-  const int pb = a.ws ? (max(a.ws[b], 0) >> logS) % a.M : 0;
-  auto ring = [&](int pg) { const int e = pg + pb; return e >= a.M ? e - a.M : e; };
+  const int pb = (kGen && a.ws) ? (max(a.ws[b], 0) >> logS) % a.M : 0;
+  auto ring = [&](int pg) {
+    if constexpr (!kGen) return pg;
+    const int e = pg + pb;
+    return e >= a.M ? e - a.M : e;
+  };
   const int bt_lo = lane < nwin ? bt[ring(lane)] : 0;
   const int bt_hi = lane + 64 < nwin ? bt[ring(lane + 64)] : 0;
   F qq[2], uu[2], ww[2];
@@ -156,8 +162,8 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const int cache = clampi(a.cs[b], 0, a.max_cache);
   // real frames of this stream's chunk: frames past them do not exist (not appended, not keys;
   // their output rows are zero); a stream with none is a padding lane and reads nothing
-  const int n_real = a.lens ? clampi(a.lens[b], 0, a.C) : a.C;
-  if (qt * 16 >= n_real) {
+  const int n_real = (kGen && a.lens) ? clampi(a.lens[b], 0, a.C) : a.C;
+  if (kGen && qt * 16 >= n_real) {
     for (int x = tid; x < 16 * NV; x += kThreads) {
       const int i = qt * 16 + x / NV;
       if (i < a.C)
@@ -349,26 +355,24 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       g_prev = mma(p0[1], qv[1], g_prev);
     }
     auto run = [&](StepRegs<T>& r, int s) {
-      float x[2][4];
-      floatx4 g2;
+      // the last cached page may be partly filled: frames at or past cache are then excluded,
+      // and their V is zeroed (the slots may hold anything)
+      const bool part = s == s_part;
+      if (part) zero_from(r.v, cache - (32 * s + 8 * grp));
       if constexpr (kPerKey) {
+        float x[2][4];
         per_key_scores<T>(r.k, r.p, qu, qv, x);
+        if (part) softmax_pv<T, true>(st, x, r.v, 0, cache - 32 * s);
+        else softmax_pv<T, false>(st, x, r.v, 0, 32);
       } else {
         floatx4 g1 = mma(r.p[0][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
         g1 = mma(r.p[0][1], qv[1], g1);
-        g2 = mma(r.p[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        floatx4 g2 = mma(r.p[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
         g2 = mma(r.p[1][1], qv[1], g2);
-        skew_scores<T>(r.k, qu, g_prev, g1, g2, s_g, x);
+        if (part) step_compute<T, true>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, cache - 32 * s);
+        else step_compute<T, false>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, 32);
+        g_prev = g2;
       }
-      if (s == s_part) {
-        // the last cached page is partly filled: frames at or past cache are excluded, and
-        // their V is zeroed (the slots may hold anything)
-        zero_from(r.v, cache - (32 * s + 8 * grp));
-        softmax_pv<T, true>(st, x, r.v, 0, cache - 32 * s);
-      } else {
-        softmax_pv<T, false>(st, x, r.v, 0, 32);
-      }
-      if (!kPerKey) g_prev = g2;
       if (s + 2 < s_end) load_step(r, s + 2);
       else if (s + 2 == s_end) load_tail_band(r);
     };
@@ -392,7 +396,6 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(s_vt + (16 * dt + m16) * a.vt_pitch + 32 * k + 8 * grp);
-    float x[2][4];
     if constexpr (kPerKey) {
       F pk[2][2];
       if (k == wave) {
@@ -406,7 +409,9 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       } else {
         load_key_rows(pk, j0);
       }
+      float x[2][4];
       per_key_scores<T>(kf, pk, qu, qv, x);
+      softmax_pv<T, true>(st, x, vf, 0, T_len - j0);
     } else {
       F pb[3][2];
       if (k == wave) {
@@ -434,9 +439,8 @@ chunk_attn_kernel(ChunkArgs<T> a) {
         g[t] = mma(pb[t][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
         g[t] = mma(pb[t][1], qv[1], g[t]);
       }
-      skew_scores<T>(kf, qu, g[0], g[1], g[2], s_g, x);
+      step_compute<T, true>(st, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
     }
-    softmax_pv<T, true>(st, x, vf, 0, T_len - j0);
   }
 
   // ---- 6. fused append: this tile's chunk frames from LDS into the pool ---------------------
@@ -493,7 +497,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     const int i = qt * 16 + il;
     if (i >= a.C) continue;
     T* dst = a.out + (((size_t)b * a.C + i) * a.H + h) * kD + d0;
-    if (i >= n_real) {
+    if (kGen && i >= n_real) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[k] = from_f<T>(0.f);
       continue;
@@ -522,9 +526,9 @@ chunk_attn_kernel(ChunkArgs<T> a) {
 // assignment and merge order, and with them its result bits, depend on its own length only.
 template <typename T> constexpr int waves_of() { return 4; }
 
-template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false>
+template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false, bool kGen = true>
 void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
-  auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey>;
+  auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey, kGen>;
   if (smem > 64 * 1024) {
     // beyond the default dynamic LDS size (long chunks): opt in once; MI355X allows 160 KB per
     // workgroup
@@ -538,29 +542,41 @@ void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stre
   hipLaunchKernelGGL(fn, grid, dim3(waves_of<T>() * 64), smem, stream, a);
 }
 
+// Instantiation for a call: the block sizes of the streaming workloads get constant page
+// geometry and, without chunk lengths or window starts, the lean kGen = false variant; fp32
+// (used for checking), per-key tables and the rest take the general ones.
+template <typename T, bool kFused, bool kRegTail>
+void launch_lean(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
+  const bool gen = a.lens != nullptr || a.ws != nullptr;
+  if (a.S == 16) {
+    if (gen) return launch_inst<T, kFused, 16, kRegTail, false, true>(a, grid, smem, stream);
+    return launch_inst<T, kFused, 16, kRegTail, false, false>(a, grid, smem, stream);
+  }
+  if (a.S == 32) {
+    if (gen) return launch_inst<T, kFused, 32, kRegTail, false, true>(a, grid, smem, stream);
+    return launch_inst<T, kFused, 32, kRegTail, false, false>(a, grid, smem, stream);
+  }
+  if (gen) return launch_inst<T, kFused, 0, kRegTail, false, true>(a, grid, smem, stream);
+  launch_inst<T, kFused, 0, kRegTail, false, false>(a, grid, smem, stream);
+}
+
 template <typename T, bool kFused>
 void launch_s(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
-  // the block sizes of the streaming workloads get constant page geometry; fp32 (used for
-  // checking) always takes the general instantiation
-  // WeNet's per-key tables: the general block-size instantiation
+  // register-held chunk for fused bf16 chunks of at most 32 frames (one 16-byte vector of K and
+  // one of V per thread, requested at kernel start)
+  constexpr bool kRegOk = sizeof(T) == 2 && kFused;
+  const bool reg_tail = kRegOk && a.C <= 32;
   if (a.per_key) {
-    if constexpr (sizeof(T) == 2 && kFused) {
-      if (a.C <= 32) return launch_inst<T, kFused, 0, true, true>(a, grid, smem, stream);
+    if constexpr (kRegOk) {
+      if (reg_tail) return launch_inst<T, kFused, 0, true, true>(a, grid, smem, stream);
     }
     return launch_inst<T, kFused, 0, false, true>(a, grid, smem, stream);
   }
-  // fused bf16 chunks of at most 32 frames: the chunk's K and V are one 16-byte vector each per
-  // thread, requested at kernel start and held in registers
-  if constexpr (sizeof(T) == 2 && kFused) {
-    if (a.C <= 32) {
-      if (a.S == 16) return launch_inst<T, kFused, 16, true>(a, grid, smem, stream);
-      if (a.S == 32) return launch_inst<T, kFused, 32, true>(a, grid, smem, stream);
-      return launch_inst<T, kFused, 0, true>(a, grid, smem, stream);
-    }
-  }
   if constexpr (sizeof(T) == 2) {
-    if (a.S == 16) return launch_inst<T, kFused, 16, false>(a, grid, smem, stream);
-    if (a.S == 32) return launch_inst<T, kFused, 32, false>(a, grid, smem, stream);
+    if constexpr (kRegOk) {
+      if (reg_tail) return launch_lean<T, kFused, true>(a, grid, smem, stream);
+    }
+    return launch_lean<T, kFused, false>(a, grid, smem, stream);
   }
   launch_inst<T, kFused, 0, false>(a, grid, smem, stream);
 }

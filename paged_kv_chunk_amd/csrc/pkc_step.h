@@ -124,17 +124,69 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
 }
 
-// One 32-key Transformer-XL step given its operand fragments and the three band product tiles.
-// kMask: keys at or past valid_keys are excluded.
+// One whole 32-key Transformer-XL step given its operand fragments and the three band product
+// tiles (scores already in log2 units), in one piece: the scores, the mask and the running max
+// stay between the two wave barriers of the shift, which keeps the register live ranges of the
+// hot loop short. kMask: keys at or past valid_keys are excluded (the same keys for every query
+// column, and never all of a step's keys).
 template <typename T, bool kMask>
 __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>::type (&kf)[2][2],
                                              const typename Frag<T>::type (&vf)[4],
                                              const typename Frag<T>::type (&qu)[2],
                                              const floatx4& g0, const floatx4& g1,
                                              const floatx4& g2, float* s_g, int valid_keys) {
+  typedef typename Frag<T>::type F;
+  const int lane = threadIdx.x & 63;
+  const int m16 = lane & 15;
+  const int grp = lane >> 4;
+  floatx4 sc[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    sc[tt] = mma(kf[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
+    sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
+  }
+  // Relative shift through LDS: G^T[row][query] -> s_g[query * kSkewPitch + row]; the lane then
+  // reads its 8 keys' values from its own query column, shifted by 15 - query.
+  float* colw = s_g + m16 * kSkewPitch + 4 * grp;
+  *reinterpret_cast<floatx4*>(colw) = g0;
+  *reinterpret_cast<floatx4*>(colw + 16) = g1;
+  *reinterpret_cast<floatx4*>(colw + 32) = g2;
+  __builtin_amdgcn_wave_barrier();
+  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * grp;
   float x[2][4];
-  skew_scores<T>(kf, qu, g0, g1, g2, s_g, x);
-  softmax_pv<T, kMask>(st, x, vf, 0, valid_keys);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = sc[tt][e] + colr[4 * tt + e];
+      if (kMask) v = (8 * grp + 4 * tt + e < valid_keys) ? v : -INFINITY;
+      x[tt][e] = v;
+      mx = fmaxf(mx, v);
+    }
+  __builtin_amdgcn_wave_barrier();
+  mx = column_max(mx);
+  const bool move = mx > st.m + kRescaleLog2;
+  if (__ballot(move) != 0) {
+    const float m_new = move ? mx : st.m;
+    const float alpha = fast_exp2(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
+    st.m = m_new;
+  }
+  F pf;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = fast_exp2(x[tt][e] - st.m);
+      st.l += pe;
+      set(pf, 4 * tt + e, pe);
+    }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
 }
+
 
 }  // namespace pkc
