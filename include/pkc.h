@@ -245,13 +245,19 @@ pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,
  * utterance; empty utterances are allowed. The kernel clamps cu_seqlens into [0, total_frames],
  * so malformed offsets give unspecified values but no out-of-bounds access; frames of an
  * utterance longer than max_seqlen past max_seqlen are not written.
- * Errors: as above; head_dim != 64 -> PKC_ERR_UNSUPPORTED.
+ * mask_chunk > 0 applies the chunked_limited mask [MOD nem] inside every utterance: frame i (counted
+ * from the utterance's first frame) sees only the frames of chunks i / mask_chunk -
+ * mask_left_chunks ... i / mask_chunk, and each 64-frame query block computes only over the keys
+ * its frames can see (its own frames plus the trained history). mask_chunk = 0: full context.
+ * Errors: as above; a negative mask_chunk or mask_left_chunks -> PKC_ERR_SHAPE; head_dim != 64
+ * -> PKC_ERR_UNSUPPORTED.
  */
 pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,
                                      const int32_t* cu_seqlens, int32_t num_seqs,
                                      int32_t total_frames, int32_t max_seqlen, const void* pos,
                                      const void* pos_bias_u, const void* pos_bias_v, void* out,
                                      int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                                     int32_t mask_chunk, int32_t mask_left_chunks,
                                      float softmax_scale, hipStream_t stream);
 
 #ifdef __cplusplus

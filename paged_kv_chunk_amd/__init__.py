@@ -36,7 +36,7 @@ SIGNATURES = {
                                            + [_ptr] * 3 + [_i32] * 9 + [_f32, _ptr], ctypes.c_int),
     "paged_kv_commit": ([_ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _ptr], ctypes.c_int),
     "varlen_packed_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _ptr,
-                                   _ptr, _ptr, _ptr, _i32, _i32, _i32, _f32, _ptr], ctypes.c_int),
+                                   _ptr, _ptr, _ptr] + [_i32] * 5 + [_f32, _ptr], ctypes.c_int),
 }
 
 
@@ -218,8 +218,10 @@ def paged_kv_commit(cache_seqlens, chunk, chunk_lens=None, window_start=None,
 
 
 def varlen_packed_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, max_seqlen,
-                              out=None, softmax_scale=0.0, stream=None):
-    """Attention inside each packed utterance; q [total, H, D], k/v [total, Hk, D]."""
+                              out=None, softmax_scale=0.0, mask_chunk=0, mask_left_chunks=0,
+                              stream=None):
+    """Attention inside each packed utterance; q [total, H, D], k/v [total, Hk, D]; mask_chunk > 0
+    applies the chunked_limited mask (own chunk plus mask_left_chunks earlier ones)."""
     total, H, D = q.shape
     Hk = k.shape[1]
     if out is None:
@@ -227,6 +229,7 @@ def varlen_packed_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, 
     st = lib().varlen_packed_relpos_attn(
         _dtype(q, k, v, pos, pos_bias_u, pos_bias_v, out), _p(q), _p(k), _p(v), _table(cu_seqlens),
         cu_seqlens.shape[0] - 1, total, int(max_seqlen), _p(pos), _p(pos_bias_u), _p(pos_bias_v),
-        _p(out), H, Hk, D, float(softmax_scale), _stream(stream))
+        _p(out), H, Hk, D, int(mask_chunk), int(mask_left_chunks), float(softmax_scale),
+        _stream(stream))
     _check(st, "varlen_packed_relpos_attn")
     return out

@@ -236,6 +236,7 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
                                      int32_t total_frames, int32_t max_seqlen, const void* pos,
                                      const void* pos_bias_u, const void* pos_bias_v, void* out,
                                      int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                                     int32_t mask_chunk, int32_t mask_left_chunks,
                                      float softmax_scale, hipStream_t stream) {
   pkc_status st = check_dtype(dtype);
   if (st != PKC_OK) return st;
@@ -246,13 +247,15 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
     return PKC_ERR_SHAPE;
   if ((int64_t)total_frames >= (int64_t)1 << 29 || (int64_t)max_seqlen > total_frames)
     return PKC_ERR_SHAPE;
+  if (mask_chunk < 0 || mask_left_chunks < 0) return PKC_ERR_SHAPE;
   if (head_dim != 64) return PKC_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pos) ||
       !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))
     return PKC_ERR_ALIGN;
   if (total_frames == 0 || max_seqlen == 0) return PKC_OK;
   VarlenParams p{q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, out, num_seqs, total_frames,
-                 max_seqlen, n_head, n_kv_head, head_dim, softmax_scale};
+                 max_seqlen, n_head, n_kv_head, head_dim, mask_chunk, mask_left_chunks,
+                 softmax_scale};
   return from_hip(launch_varlen_attn(dtype, p, stream));
 }
 

@@ -54,6 +54,7 @@ struct VarlenParams {
   const void* pos_bias_v;
   void* out;
   int num_seqs, total, max_seqlen, n_head, n_kv_head, head_dim;
+  int mask_chunk, mask_left_chunks;   // chunked_limited mask, or mask_chunk = 0: full context
   float softmax_scale;
 };
 

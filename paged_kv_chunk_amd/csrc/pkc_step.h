@@ -102,7 +102,9 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
   const bool move = mx > st.m + kRescaleLog2;
   if (__ballot(move) != 0) {
     const float m_new = move ? mx : st.m;
-    const float alpha = fast_exp2(st.m - m_new);
+    // (a column that does not move keeps its scale; computing it as exp2(m - m) would give NaN
+    // for a column that has seen no key yet, m = -inf)
+    const float alpha = move ? fast_exp2(st.m - m_new) : 1.f;
     st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;

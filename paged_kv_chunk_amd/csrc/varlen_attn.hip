@@ -12,6 +12,11 @@
 // staged once in double-buffered LDS and read by all four waves, while each wave fetches its own
 // band rows (the table rows its 16 queries touch) one step ahead. The per-step math is the shared
 // step engine of pkc_step.h. MFMA-bound in principle (6 L^2 D FLOP per utterance and head).
+//
+// chunked_limited mask ("Model Layer", Nemotron encoder notes; kLimited): query i sees only the
+// keys of its own chunk of `chunk` frames and of the `left` chunks before it. A workgroup then
+// walks only the keys its 64 queries can see - its own frames plus the trained history, as one
+// streaming step per query block - and each query column masks to its own range.
 #include "pkc_device.h"
 #include "pkc_launch.h"
 #include "pkc_step.h"
@@ -38,10 +43,11 @@ struct VarlenArgs {
   const T* w;
   T* out;
   int H, Hk, qtiles, total;
+  int chunk, left;            // chunked_limited mask (kLimited)
   float scale_log2;
 };
 
-template <typename T>
+template <typename T, bool kLimited>
 __global__ void __launch_bounds__(kThreads)
 varlen_attn_kernel(VarlenArgs<T> a) {
   typedef typename Frag<T>::type F;
@@ -155,23 +161,39 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float* s_g = s_skew + wave * kSkewFloats;
 
-  const int nsteps = (L + 31) >> 5;
+  // the keys this workgroup's queries can see: all of the utterance, or with the chunked_limited
+  // mask the first visible key of its first query to the last of its last query; and per query
+  // column (this lane's query, clamped into the utterance) its own range [k_lo_q, k_hi_q)
+  int j_first = 0, j_end = L, k_lo_q = 0, k_hi_q = L;
+  if constexpr (kLimited) {
+    const int left = min(a.left, L);   // more chunks than frames sees everything anyway
+    const int tq0 = qt * kQTile;
+    const int tq1 = min(tq0 + kQTile, L) - 1;
+    j_first = max(0, (tq0 / a.chunk - left) * a.chunk);
+    j_end = min(L, (tq1 / a.chunk + 1) * a.chunk);
+    const int iq = min(q0 + m16, L - 1);
+    k_lo_q = max(0, (iq / a.chunk - left) * a.chunk);
+    k_hi_q = min(L, (iq / a.chunk + 1) * a.chunk);
+  }
+  const int s_first = j_first >> 5;
+  const int nsteps = ((j_end + 31) >> 5) - s_first;
   floatx4 g_prev;
   {
-    const T* row = band_row(R0 - qlast + m16) + 8 * grp;
+    const T* row = band_row(R0 + 32 * s_first - qlast + m16) + 8 * grp;
     const F p_lo = load8(row);
     const F p_hi = load8(row + 32);
     g_prev = mma(p_lo, qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
     g_prev = mma(p_hi, qv[1], g_prev);
   }
-  fetch(ra, 0);
-  if (nsteps > 1) fetch(rb, 32);
-  fetch_band(0);
+  fetch(ra, 32 * s_first);
+  if (nsteps > 1) fetch(rb, 32 * s_first + 32);
+  fetch_band(32 * s_first);
   stash(ra, s_kv);
   __syncthreads();
-  // one step: registers `nxt` already hold step + 1, `fre` receives step + 2
+  // one step (index `step` from the first visible one): registers `nxt` already hold step + 1,
+  // `fre` receives step + 2
   auto do_step = [&](int step, Rows& nxt, Rows& fre) {
-    const int j0 = 32 * step;
+    const int j0 = 32 * (s_first + step);
     const T* cur = s_kv + (step & 1) * TILE;
     if (step + 2 < nsteps) fetch(fre, j0 + 64);
     F kf[2][2], vf[4];
@@ -188,10 +210,15 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     floatx4 g2 = mma(pb[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
     g2 = mma(pb[1][1], qv[1], g2);
     if (step + 1 < nsteps) fetch_band(j0 + 32);
-    if (j0 + 32 <= L)
+    if constexpr (kLimited) {
+      float x[2][4];
+      skew_scores<T>(kf, qu, g_prev, g1, g2, s_g, x);
+      softmax_pv<T, true>(st, x, vf, k_lo_q - j0, k_hi_q - j0);
+    } else if (j0 + 32 <= L) {
       step_compute<T, false>(st, kf, vf, qu, g_prev, g1, g2, s_g, 32);
-    else
+    } else {
       step_compute<T, true>(st, kf, vf, qu, g_prev, g1, g2, s_g, L - j0);
+    }
     g_prev = g2;
     if (step + 1 < nsteps) stash(nxt, s_kv + ((step + 1) & 1) * TILE);
     __syncthreads();
@@ -231,8 +258,13 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
   a.total = p.total;
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.chunk = p.mask_chunk;
+  a.left = p.mask_left_chunks;
   const dim3 grid((unsigned)p.num_seqs * p.n_head * a.qtiles);
-  hipLaunchKernelGGL(varlen_attn_kernel<T>, grid, dim3(kThreads), 0, stream, a);
+  if (p.mask_chunk > 0)
+    hipLaunchKernelGGL((varlen_attn_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((varlen_attn_kernel<T, false>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

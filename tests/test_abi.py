@@ -83,9 +83,9 @@ def fused(lib, k_new=P, v_new=P, **kw):
 
 
 def varlen(lib, dtype=1, q=P, k=P, v=P, cu=P, S=4, total=100, max_len=40, pos=P, u=P, w=P, out=P,
-           H=8, Hk=8, D=64):
+           H=8, Hk=8, D=64, chunk=0, left=0):
     return lib.varlen_packed_relpos_attn(dtype, q, k, v, cu, S, total, max_len, pos, u, w, out, H,
-                                         Hk, D, 0.0, None)
+                                         Hk, D, chunk, left, 0.0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -137,6 +137,7 @@ def test_fused_validation(lib):
     (dict(dtype=3), DTYPE), (dict(cu=None), NULL), (dict(k=None), NULL),
     (dict(S=0), SHAPE), (dict(H=6, Hk=4), SHAPE), (dict(max_len=101), SHAPE), (dict(D=12), SHAPE),
     (dict(D=128), UNSUP), (dict(v=BAD), ALIGN),
+    (dict(chunk=-1), SHAPE), (dict(chunk=4, left=-2), SHAPE),
 ])
 def test_varlen_validation(lib, kw, status):
     assert varlen(lib, **kw) == status

@@ -503,3 +503,47 @@ def test_per_key_fused_equals_unfused_bitwise():
     use_key_position_tables(co, [5, 0, 100, 7], per_row=True)
     co2 = clone(co)
     np.testing.assert_array_equal(bits(gpu_chunk(co)), bits(gpu_chunk(co2, fused=True)))
+
+
+# --------------------------------------------------------------------------------------------
+# The chunked_limited mask in the packed offline kernel
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,chunk,left", [(BF16, 16, 4), (BF16, 14, 5), (BF16, 4, 0),
+                                              (BF16, 100, 1), (BF16, 8, 1000), (F32, 13, 2)])
+def test_varlen_chunked_limited_parity(dtype, chunk, left):
+    """Utterances of many lengths (shorter than a chunk, not a multiple of it, several query
+    blocks) under the chunked_limited mask, against the oracle."""
+    co = make_varlen_cohort([1, 37, 0, 130, 64, 200, 5], 2, 64, dtype=dtype, seed=30, device=DEV)
+    ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
+                                    co.cu_seqlens.cpu().numpy(), host64(co.pos),
+                                    host64(co.pos_bias_u), host64(co.pos_bias_v), chunk=chunk,
+                                    left_chunks=left)
+    out = pkc.varlen_packed_relpos_attn(co.q, co.k, co.v, co.cu_seqlens, co.pos, co.pos_bias_u,
+                                        co.pos_bias_v, max(co.lengths), mask_chunk=chunk,
+                                        mask_left_chunks=left)
+    assert max_err(out, ref) <= TOL[dtype], (chunk, left, max_err(out, ref))
+
+
+def test_varlen_chunked_limited_sampled_workload():
+    """The packed offline workload under a 16-frame chunk with 4 left chunks, checked on sampled
+    rows of the longest, shortest, first and last utterances."""
+    co = make_config(4, device=DEV)
+    out = pkc.varlen_packed_relpos_attn(co.q, co.k, co.v, co.cu_seqlens, co.pos, co.pos_bias_u,
+                                        co.pos_bias_v, max(co.lengths), mask_chunk=16,
+                                        mask_left_chunks=4)
+    lengths = co.lengths
+    segs = sorted({int(np.argmax(lengths)), int(np.argmin(lengths)), 0, len(lengths) - 1})
+    rng = np.random.default_rng(31)
+
+    def rows(n):
+        pick = set(range(min(20, n))) | set(range(max(0, n - 20), n))
+        pick |= set(rng.choice(n, size=min(20, n), replace=False).tolist())
+        return sorted(pick)
+    ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
+                                    co.cu_seqlens.cpu().numpy(), host64(co.pos),
+                                    host64(co.pos_bias_u), host64(co.pos_bias_v),
+                                    segments=segs, query_rows=rows, chunk=16, left_chunks=4)
+    have = ~np.isnan(ref[:, 0, 0])
+    o = out.detach().cpu().double().numpy()
+    assert np.abs(o[have] - ref[have]).max() <= TOL[BF16]
