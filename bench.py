@@ -84,7 +84,11 @@ def algorithmic_bytes(co):
     qo = sum(lens) * H * D * eb + B * C * H * D * eb
     new = 4 * sum(lens) * Hk * D * eb
     cached = 2 * sum(c for c, _ in live) * Hk * D * eb
-    if co.per_row_pos:
+    if getattr(co, "per_key_pos", False):
+        # one table row per key: c + n rows per stream, or the longest for a shared table
+        rows = [c + n for c, n in live]
+        band = (sum(rows) if co.per_row_pos else max(rows, default=0)) * H * D * eb
+    elif co.per_row_pos:
         band = sum(c + C + n - 1 for c, n in live) * H * D * eb
     else:
         band = max((c + C + n - 1 for c, n in live), default=0) * H * D * eb
@@ -115,7 +119,8 @@ def launch_layer(pkc, co, stream):
     pkc.paged_kv_append_relpos_attn(co.q, co.k_new, co.v_new, co.k_pool, co.v_pool,
                                     co.block_tables, co.cache_seqlens, co.pos, co.pos_bias_u,
                                     co.pos_bias_v, co.max_cache_seqlen,
-                                    per_row_pos=co.per_row_pos, out=co.out,
+                                    per_row_pos=co.per_row_pos, per_key_pos=co.per_key_pos,
+                                    out=co.out,
                                     chunk_lens=getattr(co, "chunk_lens", None), stream=stream)
 
 
@@ -159,7 +164,7 @@ def cpu_baseline(co, min_seconds):
     while True:
         kp, vp = oracle.paged_kv_append(*args, bt, cs, lens)
         oracle.chunk_relpos_attn(q, kp, vp, bt, cs, pos, u, w, per_row_pos=co.per_row_pos,
-                                 chunk_lens=lens)
+                                 chunk_lens=lens, per_key_pos=getattr(co, "per_key_pos", False))
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
@@ -171,11 +176,22 @@ def cpu_baseline(co, min_seconds):
                        f"append + attention in float64 numpy, {el:.1f} s")
 
 
-def varlen_flops(co):
-    """Algorithmic FLOPs of the packed offline attention: per utterance and head, L^2 dot products
-    of length D for each of the content term, the position term and the PV product."""
+def visible_pairs(L, chunk=0, left=0):
+    """(query, key) pairs of one utterance: all L^2, or under the chunked_limited mask the keys of
+    each query's own chunk and of the ``left`` chunks before it."""
+    if chunk <= 0:
+        return L * L
+    i = np.arange(L)
+    a = i // chunk
+    return int((np.minimum(L, (a + 1) * chunk) - np.maximum(0, (a - left) * chunk)).sum())
+
+
+def varlen_flops(co, chunk=0, left=0):
+    """Algorithmic FLOPs of the packed offline attention: per utterance and head, one dot product
+    of length D for each of the content term, the position term and the PV product per visible
+    (query, key) pair (L^2 without a mask)."""
     H, D = co.q.shape[1], co.q.shape[2]
-    return sum(6 * L * L * D * H for L in co.lengths)
+    return sum(6 * visible_pairs(L, chunk, left) * D * H for L in co.lengths)
 
 
 def varlen_bytes(co):
@@ -197,7 +213,9 @@ def bench_varlen(args, cfg, pkc):
 
     def call(co, st):
         pkc.varlen_packed_relpos_attn(co.q, co.k, co.v, co.cu_seqlens, co.pos, co.pos_bias_u,
-                                      co.pos_bias_v, max(co.lengths), out=co.out, stream=st)
+                                      co.pos_bias_v, max(co.lengths), out=co.out,
+                                      mask_chunk=args.mask_chunk, mask_left_chunks=args.mask_left,
+                                      stream=st)
 
     for co in sets:
         call(co, stream)
@@ -224,7 +242,7 @@ def bench_varlen(args, cfg, pkc):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    flops = sum(varlen_flops(co) for co in sets) / len(sets)
+    flops = sum(varlen_flops(co, args.mask_chunk, args.mask_left) for co in sets) / len(sets)
     nbytes = sum(varlen_bytes(co) for co in sets) / len(sets)
     units = sum(len(co.lengths) * co.q.shape[1] for co in sets) / len(sets)
     tflops = flops / (ms / 1e3) / 1e12
@@ -237,10 +255,14 @@ def bench_varlen(args, cfg, pkc):
         "data": "synthetic",
         "config": {"workload": f"{cfg['name']}: {cfg['n_seqs']} utterances, lengths uniform in "
                                f"[{cfg['len_lo']}, {cfg['len_hi']}], H={cfg['H']}, head_dim={cfg['D']}, "
-                               "per-utterance tables, no cache", "rotated_batches": len(sets),
-                   "launch": "graph"},
+                               "per-utterance tables, no cache" + (
+                                   f", chunked_limited mask (chunk {args.mask_chunk} frames, "
+                                   f"{args.mask_left} left chunks)" if args.mask_chunk else ""),
+                   "rotated_batches": len(sets), "launch": "graph",
+                   "mask_chunk": args.mask_chunk, "mask_left_chunks": args.mask_left},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": tflops / 2500.0, "traffic": stored_traffic("varlen_cfg4", "varlen"),
+                     "frac": tflops / 2500.0,
+                     "traffic": None if args.mask_chunk else stored_traffic("varlen_cfg4", "varlen"),
                      "kernel": "varlen_attn_kernel<bf16>", "kernel_us": ms * 1e3,
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes,
@@ -266,6 +288,12 @@ def main():
                     help="the last N streams of the cohort are padding lanes (chunk length 0)")
     ap.add_argument("--short-frac", type=float, default=0.0,
                     help="fraction of the real streams in a short final window (1..C-1 frames)")
+    ap.add_argument("--mask-chunk", type=int, default=0,
+                    help="packed offline workload: chunked_limited mask chunk (frames); 0 = none")
+    ap.add_argument("--mask-left", type=int, default=0,
+                    help="packed offline workload: left chunks of the chunked_limited mask")
+    ap.add_argument("--per-key", action="store_true",
+                    help="cohort workloads: WeNet per-key tables instead of Transformer-XL ones")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the workload, time a plain device copy of this many MiB "
                          "(reference for HBM counters and achievable bandwidth)")
@@ -309,6 +337,13 @@ def main():
     lens_mode = bool(args.pad_lanes or args.short_frac)
     if lens_mode:
         set_chunk_lens(sets, args.pad_lanes, args.short_frac)
+    if args.per_key:
+        from synth import use_key_position_tables
+        for layers in sets:
+            for co in layers:
+                # keys' absolute positions start at offset - cache; here every stream's offset is
+                # its cache length (unlimited history), so positions start at 0
+                use_key_position_tables(co, [0] * co.q.shape[0], per_row=co.per_row_pos)
     stream = torch.cuda.current_stream()
     co0 = sets[0][0]
     B, C, H, D = co0.q.shape
@@ -378,7 +413,8 @@ def main():
     bytes_per_launch = algorithmic_bytes(co0)
     achieved = bytes_per_launch / (kernel_ms / 1e3) / 1e9
 
-    traffic = None if lens_mode else stored_traffic(f"fused_cfg{args.config}", "chunk")
+    traffic = (None if lens_mode or args.per_key
+               else stored_traffic(f"fused_cfg{args.config}", "chunk"))
 
     result = {
         "metric": METRIC,
@@ -401,6 +437,7 @@ def main():
             "cache_frames": co0.max_cache_seqlen, "block_size": co0.block_size,
             "layers": n_layers, "rotated_cohorts": len(sets), "launch": mode,
             "shared_pos_table": not co0.per_row_pos,
+            "pos_convention": "per-key (WeNet, no shift)" if args.per_key else "Transformer-XL",
         },
         "roofline": {
             "bound": "hbm",
