@@ -32,8 +32,10 @@ Readings where the pages are silent (each is listed, with its reason, in the des
   distance ``center - r`` (row 0 is the largest positive distance). A shared table is centred at
   (P - 1) / 2; a per-row table of stream b holds 2 T_b - 1 rows centred at T_b - 1, T_b = c_b + C.
 * GQA: query head h reads kv head h * Hk // H.
-* Page layout (the pages give none): k_pool[n, g, s, d] and v_pool[n, g, d, s] (V transposed inside
-  each page); logical frame t of stream b sits in block block_tables[b, t // S], slot t % S.
+* Page layout (the pages give none): v_pool[n, g, d, s] (V transposed inside each page), and K
+  either k_pool[n, g, s, d] or, in column blocks of w dims, k_pool[n, g, c, s, e] holding dim
+  c w + e of slot s (the kernels' layout, w = 32: a page keeps each 32-dim half of every slot's
+  row together); logical frame t of stream b sits in block block_tables[b, t // S], slot t % S.
 * Bounded history ("ASR Engine", section 6, num_left_chunks and recycle_streaming_history;
   section 9, cached_frames held at max_logical_blocks - 1 blocks, positions unaffected): a stream
   may carry a window start w_b, the absolute position of its first cached frame, a multiple of S.
@@ -52,8 +54,25 @@ from __future__ import annotations
 
 import numpy as np
 
-DEFAULT_LAYOUT = {"k_pool": "[num_blocks, n_kv_head, block_size, head_dim]",
+DEFAULT_LAYOUT = {"k_pool": "[num_blocks, n_kv_head, head_dim / 32, block_size, 32]",
                   "v_pool": "[num_blocks, n_kv_head, head_dim, block_size]"}
+
+
+def _k_put(k_pool, block, slot, rows):
+    """Write one slot's K rows [Hk, D] into a plain or column-blocked K pool."""
+    if k_pool.ndim == 5:
+        n_kv, nb, w = k_pool.shape[1], k_pool.shape[2], k_pool.shape[4]
+        k_pool[block, :, :, slot, :] = np.asarray(rows).reshape(n_kv, nb, w)
+    else:
+        k_pool[block, :, slot, :] = rows
+
+
+def _k_get(k_pool, block, slot):
+    """One slot's K rows [Hk, D] from a plain or column-blocked K pool."""
+    if k_pool.ndim == 5:
+        n_kv, nb, w = k_pool.shape[1], k_pool.shape[2], k_pool.shape[4]
+        return k_pool[block, :, :, slot, :].reshape(n_kv, nb * w)
+    return k_pool[block, :, slot, :]
 
 
 def _slot(block_table_row, p, block_size):
@@ -79,14 +98,14 @@ def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, cache_seqlens, c
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     n_streams, chunk = k_new.shape[0], k_new.shape[1]
-    block_size = k_pool.shape[2]
+    block_size = v_pool.shape[3]
     for b in range(n_streams):
         n_real = chunk if chunk_lens is None else int(chunk_lens[b])
         start = 0 if window_start is None else int(window_start[b])
         for t in range(n_real):
             frame = start + int(cache_seqlens[b]) + t
             block, slot = _slot(block_tables[b], frame, block_size)
-            k_out[block, :, slot, :] = k_new[b, t]
+            _k_put(k_out, block, slot, k_new[b, t])
             v_out[block, :, :, slot] = v_new[b, t]
     return k_out, v_out
 
@@ -118,11 +137,11 @@ def gather_stream(k_pool, v_pool, block_table_row, n_frames, start=0):
     Returns K, V as [n_frames, Hk, D] arrays in the pool's dtype ("Scheduler" section 4.3: the
     attention reads the paged pool through each stream's table).
     """
-    block_size = k_pool.shape[2]
+    block_size = v_pool.shape[3]
     ks, vs = [], []
     for t in range(start, start + n_frames):
         block, slot = _slot(block_table_row, t, block_size)
-        ks.append(k_pool[block, :, slot, :])
+        ks.append(_k_get(k_pool, block, slot))
         vs.append(v_pool[block, :, :, slot])
     return np.stack(ks), np.stack(vs)
 

@@ -727,3 +727,34 @@ def test_chunked_limited_offline_equals_streaming_with_the_trained_window(chunk,
                 torch.from_numpy(q[lo:lo + n, h] + u[h])[None], torch.from_numpy(k[lo:lo + n, h])[None],
                 torch.from_numpy(v[lo:lo + n, h])[None], attn_mask=torch.from_numpy(bias)[None])
             assert np.abs(ref[0].numpy() - out[lo:lo + n, h]).max() < 1e-12
+
+
+def test_column_blocked_k_pages():
+    """The kernels' K page layout keeps each 32-dim block of every slot's row together:
+    element (block, g, c, slot, e) holds dim 32 c + e of the frame in that slot. Appending into
+    such a pool puts every value where that definition says, and reading back through it
+    returns the same frames as the plain [slot][dim] layout."""
+    rng = np.random.default_rng(81)
+    B, C, Hk, D, S, N = 2, 5, 2, 64, 8, 6
+    bt = np.array([[4, 1, 5], [0, 3, 2]])
+    cs = np.array([3, 9])
+    k_new = rng.standard_normal((B, C, Hk, D))
+    v_new = rng.standard_normal((B, C, Hk, D))
+    plain = np.full((N, Hk, S, D), np.nan)
+    blocked = np.full((N, Hk, D // 32, S, 32), np.nan)
+    vp = np.full((N, Hk, D, S), np.nan)
+    kp1, vp1 = oracle.paged_kv_append(plain, vp, k_new, v_new, bt, cs)
+    kp2, vp2 = oracle.paged_kv_append(blocked, vp, k_new, v_new, bt, cs)
+    np.testing.assert_array_equal(vp1, vp2)
+    for b in range(B):
+        for t in range(C):
+            f = cs[b] + t
+            blk, slot = bt[b, f // S], f % S
+            for c in range(D // 32):
+                np.testing.assert_array_equal(kp2[blk, :, c, slot, :], k_new[b, t, :, 32 * c:32 * c + 32])
+    assert np.isnan(kp2).sum() == np.isnan(kp1).sum()
+    for b in range(B):
+        k1, v1 = oracle.gather_stream(kp1, vp1, bt[b], cs[b] + C)
+        k2, v2 = oracle.gather_stream(kp2, vp2, bt[b], cs[b] + C)
+        np.testing.assert_array_equal(k1, k2)
+        np.testing.assert_array_equal(v1, v2)
