@@ -38,7 +38,11 @@
  * D = head_dim, S = block_size, N = num_blocks, M = max_blocks_per_seq:
  *   q, out          [B, C, H, D]
  *   k_new, v_new    [B, C, Hk, D]
- *   k_pool          [N, Hk, S, D]            one pool per layer
+ *   k_pool          [N, Hk, D / 32, S, 32]   one pool per layer; K pages in 32-dim column
+ *                                            blocks: dim d of slot s is element (d / 32, s,
+ *                                            d % 32), so each 32-dim half of every slot's row
+ *                                            is contiguous (an MFMA fragment's half-row loads
+ *                                            then cover whole 128-byte lines)
  *   v_pool          [N, Hk, D, S]            V is stored transposed inside each page
  *   block_tables    int32 [B, M]             logical frame t of stream b is in block
  *                                            block_tables[b][t / S], slot t % S
@@ -117,12 +121,13 @@ const char* pkc_status_string(int status);
  *
  * For b < batch and t < n_b (chunk_lens[b], or chunk_size when chunk_lens is NULL), with
  * L = cache_seqlens[b] + t:
- *     k_pool[block_tables[b][L / S]][g][L % S][:] = k_new[b][t][g][:]
+ *     k_pool[block_tables[b][L / S]][g][c][L % S][:] = k_new[b][t][g][32 c : 32 c + 32]
  *     v_pool[block_tables[b][L / S]][g][:][L % S] = v_new[b][t][g][:]
  * for every kv head g. No other pool element is touched; the copy is bit-exact. The caller then
  * runs the attention and afterwards advances cache_seqlens by n_b itself.
  * Errors: NULL pointers -> PKC_ERR_NULL; non-positive sizes or head_dim not a multiple of 8 ->
- * PKC_ERR_SHAPE; max_cache_seqlen + chunk_size > max_blocks_per_seq * block_size ->
+ * PKC_ERR_SHAPE; head_dim not a multiple of 32 -> PKC_ERR_UNSUPPORTED;
+ * max_cache_seqlen + chunk_size > max_blocks_per_seq * block_size ->
  * PKC_ERR_CAPACITY (the analogue of the pool/table ceiling errors of [ENG 6]).
  */
 pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new, void* k_pool,

@@ -117,16 +117,26 @@ def _stream(stream):
 
 def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, max_cache_seqlen,
                     chunk_lens=None, window_start=None, stream=None):
-    """Write k_new / v_new [B, C, Hk, D] into k_pool [N, Hk, S, D] / v_pool [N, Hk, D, S]
+    """Write k_new / v_new [B, C, Hk, D] into k_pool [N, Hk, D / 32, S, 32] / v_pool [N, Hk, D, S]
     (only the first chunk_lens[b] frames of stream b when chunk_lens is given; window_start
     int32 [B] addresses the table rows as rings)."""
     B, C, Hk, D = k_new.shape
-    N, _, S, _ = k_pool.shape
+    N, _, S = _pool_geom(k_pool, v_pool, D)
     st = lib().paged_kv_append(_dtype(k_new, v_new, k_pool, v_pool), _p(k_new), _p(v_new),
                                _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
                                _table(chunk_lens), _table(window_start), B, C, Hk, D, S, N,
                                block_tables.shape[1], int(max_cache_seqlen), _stream(stream))
     _check(st, "paged_kv_append")
+
+
+def _pool_geom(k_pool, v_pool, head_dim):
+    """(N, Hk, S) of a K pool [N, Hk, D / 32, S, 32] and V pool [N, Hk, D, S]."""
+    if k_pool.dim() != 5 or k_pool.shape[2] * k_pool.shape[4] != head_dim or k_pool.shape[4] != 32:
+        raise ValueError("k_pool must be [num_blocks, n_kv_head, head_dim / 32, block_size, 32]")
+    N, Hk, _, S, _ = k_pool.shape
+    if tuple(v_pool.shape) != (N, Hk, head_dim, S):
+        raise ValueError("v_pool must be [num_blocks, n_kv_head, head_dim, block_size]")
+    return N, Hk, S
 
 
 def _table_rows(pos, per_row_pos):
@@ -141,7 +151,7 @@ def chunk_paged_relpos_attn(q, k_pool, v_pool, block_tables, cache_seqlens, pos,
     distance (Transformer-XL) or, with per_key_pos, by key (WeNet); chunk_lens int32 [B]
     (optional): real frames per stream; window_start int32 [B] (optional): bounded history."""
     B, C, H, D = q.shape
-    N, Hk, S, _ = k_pool.shape
+    N, Hk, S = _pool_geom(k_pool, v_pool, D)
     if out is None:
         out = torch.empty_like(q)
     st = lib().chunk_paged_relpos_attn(
@@ -161,7 +171,7 @@ def paged_kv_append_relpos_attn(q, k_new, v_new, k_pool, v_pool, block_tables, c
     """Append and attention of one layer in one launch (pools are written); arguments as
     chunk_paged_relpos_attn plus k_new / v_new [B, C, Hk, D]."""
     B, C, H, D = q.shape
-    N, Hk, S, _ = k_pool.shape
+    N, Hk, S = _pool_geom(k_pool, v_pool, D)
     if out is None:
         out = torch.empty_like(q)
     st = lib().paged_kv_append_relpos_attn(
@@ -190,7 +200,7 @@ def paged_kv_append_relpos_attn_layers(layers, block_tables, cache_seqlens, max_
     layer, same shapes); block tables, cache and chunk lengths and window starts are shared."""
     l0 = layers[0]
     B, C, H, D = l0.q.shape
-    N, Hk, S, _ = l0.k_pool.shape
+    N, Hk, S = _pool_geom(l0.k_pool, l0.v_pool, D)
     names = ["q", "k_new", "v_new", "k_pool", "v_pool", "pos", "pos_bias_u", "pos_bias_v", "out"]
     for x in layers:
         for n in names:

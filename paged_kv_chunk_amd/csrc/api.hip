@@ -25,6 +25,7 @@ pkc_status check_pool(int32_t batch, int32_t chunk, int32_t n_kv_head, int32_t h
       num_blocks <= 0 || max_blocks <= 0 || max_cache < 0)
     return PKC_ERR_SHAPE;
   if (head_dim % 8 != 0) return PKC_ERR_SHAPE;
+  if (head_dim % 32 != 0) return PKC_ERR_UNSUPPORTED;   // K pages are in 32-dim column blocks
   if ((int64_t)max_cache + chunk > (int64_t)max_blocks * block_size) return PKC_ERR_CAPACITY;
   // every index below fits in int32 arithmetic inside the kernels except the flat offsets,
   // which the kernels form in size_t

@@ -233,18 +233,21 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   // ---- 2. loads of the first two body steps (band tile 0 of the first one too) ----------------
   auto load_step = [&](StepRegs<T>& r, int s) {
     const int j0 = 32 * s;
+    // K pages are in 32-dim column blocks ([2][S][32] per page): half h of slot s's row is at
+    // (h S + s) 32, so each load instruction covers whole 128-byte lines (4 consecutive slots'
+    // halves, two lines, per key group)
     const int key = j0 + 8 * (m16 >> 2) + (m16 & 3);          // key of tile 0; tile 1 is key + 4
     const T* krow = kp + (uint64_t)block_of(key >> logS) * blk_stride +
-                    (uint32_t)((key & (S - 1)) * kD + 8 * grp);
-    r.k[0][0] = load8(krow);
-    r.k[0][1] = load8(krow + 32);
-    r.k[1][0] = load8(krow + 4 * kD);
-    r.k[1][1] = load8(krow + 4 * kD + 32);
+                    (uint32_t)((key & (S - 1)) * 32 + 8 * grp);
+    r.k[0][0] = load8_stream(krow);
+    r.k[0][1] = load8_stream(krow + S * 32);
+    r.k[1][0] = load8_stream(krow + 4 * 32);
+    r.k[1][1] = load8_stream(krow + S * 32 + 4 * 32);
     const int kg = j0 + 8 * grp;
     const T* vb = vp + (uint64_t)block_of(kg >> logS) * blk_stride +
                   (uint32_t)(m16 * S + (kg & (S - 1)));
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) r.v[dt] = load8(vb + 16 * dt * S);
+    for (int dt = 0; dt < 4; ++dt) r.v[dt] = load8_stream(vb + 16 * dt * S);
     if constexpr (kPerKey) {
       load_key_rows(r.p, j0);
     } else {
@@ -298,7 +301,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
         const int key = cache + t;
         const T* src = kFused ? a.k_new + ((size_t)(b * a.C + t) * a.Hk + hk) * kD + dv
                               : kp + (uint64_t)block_of(key >> logS) * blk_stride +
-                                    (uint32_t)((key & (S - 1)) * kD + dv);
+                                    (uint32_t)(((dv >> 5) * S + (key & (S - 1))) * 32 + (dv & 31));
         *reinterpret_cast<uint4*>(s_kt + t * KTP + dv) = *reinterpret_cast<const uint4*>(src);
       }
     }
@@ -454,7 +457,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       const int dv = (x % NV) * VEC;
       const int key = cache + t;
       T* dst = a.k_pool_w + (size_t)hk * page + (uint64_t)block_of(key >> logS) * blk_stride +
-               (uint32_t)((key & (S - 1)) * kD + dv);
+               (uint32_t)(((dv >> 5) * S + (key & (S - 1))) * 32 + (dv & 31));
       *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s_kt + t * KTP + dv);
     }
     // V: 8-frame groups of one dimension, aligned to the page slots (never across a page: block

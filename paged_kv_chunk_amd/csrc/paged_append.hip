@@ -9,7 +9,7 @@
 // through its table row used as a ring: block block_tables[b][(p / S) % M], slot p % S.
 //
 // One workgroup per (stream, kv head). K rows are copied 16 bytes per lane straight into their
-// slots (rows of the K page are contiguous). V pages are stored transposed ([head_dim][block_size])
+// slots (K pages are stored in 32-dim column blocks, [head_dim / 32][block_size][32]). V pages are stored transposed ([head_dim][block_size])
 // so that attention can read 8 consecutive frames of one dimension with one 16-byte load; the
 // workgroup therefore stages the chunk's V rows in LDS and writes each dimension's run of frames,
 // consecutive lanes writing consecutive slots.
@@ -55,7 +55,9 @@ paged_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new, T*
       const int slot = frame % block_size;
       const size_t src = (((size_t)b * chunk + t) * n_kv_head + g) * head_dim + dv;
       const uint4 kv = *reinterpret_cast<const uint4*>(k_new + src);
-      *reinterpret_cast<uint4*>(k_pool + (((size_t)blk * n_kv_head + g) * block_size + slot) * head_dim + dv) = kv;
+      // K pages in 32-dim column blocks: dim d of slot s at ((d / 32) S + s) 32 + d % 32
+      *reinterpret_cast<uint4*>(k_pool + ((size_t)blk * n_kv_head + g) * block_size * head_dim +
+                                ((dv >> 5) * block_size + slot) * 32 + (dv & 31)) = kv;
       *reinterpret_cast<uint4*>(sv + (x / nvec) * pitch + dv) = *reinterpret_cast<const uint4*>(v_new + src);
     }
     __syncthreads();

@@ -39,6 +39,18 @@ __device__ __forceinline__ f32x8 load8(const float* p) {
   return r;
 }
 
+// Streaming loads (non-temporal hint): data read once per launch, such as the cached K/V pages,
+// so that what every launch re-reads (block tables, shared positional tables) stays in L2.
+__device__ __forceinline__ bf16x8 load8_stream(const bf16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+}
+__device__ __forceinline__ f32x8 load8_stream(const float* p) {
+  f32x8 r;
+  r.lo = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+  r.hi = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + 4));
+  return r;
+}
+
 __device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 __device__ __forceinline__ void store8(float* p, f32x8 v) {
   *reinterpret_cast<floatx4*>(p) = v.lo;

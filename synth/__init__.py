@@ -16,6 +16,7 @@ from .cohorts import (  # noqa: F401
     relpos_projection,
     embed_distances,
     descending_table,
+    column_blocked,
     key_position_tables,
     use_key_position_tables,
 )

@@ -12,8 +12,8 @@ Structure recipe: each stream gets ceil((cache + C) / block_size) pages, whose p
 from a seeded random permutation of the pool; table columns past a stream's pages hold -1. The
 whole pool is filled with N(0, 1), so whatever a stream's table points at is its cached K/V.
 
-Page layout: k_pool [num_blocks, n_kv_head, block_size, head_dim] and
-v_pool [num_blocks, n_kv_head, head_dim, block_size] (V transposed inside each page).
+Page layout: k_pool [num_blocks, n_kv_head, head_dim / 32, block_size, 32] (32-dim column blocks)
+and v_pool [num_blocks, n_kv_head, head_dim, block_size] (V transposed inside each page).
 
 Table layout: row r of a table with centre ``center`` holds the embedding of distance center - r.
 A shared table has 2 (max_cache + C) - 1 rows. Per-row tables are packed as
@@ -63,6 +63,13 @@ def descending_table(center, proj, n_head, head_dim):
     return embed_distances(dist, proj, n_head, head_dim)
 
 
+def column_blocked(k_pool):
+    """A K pool [N, Hk, S, D] (D a multiple of 32) re-laid out in 32-dim column blocks
+    [N, Hk, D / 32, S, 32], the layout the kernels read: the same frames, another order."""
+    n, hk, s, d = k_pool.shape
+    return k_pool.reshape(n, hk, s, d // 32, 32).permute(0, 1, 3, 2, 4).contiguous()
+
+
 def key_position_tables(proj, starts, width, n_head, head_dim):
     """Per-key tables (WeNet's convention): row j of table b is the projected sinusoid of the
     absolute position starts[b] + j; float64 [len(starts), width, n_head, head_dim]."""
@@ -97,7 +104,7 @@ class ChunkCohort:
     q: torch.Tensor               # [B, C, H, D]
     k_new: torch.Tensor           # [B, C, Hk, D]
     v_new: torch.Tensor           # [B, C, Hk, D]
-    k_pool: torch.Tensor          # [N, Hk, S, D]
+    k_pool: torch.Tensor          # [N, Hk, D / 32, S, 32] (32-dim column blocks)
     v_pool: torch.Tensor          # [N, Hk, D, S]
     block_tables: torch.Tensor    # [B, M] int32
     cache_seqlens: torch.Tensor   # [B] int32
@@ -152,7 +159,7 @@ def make_chunk_cohort(B, H, D, C, block_size, cache_seqlens, *, Hk=None, dtype=B
     q = _randn((B, C, H, D), dgen, device, dtype)
     k_new = _randn((B, C, Hk, D), dgen, device, dtype)
     v_new = _randn((B, C, Hk, D), dgen, device, dtype)
-    k_pool = _randn((num_blocks, Hk, block_size, D), dgen, device, dtype)
+    k_pool = column_blocked(_randn((num_blocks, Hk, block_size, D), dgen, device, dtype))
     v_pool = _randn((num_blocks, Hk, D, block_size), dgen, device, dtype)
     u = _randn((H, D), gen, "cpu", dtype, 0.02).to(device)
     w = _randn((H, D), gen, "cpu", dtype, 0.02).to(device)

@@ -38,7 +38,7 @@ def poison(co):
     past each stream's 2 T_b - 1."""
     live = torch.from_numpy(live_slot_mask(co)).to(co.k_pool.device)
     nan = float("nan")
-    co.k_pool.masked_fill_(~live[:, None, :, None], nan)
+    co.k_pool.masked_fill_(~live[:, None, None, :, None], nan)     # [N, Hk, D/32, S, 32]
     co.v_pool.masked_fill_(~live[:, None, None, :], nan)
     if co.per_row_pos:
         C = co.q.shape[1]
@@ -104,7 +104,7 @@ def poison_padding(co, chunk_lens):
         co.v_new[b, n:] = nan
         for t in range(int(cs[b]) + n, int(cs[b]) + C):
             blk, slot = int(bt[b, t // S]), t % S
-            co.k_pool[blk, :, slot, :] = nan
+            co.k_pool[blk, :, :, slot, :] = nan
             co.v_pool[blk, :, :, slot] = nan
     return co
 
