@@ -260,22 +260,23 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       }
     }
   };
-  // band tiles of this wave's first tail step, into a register set the body no longer needs
-  // (tiles 0, 1, 2 in k[0], p[0], p[1]): the tail step then waits on nothing
-  auto load_tail_band = [&](StepRegs<T>& r) {
-    if (kPerKey) {
-      if (wave < ntail) load_key_rows(r.p, cache + 32 * wave);
-    } else if (wave < ntail) {
+  // table rows of this wave's first tail step (band tiles 0, 1, 2, or the 32 keys' rows of a
+  // per-key table in tb[0..1]): requested first, so that waiting for them waits for nothing
+  // else; the tail step then runs while the body's data is still on its way
+  F tb[3][2];
+  if (wave < ntail) {
+    if constexpr (kPerKey) {
+      load_key_rows(*reinterpret_cast<F(*)[2][2]>(&tb[0]), cache + 32 * wave);
+    } else {
       const int rb = R0 + cache + 32 * wave - qlast;
-      F* dst[3] = {r.k[0], r.p[0], r.p[1]};
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
-        dst[t][0] = load8(row);
-        dst[t][1] = load8(row + 32);
+        tb[t][0] = load8(row);
+        tb[t][1] = load8(row + 32);
       }
     }
-  };
+  }
   StepRegs<T> ra, rb2;
   F p0[2];
   if (nmine > 0) {
@@ -286,9 +287,6 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     }
     load_step(ra, s_begin);
     if (nmine > 1) load_step(rb2, s_begin + 1);
-    else load_tail_band(rb2);
-  } else {
-    load_tail_band(ra);
   }
 
   // ---- 3. long chunks: the chunk's frames into the LDS tail with a loop ------------------------
@@ -343,7 +341,6 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       set(qv[half], e, (get(qq[half], e) + get(ww[half], e)) * a.scale_log2);
     }
 
-  // ---- 4. body steps, two register sets in turn ------------------------------------------------
   float* s_g = s_wave + wave * kWaveLds;
   Softmax st;
   st.m = -INFINITY;
@@ -351,6 +348,61 @@ chunk_attn_kernel(ChunkArgs<T> a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // ---- 4. tail steps over the chunk's frames, from LDS, first (the one workgroup barrier: the
+  // tail was staged by all threads; the body below uses only the wave's own registers and LDS).
+  // The wave with a tail step runs it while its body data is still arriving. ----------------
+  __syncthreads();
+  for (int k = wave; k < ntail; k += kWaves) {
+    const int j0 = cache + 32 * k;
+    F kf[2][2], vf[4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const T* row = s_kt + (32 * k + 8 * (m16 >> 2) + 4 * tt + (m16 & 3)) * KTP + 8 * grp;
+      kf[tt][0] = load8(row);
+      kf[tt][1] = load8(row + 32);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(s_vt + (16 * dt + m16) * a.vt_pitch + 32 * k + 8 * grp);
+    if constexpr (kPerKey) {
+      F pk[2][2];
+      if (k == wave) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) pk[tt][half] = tb[tt][half];   // prefetched
+      } else {
+        load_key_rows(pk, j0);
+      }
+      float x[2][4];
+      per_key_scores<T>(kf, pk, qu, qv, x);
+      softmax_pv<T, true>(st, x, vf, 0, T_len - j0);
+    } else {
+      F pb[3][2];
+      if (k == wave) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) pb[t][half] = tb[t][half];   // prefetched
+      } else {
+        const int rb = R0 + j0 - qlast;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
+          pb[t][0] = load8(row);
+          pb[t][1] = load8(row + 32);
+        }
+      }
+      floatx4 g[3];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        g[t] = mma(pb[t][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        g[t] = mma(pb[t][1], qv[1], g[t]);
+      }
+      step_compute<T, true>(st, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
+    }
+  }
+
+  // ---- 5. body steps, two register sets in turn ------------------------------------------------
   if (nmine > 0) {
     floatx4 g_prev;
     if (!kPerKey) {
@@ -377,72 +429,10 @@ chunk_attn_kernel(ChunkArgs<T> a) {
         g_prev = g2;
       }
       if (s + 2 < s_end) load_step(r, s + 2);
-      else if (s + 2 == s_end) load_tail_band(r);
     };
     for (int s = s_begin; s < s_end; s += 2) {
       run(ra, s);
       if (s + 1 < s_end) run(rb2, s + 1);
-    }
-  }
-
-  // ---- 5. tail steps over the chunk's frames, from LDS (the one workgroup barrier: the tail was
-  // staged by all threads; body steps above use only the wave's own registers and LDS) ---------
-  __syncthreads();
-  for (int k = wave; k < ntail; k += kWaves) {
-    const int j0 = cache + 32 * k;
-    F kf[2][2], vf[4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const T* row = s_kt + (32 * k + 8 * (m16 >> 2) + 4 * tt + (m16 & 3)) * KTP + 8 * grp;
-      kf[tt][0] = load8(row);
-      kf[tt][1] = load8(row + 32);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(s_vt + (16 * dt + m16) * a.vt_pitch + 32 * k + 8 * grp);
-    if constexpr (kPerKey) {
-      F pk[2][2];
-      if (k == wave) {
-        // prefetched into the register set the body left free (ra after an even number of
-        // body steps, rb2 after an odd one)
-        const StepRegs<T>& r = (nmine & 1) ? rb2 : ra;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int half = 0; half < 2; ++half) pk[tt][half] = r.p[tt][half];
-      } else {
-        load_key_rows(pk, j0);
-      }
-      float x[2][4];
-      per_key_scores<T>(kf, pk, qu, qv, x);
-      softmax_pv<T, true>(st, x, vf, 0, T_len - j0);
-    } else {
-      F pb[3][2];
-      if (k == wave) {
-        // prefetched: in the register set the body left free (ra after an even number of body
-        // steps, rb2 after an odd one)
-        const StepRegs<T>& r = (nmine & 1) ? rb2 : ra;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          pb[0][half] = r.k[0][half];
-          pb[1][half] = r.p[0][half];
-          pb[2][half] = r.p[1][half];
-        }
-      } else {
-        const int rb = R0 + j0 - qlast;
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
-          pb[t][0] = load8(row);
-          pb[t][1] = load8(row + 32);
-        }
-      }
-      floatx4 g[3];
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        g[t] = mma(pb[t][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-        g[t] = mma(pb[t][1], qv[1], g[t]);
-      }
-      step_compute<T, true>(st, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
     }
   }
 
