@@ -30,6 +30,9 @@ def command(out=LIB, extra=()):
             # keep the compiler from forming packed fp32 VALU ops (device pass only; the host
             # pass warns that it does not know the feature)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in VGPRs: the online-softmax rescale of the output tiles is then a
+            # plain multiply, with no copies between the accumulation and arithmetic registers
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-command-line-argument",
             f"-I{INCLUDE}", f"-I{CSRC}", *extra, *sources, "-o", out]
 

@@ -51,6 +51,18 @@ __device__ __forceinline__ f32x8 load8_stream(const float* p) {
   return r;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16, gfx950): within each group of 16 lanes, the four
+// 8-byte rows addressed by lanes 4 r .. 4 r + 3 form row r of a 4 x 16 matrix of 16-bit values,
+// and lane i receives its column i. Two reads (rows lo and hi) give 8 elements: [lo col, hi col].
+typedef short lds_short4 __attribute__((ext_vector_type(4)));
+typedef short lds_short8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 load8_tr(const bf16* lo, const bf16* hi) {
+  typedef __attribute__((address_space(3))) lds_short4 LdsShort4;
+  const lds_short4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsShort4*)(lo));
+  const lds_short4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsShort4*)(hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 __device__ __forceinline__ void store8(float* p, f32x8 v) {
   *reinterpret_cast<floatx4*>(p) = v.lo;

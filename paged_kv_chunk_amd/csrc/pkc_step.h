@@ -19,7 +19,8 @@
 namespace pkc {
 
 constexpr int kD = 64;                  // head_dim of the attention kernels
-constexpr int kSkewPitch = 48;          // floats per query column of the skew tile (47 rows used)
+constexpr int kSkewPitch = 52;          // floats per query column of the skew tile (48 rows used;
+                                        // 52 puts the 16-byte writes of 8 columns on distinct banks)
 constexpr int kSkewFloats = kSkewPitch * 16;
 constexpr float kRescaleLog2 = 8.f;     // headroom before the running max moves
 

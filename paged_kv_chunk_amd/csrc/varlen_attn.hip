@@ -8,10 +8,16 @@
 //
 // Work decomposition. One workgroup of 4 waves per (utterance, head, 64-query tile); wave w owns
 // queries [64 t + 16 w, + 16) outright (its own online softmax, no merge). The workgroup walks the
-// utterance's keys in 32-key steps: every step's K rows and V (transposed to [head_dim][key]) are
-// staged once in double-buffered LDS and read by all four waves, while each wave fetches its own
+// utterance's keys in 32-key steps: every step's K rows and V rows are staged once in
+// double-buffered LDS and read by all four waves, while each wave fetches its own
 // band rows (the table rows its 16 queries touch) one step ahead. The per-step math is the shared
 // step engine of pkc_step.h. MFMA-bound in principle (6 L^2 D FLOP per utterance and head).
+//
+// V staging. For bf16, V rows stay in their natural [key][head_dim] order in LDS (one 16-byte
+// write per thread) and the PV operand - 8 consecutive keys of one dimension per lane - comes
+// from two transposing reads; the 4-dimension chunks of row r are XOR-swizzled by
+// 4 ((r & 3) ^ ((r >> 3) & 1)), which gives each of the 8 rows one read of 32 lanes touches its
+// own 32-byte bank slot. fp32 stages V transposed to [head_dim][key].
 //
 // chunked_limited mask ("Model Layer", Nemotron encoder notes; kLimited): query i sees only the
 // keys of its own chunk of `chunk` frames and of the `left` chunks before it. A workgroup then
@@ -30,7 +36,10 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kQTile = 16 * kWaves;     // queries per workgroup
 
 template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // K tile row pitch
-template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch
+template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch (fp32)
+template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
+// swizzle of the 4-dimension chunks of natural V row r (bf16)
+__device__ __forceinline__ int v_swz(int r) { return 4 * ((r & 3) ^ ((r >> 3) & 1)); }
 
 template <typename T>
 struct VarlenArgs {
@@ -55,7 +64,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   constexpr int NV = kD / VEC;
   constexpr int KP = kKP<T>;
   constexpr int VP = kVP<T>;
-  constexpr int TILE = 32 * KP + kD * VP;            // elements of one K + V^T stage
+  constexpr int TILE = 32 * KP + (kTrV<T> ? 32 * kD : kD * VP);   // elements of one K + V stage
 
   __shared__ __align__(16) T s_kv[2 * TILE];
   __shared__ __align__(16) float s_skew[kWaves * kSkewFloats];
@@ -137,9 +146,13 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       const int r = idx / NV;
       const int dv = (idx % NV) * VEC;
       *reinterpret_cast<uint4*>(sk + r * KP + dv) = kr[it];
-      const T* e = reinterpret_cast<const T*>(&vr[it]);
+      if constexpr (kTrV<T>) {
+        *reinterpret_cast<uint4*>(sv + r * kD + 4 * ((dv >> 2) ^ v_swz(r))) = vr[it];
+      } else {
+        const T* e = reinterpret_cast<const T*>(&vr[it]);
 #pragma unroll
-      for (int c = 0; c < VEC; ++c) sv[(dv + c) * VP + r] = e[c];
+        for (int c = 0; c < VEC; ++c) sv[(dv + c) * VP + r] = e[c];
+      }
     }
   };
   // band tiles 1 and 2 of a step (tile 0 is the previous step's tile 2)
@@ -203,8 +216,20 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       kf[tt][0] = load8(row);
       kf[tt][1] = load8(row + 32);
     }
+    if constexpr (kTrV<T>) {
+      // lane m16 of the group addresses row 8 grp + m16 / 4 (+ 4), dimensions 16 dt + 4 (m16 % 4)
+      const int r = 8 * grp + (m16 >> 2);
+      const T* lo = cur + 32 * KP + r * kD;
+      const int sw = v_swz(r);   // the same for row r + 4
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(cur + 32 * KP + (16 * dt + m16) * VP + 8 * grp);
+      for (int dt = 0; dt < 4; ++dt) {
+        const int c = 4 * (((4 * dt) + (m16 & 3)) ^ sw);
+        vf[dt] = load8_tr(lo + c, lo + 4 * kD + c);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(cur + 32 * KP + (16 * dt + m16) * VP + 8 * grp);
+    }
     floatx4 g1 = mma(pb[0][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
     g1 = mma(pb[0][1], qv[1], g1);
     floatx4 g2 = mma(pb[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
