@@ -6,12 +6,15 @@
 // utterance of length L is the chunk case with no cache and C = L: query i and key j read table
 // row L - 1 + j - i of the utterance's 2 L - 1 rows.
 //
-// Work decomposition. One workgroup of 4 waves per (utterance, head, 64-query tile); wave w owns
+// Work decomposition. One workgroup of 4 waves per (utterance, 64-query tile, head), the head
+// varying fastest over the grid so that all tiles of one head share an XCD; wave w owns
 // queries [64 t + 16 w, + 16) outright (its own online softmax, no merge). The workgroup walks the
 // utterance's keys in 32-key steps: every step's K rows and V rows are staged once in
-// double-buffered LDS and read by all four waves, while each wave fetches its own
-// band rows (the table rows its 16 queries touch) one step ahead. The per-step math is the shared
-// step engine of pkc_step.h. MFMA-bound in principle (6 L^2 D FLOP per utterance and head).
+// double-buffered LDS and read by all four waves. The band rows (the table rows the queries
+// touch) go through an LDS ring of 128 rows: the four waves' windows overlap, so a step brings in
+// only the 32 rows that enter the workgroup's window, instead of 32 rows per wave. Every global
+// read is issued two steps ahead. The per-step math is the shared step engine of pkc_step.h.
+// MFMA-bound in principle (6 L^2 D FLOP per utterance and head).
 //
 // V staging. For bf16, V rows stay in their natural [key][head_dim] order in LDS (one 16-byte
 // write per thread) and the PV operand - 8 consecutive keys of one dimension per lane - comes
@@ -38,6 +41,7 @@ constexpr int kQTile = 16 * kWaves;     // queries per workgroup
 template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // K tile row pitch
 template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch (fp32)
 template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
+constexpr int kRing = 128;   // rows of the band ring (a step reads 80 and stages the next 32)
 // swizzle of the 4-dimension chunks of natural V row r (bf16)
 __device__ __forceinline__ int v_swz(int r) { return 4 * ((r & 3) ^ ((r >> 3) & 1)); }
 
@@ -56,8 +60,9 @@ struct VarlenArgs {
   float scale_log2;
 };
 
+// (three workgroups per CU: the register budget of 3 waves per SIMD)
 template <typename T, bool kLimited>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 varlen_attn_kernel(VarlenArgs<T> a) {
   typedef typename Frag<T>::type F;
   constexpr int VEC = 16 / sizeof(T);
@@ -67,6 +72,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   constexpr int TILE = 32 * KP + (kTrV<T> ? 32 * kD : kD * VP);   // elements of one K + V stage
 
   __shared__ __align__(16) T s_kv[2 * TILE];
+  __shared__ __align__(16) T s_band[kRing * KP];   // row x of the table in slot x % 128
   __shared__ __align__(16) float s_skew[kWaves * kSkewFloats];
 
   const int tid = threadIdx.x;
@@ -75,11 +81,13 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   const int m16 = lane & 15;
   const int grp = lane >> 4;
 
+  // head fastest: workgroups go to the 8 XCDs round-robin, so with H a multiple of 8 every tile
+  // of one head lands on the same XCD and that head's tables and K/V rows stay in its L2
   int id = blockIdx.x;
-  const int qt = id % a.qtiles;
-  id /= a.qtiles;
   const int h = id % a.H;
-  const int s = id / a.H;
+  id /= a.H;
+  const int qt = id % a.qtiles;
+  const int s = id / a.qtiles;
   const int lo = clampi(a.cu[s], 0, a.total);
   const int L = clampi(a.cu[s + 1], lo, a.total) - lo;
   if (qt * kQTile >= L) return;  // uniform over the workgroup
@@ -92,8 +100,6 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   const int q0 = qt * kQTile + 16 * wave;       // this wave's first query
   const int R0 = L - 1;                         // table row of (i, j) is R0 + j - i
   const int rlo = 0, rhi = 2 * L - 2;
-  const int qlast = q0 + 15;
-  auto band_row = [&](int r) { return ptab + (size_t)(uint32_t)clampi(r, rlo, rhi) * prow; };
 
   // queries with the biases, pre-scaled into log2 units
   F qu[2], qv[2];
@@ -113,57 +119,53 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     }
   }
 
-  // cooperative staging of one 32-key step: 32 K rows and the same 32 V rows, transposed
-  // (keys past L are zero in V, so masked probabilities meet finite values)
-  constexpr int NLD = (32 * NV + kThreads - 1) / kThreads;   // 16-byte vectors per thread per tensor
-  struct Rows { uint4 k[NLD], v[NLD]; };
+  // Band window. At the step whose first key is j0 the workgroup's waves read table rows
+  // [xw + j0 + 16, xw + j0 + 96), xw = R0 - (64 t + 63) for query tile t (wave w: tiles 1 and 2 of
+  // its step at xw + j0 + 64 - 16 w; tile 0 is the previous step's tile 2), and the rows
+  // [xw + j0 + 64, xw + j0 + 96) enter the window. Slots x % 128 of the rows staged at the end
+  // of a step never hold a row that step still reads, and a row is overwritten only after the
+  // barrier that ends its last use.
+  const int xw = R0 - (qt * kQTile + kQTile - 1);
+  auto band_src = [&](int x) { return ptab + (size_t)(uint32_t)clampi(x, rlo, rhi) * prow; };
+  auto band_slot = [&](int x) { return s_band + (x & (kRing - 1)) * KP; };
+
+  // cooperative staging of one 32-key step: 32 K rows, the same 32 V rows and the 32 band rows
+  // entering the window. Rows past the utterance read its last frame instead: every staged value
+  // is finite, so a masked key (probability exactly 0) adds nothing, and every load is
+  // unconditional - a wait never has to drain loads requested for a later step.
+  constexpr int NLD = 32 * NV / kThreads;   // 16-byte vectors per thread per tensor
+  static_assert(NLD * kThreads == 32 * NV, "the staging threads cover the 32 rows exactly");
+  struct Rows { u32x4 k[NLD], v[NLD], b[NLD]; };
   Rows ra, rb;   // two steps in flight
   auto fetch = [&](Rows& rr, int j0) {
-    uint4* kr = rr.k;
-    uint4* vr = rr.v;
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
-      const int r = idx / NV;
-      const int dv = (idx % NV) * VEC;
-      kr[it] = uint4{0u, 0u, 0u, 0u};
-      vr[it] = uint4{0u, 0u, 0u, 0u};
-      if (idx < 32 * NV && j0 + r < L) {
-        kr[it] = *reinterpret_cast<const uint4*>(kseg + (size_t)(j0 + r) * krow + dv);
-        vr[it] = *reinterpret_cast<const uint4*>(vseg + (size_t)(j0 + r) * krow + dv);
-      }
+      const size_t off = (size_t)min(j0 + idx / NV, L - 1) * krow + (idx % NV) * VEC;
+      rr.k[it] = *reinterpret_cast<const u32x4*>(kseg + off);
+      rr.v[it] = *reinterpret_cast<const u32x4*>(vseg + off);
+      rr.b[it] = *reinterpret_cast<const u32x4*>(band_src(xw + j0 + 64 + idx / NV) + (idx % NV) * VEC);
     }
   };
-  auto stash = [&](const Rows& rr, T* st) {
-    const uint4* kr = rr.k;
-    const uint4* vr = rr.v;
+  auto stash = [&](const Rows& rr, T* st, int j0) {
+    const u32x4* kr = rr.k;
+    const u32x4* vr = rr.v;
     T* sk = st;
     T* sv = st + 32 * KP;
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
-      if (idx >= 32 * NV) continue;
       const int r = idx / NV;
       const int dv = (idx % NV) * VEC;
-      *reinterpret_cast<uint4*>(sk + r * KP + dv) = kr[it];
+      *reinterpret_cast<u32x4*>(band_slot(xw + j0 + 64 + r) + dv) = rr.b[it];
+      *reinterpret_cast<u32x4*>(sk + r * KP + dv) = kr[it];
       if constexpr (kTrV<T>) {
-        *reinterpret_cast<uint4*>(sv + r * kD + 4 * ((dv >> 2) ^ v_swz(r))) = vr[it];
+        *reinterpret_cast<u32x4*>(sv + r * kD + 4 * ((dv >> 2) ^ v_swz(r))) = vr[it];
       } else {
         const T* e = reinterpret_cast<const T*>(&vr[it]);
 #pragma unroll
         for (int c = 0; c < VEC; ++c) sv[(dv + c) * VP + r] = e[c];
       }
-    }
-  };
-  // band tiles 1 and 2 of a step (tile 0 is the previous step's tile 2)
-  F pb[2][2];
-  auto fetch_band = [&](int j0) {
-    const int rb = R0 + j0 - qlast;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const T* row = band_row(rb + 16 * (t + 1) + m16) + 8 * grp;
-      pb[t][0] = load8(row);
-      pb[t][1] = load8(row + 32);
     }
   };
 
@@ -190,25 +192,41 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   }
   const int s_first = j_first >> 5;
   const int nsteps = ((j_end + 31) >> 5) - s_first;
+  // band tile (16 rows from x, this lane's row x + m16) from the ring
+  const int xl = xw + 64 - 16 * wave + m16;   // + j0 + 16 t: this lane's row of tile t + 1
+  auto band_tile = [&](int x, F& p_lo, F& p_hi) {
+    const T* row = band_slot(x) + 8 * grp;
+    p_lo = load8(row);
+    p_hi = load8(row + 32);
+  };
+  const int J = 32 * s_first;
+  fetch(ra, J);
+  fetch(rb, J + 32);
+  // the window's first 64 rows at the first step, staged directly (once)
+#pragma unroll
+  for (int part = 0; part < 2; ++part)
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int idx = tid + kThreads * it;
+      const int x = xw + J + 32 * part + idx / NV;
+      const int dv = (idx % NV) * VEC;
+      *reinterpret_cast<u32x4*>(band_slot(x) + dv) = *reinterpret_cast<const u32x4*>(band_src(x) + dv);
+    }
+  stash(ra, s_kv, J);
+  __syncthreads();
   floatx4 g_prev;
   {
-    const T* row = band_row(R0 + 32 * s_first - qlast + m16) + 8 * grp;
-    const F p_lo = load8(row);
-    const F p_hi = load8(row + 32);
+    F p_lo, p_hi;
+    band_tile(xl + J - 16, p_lo, p_hi);
     g_prev = mma(p_lo, qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
     g_prev = mma(p_hi, qv[1], g_prev);
   }
-  fetch(ra, 32 * s_first);
-  if (nsteps > 1) fetch(rb, 32 * s_first + 32);
-  fetch_band(32 * s_first);
-  stash(ra, s_kv);
-  __syncthreads();
   // one step (index `step` from the first visible one): registers `nxt` already hold step + 1,
   // `fre` receives step + 2
   auto do_step = [&](int step, Rows& nxt, Rows& fre) {
-    const int j0 = 32 * (s_first + step);
+    const int j0 = J + 32 * step;
     const T* cur = s_kv + (step & 1) * TILE;
-    if (step + 2 < nsteps) fetch(fre, j0 + 64);
+    fetch(fre, j0 + 64);   // (past the last step: harmless re-reads of the last frame)
     F kf[2][2], vf[4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -230,11 +248,13 @@ varlen_attn_kernel(VarlenArgs<T> a) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(cur + 32 * KP + (16 * dt + m16) * VP + 8 * grp);
     }
+    F pb[2][2];
+    band_tile(xl + j0, pb[0][0], pb[0][1]);
+    band_tile(xl + j0 + 16, pb[1][0], pb[1][1]);
     floatx4 g1 = mma(pb[0][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
     g1 = mma(pb[0][1], qv[1], g1);
     floatx4 g2 = mma(pb[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
     g2 = mma(pb[1][1], qv[1], g2);
-    if (step + 1 < nsteps) fetch_band(j0 + 32);
     if constexpr (kLimited) {
       float x[2][4];
       skew_scores<T>(kf, qu, g_prev, g1, g2, s_g, x);
@@ -245,7 +265,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       step_compute<T, true>(st, kf, vf, qu, g_prev, g1, g2, s_g, L - j0);
     }
     g_prev = g2;
-    if (step + 1 < nsteps) stash(nxt, s_kv + ((step + 1) & 1) * TILE);
+    if (step + 1 < nsteps) stash(nxt, s_kv + ((step + 1) & 1) * TILE, j0 + 32);
     __syncthreads();
   };
   for (int step = 0; step < nsteps; step += 2) {
