@@ -136,8 +136,12 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     const int e = pg + pb;
     return e >= a.M ? e - a.M : e;
   };
-  const int bt_lo = lane < nwin ? bt[ring(lane)] : 0;
-  const int bt_hi = lane + 64 < nwin ? bt[ring(lane + 64)] : 0;
+  // (every load up to the body's first two steps is issued unconditionally, from a valid
+  // address, so that each wait below counts exactly the loads issued after the one it needs)
+  const int bt_lo_raw = bt[ring(min(lane, nwin - 1))];
+  const int bt_hi_raw = bt[ring(min(lane + 64, nwin - 1))];
+  const int bt_lo = lane < nwin ? bt_lo_raw : 0;
+  const int bt_hi = lane + 64 < nwin ? bt_hi_raw : 0;
   F qq[2], uu[2], ww[2];
   {
     const int iq = min(qt * 16 + m16, a.C - 1);
@@ -151,13 +155,11 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     }
   }
   // the chunk's own frames (fused, short chunks: one 16-byte vector of K and of V per thread)
-  uint4 nk, nv;
+  u32x4 nk, nv;
   if constexpr (kRegTail) {
-    if (tid < a.C * NV) {
-      const size_t row = ((size_t)(b * a.C + tid / NV) * a.Hk + hk) * kD + (tid % NV) * VEC;
-      nk = *reinterpret_cast<const uint4*>(a.k_new + row);
-      nv = *reinterpret_cast<const uint4*>(a.v_new + row);
-    }
+    const size_t row = ((size_t)(b * a.C + min(tid / NV, a.C - 1)) * a.Hk + hk) * kD + (tid % NV) * VEC;
+    nk = *reinterpret_cast<const u32x4*>(a.k_new + row);
+    nv = *reinterpret_cast<const u32x4*>(a.v_new + row);
   }
   const int cache = clampi(a.cs[b], 0, a.max_cache);
   // real frames of this stream's chunk: frames past them do not exist (not appended, not keys;
@@ -220,8 +222,8 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     if (tid < n_real * NV) {
       const int t = tid / NV;
       const int dv = (tid % NV) * VEC;
-      *reinterpret_cast<uint4*>(s_kt + t * KTP + dv) = nk;
-      const uint32_t wd[4] = {nv.x, nv.y, nv.z, nv.w};
+      *reinterpret_cast<u32x4*>(s_kt + t * KTP + dv) = nk;
+      const uint32_t wd[4] = {nv[0], nv[1], nv[2], nv[3]};
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         reinterpret_cast<uint16_t*>(s_vt)[(dv + c) * a.vt_pitch + t] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
@@ -262,13 +264,15 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   };
   // table rows of this wave's first tail step (band tiles 0, 1, 2, or the 32 keys' rows of a
   // per-key table in tb[0..1]): requested first, so that waiting for them waits for nothing
-  // else; the tail step then runs while the body's data is still on its way
+  // else; the tail step then runs while the body's data is still on its way. A wave without a
+  // tail step requests wave 0's rows (the same lines: cache hits).
   F tb[3][2];
-  if (wave < ntail) {
+  {
+    const int k0 = wave < ntail ? wave : 0;
     if constexpr (kPerKey) {
-      load_key_rows(*reinterpret_cast<F(*)[2][2]>(&tb[0]), cache + 32 * wave);
+      load_key_rows(*reinterpret_cast<F(*)[2][2]>(&tb[0]), cache + 32 * k0);
     } else {
-      const int rb = R0 + cache + 32 * wave - qlast;
+      const int rb = R0 + cache + 32 * k0 - qlast;
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
@@ -277,16 +281,19 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       }
     }
   }
+  // the wave's first two body steps (a wave with fewer requests the last body step again, or
+  // step 0 when there is none; those registers are never used)
+  const int s_last = max(nbody - 1, 0);
   StepRegs<T> ra, rb2;
   F p0[2];
-  if (nmine > 0) {
+  {
     if (!kPerKey) {
-      const T* row = band_row(R0 + 32 * s_begin - qlast + m16) + 8 * grp;
+      const T* row = band_row(R0 + 32 * min(s_begin, s_last) - qlast + m16) + 8 * grp;
       p0[0] = load8(row);
       p0[1] = load8(row + 32);
     }
-    load_step(ra, s_begin);
-    if (nmine > 1) load_step(rb2, s_begin + 1);
+    load_step(ra, min(s_begin, s_last));
+    load_step(rb2, min(s_begin + 1, s_last));
   }
 
   // ---- 3. long chunks: the chunk's frames into the LDS tail with a loop ------------------------
