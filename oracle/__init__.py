@@ -22,3 +22,11 @@ from .relpos_attn import (  # noqa: F401
     chunked_limited_keep,
     varlen_relpos_attn,
 )
+from .projections import (  # noqa: F401
+    linear,
+    sinusoid,
+    table_positions,
+    rel_pos_projection,
+    qkv_project,
+    qkv_append,
+)

@@ -758,3 +758,155 @@ def test_column_blocked_k_pages():
         k2, v2 = oracle.gather_stream(kp2, vp2, bt[b], cs[b] + C)
         np.testing.assert_array_equal(k1, k2)
         np.testing.assert_array_equal(v1, v2)
+
+
+# --------------------------------------------------------------------------------------------
+# The GEMMs either side: linear, the sinusoidal table and its projection, the Q/K/V append
+# --------------------------------------------------------------------------------------------
+
+def test_linear_matches_brute_force():
+    rng = np.random.default_rng(40)
+    x = rng.normal(size=(2, 3, 5))
+    w = rng.normal(size=(4, 5))
+    b = rng.normal(size=4)
+    y = oracle.linear(x, w, b)
+    assert y.shape == (2, 3, 4)
+    for i in range(2):
+        for t in range(3):
+            for n in range(4):
+                acc = b[n]
+                for k in range(5):
+                    acc += x[i, t, k] * w[n, k]
+                assert abs(y[i, t, n] - acc) < 1e-12
+    assert np.allclose(oracle.linear(x, w), y - b, atol=1e-12)
+
+
+def test_sinusoid_closed_forms():
+    d = 8
+    e = oracle.sinusoid([0, 1, -1, 2, 3, 5, 37], d)
+    # position 0: sin 0 = 0 in even columns, cos 0 = 1 in odd columns
+    assert np.array_equal(e[0], np.array([0.0, 1.0] * (d // 2)))
+    # position 1, first pair: frequency 1
+    assert abs(e[1, 0] - 0.8414709848078965) < 1e-15 and abs(e[1, 1] - 0.5403023058681398) < 1e-15
+    # frequencies 10000^(-2i/d), read back from position 1's angles
+    for i in range(d // 2):
+        assert abs(math.atan2(e[1, 2 * i], e[1, 2 * i + 1]) - math.pow(10000.0, -2.0 * i / d)) < 1e-13
+    # every (sin, cos) pair has unit norm
+    assert np.allclose(e[:, 0::2] ** 2 + e[:, 1::2] ** 2, 1.0, atol=1e-14)
+    # odd sine, even cosine
+    assert np.allclose(e[2, 0::2], -e[1, 0::2], atol=1e-15) and np.allclose(e[2, 1::2], e[1, 1::2], atol=1e-15)
+    # angle addition: PE(2 + 3) from PE(2) and PE(3)
+    s2, c2, s3, c3 = e[3, 0::2], e[3, 1::2], e[4, 0::2], e[4, 1::2]
+    assert np.allclose(e[5, 0::2], s2 * c3 + c2 * s3, atol=1e-13)
+    assert np.allclose(e[5, 1::2], c2 * c3 - s2 * s3, atol=1e-13)
+
+
+def test_rel_pos_projection_matches_brute_force():
+    rng = np.random.default_rng(41)
+    d, n_out, rows = 6, 4, 5
+    w = rng.normal(size=(n_out, d))
+    starts, step = [3, -2], -1
+    got = oracle.rel_pos_projection(w, starts, step, rows)
+    assert got.shape == (2, rows, n_out)
+    for t, s0 in enumerate(starts):
+        for r in range(rows):
+            p = s0 + step * r
+            emb = []
+            for i in range(d // 2):
+                ang = p * math.pow(10000.0, -2.0 * i / d)
+                emb += [math.sin(ang), math.cos(ang)]
+            for n in range(n_out):
+                assert abs(got[t, r, n] - sum(emb[k] * w[n, k] for k in range(d))) < 1e-12
+
+
+def test_rel_pos_projection_orientation_and_shift():
+    rng = np.random.default_rng(42)
+    d, n_out = 8, 6
+    w = rng.normal(size=(n_out, d))
+    center = 4
+    tab = oracle.rel_pos_projection(w, [center], -1, 2 * center + 1)[0]
+    # row `center` holds distance 0: sin terms vanish, cos terms are 1
+    assert np.allclose(tab[center], w[:, 1::2].sum(axis=1), atol=1e-13)
+    # row r holds distance center - r: row 0 is the largest positive distance
+    assert np.allclose(tab[0], oracle.linear(oracle.sinusoid([center], d), w)[0], atol=1e-13)
+    # a table centred 2 further is the same rows shifted by 2
+    tab2 = oracle.rel_pos_projection(w, [center + 2], -1, 2 * center + 1)[0]
+    assert np.allclose(tab2[2:], tab[:-2], atol=1e-13)
+    # ascending (WeNet) tables: row j of start s is position s + j
+    asc = oracle.rel_pos_projection(w, [-3], 1, 7)[0]
+    assert np.allclose(asc[3], w[:, 1::2].sum(axis=1), atol=1e-13)
+
+
+def test_qkv_append_addresses_and_order():
+    rng = np.random.default_rng(43)
+    B, C, dm, H, Hk, D, S, N, M = 2, 3, 6, 2, 1, 4, 2, 9, 4
+    x = rng.normal(size=(B, C, dm))
+    w = rng.normal(size=((H + 2 * Hk) * D, dm))
+    bias = rng.normal(size=(H + 2 * Hk) * D)
+    k_pool = rng.normal(size=(N, Hk, S, D))
+    v_pool = rng.normal(size=(N, Hk, D, S))
+    bt = np.array([[5, 2, 7, 0], [1, 8, 3, 6]])
+    cs = np.array([1, 4])
+    lens = np.array([3, 2])
+    q, k_out, v_out = oracle.qkv_append(x, w, bias, k_pool, v_pool, bt, cs, H, Hk, D, chunk_lens=lens)
+    k_ref, v_ref = k_pool.copy(), v_pool.copy()
+    for b in range(B):
+        for t in range(C):
+            row = [sum(x[b, t, c] * w[n, c] for c in range(dm)) + bias[n] for n in range(w.shape[0])]
+            for h in range(H):
+                assert np.allclose(q[b, t, h], row[h * D:(h + 1) * D], atol=1e-12)
+            if t >= lens[b]:
+                continue
+            frame = cs[b] + t
+            blk, slot = bt[b][frame // S], frame % S
+            for g in range(Hk):
+                k_ref[blk, g, slot, :] = row[H * D + g * D:H * D + (g + 1) * D]
+                v_ref[blk, g, :, slot] = row[(H + Hk) * D + g * D:(H + Hk) * D + (g + 1) * D]
+    assert np.allclose(k_out, k_ref, atol=1e-12) and np.allclose(v_out, v_ref, atol=1e-12)
+
+
+_PROJ_PINS = [test_linear_matches_brute_force, test_sinusoid_closed_forms,
+              test_rel_pos_projection_matches_brute_force, test_rel_pos_projection_orientation_and_shift,
+              test_qkv_append_addresses_and_order]
+
+
+@pytest.mark.parametrize("slip", ["sin_cos_swapped", "frequency_exponent", "no_bias", "step_sign", "kv_order"])
+def test_planted_projection_mistakes_are_caught(monkeypatch, slip):
+    import oracle.projections as prj
+    real_sin, real_lin, real_pos, real_qkv = prj.sinusoid, prj.linear, prj.table_positions, prj.qkv_project
+    if slip == "sin_cos_swapped":
+        def bad(positions, d_model):
+            e = real_sin(positions, d_model)
+            return np.ascontiguousarray(e[:, [c ^ 1 for c in range(d_model)]])
+        monkeypatch.setattr(prj, "sinusoid", bad)
+        monkeypatch.setattr(oracle, "sinusoid", bad)
+    elif slip == "frequency_exponent":
+        def bad(positions, d_model):
+            p = np.asarray(positions, dtype=np.float64)[:, None]
+            f = np.power(10000.0, -np.arange(d_model // 2)[None, :] / d_model)
+            e = np.empty((p.shape[0], d_model))
+            e[:, 0::2], e[:, 1::2] = np.sin(p * f), np.cos(p * f)
+            return e
+        monkeypatch.setattr(prj, "sinusoid", bad)
+        monkeypatch.setattr(oracle, "sinusoid", bad)
+    elif slip == "no_bias":
+        bad = lambda x, w, bias=None: real_lin(x, w)
+        monkeypatch.setattr(prj, "linear", bad)
+        monkeypatch.setattr(oracle, "linear", bad)
+    elif slip == "step_sign":
+        bad = lambda s, step, rows: real_pos(s, -step, rows)
+        monkeypatch.setattr(prj, "table_positions", bad)
+        monkeypatch.setattr(oracle, "table_positions", bad)
+    elif slip == "kv_order":
+        def bad(x, w, b, H, Hk, D):
+            q, k, v = real_qkv(x, w, b, H, Hk, D)
+            return q, v, k
+        monkeypatch.setattr(prj, "qkv_project", bad)
+        monkeypatch.setattr(oracle, "qkv_project", bad)
+    failed = 0
+    for pin in _PROJ_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"no pin caught the planted {slip}"
