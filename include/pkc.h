@@ -28,6 +28,11 @@
  *   [ENG 9]    "ASR Engine", section 4.3 step 6 and sections 8-9: each stream commits its actual
  *              frames (a final window may be short); a cohort is padded to a wider graph shape
  *              through a padding lane whose rows compute only for themselves.
+ *   [ENG 9p]   "ASR Engine", section 9: the positional projection of the relative-position table
+ *              is sized by the cache rung (one projected row per table row).
+ *   [MOD dec]  "Model Layer", the decoder notes (WeNet's linear_q / linear_k / linear_v /
+ *              linear_out over the shared attention core; an activation folded into the GEMM
+ *              epilogue) and "Heads" (projections at a GEMM-aligned width).
  *
  * Score of chunk query i (absolute position cache + i) against key j (0 <= j < cache + C):
  *     s[i][j] = ((q_i + u) . k_j + (q_i + v) . p[cache + i - j]) * softmax_scale
@@ -264,6 +269,66 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
                                      int32_t n_head, int32_t n_kv_head, int32_t head_dim,
                                      int32_t mask_chunk, int32_t mask_left_chunks,
                                      float softmax_scale, hipStream_t stream);
+
+/*
+ * pkc_linear - y = x W^T + b, a linear layer [MOD dec] (linear_out, or any projection beside
+ * the attention), on MFMA with fp32 accumulation.
+ *
+ * x [M, K], w [N, K] (out_features x in_features, the nn.Linear storage), bias [N] or NULL,
+ * y [M, N]; all row-major, one dtype. y is written in full; nothing else is touched.
+ * Errors: NULL x, w or y -> PKC_ERR_NULL; a non-positive size -> PKC_ERR_SHAPE; K not a multiple
+ * of 32 or N not a multiple of 16 -> PKC_ERR_UNSUPPORTED; a pointer not 16-byte aligned ->
+ * PKC_ERR_ALIGN.
+ */
+pkc_status pkc_linear(pkc_dtype dtype, const void* x, const void* w, const void* bias, void* y,
+                      int32_t M, int32_t N, int32_t K, hipStream_t stream);
+
+/*
+ * paged_kv_qkv_append - the chunk's Q/K/V projection [MOD dec] with the append [ENG 4.3] as
+ * its epilogue: the chunk's K/V rows go from the GEMM straight into the stream's pages.
+ *
+ * x [B, C, d_model]; w_qkv [(H + 2 Hk) D, d_model] stacks the rows of linear_q, linear_k and
+ * linear_v in that order, b_qkv [(H + 2 Hk) D] or NULL likewise. With y = x w_qkv^T + b_qkv:
+ *     q_out[b][t][h][:] = y[b][t][h D : (h + 1) D]                    (every t < C)
+ * and, for t < n_b only, K = y[.., H D + g D : ...] and V = y[.., (H + Hk) D + g D : ...] are
+ * written exactly where paged_kv_append would write k_new / v_new (same pools, layouts, block
+ * tables, cache lengths, chunk lengths and window starts). K/V are rounded to the pool's dtype
+ * once; no other pool element is touched. cache_seqlens is not advanced.
+ * Errors: as paged_kv_append; n_head % n_kv_head != 0 -> PKC_ERR_SHAPE; d_model not a multiple
+ * of 32 -> PKC_ERR_UNSUPPORTED; any of x, w_qkv, b_qkv, q_out not 16-byte aligned ->
+ * PKC_ERR_ALIGN.
+ */
+pkc_status paged_kv_qkv_append(pkc_dtype dtype, const void* x, const void* w_qkv,
+                               const void* b_qkv, void* q_out, void* k_pool, void* v_pool,
+                               const int32_t* block_tables, const int32_t* cache_seqlens,
+                               const int32_t* chunk_lens, const int32_t* window_start,
+                               int32_t batch, int32_t chunk_size, int32_t d_model, int32_t n_head,
+                               int32_t n_kv_head, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_cache_seqlen, hipStream_t stream);
+
+/*
+ * rel_pos_projection - linear_pos over sinusoidal tables [ENG 9p], [MOD fix]: the positional
+ * tables the attention reads, without materialising the sinusoid.
+ *
+ * Row r of table t holds position p = pos_start[t] + pos_step r (pos_start int32 [n_tables] on
+ * the device, or NULL for pos_first in every table). Its sinusoid e has, for i < d_model / 2,
+ * e[2 i] = sin(p f_i) and e[2 i + 1] = cos(p f_i), f_i = 10000^(-2 i / d_model), and
+ *     pos_out[t][r][:] = e W_pos^T      (w_pos [out_features, d_model], no bias)
+ * pos_out [n_tables, rows, out_features]. A Transformer-XL table by distance centred at c
+ * (row r holds distance c - r, the layout chunk_paged_relpos_attn reads) is pos_first = c,
+ * pos_step = -1, rows = 2 c + 1; WeNet's per-key table of stream b [MOD nem] is
+ * pos_start[b] = offset_b - cache_seqlens[b], pos_step = +1. The sinusoid is computed in fp32
+ * and rounded to the dtype before the product.
+ * Errors: NULL w_pos or pos_out -> PKC_ERR_NULL; non-positive n_tables or rows, or positions
+ * beyond +-2^24 (fp32-exact integers; checked for pos_first, the caller's precondition for
+ * pos_start) -> PKC_ERR_SHAPE; d_model not a multiple of 32 or out_features not a multiple of
+ * 16 -> PKC_ERR_UNSUPPORTED; a pointer not 16-byte aligned -> PKC_ERR_ALIGN.
+ */
+pkc_status rel_pos_projection(pkc_dtype dtype, const void* w_pos, const int32_t* pos_start,
+                              int32_t pos_first, int32_t pos_step, int32_t n_tables, int32_t rows,
+                              int32_t d_model, int32_t out_features, void* pos_out,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

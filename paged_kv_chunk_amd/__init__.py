@@ -37,6 +37,9 @@ SIGNATURES = {
     "paged_kv_commit": ([_ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _ptr], ctypes.c_int),
     "varlen_packed_relpos_attn": ([ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _ptr,
                                    _ptr, _ptr, _ptr] + [_i32] * 5 + [_f32, _ptr], ctypes.c_int),
+    "pkc_linear": ([ctypes.c_int] + [_ptr] * 4 + [_i32] * 3 + [_ptr], ctypes.c_int),
+    "paged_kv_qkv_append": ([ctypes.c_int] + [_ptr] * 10 + [_i32] * 10 + [_ptr], ctypes.c_int),
+    "rel_pos_projection": ([ctypes.c_int, _ptr, _ptr] + [_i32] * 6 + [_ptr, _ptr], ctypes.c_int),
 }
 
 
@@ -243,3 +246,57 @@ def varlen_packed_relpos_attn(q, k, v, cu_seqlens, pos, pos_bias_u, pos_bias_v, 
         _stream(stream))
     _check(st, "varlen_packed_relpos_attn")
     return out
+
+
+def linear(x, w, bias=None, out=None, stream=None):
+    """y = x w^T + bias: x [..., K], w [N, K], bias [N] or None -> y [..., N] (new tensor unless
+    ``out`` is given)."""
+    K = x.shape[-1]
+    M = x.numel() // K
+    N = w.shape[0]
+    if w.shape[1] != K or (bias is not None and tuple(bias.shape) != (N,)):
+        raise ValueError("linear: w must be [N, K] and bias [N]")
+    y = torch.empty(*x.shape[:-1], N, dtype=x.dtype, device=x.device) if out is None else out
+    dt = _dtype(x, w, y, *([bias] if bias is not None else []))
+    st = lib().pkc_linear(dt, _p(x), _p(w), _p(bias), _p(y), M, N, K, _stream(stream))
+    _check(st, "pkc_linear")
+    return y
+
+
+def paged_kv_qkv_append(x, w_qkv, b_qkv, k_pool, v_pool, block_tables, cache_seqlens,
+                        max_cache_seqlen, n_head, q_out=None, chunk_lens=None, window_start=None,
+                        stream=None):
+    """The chunk's Q/K/V projection with the append as its epilogue. x [B, C, d_model],
+    w_qkv [(H + 2 Hk) D, d_model] (rows of linear_q, linear_k, linear_v), b_qkv or None.
+    Returns q [B, C, H, D]; the chunk's K/V rows are written into the pools."""
+    B, C, dm = x.shape
+    N, Hk, S = k_pool.shape[0], k_pool.shape[1], k_pool.shape[3]
+    D = w_qkv.shape[0] // (n_head + 2 * Hk)
+    _pool_geom(k_pool, v_pool, D)
+    if w_qkv.shape != (D * (n_head + 2 * Hk), dm):
+        raise ValueError("paged_kv_qkv_append: w_qkv must be [(H + 2 Hk) D, d_model]")
+    q = torch.empty(B, C, n_head, D, dtype=x.dtype, device=x.device) if q_out is None else q_out
+    tensors = [x, w_qkv, q, k_pool, v_pool] + ([b_qkv] if b_qkv is not None else [])
+    st = lib().paged_kv_qkv_append(_dtype(*tensors), _p(x), _p(w_qkv), _p(b_qkv), _p(q),
+                                   _p(k_pool), _p(v_pool), _table(block_tables),
+                                   _table(cache_seqlens), _table(chunk_lens), _table(window_start),
+                                   B, C, dm, n_head, Hk, D, S, N, block_tables.shape[1],
+                                   int(max_cache_seqlen), _stream(stream))
+    _check(st, "paged_kv_qkv_append")
+    return q
+
+
+def rel_pos_projection(w_pos, rows, pos_start=None, pos_first=0, pos_step=-1, n_tables=None,
+                       out=None, stream=None):
+    """linear_pos over sinusoidal tables: [n_tables, rows, out_features]. Row r of table t holds
+    position pos_start[t] + pos_step r (pos_start int32 [n_tables] on the GPU), or
+    pos_first + pos_step r for every table when pos_start is None."""
+    n_out, dm = w_pos.shape
+    if n_tables is None:
+        n_tables = 1 if pos_start is None else pos_start.shape[0]
+    y = torch.empty(n_tables, rows, n_out, dtype=w_pos.dtype, device=w_pos.device) if out is None else out
+    st = lib().rel_pos_projection(_dtype(w_pos, y), _p(w_pos), _table(pos_start), int(pos_first),
+                                  int(pos_step), int(n_tables), int(rows), dm, n_out, _p(y),
+                                  _stream(stream))
+    _check(st, "rel_pos_projection")
+    return y

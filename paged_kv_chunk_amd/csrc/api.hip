@@ -9,7 +9,7 @@ using namespace pkc;
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0: chunk lengths, bounded history, multi-layer step
+constexpr int kVersion = 400;  // 0.4.0: the projections either side of the attention
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -54,6 +54,14 @@ pkc_status check_attn(int32_t chunk, int32_t n_head, int32_t n_kv_head, int32_t 
 }
 
 pkc_status from_hip(hipError_t e) { return e == hipSuccess ? PKC_OK : PKC_ERR_HIP; }
+
+// GEMM shapes the kernel is built for: whole 32-deep contraction stages, 16-feature output tiles
+pkc_status check_gemm(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return PKC_ERR_SHAPE;
+  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 30)) return PKC_ERR_SHAPE;
+  if (K % 32 != 0 || N % 16 != 0) return PKC_ERR_UNSUPPORTED;
+  return PKC_OK;
+}
 
 }  // namespace
 
@@ -258,6 +266,68 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
                  max_seqlen, n_head, n_kv_head, head_dim, mask_chunk, mask_left_chunks,
                  softmax_scale};
   return from_hip(launch_varlen_attn(dtype, p, stream));
+}
+
+
+pkc_status pkc_linear(pkc_dtype dtype, const void* x, const void* w, const void* bias, void* y,
+                      int32_t M, int32_t N, int32_t K, hipStream_t stream) {
+  pkc_status st = check_dtype(dtype);
+  if (st != PKC_OK) return st;
+  if (!x || !w || !y) return PKC_ERR_NULL;
+  st = check_gemm(M, N, K);
+  if (st != PKC_OK) return st;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias))) return PKC_ERR_ALIGN;
+  GemmParams p{x, w, bias, y, M, N, K};
+  return from_hip(launch_linear(dtype, p, stream));
+}
+
+pkc_status paged_kv_qkv_append(pkc_dtype dtype, const void* x, const void* w_qkv,
+                               const void* b_qkv, void* q_out, void* k_pool, void* v_pool,
+                               const int32_t* block_tables, const int32_t* cache_seqlens,
+                               const int32_t* chunk_lens, const int32_t* window_start,
+                               int32_t batch, int32_t chunk_size, int32_t d_model, int32_t n_head,
+                               int32_t n_kv_head, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_cache_seqlen, hipStream_t stream) {
+  pkc_status st = check_dtype(dtype);
+  if (st != PKC_OK) return st;
+  if (!x || !w_qkv || !q_out || !k_pool || !v_pool || !block_tables || !cache_seqlens)
+    return PKC_ERR_NULL;
+  st = check_pool(batch, chunk_size, n_kv_head, head_dim, block_size, num_blocks,
+                  max_blocks_per_seq, max_cache_seqlen);
+  if (st != PKC_OK) return st;
+  if (n_head <= 0 || n_head % n_kv_head != 0) return PKC_ERR_SHAPE;
+  st = check_gemm((int64_t)batch * chunk_size, (int64_t)(n_head + 2 * n_kv_head) * head_dim, d_model);
+  if (st != PKC_OK) return st;
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q_out) || !aligned16(k_pool) ||
+      !aligned16(v_pool) || (b_qkv && !aligned16(b_qkv)))
+    return PKC_ERR_ALIGN;
+  QkvParams p{x, w_qkv, b_qkv, q_out, k_pool, v_pool, block_tables, cache_seqlens, chunk_lens,
+              window_start, batch, chunk_size, d_model, n_head, n_kv_head, head_dim, block_size,
+              num_blocks, max_blocks_per_seq, max_cache_seqlen};
+  return from_hip(launch_qkv_append(dtype, p, stream));
+}
+
+pkc_status rel_pos_projection(pkc_dtype dtype, const void* w_pos, const int32_t* pos_start,
+                              int32_t pos_first, int32_t pos_step, int32_t n_tables, int32_t rows,
+                              int32_t d_model, int32_t out_features, void* pos_out,
+                              hipStream_t stream) {
+  pkc_status st = check_dtype(dtype);
+  if (st != PKC_OK) return st;
+  if (!w_pos || !pos_out) return PKC_ERR_NULL;
+  if (n_tables <= 0 || rows <= 0) return PKC_ERR_SHAPE;
+  st = check_gemm((int64_t)n_tables * rows, out_features, d_model);
+  if (st != PKC_OK) return st;
+  // positions are carried in fp32: they must be integers it holds exactly
+  const int64_t last = (int64_t)pos_first + (int64_t)pos_step * (rows - 1);
+  const int64_t span = (int64_t)1 << 24;
+  if (!pos_start && (pos_first > span || pos_first < -span || last > span || last < -span))
+    return PKC_ERR_SHAPE;
+  if ((int64_t)pos_step * (rows - 1) > span || (int64_t)pos_step * (rows - 1) < -span) return PKC_ERR_SHAPE;
+  if (!aligned16(w_pos) || !aligned16(pos_out)) return PKC_ERR_ALIGN;
+  PosProjParams p{w_pos, pos_out, pos_start, pos_first, pos_step, n_tables, rows, d_model,
+                  out_features};
+  return from_hip(launch_pos_projection(dtype, p, stream));
 }
 
 }  // extern "C"

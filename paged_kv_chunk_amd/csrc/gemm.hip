@@ -1,0 +1,338 @@
+// The GEMMs either side of the paged attention, for gfx950: y = x W^T (+ b) on MFMA.
+//
+// Sources: OASR docs, "Model Layer", the decoder notes (WeNet's linear_q / linear_k / linear_v /
+// linear_out over the attention core, an activation folded into the GEMM epilogue) and "Heads";
+// "ASR Engine", section 9 (the positional projection of the relative-position table, sized by the
+// cache rung) and "Model Layer", "Three optional encoder declarations" (one shared table, or a
+// projection per row); "ASR Engine", section 4.3 (the chunk's K/V go into the stream's pages
+// before the attention reads them).
+//
+// One kernel, three uses, picked at compile time:
+//   plain       y[M, N] = x[M, K] W[N, K]^T + b                       (linear_out, any linear)
+//   Q/K/V       the chunk's fused projection; the epilogue writes q [B, C, H, D] and appends the
+//               K/V rows straight into the stream's pages (column-blocked K, transposed V), the
+//               way paged_kv_append does, so the chunk's K/V never go through HBM twice
+//   positional  x is the sinusoidal table itself, generated in registers (row m = t rows + r
+//               holds position pos_start[t] + step r), so only W is read: linear_pos
+//
+// Work decomposition. A workgroup of 4 waves computes a BM x BN tile of y (128 x 128, or 64 x 64
+// when the larger tiles would leave the 256 CUs idle), each wave a quarter. The contraction runs
+// in 32-deep stages: every stage's x and W rows are staged once in double-buffered LDS (row
+// pitch 32 + 16 B, so the 16 rows of a fragment read fall on distinct banks) and read by the
+// waves that share them; the rows of the stage after next are requested into registers before
+// the current stage's products, unconditionally (the last stage's rows again at the end), so
+// every wait counts exactly the loads issued after the one it needs. W is the MFMA's first
+// operand: a lane ends with 4 consecutive output features of one row, stored with one 8-byte
+// (bf16) or 16-byte (fp32) write.
+#include <math.h>
+
+#include "pkc_device.h"
+#include "pkc_launch.h"
+
+namespace pkc {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 32;   // contraction depth of one stage
+
+enum Epilogue { kPlain = 0, kQKV = 1 };
+
+template <typename T> constexpr int kLP = kBK + 16 / (int)sizeof(T);   // LDS row pitch (elements)
+
+template <typename T>
+struct GemmArgs {
+  const T* x;             // [M, K]; unused for the positional source
+  const T* w;             // [N, K]
+  const T* bias;          // [N] or null
+  T* y;                   // [M, N]; the Q/K/V epilogue: q [B, C, H, D], its first H D columns
+  int M, N, K, tiles_n;
+  // positional source: row m = t rows + r holds position pos0 + step r, pos0 = pos_start[t] or
+  // pos_first; column 2 i / 2 i + 1 is sin / cos of position 10000^(-2 i / K)
+  const int32_t* pos_start;
+  int pos_first, pos_step, rows;
+  float neg_log2_base_per_col;   // -log2(10000) / K
+  // Q/K/V epilogue
+  T* k_pool;
+  T* v_pool;
+  const int32_t* bt;
+  const int32_t* cs;
+  const int32_t* lens;
+  const int32_t* ws;
+  int C, HD, Hk, D, S, num_blocks, max_blocks, max_cache;
+};
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float (&v)[4]);
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, const float (&v)[4]) {
+  bf16x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
+  *reinterpret_cast<floatx4*>(p) = floatx4{v[0], v[1], v[2], v[3]};
+}
+
+template <typename T, int BM, int BN, int kEpi, bool kSin>
+__global__ void __launch_bounds__(kThreads)
+gemm_kernel(GemmArgs<T> a) {
+  typedef typename Frag<T>::type F;
+  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte vector
+  constexpr int RV = kBK / VEC;                // vectors per staged row
+  constexpr int LP = kLP<T>;
+  constexpr int WM = BM / 2, WN = BN / 2;      // wave tile (2 x 2 waves)
+  constexpr int FM = WM / 16, FN = WN / 16;    // 16 x 16 products per wave
+  constexpr int NX = kSin ? 0 : BM * RV / kThreads;   // x vectors per thread per stage
+  constexpr int NW = BN * RV / kThreads;              // W vectors per thread per stage
+  static_assert((kSin || NX * kThreads == BM * RV) && NW * kThreads == BN * RV, "staging covers the tiles");
+
+  __shared__ __align__(16) T s_x[kSin ? 1 : 2 * BM * LP];
+  __shared__ __align__(16) T s_w[2 * BN * LP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m16 = lane & 15;
+  const int grp = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tn = blockIdx.x % a.tiles_n;
+  const int tm = blockIdx.x / a.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = a.K / kBK;
+
+  struct Regs { u32x4 x[NX > 0 ? NX : 1], w[NW]; };
+  // rows past M or N read the last row (their results are never stored)
+  auto fetch = [&](Regs& r, int s) {
+    const int k0 = kBK * s;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int idx = tid + kThreads * i;
+      const int row = min(m0 + idx / RV, a.M - 1);
+      r.x[i] = *reinterpret_cast<const u32x4*>(a.x + (size_t)row * a.K + k0 + (idx % RV) * VEC);
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int idx = tid + kThreads * i;
+      const int row = min(n0 + idx / RV, a.N - 1);
+      r.w[i] = *reinterpret_cast<const u32x4*>(a.w + (size_t)row * a.K + k0 + (idx % RV) * VEC);
+    }
+  };
+  auto stash = [&](const Regs& r, int buf) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int idx = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(s_x + buf * BM * LP + (idx / RV) * LP + (idx % RV) * VEC) = r.x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int idx = tid + kThreads * i;
+      *reinterpret_cast<u32x4*>(s_w + buf * BN * LP + (idx / RV) * LP + (idx % RV) * VEC) = r.w[i];
+    }
+  };
+
+  // positional source: this lane's positions (one per row fragment)
+  float pos[FM];
+  if constexpr (kSin) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = min(m0 + wm * WM + fm * 16 + m16, a.M - 1);
+      const int t = m / a.rows;
+      const int r = m - t * a.rows;
+      pos[fm] = (float)((a.pos_start ? a.pos_start[t] : a.pos_first) + a.pos_step * r);
+    }
+  }
+
+  floatx4 acc[FN][FM];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int s, int buf) {
+    F xf[FM], wf[FN];
+    if constexpr (kSin) {
+      // columns k0 + 8 grp + [0, 8): four (sin, cos) pairs, frequencies 10000^(-2 i / K)
+      const int i0 = (kBK * s + 8 * grp) >> 1;
+      float freq[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) freq[e] = exp2f((float)(2 * (i0 + e)) * a.neg_log2_base_per_col);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float sn, cs;
+          sincosf(pos[fm] * freq[e], &sn, &cs);
+          set(xf[fm], 2 * e, sn);
+          set(xf[fm], 2 * e + 1, cs);
+        }
+    } else {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        xf[fm] = load8(s_x + buf * BM * LP + (wm * WM + fm * 16 + m16) * LP + 8 * grp);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      wf[fn] = load8(s_w + buf * BN * LP + (wn * WN + fn * 16 + m16) * LP + 8 * grp);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mma(wf[fn], xf[fm], acc[fn][fm]);
+  };
+
+  Regs ra, rb;
+  fetch(ra, 0);
+  fetch(rb, min(1, nk - 1));
+  stash(ra, 0);
+  __syncthreads();
+  // stage s: registers `nxt` hold stage s + 1, `fre` receives stage s + 2
+  auto step = [&](int s, Regs& nxt, Regs& fre) {
+    fetch(fre, min(s + 2, nk - 1));
+    compute(s, s & 1);
+    if (s + 1 < nk) stash(nxt, (s + 1) & 1);
+    __syncthreads();
+  };
+  for (int s = 0; s < nk; s += 2) {
+    step(s, rb, ra);
+    if (s + 1 < nk) step(s + 1, ra, rb);
+  }
+
+  // ---- epilogue: lane holds y[m][n .. n + 3] of every product tile ----------------------------
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int n = n0 + wn * WN + fn * 16 + 4 * grp;
+    if (n >= a.N) continue;
+    float bias[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bias[e] = to_f(a.bias[n + e]);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = m0 + wm * WM + fm * 16 + m16;
+      if (m >= a.M) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[fn][fm][e] + bias[e];
+      if constexpr (kEpi == kPlain) {
+        store4<T>(a.y + (size_t)m * a.N + n, v);
+      } else {
+        // Q/K/V: q columns [0, H D), then K [H D, H D + Hk D), then V; a 16-column product tile
+        // lies inside one of them (H D and Hk D are multiples of 32)
+        if (n < a.HD) {
+          store4<T>(a.y + (size_t)m * a.HD + n, v);
+          continue;
+        }
+        const int b = m / a.C;
+        const int t = m - b * a.C;
+        const int n_real = a.lens ? clampi(a.lens[b], 0, a.C) : a.C;
+        if (t >= n_real) continue;   // frames past the stream's real ones are not appended
+        const int start = a.ws ? max(a.ws[b], 0) / a.S * a.S : 0;
+        const int frame = start + clampi(a.cs[b], 0, a.max_cache) + t;
+        const int blk = clampi(a.bt[(size_t)b * a.max_blocks + (frame / a.S) % a.max_blocks], 0,
+                               a.num_blocks - 1);
+        const int slot = frame % a.S;
+        const int kv = n - a.HD;
+        const int hkd = a.Hk * a.D;
+        if (kv < hkd) {
+          const int g = kv / a.D, d = kv - (kv / a.D) * a.D;
+          // K pages in 32-dim column blocks: dim d of slot s at ((d / 32) S + s) 32 + d % 32
+          store4<T>(a.k_pool + ((size_t)blk * a.Hk + g) * a.S * a.D +
+                        ((d >> 5) * a.S + slot) * 32 + (d & 31), v);
+        } else {
+          const int g = (kv - hkd) / a.D, d = (kv - hkd) - ((kv - hkd) / a.D) * a.D;
+          T* col = a.v_pool + (((size_t)blk * a.Hk + g) * a.D + d) * a.S + slot;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) col[(size_t)e * a.S] = from_f<T>(v[e]);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int kEpi, bool kSin>
+hipError_t launch_tiles(GemmArgs<T> a, hipStream_t stream) {
+  // 128 x 128 tiles when they give at least one workgroup per CU, else 64 x 64
+  const int big = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (big >= 256) {
+    a.tiles_n = (a.N + 127) / 128;
+    hipLaunchKernelGGL((gemm_kernel<T, 128, 128, kEpi, kSin>), dim3((unsigned)big), dim3(kThreads), 0,
+                       stream, a);
+  } else {
+    a.tiles_n = (a.N + 63) / 64;
+    const int n = ((a.M + 63) / 64) * a.tiles_n;
+    hipLaunchKernelGGL((gemm_kernel<T, 64, 64, kEpi, kSin>), dim3((unsigned)n), dim3(kThreads), 0,
+                       stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+GemmArgs<T> base_args(const GemmParams& p) {
+  GemmArgs<T> a{};
+  a.x = (const T*)p.x;
+  a.w = (const T*)p.w;
+  a.bias = (const T*)p.bias;
+  a.y = (T*)p.y;
+  a.M = p.M;
+  a.N = p.N;
+  a.K = p.K;
+  return a;
+}
+
+template <typename T>
+hipError_t launch_linear_t(const GemmParams& p, hipStream_t stream) {
+  return launch_tiles<T, kPlain, false>(base_args<T>(p), stream);
+}
+
+template <typename T>
+hipError_t launch_qkv_t(const QkvParams& q, hipStream_t stream) {
+  GemmParams g{q.x, q.w, q.bias, q.q_out, q.batch * q.chunk,
+               (q.n_head + 2 * q.n_kv_head) * q.head_dim, q.d_model};
+  GemmArgs<T> a = base_args<T>(g);
+  a.k_pool = (T*)q.k_pool;
+  a.v_pool = (T*)q.v_pool;
+  a.bt = q.block_tables;
+  a.cs = q.cache_seqlens;
+  a.lens = q.chunk_lens;
+  a.ws = q.window_start;
+  a.C = q.chunk;
+  a.HD = q.n_head * q.head_dim;
+  a.Hk = q.n_kv_head;
+  a.D = q.head_dim;
+  a.S = q.block_size;
+  a.num_blocks = q.num_blocks;
+  a.max_blocks = q.max_blocks;
+  a.max_cache = q.max_cache;
+  return launch_tiles<T, kQKV, false>(a, stream);
+}
+
+template <typename T>
+hipError_t launch_pos_t(const PosProjParams& q, hipStream_t stream) {
+  GemmParams g{nullptr, q.w, nullptr, q.out, q.n_tables * q.rows, q.out_features, q.d_model};
+  GemmArgs<T> a = base_args<T>(g);
+  a.pos_start = q.pos_start;
+  a.pos_first = q.pos_first;
+  a.pos_step = q.pos_step;
+  a.rows = q.rows;
+  a.neg_log2_base_per_col = -13.287712379549449f / (float)q.d_model;   // log2(10000) = 13.2877...
+  return launch_tiles<T, kPlain, true>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_linear(pkc_dtype dtype, const GemmParams& p, hipStream_t stream) {
+  return dtype == PKC_BF16 ? launch_linear_t<bf16>(p, stream) : launch_linear_t<float>(p, stream);
+}
+
+hipError_t launch_qkv_append(pkc_dtype dtype, const QkvParams& p, hipStream_t stream) {
+  return dtype == PKC_BF16 ? launch_qkv_t<bf16>(p, stream) : launch_qkv_t<float>(p, stream);
+}
+
+hipError_t launch_pos_projection(pkc_dtype dtype, const PosProjParams& p, hipStream_t stream) {
+  return dtype == PKC_BF16 ? launch_pos_t<bf16>(p, stream) : launch_pos_t<float>(p, stream);
+}
+
+}  // namespace pkc

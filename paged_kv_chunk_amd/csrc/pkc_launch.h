@@ -58,7 +58,43 @@ struct VarlenParams {
   float softmax_scale;
 };
 
+// The GEMMs either side of the attention (gemm.hip): y[M, N] = x[M, K] w[N, K]^T (+ bias)
+struct GemmParams {
+  const void* x;
+  const void* w;
+  const void* bias;   // [N] or null
+  void* y;
+  int M, N, K;
+};
+
+// The chunk's fused Q/K/V projection, appending K/V into the pages as its epilogue
+struct QkvParams {
+  const void* x;      // [B, C, d_model]
+  const void* w;      // [(H + 2 Hk) D, d_model]: rows of linear_q, linear_k, linear_v
+  const void* bias;   // [(H + 2 Hk) D] or null
+  void* q_out;        // [B, C, H, D]
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* cache_seqlens;
+  const int32_t* chunk_lens;
+  const int32_t* window_start;
+  int batch, chunk, d_model, n_head, n_kv_head, head_dim, block_size, num_blocks, max_blocks,
+      max_cache;
+};
+
+// linear_pos over sinusoidal tables generated in the kernel
+struct PosProjParams {
+  const void* w;              // [out_features, d_model]
+  void* out;                  // [n_tables, rows, out_features]
+  const int32_t* pos_start;   // [n_tables] or null: pos_first for every table
+  int pos_first, pos_step, n_tables, rows, d_model, out_features;
+};
+
 hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream);
+hipError_t launch_linear(pkc_dtype dtype, const GemmParams& p, hipStream_t stream);
+hipError_t launch_qkv_append(pkc_dtype dtype, const QkvParams& p, hipStream_t stream);
+hipError_t launch_pos_projection(pkc_dtype dtype, const PosProjParams& p, hipStream_t stream);
 hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int32_t* window_start,
                          int max_cached, int block_size, int batch, int chunk, hipStream_t stream);
 hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream);

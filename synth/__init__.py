@@ -1,8 +1,8 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
 This package only draws and lays out inputs (random values, block tables, cache lengths, the
-sinusoidal positional tables that feed the attention). It contains none of the attention's
-arithmetic and imports neither the oracle nor the HIP path.
+sinusoidal positional tables that feed the attention, linear-layer weights and activations). It
+contains none of the path's arithmetic and imports neither the oracle nor the HIP path.
 """
 
 from .cohorts import (  # noqa: F401
@@ -19,4 +19,6 @@ from .cohorts import (  # noqa: F401
     column_blocked,
     key_position_tables,
     use_key_position_tables,
+    linear_weights,
+    activations,
 )

@@ -97,6 +97,22 @@ def _randn(shape, gen, device, dtype, std=1.0):
     return x.to(dtype)
 
 
+def linear_weights(n_out, d_in, *, seed=0, dtype=BF16, device="cpu", bias=True):
+    """Seeded weights of a linear layer: W [n_out, d_in] with N(0, 1/d_in) entries (unit-variance
+    outputs for unit-variance inputs) and, if ``bias``, b [n_out] with N(0, 0.02^2) entries.
+    Drawn on the CPU. Returns (W, b or None)."""
+    gen = torch.Generator().manual_seed(seed)
+    w = (torch.randn(n_out, d_in, generator=gen) / math.sqrt(d_in)).to(dtype).to(device)
+    b = (torch.randn(n_out, generator=gen) * 0.02).to(dtype).to(device) if bias else None
+    return w, b
+
+
+def activations(shape, *, seed=0, dtype=BF16, device="cpu"):
+    """Seeded N(0, 1) activations of the given shape (drawn on the CPU)."""
+    gen = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=gen).to(dtype).to(device)
+
+
 @dataclass
 class ChunkCohort:
     """One layer's inputs for a cohort of streams (all tensors on one device)."""

@@ -113,3 +113,22 @@ def max_err(gpu, ref):
     g = gpu.detach().cpu().double().numpy() if torch.is_tensor(gpu) else gpu
     assert np.isfinite(g).all(), "non-finite output"
     return float(np.abs(g - ref).max())
+
+
+def ring_tables(co, seed, wraps=3):
+    """Window starts and ring-rotated table rows for a cohort: stream b's window starts at
+    k_b S (k_b drawn in [0, wraps M)) and its row is rotated so that absolute position
+    k_b S + t finds the block the plain row gives frame t. Returns (starts as a list, ring
+    tables on the cohort's device)."""
+    rng = np.random.default_rng(seed)
+    bt = co.block_tables.cpu().numpy()
+    M = bt.shape[1]
+    S = co.block_size
+    ring = np.full_like(bt, -1)
+    starts = []
+    for b in range(bt.shape[0]):
+        k = int(rng.integers(0, wraps * M))
+        starts.append(k * S)
+        for i in range(M):
+            ring[b, (k + i) % M] = bt[b, i]
+    return starts, torch.from_numpy(ring).to(co.block_tables.device)

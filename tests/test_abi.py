@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["paged_kv_append", "chunk_paged_relpos_attn", "paged_kv_append_relpos_attn",
               "paged_kv_append_relpos_attn_layers", "paged_kv_commit",
-              "varlen_packed_relpos_attn", "pkc_version", "pkc_status_string"]:
+              "varlen_packed_relpos_attn", "pkc_linear", "paged_kv_qkv_append",
+              "rel_pos_projection", "pkc_version", "pkc_status_string"]:
         assert n in names
 
 
@@ -189,3 +190,55 @@ def test_commit_validation(lib):
     assert lib.paged_kv_commit(P, None, None, 0, 4, 0, 16, None) == SHAPE
     assert lib.paged_kv_commit(P, None, P, 64, 4, 16, 0, None) == SHAPE
     assert lib.paged_kv_commit(P, None, P, -1, 4, 16, 16, None) == SHAPE
+
+
+# --------------------------------------------------------------------------------------------
+# The projections either side of the attention
+# --------------------------------------------------------------------------------------------
+
+def linear_call(lib, dtype=1, x=P, w=P, bias=None, y=P, M=100, N=64, K=256):
+    return lib.pkc_linear(dtype, x, w, bias, y, M, N, K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), DTYPE), (dict(x=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL),
+    (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(K=-32), SHAPE),
+    (dict(K=48), UNSUP), (dict(N=40), UNSUP),
+    (dict(x=BAD), ALIGN), (dict(y=BAD), ALIGN), (dict(bias=BAD), ALIGN),
+])
+def test_linear_validation(lib, kw, status):
+    assert linear_call(lib, **kw) == status
+
+
+def qkv_call(lib, dtype=1, x=P, w=P, b=P, q=P, k_pool=P, v_pool=P, bt=P, cs=P, B=2, C=16, dm=256,
+             H=4, Hk=4, D=64, S=16, N=32, M=8, max_cache=64):
+    return lib.paged_kv_qkv_append(dtype, x, w, b, q, k_pool, v_pool, bt, cs, None, None, B, C, dm,
+                                   H, Hk, D, S, N, M, max_cache, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), DTYPE), (dict(x=None), NULL), (dict(w=None), NULL), (dict(q=None), NULL),
+    (dict(k_pool=None), NULL), (dict(bt=None), NULL), (dict(cs=None), NULL),
+    (dict(B=0), SHAPE), (dict(H=6, Hk=4), SHAPE), (dict(H=0), SHAPE), (dict(dm=0), SHAPE),
+    (dict(dm=100), UNSUP), (dict(D=48), UNSUP),
+    (dict(max_cache=113), CAP),
+    (dict(x=BAD), ALIGN), (dict(b=BAD), ALIGN), (dict(v_pool=BAD), ALIGN),
+])
+def test_qkv_append_validation(lib, kw, status):
+    assert qkv_call(lib, **kw) == status
+
+
+def pos_call(lib, dtype=1, w=P, start=None, first=80, step=-1, n_tables=1, rows=161, dm=256,
+             n_out=256, out=P):
+    return lib.rel_pos_projection(dtype, w, start, first, step, n_tables, rows, dm, n_out, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), DTYPE), (dict(w=None), NULL), (dict(out=None), NULL),
+    (dict(rows=0), SHAPE), (dict(n_tables=0), SHAPE),
+    (dict(first=1 << 25), SHAPE), (dict(first=0, step=1 << 20, rows=100), SHAPE),
+    (dict(dm=72), UNSUP), (dict(n_out=100), UNSUP),
+    (dict(w=BAD), ALIGN), (dict(out=BAD), ALIGN),
+])
+def test_rel_pos_projection_validation(lib, kw, status):
+    assert pos_call(lib, **kw) == status
