@@ -45,6 +45,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {
     "chunk": ["chunk_attn.hip", "pkc_step.h", "pkc_device.h", "pkc_launch.h"],
     "varlen": ["varlen_attn.hip", "pkc_step.h", "pkc_device.h", "pkc_launch.h"],
+    "gemm": ["gemm.hip", "pkc_device.h", "pkc_launch.h"],
 }
 
 
@@ -271,6 +272,137 @@ def bench_varlen(args, cfg, pkc):
     print(json.dumps(result), flush=True)
 
 
+def proj_layer_shapes(co):
+    """(M, N, K) of one layer's three projections: the chunk's Q/K/V projection, linear_pos over
+    the shared table (2 (max_cache + C) - 1 rows, the cache rung's width) and linear_out."""
+    B, C, H, D = co.q.shape
+    Hk = co.k_new.shape[2]
+    dm = H * D
+    rows = 2 * (co.max_cache_seqlen + C) - 1
+    return {"qkv": (B * C, (H + 2 * Hk) * D, dm), "pos": (rows, H * D, dm), "out": (B * C, dm, H * D)}
+
+
+def proj_bytes(co, kind):
+    """Algorithmic bytes of one projection launch: read x (not for the generated sinusoid) and W
+    (and b), write y; the Q/K/V epilogue writes q and the chunk's K/V into the pages."""
+    (M, N, K) = proj_layer_shapes(co)[kind]
+    eb = co.q.element_size()
+    x = 0 if kind == "pos" else M * K * eb
+    bias = 0 if kind == "pos" else N * eb
+    return x + N * K * eb + bias + M * N * eb
+
+
+def bench_proj(args, cfg, pkc):
+    """The GEMMs either side of the attention for a cohort workload: per layer, the chunk's Q/K/V
+    projection with the paged append as its epilogue, linear_pos over the shared table and
+    linear_out. Each kind is timed alone (12 launches replayed from HIP graphs over the rotated
+    sets), then all three together per step."""
+    from synth import activations, linear_weights
+    n_layers = cfg["n_layers"]
+    sets = build_sets(args.config, args.rotate, n_layers, "cuda")
+    co0 = sets[0][0]
+    B, C, H, D = co0.q.shape
+    Hk = co0.k_new.shape[2]
+    dm = H * D
+    shapes = proj_layer_shapes(co0)
+    rows = shapes["pos"][0]
+    center = (rows - 1) // 2
+    for r, layers in enumerate(sets):
+        for l, co in enumerate(layers):
+            sd = 1000 * r + 10 * l
+            co.x = activations((B, C, dm), seed=sd, device="cuda")
+            co.w_qkv, co.b_qkv = linear_weights((H + 2 * Hk) * D, dm, seed=sd + 1, device="cuda")
+            co.w_pos, _ = linear_weights(H * D, dm, seed=sd + 2, device="cuda", bias=False)
+            co.w_out, co.b_out = linear_weights(dm, H * D, seed=sd + 3, device="cuda")
+            co.attn = activations((B * C, H * D), seed=sd + 4, device="cuda")
+            co.q_out = torch.empty_like(co.q)
+            co.pos_out = torch.empty(1, rows, H * D, dtype=co.q.dtype, device="cuda")
+            co.y_out = torch.empty(B * C, dm, dtype=co.q.dtype, device="cuda")
+
+    def launch(co, kind, st):
+        if kind == "qkv":
+            pkc.paged_kv_qkv_append(co.x, co.w_qkv, co.b_qkv, co.k_pool, co.v_pool, co.block_tables,
+                                    co.cache_seqlens, co.max_cache_seqlen, H, q_out=co.q_out,
+                                    stream=st)
+        elif kind == "pos":
+            pkc.rel_pos_projection(co.w_pos, rows, pos_first=center, pos_step=-1, out=co.pos_out,
+                                   stream=st)
+        else:
+            pkc.linear(co.attn, co.w_out, co.b_out, out=co.y_out, stream=st)
+
+    stream = torch.cuda.current_stream()
+    kinds = ("qkv", "pos", "out")
+
+    def timed(kind_list):
+        for layers in sets:
+            for co in layers:
+                for k in kind_list:
+                    launch(co, k, stream)
+        torch.cuda.synchronize()
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for layers in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for co in layers:
+                        for k in kind_list:
+                            launch(co, k, cap)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    per_kind = {}
+    for k in kinds:
+        ms = timed([k])
+        (M, N, K) = shapes[k]
+        us = ms * 1e3 / n_layers
+        per_kind[k] = dict(us=us, M=M, N=N, K=K, flops=2.0 * M * N * K, bytes=proj_bytes(co0, k),
+                           tflops=2.0 * M * N * K / (us * 1e-6) / 1e12)
+        per_kind[k]["hbm_frac"] = per_kind[k]["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+    ms_step = timed(list(kinds))
+    flops_layer = sum(v["flops"] for v in per_kind.values())
+    dom = max(kinds, key=lambda k: per_kind[k]["us"])
+    d = per_kind[dom]
+    kernel_name = {"qkv": "gemm_kernel<bf16, Q/K/V paged epilogue>",
+                   "pos": "gemm_kernel<bf16, sinusoid source>", "out": "gemm_kernel<bf16, plain>"}
+    result = {
+        "metric": "Q/K/V, positional and output projections per layer: tokens/sec + % of bf16 MFMA roofline, 1 GPU",
+        "value": B * C * n_layers / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: the projections either side of the attention "
+                               f"(B={B}, C={C}, d_model={dm}, H={H}, head_dim={D}, {n_layers} layers; "
+                               f"Q/K/V + append, linear_pos over {rows} table rows, linear_out)",
+                   "rotated_cohorts": len(sets), "launch": "graph",
+                   "per_kind_us": {k: round(v["us"], 3) for k, v in per_kind.items()},
+                   "per_kind_tflops": {k: round(v["tflops"], 1) for k, v in per_kind.items()},
+                   "per_kind_hbm_frac": {k: round(v["hbm_frac"], 3) for k, v in per_kind.items()},
+                   "flops_per_layer": flops_layer},
+        "roofline": {"bound": "mfma", "achieved": d["tflops"], "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": d["tflops"] / 2500.0,
+                     "traffic": stored_traffic(f"proj_{dom}_cfg{args.config}", "gemm"),
+                     "kernel": kernel_name[dom], "kernel_us": d["us"],
+                     "algorithmic_flops_per_launch": d["flops"],
+                     "algorithmic_bytes_per_launch": d["bytes"], "hbm_frac": d["hbm_frac"]},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +426,9 @@ def main():
                     help="packed offline workload: left chunks of the chunked_limited mask")
     ap.add_argument("--per-key", action="store_true",
                     help="cohort workloads: WeNet per-key tables instead of Transformer-XL ones")
+    ap.add_argument("--proj", action="store_true",
+                    help="cohort workloads: time the projections either side of the attention "
+                         "(Q/K/V with the paged append, linear_pos, linear_out) instead")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the workload, time a plain device copy of this many MiB "
                          "(reference for HBM counters and achievable bandwidth)")
@@ -331,6 +466,8 @@ def main():
     cfg = CONFIGS[args.config]
     if cfg["kind"] == "varlen":
         return bench_varlen(args, cfg, pkc)
+    if args.proj:
+        return bench_proj(args, cfg, pkc)
     n_layers = cfg["n_layers"]
     dev = "cuda"
     sets = build_sets(args.config, args.rotate, n_layers, dev)

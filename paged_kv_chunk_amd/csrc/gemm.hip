@@ -15,15 +15,22 @@
 //   positional  x is the sinusoidal table itself, generated in registers (row m = t rows + r
 //               holds position pos_start[t] + step r), so only W is read: linear_pos
 //
-// Work decomposition. A workgroup of 4 waves computes a BM x BN tile of y (128 x 128, or 64 x 64
-// when the larger tiles would leave the 256 CUs idle), each wave a quarter. The contraction runs
-// in 32-deep stages: every stage's x and W rows are staged once in double-buffered LDS (row
-// pitch 32 + 16 B, so the 16 rows of a fragment read fall on distinct banks) and read by the
-// waves that share them; the rows of the stage after next are requested into registers before
-// the current stage's products, unconditionally (the last stage's rows again at the end), so
-// every wait counts exactly the loads issued after the one it needs. W is the MFMA's first
-// operand: a lane ends with 4 consecutive output features of one row, stored with one 8-byte
-// (bf16) or 16-byte (fp32) write.
+// Work decomposition. A workgroup of 4 waves computes a BM x BN tile of y (128 x 128, 128 x 64
+// or 64 x 64: whichever gives the least work on the busiest CU when all tiles run at once), each
+// wave a quarter. The contraction runs in 32-deep stages, each stage's x and W rows staged once in
+// LDS and read by the waves that share them. W is the MFMA's first operand: a lane ends with 4
+// consecutive output features of one row, stored with one 8-byte (bf16) or 16-byte (fp32) write.
+//
+// Staging, bf16 with d_model 256, 512 or 1024 (the projections of the streaming cohorts): direct
+// global -> LDS loads (global_load_lds_dwordx4; each lane's 16 bytes land at the wave's LDS base
+// + 16 lane, probed on the GPU) into a ring of 4 stages, 3 in flight. A stage is a run of 1 KB
+// blocks of 16 rows x 32 dims; the 16-byte chunk c of block row r sits at chunk
+// c ^ (((r >> 1) ^ (r >> 3)) & 3), so the 16 rows of a fragment read fall on distinct banks (for
+// 32 banks per quarter-wave and 64 per half-wave alike). The stage loop is unrolled at compile
+// time (the stage count is a template argument): every ring slot is its own LDS array and every
+// wait names its exact count, so the compiler can tell a slot being read from one being filled.
+// Otherwise (fp32, the generated sinusoid, other widths) the rows go through registers, two
+// stages ahead, into double-buffered LDS with a padded row pitch.
 #include <math.h>
 
 #include "pkc_device.h"
@@ -76,6 +83,77 @@ __device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
   *reinterpret_cast<floatx4*>(p) = floatx4{v[0], v[1], v[2], v[3]};
 }
 
+// Tile of a workgroup. Workgroups go to the 8 XCDs round-robin (block b to XCD b % 8); each XCD
+// takes one contiguous run of the row-major tile order instead, so the x rows of a tile row are
+// read into one XCD's L2 (only the small W is read by every XCD).
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int xcd = b & 7, local = b >> 3;
+  const int per = total >> 3, extra = total & 7;
+  const int logical = xcd < extra ? xcd * (per + 1) + local
+                                  : extra * (per + 1) + (xcd - extra) * per + local;
+  tm = logical / tiles_n;
+  tn = logical - tm * tiles_n;
+}
+
+// Epilogue: the lane holds y[m][n .. n + 3] of every 16 x 16 product tile (rows mb + 16 fm + m16,
+// features nb + 16 fn + 4 grp); plain rows, or the Q/K/V split with the K/V rows appended into
+// the pages.
+template <typename T, int kEpi, int FM, int FN>
+__device__ __forceinline__ void store_tiles(const GemmArgs<T>& a, const floatx4 (&acc)[FN][FM],
+                                            int mb, int nb, int m16, int grp) {
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int n = nb + fn * 16 + 4 * grp;
+    if (n >= a.N) continue;
+    float bias[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bias[e] = to_f(a.bias[n + e]);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = mb + fm * 16 + m16;
+      if (m >= a.M) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[fn][fm][e] + bias[e];
+      if constexpr (kEpi == kPlain) {
+        store4<T>(a.y + (size_t)m * a.N + n, v);
+      } else {
+        // Q/K/V: q columns [0, H D), then K [H D, H D + Hk D), then V; a 16-column product tile
+        // lies inside one of them (H D and Hk D are multiples of 32)
+        if (n < a.HD) {
+          store4<T>(a.y + (size_t)m * a.HD + n, v);
+          continue;
+        }
+        const int b = m / a.C;
+        const int t = m - b * a.C;
+        const int n_real = a.lens ? clampi(a.lens[b], 0, a.C) : a.C;
+        if (t >= n_real) continue;   // frames past the stream's real ones are not appended
+        const int start = a.ws ? max(a.ws[b], 0) / a.S * a.S : 0;
+        const int frame = start + clampi(a.cs[b], 0, a.max_cache) + t;
+        const int blk = clampi(a.bt[(size_t)b * a.max_blocks + (frame / a.S) % a.max_blocks], 0,
+                               a.num_blocks - 1);
+        const int slot = frame % a.S;
+        const int kv = n - a.HD;
+        const int hkd = a.Hk * a.D;
+        if (kv < hkd) {
+          const int g = kv / a.D, d = kv - (kv / a.D) * a.D;
+          // K pages in 32-dim column blocks: dim d of slot s at ((d / 32) S + s) 32 + d % 32
+          store4<T>(a.k_pool + ((size_t)blk * a.Hk + g) * a.S * a.D +
+                        ((d >> 5) * a.S + slot) * 32 + (d & 31), v);
+        } else {
+          const int g = (kv - hkd) / a.D, d = (kv - hkd) - ((kv - hkd) / a.D) * a.D;
+          T* col = a.v_pool + (((size_t)blk * a.Hk + g) * a.D + d) * a.S + slot;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) col[(size_t)e * a.S] = from_f<T>(v[e]);
+        }
+      }
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int kEpi, bool kSin>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(GemmArgs<T> a) {
@@ -98,8 +176,8 @@ gemm_kernel(GemmArgs<T> a) {
   const int m16 = lane & 15;
   const int grp = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tn = blockIdx.x % a.tiles_n;
-  const int tm = blockIdx.x / a.tiles_n;
+  int tm, tn;
+  tile_of(blockIdx.x, (a.M + BM - 1) / BM, a.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = a.K / kBK;
 
@@ -199,74 +277,157 @@ gemm_kernel(GemmArgs<T> a) {
     if (s + 1 < nk) step(s + 1, ra, rb);
   }
 
-  // ---- epilogue: lane holds y[m][n .. n + 3] of every product tile ----------------------------
+  store_tiles<T, kEpi, FM, FN>(a, acc, m0 + wm * WM, n0 + wn * WN, m16, grp);
+}
+
+// ---- bf16, direct global -> LDS staging, NK stages unrolled ------------------------------------
+
+__device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Wait until at most N of this wave's direct loads are in flight and its LDS accesses are done
+// (s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at 7, lgkmcnt 11:8 at 0).
+template <int N>
+__device__ __forceinline__ void wait_stage() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int BM, int BN, int kEpi, int NK>
+__global__ void __launch_bounds__(kThreads)
+gemm_dma_kernel(GemmArgs<bf16> a) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int NBX = BM / 16, NB = (BM + BN) / 16;   // 1 KB blocks per stage (x, then W)
+  constexpr int DPW = NB / 4;                          // direct loads per wave per stage
+  constexpr int SLOT = NB * 512;                       // bf16 elements of one ring slot
+  static_assert(DPW * 4 == NB, "blocks split evenly over the waves");
+
+  __shared__ __align__(16) bf16 s0[SLOT];
+  __shared__ __align__(16) bf16 s1[SLOT];
+  __shared__ __align__(16) bf16 s2[SLOT];
+  __shared__ __align__(16) bf16 s3[SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m16 = lane & 15;
+  const int grp = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, (a.M + BM - 1) / BM, a.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // this wave's blocks: lane l loads row l / 4 of the block, the chunk that belongs at chunk
+  // position l % 4 (rows past M or N read the last row; their results are never stored)
+  const bf16* src[DPW];
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const int n = n0 + wn * WN + fn * 16 + 4 * grp;
-    if (n >= a.N) continue;
-    float bias[4] = {0.f, 0.f, 0.f, 0.f};
-    if (a.bias) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bias[e] = to_f(a.bias[n + e]);
-    }
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int m = m0 + wm * WM + fm * 16 + m16;
-      if (m >= a.M) continue;
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[fn][fm][e] + bias[e];
-      if constexpr (kEpi == kPlain) {
-        store4<T>(a.y + (size_t)m * a.N + n, v);
-      } else {
-        // Q/K/V: q columns [0, H D), then K [H D, H D + Hk D), then V; a 16-column product tile
-        // lies inside one of them (H D and Hk D are multiples of 32)
-        if (n < a.HD) {
-          store4<T>(a.y + (size_t)m * a.HD + n, v);
-          continue;
-        }
-        const int b = m / a.C;
-        const int t = m - b * a.C;
-        const int n_real = a.lens ? clampi(a.lens[b], 0, a.C) : a.C;
-        if (t >= n_real) continue;   // frames past the stream's real ones are not appended
-        const int start = a.ws ? max(a.ws[b], 0) / a.S * a.S : 0;
-        const int frame = start + clampi(a.cs[b], 0, a.max_cache) + t;
-        const int blk = clampi(a.bt[(size_t)b * a.max_blocks + (frame / a.S) % a.max_blocks], 0,
-                               a.num_blocks - 1);
-        const int slot = frame % a.S;
-        const int kv = n - a.HD;
-        const int hkd = a.Hk * a.D;
-        if (kv < hkd) {
-          const int g = kv / a.D, d = kv - (kv / a.D) * a.D;
-          // K pages in 32-dim column blocks: dim d of slot s at ((d / 32) S + s) 32 + d % 32
-          store4<T>(a.k_pool + ((size_t)blk * a.Hk + g) * a.S * a.D +
-                        ((d >> 5) * a.S + slot) * 32 + (d & 31), v);
-        } else {
-          const int g = (kv - hkd) / a.D, d = (kv - hkd) - ((kv - hkd) / a.D) * a.D;
-          T* col = a.v_pool + (((size_t)blk * a.Hk + g) * a.D + d) * a.S + slot;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) col[(size_t)e * a.S] = from_f<T>(v[e]);
-        }
-      }
+  for (int i = 0; i < DPW; ++i) {
+    const int blk = wave * DPW + i;
+    const int r = lane >> 2;
+    const int c = (lane & 3) ^ dma_swz(r);
+    if (blk < NBX) {
+      src[i] = a.x + (size_t)min(m0 + 16 * blk + r, a.M - 1) * a.K + 8 * c;
+    } else {
+      src[i] = a.w + (size_t)min(n0 + 16 * (blk - NBX) + r, a.N - 1) * a.K + 8 * c;
     }
   }
+  auto slot = [&](int k) -> bf16* {
+    switch (k & 3) {
+      case 0: return s0;
+      case 1: return s1;
+      case 2: return s2;
+      default: return s3;
+    }
+  };
+  auto issue = [&](int s) {
+    bf16* base = slot(s);
+#pragma unroll
+    for (int i = 0; i < DPW; ++i)
+      load_lds16(src[i] + kBK * s, base + (wave * DPW + i) * 512);
+  };
+  // fragment reads: row m16 of a block, the lane's 16-byte chunk grp at its swizzled position
+  const int fo = m16 * 32 + 8 * (grp ^ dma_swz(m16));
+
+  floatx4 acc[FN][FM];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < 3 && s < NK; ++s) issue(s);
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    // stage s in LDS for every wave (this wave's loads: all but the two later stages'), and
+    // every wave done reading the slot stage s + 3 refills
+    if (s + 2 < NK) wait_stage<2 * DPW>();
+    else if (s + 1 < NK) wait_stage<DPW>();
+    else wait_stage<0>();
+    // (the empty asm statements keep the compiler from moving LDS accesses across the barrier,
+    // which it would otherwise treat as touching no memory)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s + 3 < NK) issue(s + 3);
+    const bf16* cur = slot(s);
+    bf16x8 xf[FM], wf[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) xf[fm] = load8(cur + ((wm * WM) / 16 + fm) * 512 + fo);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) wf[fn] = load8(cur + (NBX + (wn * WN) / 16 + fn) * 512 + fo);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mma(wf[fn], xf[fm], acc[fn][fm]);
+  }
+  store_tiles<bf16, kEpi, FM, FN>(a, acc, m0 + wm * WM, n0 + wn * WN, m16, grp);
+}
+
+// Tile shape: the least work on the busiest CU with every tile resident at once (ties: the larger
+// tile, which re-reads less), over 128 x 128, 128 x 64 and 64 x 64.
+inline int pick_tile(int M, int N) {
+  const int cand[3][2] = {{128, 128}, {128, 64}, {64, 64}};
+  int best = 0;
+  long best_cost = -1;
+  for (int i = 0; i < 3; ++i) {
+    const long tiles = (long)((M + cand[i][0] - 1) / cand[i][0]) * ((N + cand[i][1] - 1) / cand[i][1]);
+    const long cost = ((tiles + 255) / 256) * cand[i][0] * cand[i][1];
+    if (best_cost < 0 || cost < best_cost) {
+      best = i;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <int BM, int BN, int kEpi>
+hipError_t launch_dma(GemmArgs<bf16>& a, dim3 grid, hipStream_t stream) {
+  switch (a.K / kBK) {
+    case 8: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, kEpi, 8>), grid, dim3(kThreads), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, kEpi, 16>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, kEpi, 32>), grid, dim3(kThreads), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int BM, int BN, int kEpi, bool kSin>
+hipError_t launch_shape(GemmArgs<T> a, hipStream_t stream) {
+  a.tiles_n = (a.N + BN - 1) / BN;
+  const dim3 grid((unsigned)(((a.M + BM - 1) / BM) * a.tiles_n));
+  if constexpr (sizeof(T) == 2 && !kSin) {
+    if (a.K == 256 || a.K == 512 || a.K == 1024) return launch_dma<BM, BN, kEpi>(a, grid, stream);
+  }
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, kEpi, kSin>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <typename T, int kEpi, bool kSin>
 hipError_t launch_tiles(GemmArgs<T> a, hipStream_t stream) {
-  // 128 x 128 tiles when they give at least one workgroup per CU, else 64 x 64
-  const int big = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if (big >= 256) {
-    a.tiles_n = (a.N + 127) / 128;
-    hipLaunchKernelGGL((gemm_kernel<T, 128, 128, kEpi, kSin>), dim3((unsigned)big), dim3(kThreads), 0,
-                       stream, a);
-  } else {
-    a.tiles_n = (a.N + 63) / 64;
-    const int n = ((a.M + 63) / 64) * a.tiles_n;
-    hipLaunchKernelGGL((gemm_kernel<T, 64, 64, kEpi, kSin>), dim3((unsigned)n), dim3(kThreads), 0,
-                       stream, a);
+  switch (pick_tile(a.M, a.N)) {
+    case 0: return launch_shape<T, 128, 128, kEpi, kSin>(a, stream);
+    case 1: return launch_shape<T, 128, 64, kEpi, kSin>(a, stream);
+    default: return launch_shape<T, 64, 64, kEpi, kSin>(a, stream);
   }
-  return hipGetLastError();
 }
 
 template <typename T>

@@ -63,6 +63,16 @@ __device__ __forceinline__ bf16x8 load8_tr(const bf16* lo, const bf16* hi) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Direct global -> LDS load (global_load_lds_dwordx4, gfx950): every lane reads 16 bytes at its
+// own src, and lane l's bytes land at lds + 16 l (lds is the same for the whole wave). The
+// builtin exists only for the device; the host pass, which never runs a kernel body, sees none
+// (a host compile of it drops the whole kernel, stub included).
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 __device__ __forceinline__ void store8(float* p, f32x8 v) {
   *reinterpret_cast<floatx4*>(p) = v.lo;
