@@ -23,10 +23,11 @@
 //
 // Staging, bf16 with d_model 256, 512 or 1024 (the projections of the streaming cohorts): direct
 // global -> LDS loads (global_load_lds_dwordx4; each lane's 16 bytes land at the wave's LDS base
-// + 16 lane, probed on the GPU) into a ring of 4 stages, 3 in flight. A stage is a run of 1 KB
-// blocks of 16 rows x 32 dims; the 16-byte chunk c of block row r sits at chunk
-// c ^ (((r >> 1) ^ (r >> 3)) & 3), so the 16 rows of a fragment read fall on distinct banks (for
-// 32 banks per quarter-wave and 64 per half-wave alike). The stage loop is unrolled at compile
+// + 16 lane, probed on the GPU) into a ring of 3 stages, 2 in flight. A stage is 64 dims deep,
+// so each row's whole 128-byte line is one request; it is a run of 1 KB blocks of 8 rows, the
+// 16-byte chunk c of row r (within its group of 16) at chunk c ^ (((r >> 1) ^ (r << 2)) & 7), so
+// the 16 rows of a fragment read fall on distinct banks (for 32 banks per quarter-wave and 64 per
+// half-wave alike; checked on the CPU). The stage loop is unrolled at compile
 // time (the stage count is a template argument): every ring slot is its own LDS array and every
 // wait names its exact count, so the compiler can tell a slot being read from one being filled.
 // Otherwise (fp32, the generated sinusoid, other widths) the rows go through registers, two
@@ -98,56 +99,124 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm
 
 // Epilogue: the lane holds y[m][n .. n + 3] of every 16 x 16 product tile (rows mb + 16 fm + m16,
 // features nb + 16 fn + 4 grp); plain rows, or the Q/K/V split with the K/V rows appended into
-// the pages.
+// the pages. Two neighbouring tiles go out together: after one row swap between lane groups
+// (v_permlane16_swap: groups 0 <-> 1 and 2 <-> 3), every lane holds 8 consecutive features of
+// its row - tile fn's [0, 8) or [8, 16) for groups 0 and 2, tile fn + 1's for groups 1 and 3 -
+// stored with one 16-byte write (two in fp32), so a row's 32 features leave as 64 (128)
+// contiguous bytes. V (transposed pages: consecutive features are S slots apart) is written
+// element by element.
+
+// 8 consecutive features: v[0..3] of tile A and of tile B before the swap, the lane's 8 after
+template <typename T>
+__device__ __forceinline__ void swap_pair(const float (&va)[4], const float (&vb)[4], T* dst);
+template <>
+__device__ __forceinline__ void swap_pair<bf16>(const float (&va)[4], const float (&vb)[4], bf16* dst) {
+  uint32_t a[2], b[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    bf16x2_t pa{(bf16)va[2 * h], (bf16)va[2 * h + 1]};
+    bf16x2_t pb{(bf16)vb[2 * h], (bf16)vb[2 * h + 1]};
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, pa),
+                                                    __builtin_bit_cast(uint32_t, pb), false, false);
+    a[h] = r[0];
+    b[h] = r[1];
+  }
+  *reinterpret_cast<u32x4*>(dst) = u32x4{a[0], a[1], b[0], b[1]};
+}
+template <>
+__device__ __forceinline__ void swap_pair<float>(const float (&va)[4], const float (&vb)[4], float* dst) {
+  float a[4], b[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(va[e]), __float_as_uint(vb[e]),
+                                                    false, false);
+    a[e] = __uint_as_float(r[0]);
+    b[e] = __uint_as_float(r[1]);
+  }
+  *reinterpret_cast<floatx4*>(dst) = floatx4{a[0], a[1], a[2], a[3]};
+  *reinterpret_cast<floatx4*>(dst + 4) = floatx4{b[0], b[1], b[2], b[3]};
+}
+
 template <typename T, int kEpi, int FM, int FN>
 __device__ __forceinline__ void store_tiles(const GemmArgs<T>& a, const floatx4 (&acc)[FN][FM],
                                             int mb, int nb, int m16, int grp) {
+  static_assert(FN % 2 == 0, "tiles go out in pairs");
+  // this lane's 8 features after the swap, relative to the pair's first column
+  const int sw_col = 16 * (grp & 1) + 8 * (grp >> 1);
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const int n = nb + fn * 16 + 4 * grp;
-    if (n >= a.N) continue;
-    float bias[4] = {0.f, 0.f, 0.f, 0.f};
-    if (a.bias) {
+  for (int fp = 0; fp < FN; fp += 2) {
+    const int np = nb + fp * 16;         // the pair's first feature (a multiple of 32)
+    if (np >= a.N) continue;             // (N is a multiple of 16: a pair is in or out whole...
+    const bool second = np + 16 < a.N;   // ...but its second tile may be past N)
+    float bias[2][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bias[e] = to_f(a.bias[n + e]);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = np + 16 * h + 4 * grp + e;
+        bias[h][e] = (a.bias && n < a.N) ? to_f(a.bias[n]) : 0.f;
+      }
+    // the region of the pair (the Q/K/V boundaries are multiples of 32)
+    const bool is_v = kEpi == kQKV && np >= a.HD + a.Hk * a.D;
+    const bool is_k = kEpi == kQKV && !is_v && np >= a.HD;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int m = mb + fm * 16 + m16;
-      if (m >= a.M) continue;
-      float v[4];
+      float va[4], vb[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[fn][fm][e] + bias[e];
-      if constexpr (kEpi == kPlain) {
-        store4<T>(a.y + (size_t)m * a.N + n, v);
-      } else {
-        // Q/K/V: q columns [0, H D), then K [H D, H D + Hk D), then V; a 16-column product tile
-        // lies inside one of them (H D and Hk D are multiples of 32)
-        if (n < a.HD) {
-          store4<T>(a.y + (size_t)m * a.HD + n, v);
-          continue;
+      for (int e = 0; e < 4; ++e) {
+        va[e] = acc[fp][fm][e] + bias[0][e];
+        vb[e] = acc[fp + 1][fm][e] + bias[1][e];
+      }
+      if (!is_v) {
+        // every lane takes part in the swap (rows past M included); only the store is masked
+        T tmp[8];
+        swap_pair<T>(va, vb, tmp);
+        const int n = np + sw_col;
+        if (m >= a.M || (!second && n >= np + 16)) continue;
+        T* dst;
+        if constexpr (kEpi == kPlain) {
+          dst = a.y + (size_t)m * a.N + n;
+        } else if (!is_k) {
+          dst = a.y + (size_t)m * a.HD + n;
+        } else {
+          const int b = m / a.C;
+          const int t = m - b * a.C;
+          const int n_real = a.lens ? clampi(a.lens[b], 0, a.C) : a.C;
+          if (t >= n_real) continue;   // frames past the stream's real ones are not appended
+          const int start = a.ws ? max(a.ws[b], 0) / a.S * a.S : 0;
+          const int frame = start + clampi(a.cs[b], 0, a.max_cache) + t;
+          const int blk = clampi(a.bt[(size_t)b * a.max_blocks + (frame / a.S) % a.max_blocks], 0,
+                                 a.num_blocks - 1);
+          const int slot = frame % a.S;
+          const int kv = n - a.HD;
+          const int g = kv / a.D, d = kv - g * a.D;
+          // K pages in 32-dim column blocks: dim d of slot s at ((d / 32) S + s) 32 + d % 32
+          dst = a.k_pool + ((size_t)blk * a.Hk + g) * a.S * a.D + ((d >> 5) * a.S + slot) * 32 + (d & 31);
         }
+#pragma unroll
+        for (int e = 0; e < 8; e += 16 / (int)sizeof(T))
+          *reinterpret_cast<u32x4*>(dst + e) = *reinterpret_cast<const u32x4*>(tmp + e);
+      } else {
+        if (m >= a.M) continue;
         const int b = m / a.C;
         const int t = m - b * a.C;
         const int n_real = a.lens ? clampi(a.lens[b], 0, a.C) : a.C;
-        if (t >= n_real) continue;   // frames past the stream's real ones are not appended
+        if (t >= n_real) continue;
         const int start = a.ws ? max(a.ws[b], 0) / a.S * a.S : 0;
         const int frame = start + clampi(a.cs[b], 0, a.max_cache) + t;
         const int blk = clampi(a.bt[(size_t)b * a.max_blocks + (frame / a.S) % a.max_blocks], 0,
                                a.num_blocks - 1);
         const int slot = frame % a.S;
-        const int kv = n - a.HD;
         const int hkd = a.Hk * a.D;
-        if (kv < hkd) {
-          const int g = kv / a.D, d = kv - (kv / a.D) * a.D;
-          // K pages in 32-dim column blocks: dim d of slot s at ((d / 32) S + s) 32 + d % 32
-          store4<T>(a.k_pool + ((size_t)blk * a.Hk + g) * a.S * a.D +
-                        ((d >> 5) * a.S + slot) * 32 + (d & 31), v);
-        } else {
-          const int g = (kv - hkd) / a.D, d = (kv - hkd) - ((kv - hkd) / a.D) * a.D;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1 && !second) continue;
+          const int kv = np + 16 * h + 4 * grp - a.HD - hkd;
+          const int g = kv / a.D, d = kv - g * a.D;
           T* col = a.v_pool + (((size_t)blk * a.Hk + g) * a.D + d) * a.S + slot;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) col[(size_t)e * a.S] = from_f<T>(v[e]);
+          for (int e = 0; e < 4; ++e) col[(size_t)e * a.S] = from_f<T>(h ? vb[e] : va[e]);
         }
       }
     }
@@ -282,7 +351,10 @@ gemm_kernel(GemmArgs<T> a) {
 
 // ---- bf16, direct global -> LDS staging, NK stages unrolled ------------------------------------
 
-__device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+constexpr int kDK = 64;   // contraction depth of one directly loaded stage: a row's whole 128-byte
+                          // line per request
+
+__device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
 
 // Wait until at most N of this wave's direct loads are in flight and its LDS accesses are done
 // (s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at 7, lgkmcnt 11:8 at 0).
@@ -297,15 +369,15 @@ __global__ void __launch_bounds__(kThreads)
 gemm_dma_kernel(GemmArgs<bf16> a) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int NBX = BM / 16, NB = (BM + BN) / 16;   // 1 KB blocks per stage (x, then W)
-  constexpr int DPW = NB / 4;                          // direct loads per wave per stage
-  constexpr int SLOT = NB * 512;                       // bf16 elements of one ring slot
+  constexpr int NBX = BM / 8, NB = (BM + BN) / 8;   // 1 KB blocks (8 rows x 64 dims) per stage
+  constexpr int DPW = NB / 4;                        // direct loads per wave per stage
+  constexpr int SLOT = NB * 512;                     // bf16 elements of one ring slot
   static_assert(DPW * 4 == NB, "blocks split evenly over the waves");
 
+  // a ring of 3 stages (2 in flight), each slot its own array
   __shared__ __align__(16) bf16 s0[SLOT];
   __shared__ __align__(16) bf16 s1[SLOT];
   __shared__ __align__(16) bf16 s2[SLOT];
-  __shared__ __align__(16) bf16 s3[SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -317,36 +389,38 @@ gemm_dma_kernel(GemmArgs<bf16> a) {
   tile_of(blockIdx.x, (a.M + BM - 1) / BM, a.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // this wave's blocks: lane l loads row l / 4 of the block, the chunk that belongs at chunk
-  // position l % 4 (rows past M or N read the last row; their results are never stored)
+  // this wave's blocks: lane l loads row l / 8 of the block, the 16-byte chunk that belongs at
+  // chunk position l % 8 (rows past M or N read the last row; their results are never stored)
   const bf16* src[DPW];
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int blk = wave * DPW + i;
-    const int r = lane >> 2;
-    const int c = (lane & 3) ^ dma_swz(r);
+    const int r = 8 * blk + (lane >> 3);               // row of the stage (x rows, then W rows)
+    const int c = (lane & 7) ^ dma_swz(r & 15);
     if (blk < NBX) {
-      src[i] = a.x + (size_t)min(m0 + 16 * blk + r, a.M - 1) * a.K + 8 * c;
+      src[i] = a.x + (size_t)min(m0 + r, a.M - 1) * a.K + 8 * c;
     } else {
-      src[i] = a.w + (size_t)min(n0 + 16 * (blk - NBX) + r, a.N - 1) * a.K + 8 * c;
+      src[i] = a.w + (size_t)min(n0 + r - BM, a.N - 1) * a.K + 8 * c;
     }
   }
   auto slot = [&](int k) -> bf16* {
-    switch (k & 3) {
+    switch (k % 3) {
       case 0: return s0;
       case 1: return s1;
-      case 2: return s2;
-      default: return s3;
+      default: return s2;
     }
   };
   auto issue = [&](int s) {
     bf16* base = slot(s);
 #pragma unroll
-    for (int i = 0; i < DPW; ++i)
-      load_lds16(src[i] + kBK * s, base + (wave * DPW + i) * 512);
+    for (int i = 0; i < DPW; ++i) load_lds16(src[i] + kDK * s, base + (wave * DPW + i) * 512);
   };
-  // fragment reads: row m16 of a block, the lane's 16-byte chunk grp at its swizzled position
-  const int fo = m16 * 32 + 8 * (grp ^ dma_swz(m16));
+  // fragment reads: row m16 of a 16-row group (block m16 / 8, row m16 % 8 of it), the 16-byte
+  // chunk 4 kk + grp of contraction half kk at its swizzled position
+  int fo[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    fo[kk] = (m16 >> 3) * 512 + (m16 & 7) * 64 + 8 * ((4 * kk + grp) ^ dma_swz(m16));
 
   floatx4 acc[FN][FM];
 #pragma unroll
@@ -354,31 +428,33 @@ gemm_dma_kernel(GemmArgs<bf16> a) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int s = 0; s < 3 && s < NK; ++s) issue(s);
+  issue(0);
+  if (NK > 1) issue(1);
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
-    // stage s in LDS for every wave (this wave's loads: all but the two later stages'), and
-    // every wave done reading the slot stage s + 3 refills
-    if (s + 2 < NK) wait_stage<2 * DPW>();
-    else if (s + 1 < NK) wait_stage<DPW>();
+    // stage s in LDS for every wave (this wave's loads: all but the next stage's), and every
+    // wave done reading the slot stage s + 2 refills
+    if (s + 1 < NK) wait_stage<DPW>();
     else wait_stage<0>();
     // (the empty asm statements keep the compiler from moving LDS accesses across the barrier,
     // which it would otherwise treat as touching no memory)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (s + 3 < NK) issue(s + 3);
+    if (s + 2 < NK) issue(s + 2);
     const bf16* cur = slot(s);
-    bf16x8 xf[FM], wf[FN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) xf[fm] = load8(cur + ((wm * WM) / 16 + fm) * 512 + fo);
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 xf[FM], wf[FN];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) wf[fn] = load8(cur + (NBX + (wn * WN) / 16 + fn) * 512 + fo);
+      for (int fm = 0; fm < FM; ++fm) xf[fm] = load8(cur + ((wm * WM) / 16 + fm) * 1024 + fo[kk]);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
+      for (int fn = 0; fn < FN; ++fn) wf[fn] = load8(cur + (BM / 16 + (wn * WN) / 16 + fn) * 1024 + fo[kk]);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mma(wf[fn], xf[fm], acc[fn][fm]);
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mma(wf[fn], xf[fm], acc[fn][fm]);
+    }
   }
   store_tiles<bf16, kEpi, FM, FN>(a, acc, m0 + wm * WM, n0 + wn * WN, m16, grp);
 }
@@ -402,10 +478,10 @@ inline int pick_tile(int M, int N) {
 
 template <int BM, int BN, int kEpi>
 hipError_t launch_dma(GemmArgs<bf16>& a, dim3 grid, hipStream_t stream) {
-  switch (a.K / kBK) {
+  switch (a.K / kDK) {
+    case 4: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, kEpi, 4>), grid, dim3(kThreads), 0, stream, a); break;
     case 8: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, kEpi, 8>), grid, dim3(kThreads), 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, kEpi, 16>), grid, dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, kEpi, 32>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, kEpi, 16>), grid, dim3(kThreads), 0, stream, a); break;
   }
   return hipGetLastError();
 }
