@@ -57,6 +57,11 @@ def assert_within(got, ref, tol, what):
 LINEAR = {
     "tiny": (3, 16, 32),
     "ragged_rows_partial_tile": (1000, 48, 64),
+    # the directly loaded bf16 path (K of 256 / 512 / 1024), with a half pair of 16 features
+    # at the end (N = 16 mod 32) and ragged rows
+    "direct_k256_half_pair": (1000, 48, 256),
+    "direct_k1024_half_pair": (77, 1040, 1024),
+    "direct_k512_one_row": (1, 512, 512),
     "dmodel256_qkv_shape": (1024, 768, 256),
     "dmodel512_qkv_shape_large_tiles": (4096, 1536, 512),
     "out_proj_dmodel512": (4096, 512, 512),
@@ -96,6 +101,8 @@ QKV = {
     "fp32_ragged": dict(B=3, H=2, Hk=2, D=64, C=16, S=16, caches=[0, 37, 100], dm=128, dtype=F32),
     "gqa_short_chunk": dict(B=4, H=4, Hk=2, D=64, C=5, S=8, caches=[3, 0, 64, 11], dm=256, dtype=BF16),
     "dmodel256_cohort": dict(B=64, H=4, Hk=4, D=64, C=16, S=16, caches=[256] * 64, dm=256, dtype=BF16),
+    # the d_model 512 cohort at full size, in the launch configuration the projection bench times
+    "dmodel512_cohort": dict(B=256, H=8, Hk=8, D=64, C=16, S=16, caches=[512] * 256, dm=512, dtype=BF16),
 }
 
 
@@ -205,9 +212,18 @@ def _pos_bound(w64, pos, dtype, d_model, ref):
 
 
 @pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "fp32"])
-@pytest.mark.parametrize("case", ["txl_shared_dmodel256", "txl_shared_dmodel512", "wenet_per_stream"])
+@pytest.mark.parametrize("case", ["txl_shared_dmodel256", "txl_shared_dmodel512", "wenet_per_stream",
+                                  "dmodel1024_ragged_tables"])
 def test_rel_pos_projection_parity(case, dtype):
-    if case.startswith("txl"):
+    if case == "dmodel1024_ragged_tables":
+        # tables whose rows do not fill whole 64-row tiles, crossing table boundaries in a tile
+        dm, rows = 1024, 37
+        w, _ = linear_weights(512, dm, seed=13, dtype=dtype, device=DEV, bias=False)
+        starts = np.array([40, -7, 3000])
+        st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+        got = pkc.rel_pos_projection(w, rows, pos_start=st, pos_step=-1)
+        step = -1
+    elif case.startswith("txl"):
         dm = 256 if case.endswith("256") else 512
         center = 271 if dm == 256 else 527          # max cache + C - 1 of the streaming workloads
         w, _ = linear_weights(dm, dm, seed=11, dtype=dtype, device=DEV, bias=False)
