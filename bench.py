@@ -544,6 +544,23 @@ def main():
         kernel_ms = ms_step / n_layers
         kernel_src = "graph replay, timed-region time / kernel launches"
         mode = "graph"
+        # the same chain launched layer by layer from the host, with HIP events around each
+        # launch: reported beside the replay figure, labelled, never as `value`
+        n_eager = min(args.steps, 50)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)] for _ in range(n_eager)]
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_eager):
+            step(i, ev[i])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        durs = [ev[i][2 * l].elapsed_time(ev[i][2 * l + 1]) for i in range(n_eager) for l in range(n_layers)]
+        eager = {"steps": n_eager, "ms_per_step": e0.elapsed_time(e1) / n_eager,
+                 "kernel_us_mean": 1e3 * sum(durs) / len(durs),
+                 "kernel_us_median": 1e3 * float(np.median(durs)),
+                 "timed_from": "eager launches, HIP events around each launch"}
 
     units = (B - args.pad_lanes) * H * n_layers          # real streams' chunk·heads
     value = units / (ms_step / 1e3)
@@ -589,6 +606,8 @@ def main():
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
     }
+    if mode == "graph":
+        result["eager"] = eager
     if lens_mode:
         lens0 = co0.chunk_lens.cpu().numpy()
         result["config"]["workload"] += (f"; {args.pad_lanes} padding lanes, "
