@@ -177,6 +177,48 @@ def cpu_baseline(co, min_seconds):
                        f"append + attention in float64 numpy, {el:.1f} s")
 
 
+def _oracle_slice(args):
+    """Child process: the oracle (append + attention) on a slice of the cohort's streams, repeated
+    for at least ``seconds``; returns (repetitions, elapsed). Imports no GPU code."""
+    (k_pool, v_pool, k_new, v_new, bt, cs, q, pos, u, w, per_row, lens, seconds) = args
+    import time as _t
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        pass
+    import oracle
+    reps, t0 = 0, _t.perf_counter()
+    while True:
+        kp, vp = oracle.paged_kv_append(k_pool, v_pool, k_new, v_new, bt, cs, lens)
+        oracle.chunk_relpos_attn(q, kp, vp, bt, cs, pos, u, w, per_row_pos=per_row, chunk_lens=lens)
+        reps += 1
+        el = _t.perf_counter() - t0
+        if el >= seconds:
+            return reps, el
+
+
+def cpu_baseline_all_cores(co, seconds, workers):
+    """The same oracle on every host core: the cohort's streams split into ``workers`` slices, one
+    child process (started fresh, one BLAS thread) per slice; chunk·heads per second summed."""
+    import multiprocessing as mp
+    host = lambda t: t.detach().cpu().double().numpy()
+    B, C, H, D = co.q.shape
+    bt, cs = co.block_tables.cpu().numpy(), co.cache_seqlens.cpu().numpy()
+    kp, vp, kn, vn = host(co.k_pool), host(co.v_pool), host(co.k_new), host(co.v_new)
+    q, pos, u, w = host(co.q), host(co.pos), host(co.pos_bias_u), host(co.pos_bias_v)
+    groups = [g for g in np.array_split(np.arange(B), workers) if len(g)]
+    jobs = [(kp, vp, kn[g], vn[g], bt[g], cs[g], q[g], pos[g] if co.per_row_pos else pos, u, w,
+             co.per_row_pos, None, seconds) for g in groups]
+    with mp.get_context("spawn").Pool(len(groups)) as pool:
+        out = pool.map(_oracle_slice, jobs)
+    rate = sum(len(g) * H * r / el for g, (r, el) in zip(groups, out))
+    return dict(value=rate, unit="chunk·heads/s", cores=len(groups), kind="oracle",
+                sample=f"one layer of the timed cohort (B={B}, H={H}) split over {len(groups)} "
+                       f"processes by streams, each the float64 numpy oracle (append + attention) "
+                       f"repeated for {seconds:.0f} s on one thread")
+
+
 def visible_pairs(L, chunk=0, left=0):
     """(query, key) pairs of one utterance: all L^2, or under the chunked_limited mask the keys of
     each query's own chunk and of the ``left`` chunks before it."""
@@ -617,6 +659,12 @@ def main():
                                 short_windows=int(((lens0 > 0) & (lens0 < C)).sum()))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(co0, args.cpu_seconds)
+        if not lens_mode and not args.per_key:
+            # host cores this process may run on (the machine's CPU share, at most 16)
+            n_cores = min(len(os.sched_getaffinity(0)), 16)
+            if n_cores > 1:
+                result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(
+                    co0, args.cpu_seconds, n_cores)
     print(json.dumps(result), flush=True)
 
 
