@@ -586,6 +586,19 @@ def main():
         kernel_ms = ms_step / n_layers
         kernel_src = "graph replay, timed-region time / kernel launches"
         mode = "graph"
+        # the spread of single steps: a separate pass with events around every replay
+        n_pct = min(args.steps, 100)
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_pct)]
+        for i, (a0, a1) in enumerate(pev):
+            a0.record(stream)
+            graphs[i % len(graphs)].replay()
+            a1.record(stream)
+        torch.cuda.synchronize()
+        per_step = np.array([a0.elapsed_time(a1) for a0, a1 in pev])
+        step_pct = {"steps": n_pct, "p10": float(np.percentile(per_step, 10)),
+                    "p50": float(np.percentile(per_step, 50)),
+                    "p90": float(np.percentile(per_step, 90))}
         # the same chain launched layer by layer from the host, with HIP events around each
         # launch: reported beside the replay figure, labelled, never as `value`
         n_eager = min(args.steps, 50)
@@ -649,6 +662,7 @@ def main():
         },
     }
     if mode == "graph":
+        result["step_ms_percentiles"] = step_pct
         result["eager"] = eager
     if lens_mode:
         lens0 = co0.chunk_lens.cpu().numpy()
