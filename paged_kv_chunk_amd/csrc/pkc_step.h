@@ -132,7 +132,7 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
 // stay between the two wave barriers of the shift, which keeps the register live ranges of the
 // hot loop short. kMask: keys at or past valid_keys are excluded (the same keys for every query
 // column, and never all of a step's keys).
-template <typename T, bool kMask>
+template <typename T, bool kMask, bool kShiftFirst = false>
 __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>::type (&kf)[2][2],
                                              const typename Frag<T>::type (&vf)[4],
                                              const typename Frag<T>::type (&qu)[2],
@@ -142,27 +142,39 @@ __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>
   const int lane = threadIdx.x & 63;
   const int m16 = lane & 15;
   const int grp = lane >> 4;
-  floatx4 sc[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    sc[tt] = mma(kf[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
-    sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
-  }
   // Relative shift through LDS: G^T[row][query] -> s_g[query * kSkewPitch + row]; the lane then
-  // reads its 8 keys' values from its own query column, shifted by 15 - query.
+  // reads its 8 keys' values from its own query column, shifted by 15 - query. kShiftFirst: the
+  // shift comes first and its values start the content products' accumulation (no separate
+  // add, a longer dependency chain); otherwise the products overlap the LDS round trip.
+  floatx4 sc[2];
+  if constexpr (!kShiftFirst) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt] = mma(kf[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
+    }
+  }
   float* colw = s_g + m16 * kSkewPitch + 4 * grp;
   *reinterpret_cast<floatx4*>(colw) = g0;
   *reinterpret_cast<floatx4*>(colw + 16) = g1;
   *reinterpret_cast<floatx4*>(colw + 32) = g2;
   __builtin_amdgcn_wave_barrier();
   const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * grp;
+  if constexpr (kShiftFirst) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt] = mma(kf[tt][0], qu[0],
+                   floatx4{colr[4 * tt], colr[4 * tt + 1], colr[4 * tt + 2], colr[4 * tt + 3]});
+      sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
+    }
+  }
   float x[2][4];
   float mx = -INFINITY;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float v = sc[tt][e] + colr[4 * tt + e];
+      float v = kShiftFirst ? sc[tt][e] : sc[tt][e] + colr[4 * tt + e];
       if (kMask) v = (8 * grp + 4 * tt + e < valid_keys) ? v : -INFINITY;
       x[tt][e] = v;
       mx = fmaxf(mx, v);

@@ -260,9 +260,9 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       skew_scores<T>(kf, qu, g_prev, g1, g2, s_g, x);
       softmax_pv<T, true>(st, x, vf, k_lo_q - j0, k_hi_q - j0);
     } else if (j0 + 32 <= L) {
-      step_compute<T, false>(st, kf, vf, qu, g_prev, g1, g2, s_g, 32);
+      step_compute<T, false, true>(st, kf, vf, qu, g_prev, g1, g2, s_g, 32);
     } else {
-      step_compute<T, true>(st, kf, vf, qu, g_prev, g1, g2, s_g, L - j0);
+      step_compute<T, true, true>(st, kf, vf, qu, g_prev, g1, g2, s_g, L - j0);
     }
     g_prev = g2;
     if (step + 1 < nsteps) stash(nxt, s_kv + ((step + 1) & 1) * TILE, j0 + 32);
