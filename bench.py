@@ -478,13 +478,13 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the path has "
-              "no cross-GPU exchange and this build measures one GPU's share.", file=sys.stderr)
+              "no cross-GPU exchange; the figure is one GPU's throughput.", file=sys.stderr)
         sys.exit(2)
 
     global torch
     import torch
     import paged_kv_chunk_amd as pkc
-    from synth import CONFIGS
+    from synth import WORKLOADS
 
     if args.copy_mib:
         n = args.copy_mib << 20
@@ -505,7 +505,7 @@ def main():
                           "read_plus_write_GBps": 2 * n / (ms / 1e3) / 1e9}), flush=True)
         return
 
-    cfg = CONFIGS[args.config]
+    cfg = WORKLOADS[args.config]
     if cfg["kind"] == "varlen":
         return bench_varlen(args, cfg, pkc)
     if args.proj:

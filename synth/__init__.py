@@ -6,7 +6,7 @@ contains none of the path's arithmetic and imports neither the oracle nor the HI
 """
 
 from .cohorts import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     ChunkCohort,
     VarlenCohort,
     make_chunk_cohort,

@@ -247,7 +247,7 @@ def make_varlen_cohort(lengths, H, D, *, Hk=None, dtype=BF16, seed=0, device="cp
 
 
 # The five named workloads: Conformer-shaped streaming cohorts and one packed offline batch.
-CONFIGS = {
+WORKLOADS = {
     0: dict(kind="chunk", name="tiny fp32 oracle check", B=2, H=4, D=64, C=16, block_size=16,
             cache=64, dtype=F32, num_blocks=32, max_blocks_per_seq=8, n_layers=1),
     1: dict(kind="chunk", name="d_model 256 streaming cohort", B=64, H=4, D=64, C=16,
@@ -274,7 +274,7 @@ def ragged_cache(B, cache_max, new_fraction, seed, step=16):
 
 def make_config(index, layer=0, seed=0, device="cpu"):
     """Inputs of one layer of a named workload."""
-    cfg = CONFIGS[index]
+    cfg = WORKLOADS[index]
     s = 1_000_003 * seed + 1009 * index + 7919 * layer
     if cfg["kind"] == "varlen":
         gen = torch.Generator().manual_seed(s + 3)

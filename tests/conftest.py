@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped, not failed, where no GPU is visible; on a GPU machine they must run.
+    # GPU tests are skipped, not failed, where no GPU is visible; where one is, they must run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()

@@ -16,7 +16,7 @@ import torch
 import oracle
 import oracle.relpos_attn as orc
 from synth import descending_table, embed_distances, make_chunk_cohort, make_varlen_cohort, relpos_projection
-from synth import CONFIGS, make_config
+from synth import WORKLOADS, make_config
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 F64 = torch.float64
@@ -381,8 +381,8 @@ def test_workload_geometry_matches_the_pages():
     for fw in g["fixed_window"]:
         pages = (fw["window"] + fw["chunk"] + 16 - 1) // 16
         assert pages == fw["pages_per_stream"]
-    assert CONFIGS[1]["block_size"] == g["engine_defaults"]["block_size_frames"]
-    assert CONFIGS[1]["max_blocks_per_seq"] == g["engine_defaults"]["max_blocks_per_seq"]
+    assert WORKLOADS[1]["block_size"] == g["engine_defaults"]["block_size_frames"]
+    assert WORKLOADS[1]["max_blocks_per_seq"] == g["engine_defaults"]["max_blocks_per_seq"]
     co1 = make_chunk_cohort(2, 4, 64, 16, 16, [256, 256], dtype=torch.bfloat16)
     assert co1.meta["pages"] == [17, 17]
 
