@@ -258,6 +258,11 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
     return PKC_ERR_SHAPE;
   if (mask_chunk < 0 || mask_left_chunks < 0) return PKC_ERR_SHAPE;
   if (head_dim != 64) return PKC_ERR_UNSUPPORTED;
+  // (the kernel addresses an utterance's rows by 32-bit byte offsets from its first row; its
+  // table spans 2 max_seqlen rows)
+  if ((int64_t)2 * max_seqlen * (n_head > n_kv_head ? n_head : n_kv_head) * head_dim *
+          (dtype == PKC_BF16 ? 2 : 4) >= (int64_t)1 << 31)
+    return PKC_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pos) ||
       !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))
     return PKC_ERR_ALIGN;

@@ -55,7 +55,7 @@ struct VarlenArgs {
   const T* u;
   const T* w;
   T* out;
-  int H, Hk, qtiles, total;
+  int H, Hk, qtiles, total, maxlen;
   int chunk, left;            // chunked_limited mask (kLimited)
   float scale_log2;
 };
@@ -89,14 +89,19 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   const int qt = id % a.qtiles;
   const int s = id / a.qtiles;
   const int lo = clampi(a.cu[s], 0, a.total);
-  const int L = clampi(a.cu[s + 1], lo, a.total) - lo;
+  // (an utterance longer than max_seqlen is cut to max_seqlen frames: the host bounds every byte
+  // offset from an utterance's first row by 2 max_seqlen rows, so 32-bit offsets hold)
+  const int L = min(clampi(a.cu[s + 1], lo, a.total) - lo, a.maxlen);
   if (qt * kQTile >= L) return;  // uniform over the workgroup
   const int hk = h / (a.H / a.Hk);
   const size_t krow = (size_t)a.Hk * kD;      // elements between consecutive frames of k / v
-  const T* kseg = a.k + (size_t)lo * krow + (size_t)hk * kD;
-  const T* vseg = a.v + (size_t)lo * krow + (size_t)hk * kD;
   const size_t prow = (size_t)a.H * kD;
-  const T* ptab = a.pos + (size_t)(2 * lo) * prow + (size_t)h * kD;
+  // uniform segment bases; per-lane 32-bit byte offsets from them (one offset serves K and V)
+  const char* kseg = reinterpret_cast<const char*>(a.k + (size_t)lo * krow + (size_t)hk * kD);
+  const char* vseg = reinterpret_cast<const char*>(a.v + (size_t)lo * krow + (size_t)hk * kD);
+  const char* ptab = reinterpret_cast<const char*>(a.pos + (size_t)(2 * lo) * prow + (size_t)h * kD);
+  const uint32_t krow_b = (uint32_t)(krow * sizeof(T));
+  const uint32_t prow_b = (uint32_t)(prow * sizeof(T));
   const int q0 = qt * kQTile + 16 * wave;       // this wave's first query
   const int R0 = L - 1;                         // table row of (i, j) is R0 + j - i
   const int rlo = 0, rhi = 2 * L - 2;
@@ -126,7 +131,10 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   // of a step never hold a row that step still reads, and a row is overwritten only after the
   // barrier that ends its last use.
   const int xw = R0 - (qt * kQTile + kQTile - 1);
-  auto band_src = [&](int x) { return ptab + (size_t)(uint32_t)clampi(x, rlo, rhi) * prow; };
+  // (the row and column offsets are summed in 32 bits first: one offset from the uniform base)
+  auto band_src = [&](int x, uint32_t col_b) {
+    return ptab + ((uint32_t)clampi(x, rlo, rhi) * prow_b + col_b);
+  };
   auto band_slot = [&](int x) { return s_band + (x & (kRing - 1)) * KP; };
 
   // cooperative staging of one 32-key step: 32 K rows, the same 32 V rows and the 32 band rows
@@ -141,10 +149,10 @@ varlen_attn_kernel(VarlenArgs<T> a) {
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
-      const size_t off = (size_t)min(j0 + idx / NV, L - 1) * krow + (idx % NV) * VEC;
+      const uint32_t off = (uint32_t)min(j0 + idx / NV, L - 1) * krow_b + (idx % NV) * 16u;
       rr.k[it] = *reinterpret_cast<const u32x4*>(kseg + off);
       rr.v[it] = *reinterpret_cast<const u32x4*>(vseg + off);
-      rr.b[it] = *reinterpret_cast<const u32x4*>(band_src(xw + j0 + 64 + idx / NV) + (idx % NV) * VEC);
+      rr.b[it] = *reinterpret_cast<const u32x4*>(band_src(xw + j0 + 64 + idx / NV, (idx % NV) * 16u));
     }
   };
   auto stash = [&](const Rows& rr, T* st, int j0) {
@@ -210,7 +218,8 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       const int idx = tid + kThreads * it;
       const int x = xw + J + 32 * part + idx / NV;
       const int dv = (idx % NV) * VEC;
-      *reinterpret_cast<u32x4*>(band_slot(x) + dv) = *reinterpret_cast<const u32x4*>(band_src(x) + dv);
+      *reinterpret_cast<u32x4*>(band_slot(x) + dv) =
+          *reinterpret_cast<const u32x4*>(band_src(x, (idx % NV) * 16u));
     }
   stash(ra, s_kv, J);
   __syncthreads();
@@ -265,13 +274,21 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       step_compute<T, true, true>(st, kf, vf, qu, g_prev, g1, g2, s_g, L - j0);
     }
     g_prev = g2;
-    if (step + 1 < nsteps) stash(nxt, s_kv + ((step + 1) & 1) * TILE, j0 + 32);
+    // (unconditional, also after the last step: the rows are clamped re-reads going to a buffer
+    // and ring slots no later read uses, and every path back to the loop head then has the same
+    // loads in flight - a path with one more pending load made the compiler drain them all at
+    // the head, which cut the look-ahead to one step)
+    stash(nxt, s_kv + ((step + 1) & 1) * TILE, j0 + 32);
     __syncthreads();
   };
-  for (int step = 0; step < nsteps; step += 2) {
+  // steps in pairs (the two register sets swap roles), an odd last step after the loop: the
+  // loop has one exit, so no path reaches its head with the other set's loads still pending
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
     do_step(step, rb, ra);
-    if (step + 1 < nsteps) do_step(step + 1, ra, rb);
+    do_step(step + 1, ra, rb);
   }
+  if (step < nsteps) do_step(step, rb, ra);
 
   // finish: every wave owns its 16 queries
   st.l = column_sum(st.l);
@@ -301,6 +318,7 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
   a.Hk = p.n_kv_head;
   a.qtiles = (p.max_seqlen + kQTile - 1) / kQTile;
   a.total = p.total;
+  a.maxlen = p.max_seqlen;
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.chunk = p.mask_chunk;

@@ -139,6 +139,10 @@ def test_fused_validation(lib):
     (dict(S=0), SHAPE), (dict(H=6, Hk=4), SHAPE), (dict(max_len=101), SHAPE), (dict(D=12), SHAPE),
     (dict(D=128), UNSUP), (dict(v=BAD), ALIGN),
     (dict(chunk=-1), SHAPE), (dict(chunk=4, left=-2), SHAPE),
+    # an utterance's rows are addressed by 32-bit byte offsets: 2 max_seqlen rows of H D elements
+    # must stay under 2^31 bytes
+    (dict(total=2_000_000, max_len=2_000_000), UNSUP),
+    (dict(dtype=0, total=1_100_000, max_len=1_100_000, H=4, Hk=4), UNSUP),
 ])
 def test_varlen_validation(lib, kw, status):
     assert varlen(lib, **kw) == status
