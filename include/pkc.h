@@ -253,14 +253,16 @@ pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,
  * 2 L - 1 rows centred at L - 1 starting at row 2 cu_seqlens[s] of pos [2 total_frames, H, D]
  * (2 L rows are reserved per utterance, the last unused). Frames attend only within their own
  * utterance; empty utterances are allowed. The kernel clamps cu_seqlens into [0, total_frames],
- * so malformed offsets give unspecified values but no out-of-bounds access; frames of an
- * utterance longer than max_seqlen past max_seqlen are not written.
+ * so malformed offsets give unspecified values but no out-of-bounds access; an utterance longer
+ * than max_seqlen is cut to its first max_seqlen frames (frames past them are not written; the
+ * values of the rest are then unspecified).
  * mask_chunk > 0 applies the chunked_limited mask [MOD nem] inside every utterance: frame i (counted
  * from the utterance's first frame) sees only the frames of chunks i / mask_chunk -
  * mask_left_chunks ... i / mask_chunk, and each 64-frame query block computes only over the keys
  * its frames can see (its own frames plus the trained history). mask_chunk = 0: full context.
- * Errors: as above; a negative mask_chunk or mask_left_chunks -> PKC_ERR_SHAPE; head_dim != 64
- * -> PKC_ERR_UNSUPPORTED.
+ * Errors: as above; a negative mask_chunk or mask_left_chunks -> PKC_ERR_SHAPE; head_dim != 64,
+ * or 2 max_seqlen max(H, Hk) head_dim element bytes at or past 2^31 (an utterance's rows are
+ * addressed by 32-bit byte offsets) -> PKC_ERR_UNSUPPORTED.
  */
 pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,
                                      const int32_t* cu_seqlens, int32_t num_seqs,

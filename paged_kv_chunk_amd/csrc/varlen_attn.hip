@@ -38,12 +38,21 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQTile = 16 * kWaves;     // queries per workgroup
 
-template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // K tile row pitch
+template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // band / fp32 K row pitch
+template <typename T> constexpr bool kSwK = sizeof(T) == 2;            // swizzled bf16 K rows
 template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch (fp32)
 template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
 constexpr int kRing = 128;   // rows of the band ring (a step reads 80 and stages the next 32)
 // swizzle of the 4-dimension chunks of natural V row r (bf16)
 __device__ __forceinline__ int v_swz(int r) { return 4 * ((r & 3) ^ ((r >> 3) & 1)); }
+// bf16 K rows are 128 bytes, unpadded, with their eight 16-byte chunks permuted by chunk ^ k_swz(r).
+// The 16 rows one 16-lane read of a key tile touches, 8 a + 4 tt + b (a, b < 4), then sit on 16
+// distinct 16-byte bank slots of 256 bytes, and any 8 consecutive lanes on 8 slots of 128 bytes
+// (a padded 144-byte pitch gave two-way conflicts in both groupings). Bit 2 of r is not used, so
+// the tt = 1 rows share the tt = 0 rows' permutation.
+__device__ __forceinline__ int k_swz(int r) {
+  return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r ^ (r >> 4)) & 1) << 2);
+}
 
 template <typename T>
 struct VarlenArgs {
@@ -69,7 +78,8 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   constexpr int NV = kD / VEC;
   constexpr int KP = kKP<T>;
   constexpr int VP = kVP<T>;
-  constexpr int TILE = 32 * KP + (kTrV<T> ? 32 * kD : kD * VP);   // elements of one K + V stage
+  constexpr int KT = kSwK<T> ? kD : KP;                            // K tile row pitch
+  constexpr int TILE = 32 * KT + (kTrV<T> ? 32 * kD : kD * VP);   // elements of one K + V stage
 
   __shared__ __align__(16) T s_kv[2 * TILE];
   __shared__ __align__(16) T s_band[kRing * KP];   // row x of the table in slot x % 128
@@ -159,14 +169,17 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     const u32x4* kr = rr.k;
     const u32x4* vr = rr.v;
     T* sk = st;
-    T* sv = st + 32 * KP;
+    T* sv = st + 32 * KT;
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
       const int r = idx / NV;
       const int dv = (idx % NV) * VEC;
       *reinterpret_cast<u32x4*>(band_slot(xw + j0 + 64 + r) + dv) = rr.b[it];
-      *reinterpret_cast<u32x4*>(sk + r * KP + dv) = kr[it];
+      if constexpr (kSwK<T>)
+        *reinterpret_cast<u32x4*>(sk + r * kD + 8 * ((dv >> 3) ^ k_swz(r))) = kr[it];
+      else
+        *reinterpret_cast<u32x4*>(sk + r * KP + dv) = kr[it];
       if constexpr (kTrV<T>) {
         *reinterpret_cast<u32x4*>(sv + r * kD + 4 * ((dv >> 2) ^ v_swz(r))) = vr[it];
       } else {
@@ -237,16 +250,27 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     const T* cur = s_kv + (step & 1) * TILE;
     fetch(fre, j0 + 64);   // (past the last step: harmless re-reads of the last frame)
     F kf[2][2], vf[4];
+    if constexpr (kSwK<T>) {
+      const int r = 8 * (m16 >> 2) + (m16 & 3);   // tile tt reads row r + 4 tt
+      const int sw = k_swz(r);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const T* row = cur + (8 * (m16 >> 2) + 4 * tt + (m16 & 3)) * KP + 8 * grp;
-      kf[tt][0] = load8(row);
-      kf[tt][1] = load8(row + 32);
+      for (int tt = 0; tt < 2; ++tt) {
+        const T* row = cur + (r + 4 * tt) * kD;
+        kf[tt][0] = load8(row + 8 * (grp ^ sw));
+        kf[tt][1] = load8(row + 8 * ((grp + 4) ^ sw));
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const T* row = cur + (8 * (m16 >> 2) + 4 * tt + (m16 & 3)) * KP + 8 * grp;
+        kf[tt][0] = load8(row);
+        kf[tt][1] = load8(row + 32);
+      }
     }
     if constexpr (kTrV<T>) {
       // lane m16 of the group addresses row 8 grp + m16 / 4 (+ 4), dimensions 16 dt + 4 (m16 % 4)
       const int r = 8 * grp + (m16 >> 2);
-      const T* lo = cur + 32 * KP + r * kD;
+      const T* lo = cur + 32 * KT + r * kD;
       const int sw = v_swz(r);   // the same for row r + 4
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -255,7 +279,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       }
     } else {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(cur + 32 * KP + (16 * dt + m16) * VP + 8 * grp);
+      for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(cur + 32 * KT + (16 * dt + m16) * VP + 8 * grp);
     }
     F pb[2][2];
     band_tile(xl + j0, pb[0][0], pb[0][1]);
