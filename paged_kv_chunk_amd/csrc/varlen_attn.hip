@@ -40,6 +40,10 @@ constexpr int kQTile = 16 * kWaves;     // queries per workgroup
 
 template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // band / fp32 K row pitch
 template <typename T> constexpr bool kSwK = sizeof(T) == 2;            // swizzled bf16 K rows
+// band ring row pitch: 160 bytes for bf16 (a 16-lane read of 16 consecutive rows and one 16-byte
+// column hits distinct bank slots at any starting row; 144, 176 and 208 bytes measured two-way
+// conflicts on gfx950)
+template <typename T> constexpr int kBP = sizeof(T) == 2 ? kD + 16 : kKP<T>;
 template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch (fp32)
 template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
 constexpr int kRing = 128;   // rows of the band ring (a step reads 80 and stages the next 32)
@@ -82,7 +86,8 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   constexpr int TILE = 32 * KT + (kTrV<T> ? 32 * kD : kD * VP);   // elements of one K + V stage
 
   __shared__ __align__(16) T s_kv[2 * TILE];
-  __shared__ __align__(16) T s_band[kRing * KP];   // row x of the table in slot x % 128
+  constexpr int BP = kBP<T>;
+  __shared__ __align__(16) T s_band[kRing * BP];   // row x of the table in slot x % 128
   __shared__ __align__(16) float s_skew[kWaves * kSkewFloats];
 
   const int tid = threadIdx.x;
@@ -145,7 +150,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   auto band_src = [&](int x, uint32_t col_b) {
     return ptab + ((uint32_t)clampi(x, rlo, rhi) * prow_b + col_b);
   };
-  auto band_slot = [&](int x) { return s_band + (x & (kRing - 1)) * KP; };
+  auto band_slot = [&](int x) { return s_band + (x & (kRing - 1)) * BP; };
 
   // cooperative staging of one 32-key step: 32 K rows, the same 32 V rows and the 32 band rows
   // entering the window. Rows past the utterance read its last frame instead: every staged value
