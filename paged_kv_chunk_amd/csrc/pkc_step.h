@@ -2,9 +2,10 @@
 //
 // Layout convention (16x16 MFMA tiles whose columns are the 16 queries of a tile): a lane holds
 // query column m16 = lane % 16 and, after the score tiles, the 8 consecutive keys
-// 8 * (lane / 16) + [0, 8) of the step (tile 0 row 4a + e is key 8a + e, tile 1 row 4a + e is key
-// 8a + 4 + e), which are exactly the contraction elements it feeds to the PV product. Scores are
-// in log2 units (the softmax scale and log2 e are folded into q + u and q + v).
+// 8 kg + [0, 8) of the step, kg = key_group(lane / 16) (tile 0 row 4a + e is key 8 kg(a) + e, tile 1
+// row 4a + e is key 8 kg(a) + 4 + e), which are exactly the contraction elements it feeds to the
+// PV product in slots 8 (lane / 16) + [0, 8). Scores are in log2 units (the softmax scale and
+// log2 e are folded into q + u and q + v).
 //
 // Relative position: the band product G^T[r][i] = p_r . (q_i + v) for the 48 table rows
 // [rb, rb + 48) of the step, rb = R0 + j0 - (q0 + 15) (table row of query i and key j is
@@ -24,6 +25,16 @@ constexpr int kSkewPitch = 52;          // floats per query column of the skew t
 constexpr int kSkewFloats = kSkewPitch * 16;
 constexpr float kRescaleLog2 = 8.f;     // headroom before the running max moves
 
+// Key group of lane group g (lanes 16 g .. 16 g + 15) inside a 32-key step: g itself, or with
+// kPermGrp groups 1 and 2 swapped. Swapped, the two lane groups of a half-wave hold keys 16 apart,
+// and their reads of the shifted position values (one column, rows 16 apart, any odd column
+// pitch) fall on distinct banks; with the natural order the rows are 8 apart and half of them
+// pair up on a bank (measured on gfx950).
+template <bool kPermGrp>
+__device__ __forceinline__ int key_group(int g) {
+  return kPermGrp ? (((g & 1) << 1) | (g >> 1)) : g;
+}
+
 // Running softmax state of one lane (one query column, 8 keys of each step).
 struct Softmax {
   float m, l;
@@ -33,7 +44,7 @@ struct Softmax {
 // Scores of one 32-key step, Transformer-XL convention: S^T = K (q+u)^T from the two key tiles,
 // plus the band product shifted into place through the per-wave LDS tile (scores already in log2
 // units). x[tt][e] is key 8 grp + 4 tt + e of the step for this lane's query column.
-template <typename T>
+template <typename T, bool kPermGrp = false>
 __device__ __forceinline__ void skew_scores(const typename Frag<T>::type (&kf)[2][2],
                                             const typename Frag<T>::type (&qu)[2],
                                             const floatx4& g0, const floatx4& g1, const floatx4& g2,
@@ -54,7 +65,7 @@ __device__ __forceinline__ void skew_scores(const typename Frag<T>::type (&kf)[2
   *reinterpret_cast<floatx4*>(colw + 16) = g1;
   *reinterpret_cast<floatx4*>(colw + 32) = g2;
   __builtin_amdgcn_wave_barrier();
-  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * grp;
+  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * key_group<kPermGrp>(grp);
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -84,18 +95,18 @@ __device__ __forceinline__ void per_key_scores(const typename Frag<T>::type (&kf
 // Online softmax and PV of one step from its scores. kMask: only keys k_lo <= key < k_hi of the
 // step count for this lane's query column (bounds may differ between columns); a column with no
 // key seen yet contributes nothing.
-template <typename T, bool kMask>
+template <typename T, bool kMask, bool kPermGrp = false>
 __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
                                            const typename Frag<T>::type (&vf)[4], int k_lo,
                                            int k_hi) {
   typedef typename Frag<T>::type F;
-  const int grp = (threadIdx.x & 63) >> 4;
+  const int kg = key_group<kPermGrp>((threadIdx.x & 63) >> 4);
   float mx = -INFINITY;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int key = 8 * grp + 4 * tt + e;
+      const int key = 8 * kg + 4 * tt + e;
       if (kMask) x[tt][e] = (key >= k_lo && key < k_hi) ? x[tt][e] : -INFINITY;
       mx = fmaxf(mx, x[tt][e]);
     }
@@ -132,7 +143,7 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
 // stay between the two wave barriers of the shift, which keeps the register live ranges of the
 // hot loop short. kMask: keys at or past valid_keys are excluded (the same keys for every query
 // column, and never all of a step's keys).
-template <typename T, bool kMask, bool kShiftFirst = false>
+template <typename T, bool kMask, bool kShiftFirst = false, bool kPermGrp = false>
 __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>::type (&kf)[2][2],
                                              const typename Frag<T>::type (&vf)[4],
                                              const typename Frag<T>::type (&qu)[2],
@@ -159,7 +170,8 @@ __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>
   *reinterpret_cast<floatx4*>(colw + 16) = g1;
   *reinterpret_cast<floatx4*>(colw + 32) = g2;
   __builtin_amdgcn_wave_barrier();
-  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * grp;
+  const int kg = key_group<kPermGrp>(grp);
+  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * kg;
   if constexpr (kShiftFirst) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -175,7 +187,7 @@ __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float v = kShiftFirst ? sc[tt][e] : sc[tt][e] + colr[4 * tt + e];
-      if (kMask) v = (8 * grp + 4 * tt + e < valid_keys) ? v : -INFINITY;
+      if (kMask) v = (8 * kg + 4 * tt + e < valid_keys) ? v : -INFINITY;
       x[tt][e] = v;
       mx = fmaxf(mx, v);
     }

@@ -19,8 +19,13 @@
 // V staging. For bf16, V rows stay in their natural [key][head_dim] order in LDS (one 16-byte
 // write per thread) and the PV operand - 8 consecutive keys of one dimension per lane - comes
 // from two transposing reads; the 4-dimension chunks of row r are XOR-swizzled by
-// 4 ((r & 3) ^ ((r >> 3) & 1)), which gives each of the 8 rows one read of 32 lanes touches its
-// own 32-byte bank slot. fp32 stages V transposed to [head_dim][key].
+// 4 ((r & 3) ^ ((r >> 4) & 1)), which puts the rows one half-wave reads (two key groups 16 rows
+// apart) on distinct banks. fp32 stages V transposed to [head_dim][key].
+//
+// LDS layouts were chosen by measurement: a one-wave probe repeating each access pattern, read
+// through SQ_LDS_BANK_CONFLICT, found every K, V, band and shift read of a step conflict-free
+// with these layouts (the earlier padded pitches and natural key-group order cost 2 to 4 extra
+// cycles per read).
 //
 // chunked_limited mask ("Model Layer", Nemotron encoder notes; kLimited): query i sees only the
 // keys of its own chunk of `chunk` frames and of the `left` chunks before it. A workgroup then
@@ -47,8 +52,12 @@ template <typename T> constexpr int kBP = sizeof(T) == 2 ? kD + 16 : kKP<T>;
 template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch (fp32)
 template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
 constexpr int kRing = 128;   // rows of the band ring (a step reads 80 and stages the next 32)
-// swizzle of the 4-dimension chunks of natural V row r (bf16)
-__device__ __forceinline__ int v_swz(int r) { return 4 * ((r & 3) ^ ((r >> 3) & 1)); }
+// Lane group g holds the keys of key_group<true>(g) (groups 1 and 2 swapped): the shifted
+// position values are then read conflict-free.
+constexpr bool kPerm = true;
+// swizzle of the 4-dimension chunks of natural V row r (bf16): with the swapped key groups the two
+// lane groups of a half-wave read rows 16 apart, told apart by bit 4
+__device__ __forceinline__ int v_swz(int r) { return 4 * ((r & 3) ^ ((r >> 4) & 1)); }
 // bf16 K rows are 128 bytes, unpadded, with their eight 16-byte chunks permuted by chunk ^ k_swz(r).
 // The 16 rows one 16-lane read of a key tile touches, 8 a + 4 tt + b (a, b < 4), then sit on 16
 // distinct 16-byte bank slots of 256 bytes, and any 8 consecutive lanes on 8 slots of 128 bytes
@@ -256,7 +265,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     fetch(fre, j0 + 64);   // (past the last step: harmless re-reads of the last frame)
     F kf[2][2], vf[4];
     if constexpr (kSwK<T>) {
-      const int r = 8 * (m16 >> 2) + (m16 & 3);   // tile tt reads row r + 4 tt
+      const int r = 8 * key_group<kPerm>(m16 >> 2) + (m16 & 3);   // tile tt reads row r + 4 tt
       const int sw = k_swz(r);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -267,14 +276,14 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     } else {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const T* row = cur + (8 * (m16 >> 2) + 4 * tt + (m16 & 3)) * KP + 8 * grp;
+        const T* row = cur + (8 * key_group<kPerm>(m16 >> 2) + 4 * tt + (m16 & 3)) * KP + 8 * grp;
         kf[tt][0] = load8(row);
         kf[tt][1] = load8(row + 32);
       }
     }
     if constexpr (kTrV<T>) {
-      // lane m16 of the group addresses row 8 grp + m16 / 4 (+ 4), dimensions 16 dt + 4 (m16 % 4)
-      const int r = 8 * grp + (m16 >> 2);
+      // lane m16 of the group addresses row 8 kg + m16 / 4 (+ 4), dimensions 16 dt + 4 (m16 % 4)
+      const int r = 8 * key_group<kPerm>(grp) + (m16 >> 2);
       const T* lo = cur + 32 * KT + r * kD;
       const int sw = v_swz(r);   // the same for row r + 4
 #pragma unroll
@@ -284,7 +293,8 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       }
     } else {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(cur + 32 * KT + (16 * dt + m16) * VP + 8 * grp);
+      for (int dt = 0; dt < 4; ++dt)
+        vf[dt] = load8(cur + 32 * KT + (16 * dt + m16) * VP + 8 * key_group<kPerm>(grp));
     }
     F pb[2][2];
     band_tile(xl + j0, pb[0][0], pb[0][1]);
@@ -295,12 +305,12 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     g2 = mma(pb[1][1], qv[1], g2);
     if constexpr (kLimited) {
       float x[2][4];
-      skew_scores<T>(kf, qu, g_prev, g1, g2, s_g, x);
-      softmax_pv<T, true>(st, x, vf, k_lo_q - j0, k_hi_q - j0);
+      skew_scores<T, kPerm>(kf, qu, g_prev, g1, g2, s_g, x);
+      softmax_pv<T, true, kPerm>(st, x, vf, k_lo_q - j0, k_hi_q - j0);
     } else if (j0 + 32 <= L) {
-      step_compute<T, false, true>(st, kf, vf, qu, g_prev, g1, g2, s_g, 32);
+      step_compute<T, false, true, kPerm>(st, kf, vf, qu, g_prev, g1, g2, s_g, 32);
     } else {
-      step_compute<T, true, true>(st, kf, vf, qu, g_prev, g1, g2, s_g, L - j0);
+      step_compute<T, true, true, kPerm>(st, kf, vf, qu, g_prev, g1, g2, s_g, L - j0);
     }
     g_prev = g2;
     // (unconditional, also after the last step: the rows are clamped re-reads going to a buffer
