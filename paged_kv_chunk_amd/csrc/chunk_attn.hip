@@ -54,7 +54,10 @@ namespace pkc {
 
 namespace {
 
-constexpr int kWaveLds = kD * 16 + 32;  // floats per wave: O^T tile + m + l (skew tile aliases it)
+// O^T merge tile: 16 query columns per dimension row, padded to 20 floats so that the two lane
+// groups of a half-wave (4 dimension rows apart on write, 4 apart on read) sit 16 banks apart
+constexpr int kOPitch = 20;
+constexpr int kWaveLds = kD * kOPitch + 32;  // floats per wave: O^T tile + m + l (skew tile aliases it)
 constexpr int kBtWindow = 128;          // block IDs each wave keeps in its LDS window
 
 template <typename T>
@@ -485,10 +488,10 @@ chunk_attn_kernel(ChunkArgs<T> a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[(16 * dt + 4 * grp + e) * 16 + m16] = st.o[dt][e];
+    for (int e = 0; e < 4; ++e) s_o[(16 * dt + 4 * grp + e) * kOPitch + m16] = st.o[dt][e];
   if (grp == 0) {
-    s_o[kD * 16 + m16] = st.m;
-    s_o[kD * 16 + 16 + m16] = st.l;
+    s_o[kD * kOPitch + m16] = st.m;
+    s_o[kD * kOPitch + 16 + m16] = st.l;
   }
   __syncthreads();
   for (int x = tid; x < 16 * (kD / 4); x += kThreads) {
@@ -504,16 +507,16 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     }
     float mmax = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mmax = fmaxf(mmax, s_wave[w * kWaveLds + kD * 16 + il]);
+    for (int w = 0; w < kWaves; ++w) mmax = fmaxf(mmax, s_wave[w * kWaveLds + kD * kOPitch + il]);
     float lsum = 0.f;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float* so = s_wave + w * kWaveLds;
-      const float f = fast_exp2(so[kD * 16 + il] - mmax);
-      lsum += f * so[kD * 16 + 16 + il];
+      const float f = fast_exp2(so[kD * kOPitch + il] - mmax);
+      lsum += f * so[kD * kOPitch + 16 + il];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] += f * so[(d0 + k) * 16 + il];
+      for (int k = 0; k < 4; ++k) acc[k] += f * so[(d0 + k) * kOPitch + il];
     }
     const float inv = 1.f / lsum;
 #pragma unroll
