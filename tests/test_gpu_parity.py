@@ -223,6 +223,29 @@ def test_varlen_parity_small(dtype):
     assert err <= TOL[dtype], err
 
 
+def test_varlen_longer_than_max_seqlen_is_cut_in_bounds():
+    # Out of contract: utterances longer than max_seqlen. Each is cut to its first max_seqlen
+    # frames; frames past them keep what the output held, an utterance within the bound is exact,
+    # and every written value is finite (the cut utterances' values are otherwise unspecified).
+    lengths = [40, 100, 70]
+    co = make_varlen_cohort(lengths, 2, 64, dtype=BF16, seed=5, device=DEV)
+    sentinel = 7.0
+    out = torch.full_like(co.q, sentinel)
+    pkc.varlen_packed_relpos_attn(co.q, co.k, co.v, co.cu_seqlens, co.pos, co.pos_bias_u,
+                                  co.pos_bias_v, 64, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu()
+    cu = co.cu_seqlens.cpu().tolist()
+    for s, n in enumerate(lengths):
+        seg = got[cu[s]:cu[s + 1]]
+        assert torch.isfinite(seg[:64]).all()
+        assert (seg[64:] == sentinel).all()
+    ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
+                                    co.cu_seqlens.cpu().numpy(), host64(co.pos),
+                                    host64(co.pos_bias_u), host64(co.pos_bias_v))
+    assert max_err(got[:40], ref[:40]) <= TOL[BF16]
+
+
 def test_varlen_gqa_parity():
     co = make_varlen_cohort([33, 64, 7], 4, 64, Hk=2, dtype=BF16, seed=3, device=DEV)
     ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
