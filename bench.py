@@ -50,11 +50,15 @@ KERNEL_SOURCES = {
 
 
 def kernel_source_hash(kernel="chunk"):
-    """Hash of the sources one kernel is compiled from: stored counter readings are used only
-    while it matches."""
+    """Hash of the code one kernel is compiled from: stored counter readings are used only while
+    it matches. Line comments and blank lines are left out, so a comment edit keeps the readings;
+    any change to the code itself drops them."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        h.update(open(os.path.join(ROOT, "paged_kv_chunk_amd", "csrc", name), "rb").read())
+        for line in open(os.path.join(ROOT, "paged_kv_chunk_amd", "csrc", name), encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -45,9 +45,9 @@ constexpr int kQTile = 16 * kWaves;     // queries per workgroup
 
 template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // band / fp32 K row pitch
 template <typename T> constexpr bool kSwK = sizeof(T) == 2;            // swizzled bf16 K rows
-// band ring row pitch: 160 bytes for bf16 (a 16-lane read of 16 consecutive rows and one 16-byte
-// column hits distinct bank slots at any starting row; 144, 176 and 208 bytes measured two-way
-// conflicts on gfx950)
+// band ring row pitch: 160 bytes for bf16 (a read of 16 consecutive rows, one 16-byte column per
+// lane group, measured conflict-free on gfx950 at any starting row; 144, 176 and 208 bytes cost
+// 4 extra cycles per read)
 template <typename T> constexpr int kBP = sizeof(T) == 2 ? kD + 16 : kKP<T>;
 template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch (fp32)
 template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
@@ -59,10 +59,10 @@ constexpr bool kPerm = true;
 // lane groups of a half-wave read rows 16 apart, told apart by bit 4
 __device__ __forceinline__ int v_swz(int r) { return 4 * ((r & 3) ^ ((r >> 4) & 1)); }
 // bf16 K rows are 128 bytes, unpadded, with their eight 16-byte chunks permuted by chunk ^ k_swz(r).
-// The 16 rows one 16-lane read of a key tile touches, 8 a + 4 tt + b (a, b < 4), then sit on 16
-// distinct 16-byte bank slots of 256 bytes, and any 8 consecutive lanes on 8 slots of 128 bytes
-// (a padded 144-byte pitch gave two-way conflicts in both groupings). Bit 2 of r is not used, so
-// the tt = 1 rows share the tt = 0 rows' permutation.
+// A key-tile read (16 lanes per row set 8 kg(a) + 4 tt + b, a, b < 4, one 16-byte chunk per lane
+// group) measured conflict-free on gfx950 with either key-group order; a padded 144-byte pitch
+// cost 4 extra cycles per read. Bit 2 of r is not used, so the tt = 1 rows share the tt = 0 rows'
+// permutation.
 __device__ __forceinline__ int k_swz(int r) {
   return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r ^ (r >> 4)) & 1) << 2);
 }
