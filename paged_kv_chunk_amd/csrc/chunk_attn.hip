@@ -440,9 +440,16 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       }
       if (s + 2 < s_end) load_step(r, s + 2);
     };
-    for (int s = s_begin; s < s_end; s += 2) {
-      run(ra, s);
-      if (s + 1 < s_end) run(rb2, s + 1);
+    if (nmine == 2) {
+      // (straight-line: the first step's wait leaves the second step's loads outstanding; in
+      // the loop, whose head is also reached without them, the compiler drained every load)
+      run(ra, s_begin);
+      run(rb2, s_begin + 1);
+    } else {
+      for (int s = s_begin; s < s_end; s += 2) {
+        run(ra, s);
+        if (s + 1 < s_end) run(rb2, s + 1);
+      }
     }
   }
 
