@@ -478,6 +478,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the workload, time a plain device copy of this many MiB "
                          "(reference for HBM counters and achievable bandwidth)")
+    ap.add_argument("--copy-rotate", type=int, default=1,
+                    help="with --copy-mib: copy over this many buffer pairs in turn (enough to "
+                         "exceed the last-level cache makes every copy come from HBM)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -491,22 +494,30 @@ def main():
     from synth import WORKLOADS
 
     if args.copy_mib:
+        # plain device copies (torch's copy kernel): the calibration of the HBM counters, and
+        # with --copy-rotate K over K buffer pairs in turn, so that a small copy comes from HBM
+        # and not the last-level cache (a single launch's reference for the same bytes)
         n = args.copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
-        dst = torch.empty_like(src)
-        for _ in range(args.warmup):
-            dst.copy_(src)
+        pairs = []
+        for _ in range(max(args.copy_rotate, 1)):
+            src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+            pairs.append((src, torch.empty_like(src)))
+        for i in range(args.warmup):
+            d, s = pairs[i % len(pairs)][1], pairs[i % len(pairs)][0]
+            d.copy_(s)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
-        for _ in range(args.steps):
-            dst.copy_(src)
+        for i in range(args.steps):
+            d, s = pairs[i % len(pairs)][1], pairs[i % len(pairs)][0]
+            d.copy_(s)
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / args.steps
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": ms,
-                          "read_plus_write_GBps": 2 * n / (ms / 1e3) / 1e9}), flush=True)
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "buffer_pairs": len(pairs),
+                          "ms_per_copy": ms, "read_plus_write_GBps": 2 * n / (ms / 1e3) / 1e9}),
+              flush=True)
         return
 
     cfg = WORKLOADS[args.config]
