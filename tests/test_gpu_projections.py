@@ -63,6 +63,9 @@ LINEAR = {
     "direct_k1024_half_pair": (77, 1040, 1024),
     "direct_k512_one_row": (1, 512, 512),
     "dmodel256_qkv_shape": (1024, 768, 256),
+    # K = 256 on more than 256 tiles: the three-slot ring (at most 256 tiles: all stages in
+    # flight at once)
+    "direct_k256_ring": (4096, 1536, 256),
     "dmodel512_qkv_shape_large_tiles": (4096, 1536, 512),
     "out_proj_dmodel512": (4096, 512, 512),
 }
@@ -101,6 +104,9 @@ QKV = {
     "fp32_ragged": dict(B=3, H=2, Hk=2, D=64, C=16, S=16, caches=[0, 37, 100], dm=128, dtype=F32),
     "gqa_short_chunk": dict(B=4, H=4, Hk=2, D=64, C=5, S=8, caches=[3, 0, 64, 11], dm=256, dtype=BF16),
     "dmodel256_cohort": dict(B=64, H=4, Hk=4, D=64, C=16, S=16, caches=[256] * 64, dm=256, dtype=BF16),
+    # d_model 256 with 256 streams: 384 tiles, the ring path of the K = 256 epilogue
+    "dmodel256_wide_cohort": dict(B=256, H=4, Hk=4, D=64, C=16, S=16, caches=[64, 0, 17, 255] * 64,
+                                  dm=256, dtype=BF16),
     # the d_model 512 cohort at full size, in the launch configuration the projection bench times
     "dmodel512_cohort": dict(B=256, H=8, Hk=8, D=64, C=16, S=16, caches=[512] * 256, dm=512, dtype=BF16),
 }
