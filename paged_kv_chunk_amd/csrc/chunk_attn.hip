@@ -220,21 +220,6 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   auto block_of = [&](int pg) -> uint32_t {
     return (uint32_t)(pg < kBtWindow ? s_win[pg] : clampi(bt[ring(min(pg, a.M - 1))], 0, a.N - 1));
   };
-  // the chunk's frames into the LDS tail (row t = frame t; V transposed, zero past the chunk)
-  if constexpr (kRegTail) {
-    if (tid < n_real * NV) {
-      const int t = tid / NV;
-      const int dv = (tid % NV) * VEC;
-      *reinterpret_cast<u32x4*>(s_kt + t * KTP + dv) = nk;
-      const uint32_t wd[4] = {nv[0], nv[1], nv[2], nv[3]};
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        reinterpret_cast<uint16_t*>(s_vt)[(dv + c) * a.vt_pitch + t] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
-    }
-    for (int x = tid; x < (32 * ntail - n_real) * kD; x += kThreads)
-      s_vt[(x % kD) * a.vt_pitch + n_real + x / kD] = from_f<T>(0.f);
-  }
-
   // ---- 2. loads of the first two body steps (band tile 0 of the first one too) ----------------
   auto load_step = [&](StepRegs<T>& r, int s) {
     const int j0 = 32 * s;
@@ -298,6 +283,24 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     load_step(ra, min(s_begin, s_last));
     load_step(rb2, min(s_begin + 1, s_last));
   }
+
+  // the chunk's frames into the LDS tail (row t = frame t; V transposed, zero past the chunk),
+  // after the body steps' loads are requested: waiting for the frames then leaves those loads in
+  // flight, and the staging's LDS writes are not on their way
+  if constexpr (kRegTail) {
+    if (tid < n_real * NV) {
+      const int t = tid / NV;
+      const int dv = (tid % NV) * VEC;
+      *reinterpret_cast<u32x4*>(s_kt + t * KTP + dv) = nk;
+      const uint32_t wd[4] = {nv[0], nv[1], nv[2], nv[3]};
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        reinterpret_cast<uint16_t*>(s_vt)[(dv + c) * a.vt_pitch + t] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
+    }
+    for (int x = tid; x < (32 * ntail - n_real) * kD; x += kThreads)
+      s_vt[(x % kD) * a.vt_pitch + n_real + x / kD] = from_f<T>(0.f);
+  }
+
 
   // ---- 3. long chunks: the chunk's frames into the LDS tail with a loop ------------------------
   // (from k_new / v_new when fused, else from the pool, where an earlier append put them)
