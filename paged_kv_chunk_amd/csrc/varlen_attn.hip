@@ -130,21 +130,18 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   const int R0 = L - 1;                         // table row of (i, j) is R0 + j - i
   const int rlo = 0, rhi = 2 * L - 2;
 
-  // queries with the biases, pre-scaled into log2 units
-  F qu[2], qv[2];
+  // the queries and the biases, requested first; q + u and q + v (pre-scaled into log2 units) are
+  // formed after the first steps' rows are requested, so that waiting for them does not hold up
+  // those requests
+  F qq[2], uu[2], ww[2];
   {
     const T* qrow = a.q + ((size_t)(lo + min(q0 + m16, L - 1)) * a.H + h) * kD;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int d0 = 32 * half + 8 * grp;
-      const F qq = load8(qrow + d0);
-      const F uu = load8(a.u + h * kD + d0);
-      const F ww = load8(a.w + h * kD + d0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        set(qu[half], e, (get(qq, e) + get(uu, e)) * a.scale_log2);
-        set(qv[half], e, (get(qq, e) + get(ww, e)) * a.scale_log2);
-      }
+      qq[half] = load8(qrow + d0);
+      uu[half] = load8(a.u + h * kD + d0);
+      ww[half] = load8(a.w + h * kD + d0);
     }
   }
 
@@ -235,18 +232,36 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     p_hi = load8(row + 32);
   };
   const int J = 32 * s_first;
+  // requests in the order they are needed: step 0's rows and the window's first 64 band rows
+  // (staged directly, once), then step 1's rows, which the prologue's waits then leave in flight
   fetch(ra, J);
-  fetch(rb, J + 32);
-  // the window's first 64 rows at the first step, staged directly (once)
+  u32x4 pre[2][NLD];
 #pragma unroll
   for (int part = 0; part < 2; ++part)
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
       const int x = xw + J + 32 * part + idx / NV;
-      const int dv = (idx % NV) * VEC;
-      *reinterpret_cast<u32x4*>(band_slot(x) + dv) =
-          *reinterpret_cast<const u32x4*>(band_src(x, (idx % NV) * 16u));
+      pre[part][it] = *reinterpret_cast<const u32x4*>(band_src(x, (idx % NV) * 16u));
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  fetch(rb, J + 32);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int part = 0; part < 2; ++part)
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const int idx = tid + kThreads * it;
+      const int x = xw + J + 32 * part + idx / NV;
+      *reinterpret_cast<u32x4*>(band_slot(x) + (idx % NV) * VEC) = pre[part][it];
+    }
+  F qu[2], qv[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      set(qu[half], e, (get(qq[half], e) + get(uu[half], e)) * a.scale_log2);
+      set(qv[half], e, (get(qq[half], e) + get(ww[half], e)) * a.scale_log2);
     }
   stash(ra, s_kv, J);
   __syncthreads();
