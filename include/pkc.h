@@ -163,8 +163,9 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  *      + chunk_size either way.
  * softmax_scale <= 0 selects 1 / sqrt(head_dim).
  * Errors: as paged_kv_append; n_head % n_kv_head != 0 or a table too short -> PKC_ERR_SHAPE;
- * head_dim != 64, block_size not a power of two >= 8, or a chunk too long for the kernel's LDS
- * staging -> PKC_ERR_UNSUPPORTED. The kernel stages the chunk's chunk_size frames in LDS (the
+ * head_dim != 64, block_size not a power of two >= 8, a chunk too long for the kernel's LDS
+ * staging, or batch n_head ceil(chunk_size / 16) at or past 2^31 (one workgroup per 16 queries of
+ * a stream and head) -> PKC_ERR_UNSUPPORTED. The kernel stages the chunk's chunk_size frames in LDS (the
  * cached frames stream from the pages), which allows chunk_size <= 512 in bf16 and <= 256 in
  * fp32.
  */
@@ -261,8 +262,9 @@ pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,
  * mask_left_chunks ... i / mask_chunk, and each 64-frame query block computes only over the keys
  * its frames can see (its own frames plus the trained history). mask_chunk = 0: full context.
  * Errors: as above; a negative mask_chunk or mask_left_chunks -> PKC_ERR_SHAPE; head_dim != 64,
- * or 2 max_seqlen max(H, Hk) head_dim element bytes at or past 2^31 (an utterance's rows are
- * addressed by 32-bit byte offsets) -> PKC_ERR_UNSUPPORTED.
+ * 2 max_seqlen max(H, Hk) head_dim element bytes at or past 2^31 (an utterance's rows are
+ * addressed by 32-bit byte offsets), or num_seqs n_head ceil(max_seqlen / 64) at or past 2^31
+ * (one workgroup per 64 queries of an utterance and head) -> PKC_ERR_UNSUPPORTED.
  */
 pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,
                                      const int32_t* cu_seqlens, int32_t num_seqs,

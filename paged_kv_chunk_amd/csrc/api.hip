@@ -132,6 +132,8 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
   if (chunk_attn_lds_bytes(dtype == PKC_BF16 ? 2 : 4, chunk_size, max_cache_seqlen, block_size,
                            k_new != nullptr) > kMaxDynamicLds)
     return PKC_ERR_UNSUPPORTED;
+  if (chunk_attn_workgroups(batch, n_head, chunk_size) >= (int64_t)1 << 31)
+    return PKC_ERR_UNSUPPORTED;
   AttnParams p{};
   p.q = q;
   p.k_pool = k_pool;
@@ -262,6 +264,8 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
   // table spans 2 max_seqlen rows)
   if ((int64_t)2 * max_seqlen * (n_head > n_kv_head ? n_head : n_kv_head) * head_dim *
           (dtype == PKC_BF16 ? 2 : 4) >= (int64_t)1 << 31)
+    return PKC_ERR_UNSUPPORTED;
+  if (varlen_attn_workgroups(num_seqs, n_head, max_seqlen) >= (int64_t)1 << 31)
     return PKC_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pos) ||
       !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))

@@ -78,6 +78,7 @@ struct ChunkArgs {
   T* k_pool_w;
   T* v_pool_w;
   int C, H, Hk, S, logS, N, M, max_cache, pos_len, per_row, per_key, qtiles;
+  FastDiv div_qtiles, div_H, div_group;   // by qtiles, H and H / Hk
   int tail_cap, vt_pitch;            // LDS tail geometry (keys, elements per V^T row)
   int off_bt, off_kt, off_vt;        // byte offsets of the LDS regions
   float scale_log2;
@@ -121,12 +122,12 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   // Grid order (b, h, query tile), tile fastest: consecutive workgroups go round-robin to the
   // XCDs, so for H a multiple of 8 each XCD serves one head and a shared table's band for that
   // head stays in that XCD's L2.
-  int id = blockIdx.x;
-  const int qt = id % a.qtiles;
-  id /= a.qtiles;
-  const int h = id % a.H;
-  const int b = id / a.H;
-  const int hk = h / (a.H / a.Hk);
+  const int id = blockIdx.x;
+  const int bh = fdiv(id, a.div_qtiles);
+  const int qt = id - bh * a.qtiles;
+  const int b = fdiv(bh, a.div_H);
+  const int h = bh - b * a.H;
+  const int hk = fdiv(h, a.div_group);
   const int32_t* bt = a.bt + (size_t)b * a.M;
 
   // ---- 1. requests that need nothing: block IDs of pages [0, 128), queries, u, v, chunk -------
@@ -459,7 +460,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   // ---- 6. fused append: this tile's chunk frames from LDS into the pool ---------------------
   // (issued after the wave's last load, so no load wait queues behind these stores, and they
   // drain while the waves merge)
-  if (kFused && h % (a.H / a.Hk) == 0) {
+  if (kFused && h == hk * (a.H / a.Hk)) {
     const int t_lo = qt * 16;
     const int t_hi = min(n_real, t_lo + 16);
     for (int x = tid; x < (t_hi - t_lo) * NV; x += kThreads) {
@@ -625,6 +626,9 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   a.per_row = p.pos_layout & PKC_POS_PER_ROW;
   a.per_key = (p.pos_layout & PKC_POS_PER_KEY) != 0;
   a.qtiles = (p.chunk + 15) / 16;
+  a.div_qtiles = make_fastdiv(a.qtiles);
+  a.div_H = make_fastdiv(a.H);
+  a.div_group = make_fastdiv(a.H / a.Hk);
   a.tail_cap = ((p.chunk + 31) / 32) * 32;
   a.vt_pitch = a.tail_cap + 16 / (int)sizeof(T);
   constexpr int kWaves = waves_of<T>();
@@ -637,7 +641,7 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   off += (size_t)kD * a.vt_pitch * sizeof(T);
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)p.batch * p.n_head * a.qtiles);
+  const dim3 grid((unsigned)chunk_attn_workgroups(p.batch, p.n_head, p.chunk));
   if (p.k_new) launch_s<T, true>(a, grid, off, stream);
   else launch_s<T, false>(a, grid, off, stream);
   return hipGetLastError();
@@ -651,6 +655,10 @@ size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int, int, bool) {
   const int waves = dtype_bytes == 2 ? waves_of<bf16>() : waves_of<float>();
   return (size_t)waves * kWaveLds * 4 + (size_t)waves * kBtWindow * 4 +
          (size_t)tail_cap * (kD + vec) * dtype_bytes + (size_t)kD * (tail_cap + vec) * dtype_bytes;
+}
+
+int64_t chunk_attn_workgroups(int batch, int n_head, int chunk) {
+  return (int64_t)batch * n_head * ((chunk + 15) / 16);
 }
 
 hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream) {

@@ -164,4 +164,23 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Division by a launch-invariant divisor d (1 <= d < 2^31) as a multiply-high, an add and a shift
+// (Granlund and Montgomery, "Division by Invariant Integers using Multiplication", 1994, the
+// round-up method): with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1 < 2^32, the
+// quotient n / d is (mulhi(n, m) + n) >> s for 0 <= n < 2^31 (the sum stays below 2^32). The host
+// makes the pair once per launch; it replaces the reciprocal-and-correct sequence of a runtime
+// division at kernel start.
+struct FastDiv {
+  uint32_t m, s;
+};
+inline FastDiv make_fastdiv(int d) {
+  uint32_t s = 0;
+  while ((1u << s) < (uint32_t)d) ++s;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - (uint64_t)d)) / (uint64_t)d + 1;
+  return FastDiv{(uint32_t)m, s};
+}
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+  return (int)((__umulhi((uint32_t)n, f.m) + (uint32_t)n) >> f.s);
+}
+
 }  // namespace pkc

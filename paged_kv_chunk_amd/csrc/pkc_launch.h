@@ -107,4 +107,9 @@ constexpr int kMaxStagedBlocks = 4096;
 size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int max_cache, int block_size, bool fused);
 constexpr size_t kMaxDynamicLds = 160 * 1024;
 
+// Workgroups of one attention launch. The kernels split the workgroup index with 31-bit
+// multiply-shift divisions, so a launch must stay below 2^31 workgroups.
+int64_t chunk_attn_workgroups(int batch, int n_head, int chunk);
+int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen);
+
 }  // namespace pkc

@@ -78,6 +78,7 @@ struct VarlenArgs {
   const T* w;
   T* out;
   int H, Hk, qtiles, total, maxlen;
+  FastDiv div_H, div_qtiles, div_group;   // by H, qtiles and H / Hk
   int chunk, left;            // chunked_limited mask (kLimited)
   float scale_log2;
 };
@@ -107,17 +108,17 @@ varlen_attn_kernel(VarlenArgs<T> a) {
 
   // head fastest: workgroups go to the 8 XCDs round-robin, so with H a multiple of 8 every tile
   // of one head lands on the same XCD and that head's tables and K/V rows stay in its L2
-  int id = blockIdx.x;
-  const int h = id % a.H;
-  id /= a.H;
-  const int qt = id % a.qtiles;
-  const int s = id / a.qtiles;
+  const int id = blockIdx.x;
+  const int sq = fdiv(id, a.div_H);
+  const int h = id - sq * a.H;
+  const int s = fdiv(sq, a.div_qtiles);
+  const int qt = sq - s * a.qtiles;
   const int lo = clampi(a.cu[s], 0, a.total);
   // (an utterance longer than max_seqlen is cut to max_seqlen frames: the host bounds every byte
   // offset from an utterance's first row by 2 max_seqlen rows, so 32-bit offsets hold)
   const int L = min(clampi(a.cu[s + 1], lo, a.total) - lo, a.maxlen);
   if (qt * kQTile >= L) return;  // uniform over the workgroup
-  const int hk = h / (a.H / a.Hk);
+  const int hk = fdiv(h, a.div_group);
   const size_t krow = (size_t)a.Hk * kD;      // elements between consecutive frames of k / v
   const size_t prow = (size_t)a.H * kD;
   // uniform segment bases; per-lane 32-bit byte offsets from them (one offset serves K and V)
@@ -371,13 +372,16 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
   a.H = p.n_head;
   a.Hk = p.n_kv_head;
   a.qtiles = (p.max_seqlen + kQTile - 1) / kQTile;
+  a.div_H = make_fastdiv(a.H);
+  a.div_qtiles = make_fastdiv(a.qtiles);
+  a.div_group = make_fastdiv(a.H / a.Hk);
   a.total = p.total;
   a.maxlen = p.max_seqlen;
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.chunk = p.mask_chunk;
   a.left = p.mask_left_chunks;
-  const dim3 grid((unsigned)p.num_seqs * p.n_head * a.qtiles);
+  const dim3 grid((unsigned)varlen_attn_workgroups(p.num_seqs, p.n_head, p.max_seqlen));
   if (p.mask_chunk > 0)
     hipLaunchKernelGGL((varlen_attn_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
   else
@@ -386,6 +390,10 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen) {
+  return (int64_t)num_seqs * n_head * ((max_seqlen + kQTile - 1) / kQTile);
+}
 
 hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_t stream) {
   return dtype == PKC_BF16 ? launch_varlen_t<bf16>(p, stream) : launch_varlen_t<float>(p, stream);

@@ -114,6 +114,9 @@ def test_append_validation(lib, kw, status):
     (dict(per_row=3, pos_len=79), SHAPE),
     (dict(D=128), UNSUP), (dict(S=12, M=12), UNSUP), (dict(S=24, M=12), UNSUP),
     (dict(S=4, M=40), UNSUP),
+    # one workgroup per 16 queries of a stream and head: 2^31 of them are refused
+    (dict(B=1 << 24, H=128, Hk=128), UNSUP),
+    (dict(B=1 << 23, H=128, Hk=64, C=32, pos_len=2 * (64 + 32) - 1), UNSUP),
     (dict(max_cache=120), CAP),
     (dict(q=BAD), ALIGN), (dict(pos=BAD), ALIGN), (dict(out=BAD), ALIGN),
 ])
@@ -143,6 +146,9 @@ def test_fused_validation(lib):
     # must stay under 2^31 bytes
     (dict(total=2_000_000, max_len=2_000_000), UNSUP),
     (dict(dtype=0, total=1_100_000, max_len=1_100_000, H=4, Hk=4), UNSUP),
+    # one workgroup per 64 queries of an utterance and head: 2^31 of them are refused
+    (dict(S=1 << 20, total=100, max_len=64, H=2048, Hk=2048), UNSUP),
+    (dict(S=1 << 19, total=200, max_len=128, H=2048, Hk=1024), UNSUP),
 ])
 def test_varlen_validation(lib, kw, status):
     assert varlen(lib, **kw) == status
