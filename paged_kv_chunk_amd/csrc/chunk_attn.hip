@@ -129,6 +129,12 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const int h = bh - b * a.H;
   const int hk = fdiv(h, a.div_group);
   const int32_t* bt = a.bt + (size_t)b * a.M;
+  // the cache length gates every page and table address below: its request goes first (the
+  // scheduling barrier keeps the compiler from sinking it below the vector requests; scalar
+  // loads return out of order, so it also goes after every kernel-argument load the code above
+  // waits for)
+  const int cs_raw = a.cs[b];
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- 1. requests that need nothing: block IDs of pages [0, 128), queries, u, v, chunk -------
   // With bounded history the table row is a ring: the window's page pg sits at entry
@@ -165,7 +171,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     nk = *reinterpret_cast<const u32x4*>(a.k_new + row);
     nv = *reinterpret_cast<const u32x4*>(a.v_new + row);
   }
-  const int cache = clampi(a.cs[b], 0, a.max_cache);
+  const int cache = clampi(cs_raw, 0, a.max_cache);
   // real frames of this stream's chunk: frames past them do not exist (not appended, not keys;
   // their output rows are zero); a stream with none is a padding lane and reads nothing
   const int n_real = (kGen && a.lens) ? clampi(a.lens[b], 0, a.C) : a.C;
