@@ -79,6 +79,15 @@ SMALL = {
     "max_chunk_bf16": dict(B=2, H=2, D=64, C=512, block_size=32, cache_seqlens=[40, 0],
                            dtype=BF16),
     "max_chunk_fp32": dict(B=1, H=2, D=64, C=256, block_size=16, cache_seqlens=[77], dtype=F32),
+    # pages near the 128-entry block-ID window each wave keeps in LDS: blocks of 16 and 32 whose
+    # last pages (125 of 126) still lie in it, and blocks of 16 past it (133 pages: IDs past the
+    # window read from the table)
+    "window_edge_S16": dict(B=2, H=2, D=64, C=16, block_size=16, cache_seqlens=[2000, 9],
+                            dtype=BF16),
+    "window_edge_S32": dict(B=2, H=2, D=64, C=16, block_size=32, cache_seqlens=[4000, 70],
+                            dtype=BF16),
+    "past_window_S16": dict(B=2, H=2, D=64, C=16, block_size=16, cache_seqlens=[2100, 33],
+                            dtype=BF16),
 }
 
 
