@@ -102,10 +102,11 @@ def algorithmic_bytes(co):
     return qo + new + cached + band + uv + tables
 
 
-def build_sets(cfg_index, n_sets, n_layers, device):
+def build_sets(cfg_index, n_sets, n_layers, device, blocked=True):
     """n_sets independent cohorts, each of n_layers layers sharing one block table and cache
-    lengths (one block ID addresses every layer's pool)."""
-    from synth import make_config
+    lengths (one block ID addresses every layer's pool). ``blocked``: each layer also gets its
+    positional table in 32-dim column blocks, the layout the timed kernels read."""
+    from synth import make_config, add_blocked_table
     sets = []
     for r in range(n_sets):
         layers = []
@@ -115,18 +116,22 @@ def build_sets(cfg_index, n_sets, n_layers, device):
             co.block_tables = base.block_tables
             co.cache_seqlens = base.cache_seqlens
             co.out = torch.empty_like(co.q)
+            if blocked:
+                add_blocked_table(co)
             layers.append(co)
         sets.append(layers)
     return sets
 
 
 def launch_layer(pkc, co, stream):
+    blocked = co.pos_cb is not None
     pkc.paged_kv_append_relpos_attn(co.q, co.k_new, co.v_new, co.k_pool, co.v_pool,
-                                    co.block_tables, co.cache_seqlens, co.pos, co.pos_bias_u,
+                                    co.block_tables, co.cache_seqlens,
+                                    co.pos_cb if blocked else co.pos, co.pos_bias_u,
                                     co.pos_bias_v, co.max_cache_seqlen,
                                     per_row_pos=co.per_row_pos, per_key_pos=co.per_key_pos,
-                                    out=co.out,
-                                    chunk_lens=getattr(co, "chunk_lens", None), stream=stream)
+                                    out=co.out, chunk_lens=getattr(co, "chunk_lens", None),
+                                    pos_blocked=blocked, stream=stream)
 
 
 def set_chunk_lens(sets, pad_lanes, short_frac, seed=0):
@@ -470,6 +475,9 @@ def main():
                     help="packed offline workload: chunked_limited mask chunk (frames); 0 = none")
     ap.add_argument("--mask-left", type=int, default=0,
                     help="packed offline workload: left chunks of the chunked_limited mask")
+    ap.add_argument("--pos-row-major", action="store_true",
+                    help="cohort workloads: positional tables row-major [P, H, D] instead of in "
+                         "32-dim column blocks per head")
     ap.add_argument("--per-key", action="store_true",
                     help="cohort workloads: WeNet per-key tables instead of Transformer-XL ones")
     ap.add_argument("--proj", action="store_true",
@@ -527,7 +535,7 @@ def main():
         return bench_proj(args, cfg, pkc)
     n_layers = cfg["n_layers"]
     dev = "cuda"
-    sets = build_sets(args.config, args.rotate, n_layers, dev)
+    sets = build_sets(args.config, args.rotate, n_layers, dev, blocked=not args.pos_row_major)
     lens_mode = bool(args.pad_lanes or args.short_frac)
     if lens_mode:
         set_chunk_lens(sets, args.pad_lanes, args.short_frac)
@@ -538,6 +546,9 @@ def main():
                 # keys' absolute positions start at offset - cache; here every stream's offset is
                 # its cache length (unlimited history), so positions start at 0
                 use_key_position_tables(co, [0] * co.q.shape[0], per_row=co.per_row_pos)
+                if not args.pos_row_major:
+                    from synth import add_blocked_table
+                    add_blocked_table(co)
     stream = torch.cuda.current_stream()
     co0 = sets[0][0]
     B, C, H, D = co0.q.shape
@@ -662,6 +673,8 @@ def main():
             "layers": n_layers, "rotated_cohorts": len(sets), "launch": mode,
             "shared_pos_table": not co0.per_row_pos,
             "pos_convention": "per-key (WeNet, no shift)" if args.per_key else "Transformer-XL",
+            "pos_layout": "row-major [P, H, D]" if args.pos_row_major
+                          else "32-dim column blocks per head [H, D/32, P, 32]",
         },
         "roofline": {
             "bound": "hbm",

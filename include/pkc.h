@@ -16,9 +16,10 @@
  *   [SCH 4.3]  "Scheduler", section 4.3 "Heterogeneous-offset batching": attention over the
  *              paged pool with per-stream lengths from cache_seqlens and the relative-position
  *              bias matrix_bd / sqrt(d_k) added to the scores.
- *   [MOD fix]  "Model Layer", "Three optional encoder declarations", fixed_attention_window: a
- *              Transformer-XL table's distances are cache + i - j; a uniform cache_seqlens lets
- *              one shared table serve the cohort, otherwise each row needs its own table.
+ *   [MOD fix]  "Model Layer", "Three optional encoder declarations", fixed_attention_window: the
+ *              Transformer-XL row used for chunk query i and key j is picked by their offset,
+ *              cache + i - j frames; one table can serve the cohort when every stream has the
+ *              same cache_seqlens, and each stream needs its own table when they differ.
  *   [MOD surf] "Model Layer", "The engine-facing surface": forward_chunk_paged (streaming chunk
  *              entry), forward_offline_packed (gapless varlen offline forward), n_kv_head and
  *              head_dim (paged-streaming geometry).
@@ -74,6 +75,12 @@
  *                                            T_b - 1 (T_b = cache_seqlens[b] + C, the full
  *                                            chunk width whatever chunk_lens says); rows past
  *                                            that are never read
+ *   pos, with PKC_POS_COL_BLOCKED            the same tables stored in 32-dim column blocks per
+ *                   [H, D / 32, pos_len, 32] head: dim d of row r of head h is element
+ *                or [B, H, D / 32, pos_len, 32]  (h, d / 32, r, d % 32). The rows a 16-row MFMA
+ *                                            fragment reads are then contiguous (whole 128-byte
+ *                                            lines, as in the K pages); row-major rows give every
+ *                                            load instruction 16 half-lines instead
  * Query head h reads kv head h / (H / Hk). Element type: fp32 or bf16 for every floating-point
  * buffer of a call; accumulation is fp32 either way; bf16 outputs are rounded to nearest even.
  *
@@ -81,8 +88,13 @@
  *   0 <= cache_seqlens[b] <= max_cache_seqlen; block_tables[b][t / S] in [0, N) for every
  *   t < cache_seqlens[b] + n_b; no two streams own the same page. Kernels clamp cache lengths,
  *   chunk lengths and block IDs into range, so a violation gives unspecified values but never an
- *   out-of-bounds access. Table entries past a stream's last page may be read (up to 32 frames
- *   past its cached frames, inside its table row); their frames are masked, never used.
+ *   out-of-bounds access. The attention reads more of each table row than the stream's own
+ *   pages: every workgroup reads the first min(M, 128) entries of its row into LDS, whatever the
+ *   stream's length (the block IDs of later pages are read from the row as needed). When
+ *   cache_seqlens[b] is not a multiple of 32, the last 32-key step of the cached frames also
+ *   reads the frames past them: through the row's next entry, which may name another stream's
+ *   page (or hold any value, clamped into [0, N)). Those frames are masked and their V zeroed
+ *   before use, so such reads never change a result; they only touch valid pool memory.
  */
 #ifndef PKC_H
 #define PKC_H
@@ -112,7 +124,8 @@ typedef enum pkc_dtype { PKC_F32 = 0, PKC_BF16 = 1 } pkc_dtype;
 typedef enum pkc_pos_layout {
   PKC_POS_SHARED = 0,   /* one table by distance for the cohort                         */
   PKC_POS_PER_ROW = 1,  /* one table per stream                                          */
-  PKC_POS_PER_KEY = 2   /* rows are keys, not distances (WeNet's convention, no shift)   */
+  PKC_POS_PER_KEY = 2,  /* rows are keys, not distances (WeNet's convention, no shift)   */
+  PKC_POS_COL_BLOCKED = 4 /* storage in 32-dim column blocks per head (see Layouts)       */
 } pkc_pos_layout;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -161,6 +174,9 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  *      start at offset - cache_seqlens), and the position term is (q_i + v) . p[j]. Shared, or
  *      with PKC_POS_PER_ROW one table per stream pos_len rows apart; pos_len >= max_cache_seqlen
  *      + chunk_size either way.
+ *   PKC_POS_COL_BLOCKED combines with any of the above: the same tables, stored in 32-dim column
+ *      blocks per head (Layouts above). The values and the results are those of the row-major
+ *      tables; only the addresses differ.
  * softmax_scale <= 0 selects 1 / sqrt(head_dim).
  * Errors: as paged_kv_append; n_head % n_kv_head != 0 or a table too short -> PKC_ERR_SHAPE;
  * head_dim != 64, block_size not a power of two >= 8, a chunk too long for the kernel's LDS
@@ -207,10 +223,10 @@ pkc_status paged_kv_append_relpos_attn(pkc_dtype dtype, const void* q, const voi
  *
  * q, k_new, v_new, k_pool, v_pool, pos, pos_bias_u, pos_bias_v, out: HOST arrays of n_layers
  * device pointers, entry l being layer l's buffer of the layout above (entries may repeat, e.g.
- * one positional table for every layer). block_tables, cache_seqlens, chunk_lens and every size
- * window_start and every size are shared by the layers. Layer l's kernel is enqueued after layer l - 1's on the stream; the
- * results equal n_layers calls of paged_kv_append_relpos_attn. The pointer arrays are read during
- * the call only.
+ * one positional table for every layer). block_tables, cache_seqlens, chunk_lens, window_start
+ * and every size argument are shared by the layers. Layer l's kernel is enqueued after layer
+ * l - 1's on the stream; the results equal n_layers calls of paged_kv_append_relpos_attn. The
+ * pointer arrays are read during the call only.
  * Errors: those of paged_kv_append_relpos_attn for any layer, n_layers <= 0 -> PKC_ERR_SHAPE.
  * Every layer is validated before any kernel is enqueued, so an error enqueues nothing.
  */
@@ -237,6 +253,11 @@ pkc_status paged_kv_append_relpos_attn_layers(
  * dividing chunk_size; recycle_streaming_history is the ring's own capacity, at most
  * max_blocks_per_seq * block_size - chunk_size). Without it, keeping cache_seqlens within
  * max_cache_seqlen is the caller's business (the next attention call clamps, it does not fail).
+ * Only whole blocks that are already filled are dropped (at most cache_seqlens[b] / block_size
+ * of them): the next chunk is written right after the cached frames, so the window start never
+ * passes that position and cache_seqlens never goes negative; with a cap below one block a
+ * partly filled last block therefore stays (e.g. 13 cached frames, block_size 8, cap 0: one block
+ * goes, 5 frames stay). A negative stored length is written back as 0.
  * Errors: NULL cache_seqlens -> PKC_ERR_NULL; batch or chunk_size <= 0, or with window_start a
  * block_size <= 0 or a negative cap -> PKC_ERR_SHAPE.
  */
@@ -333,6 +354,29 @@ pkc_status rel_pos_projection(pkc_dtype dtype, const void* w_pos, const int32_t*
                               int32_t pos_first, int32_t pos_step, int32_t n_tables, int32_t rows,
                               int32_t d_model, int32_t out_features, void* pos_out,
                               hipStream_t stream);
+
+/*
+ * pkc_gather_read - a measurement entry, not an attention: the memory-path ceiling of one
+ * paged_kv_append_relpos_attn launch [ENG 4.3], [MOD fix]. It reads every byte that launch reads
+ * (queries, u, v, k_new, v_new, the cached pages through block_tables, the positional band rows
+ * of every 32-key step) with the attention kernel's own per-lane addresses, writes the chunk's
+ * K/V into the pools exactly as paged_kv_append does, and writes unspecified values (an XOR of
+ * what it read) into out. It does no arithmetic, so its launch time is what the access pattern
+ * costs at a launch shape: waves (4 or 8) wavefronts per workgroup and split (1, 2 or 4)
+ * workgroups per (stream, head); split > 1 omits the merge a split attention would need.
+ * Arguments are those of paged_kv_append_relpos_attn (no chunk lengths or window starts).
+ * Errors: as paged_kv_append_relpos_attn; waves or split outside those sets -> PKC_ERR_SHAPE;
+ * fp32, chunk_size > 16 or PKC_POS_PER_KEY -> PKC_ERR_UNSUPPORTED.
+ */
+pkc_status pkc_gather_read(pkc_dtype dtype, const void* q, const void* k_new, const void* v_new,
+                           void* k_pool, void* v_pool, const int32_t* block_tables,
+                           const int32_t* cache_seqlens, const void* pos, int32_t pos_len,
+                           int32_t pos_layout, const void* pos_bias_u, const void* pos_bias_v,
+                           void* out, int32_t batch, int32_t chunk_size, int32_t n_head,
+                           int32_t n_kv_head, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_cache_seqlen, int32_t waves, int32_t split,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -14,9 +14,10 @@ Sources, cited by page title and section (OASR documentation):
   with a per-stream length mask built from cache_seqlens, and the Conformer relative-position bias
   matrix_bd is added to the scores scaled by 1/sqrt(d_k); the positional embedding is built per
   stream when offsets differ and collapses to one broadcast table when they match.
-* "Model Layer", "Three optional encoder declarations" (fixed_attention_window): a Transformer-XL
-  table's distances are cache + i - j; a uniform cache_seqlens lets one shared table serve the
-  whole cohort, otherwise each row needs its own table.
+* "Model Layer", "Three optional encoder declarations" (fixed_attention_window): the query at
+  chunk row i and the key at index j sit cache + i - j frames apart, and that offset selects the
+  Transformer-XL table row; when every stream has the same cache_seqlens a single table serves
+  the cohort, and otherwise each stream gets a table of its own.
 * "Model Layer", "The engine-facing surface" (forward_offline_packed) and "ASR Engine" section 4.1
   (sequence packing): the offline forward packs utterances into one gapless varlen row and
   attention never crosses an utterance boundary.
@@ -114,7 +115,9 @@ def commit_chunk(cache_seqlens, chunk, chunk_lens=None, window_start=None, max_c
                  block_size=None):
     """After a step: cache_b += n_b ("ASR Engine" section 4.3 step 6, commit_chunk_paged). With a
     window start and a cap (bounded history, "ASR Engine" sections 6 and 9), the oldest whole
-    blocks are then dropped while cache_b exceeds the cap: w_b += S, cache_b -= S. Returns the new
+    blocks are then dropped while cache_b exceeds the cap: w_b += S, cache_b -= S, as long as a
+    whole filled block is left to drop (cache_b >= S; a cap below one block then keeps the
+    partial last block rather than dropping frames that are still to be written). Returns the new
     (cache_seqlens, window_start) as int64 arrays (window_start None when not given)."""
     cache = np.array(cache_seqlens, dtype=np.int64, copy=True)
     lens = np.full(cache.shape, chunk) if chunk_lens is None else np.asarray(chunk_lens)
@@ -124,7 +127,9 @@ def commit_chunk(cache_seqlens, chunk, chunk_lens=None, window_start=None, max_c
     start = np.array(window_start, dtype=np.int64, copy=True)
     if max_cached_frames is not None:
         for b in range(len(cache)):
-            while cache[b] > max_cached_frames:
+            # only whole blocks that are already filled can leave: the next chunk's frames are
+            # written right after the cached ones, so a block they reach stays in the window
+            while cache[b] > max_cached_frames and cache[b] >= block_size:
                 start[b] += block_size
                 cache[b] -= block_size
     return cache, start

@@ -36,7 +36,8 @@ pkc_status check_pool(int32_t batch, int32_t chunk, int32_t n_kv_head, int32_t h
 pkc_status check_attn(int32_t chunk, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
                       int32_t block_size, int32_t max_cache, int32_t pos_len, int32_t pos_layout) {
   if (n_head <= 0 || n_head % n_kv_head != 0) return PKC_ERR_SHAPE;
-  if (pos_layout < 0 || pos_layout > (PKC_POS_PER_ROW | PKC_POS_PER_KEY)) return PKC_ERR_SHAPE;
+  if (pos_layout < 0 || pos_layout > (PKC_POS_PER_ROW | PKC_POS_PER_KEY | PKC_POS_COL_BLOCKED))
+    return PKC_ERR_SHAPE;
   const int64_t longest = (int64_t)max_cache + chunk;
   if (pos_layout & PKC_POS_PER_KEY) {
     // one row per key, shared or per stream
@@ -49,7 +50,6 @@ pkc_status check_attn(int32_t chunk, int32_t n_head, int32_t n_kv_head, int32_t 
   }
   if (head_dim != 64) return PKC_ERR_UNSUPPORTED;
   if (block_size < 8 || (block_size & (block_size - 1)) != 0) return PKC_ERR_UNSUPPORTED;
-  if ((longest + block_size - 1) / block_size > kMaxStagedBlocks) return PKC_ERR_UNSUPPORTED;
   return PKC_OK;
 }
 
@@ -230,6 +230,32 @@ pkc_status paged_kv_append_relpos_attn_layers(
     }
   }
   return PKC_OK;
+}
+
+pkc_status pkc_gather_read(pkc_dtype dtype, const void* q, const void* k_new, const void* v_new,
+                           void* k_pool, void* v_pool, const int32_t* block_tables,
+                           const int32_t* cache_seqlens, const void* pos, int32_t pos_len,
+                           int32_t pos_layout, const void* pos_bias_u, const void* pos_bias_v,
+                           void* out, int32_t batch, int32_t chunk_size, int32_t n_head,
+                           int32_t n_kv_head, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_cache_seqlen, int32_t waves, int32_t split,
+                           hipStream_t stream) {
+  if (!k_new || !v_new) return PKC_ERR_NULL;
+  pkc_status st = attn_common(dtype, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool,
+                              block_tables, cache_seqlens, nullptr, nullptr, pos, pos_len,
+                              pos_layout, pos_bias_u, pos_bias_v, out, batch, chunk_size, n_head,
+                              n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                              max_cache_seqlen, 0.f, stream, false);
+  if (st != PKC_OK) return st;
+  if ((waves != 4 && waves != 8) || (split != 1 && split != 2 && split != 4)) return PKC_ERR_SHAPE;
+  if (dtype != PKC_BF16 || chunk_size > 16 || (pos_layout & PKC_POS_PER_KEY))
+    return PKC_ERR_UNSUPPORTED;
+  if (gather_read_workgroups(batch, n_head, split) >= (int64_t)1 << 31) return PKC_ERR_UNSUPPORTED;
+  GatherParams p{q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u,
+                 pos_bias_v, out, batch, chunk_size, n_head, n_kv_head, block_size, num_blocks,
+                 max_blocks_per_seq, max_cache_seqlen, pos_len, pos_layout, waves, split};
+  return from_hip(launch_gather_read(p, stream));
 }
 
 pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,

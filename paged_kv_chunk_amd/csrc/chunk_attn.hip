@@ -80,6 +80,11 @@ struct ChunkArgs {
   int C, H, Hk, S, logS, N, M, max_cache, pos_len, per_row, per_key, qtiles;
   FastDiv div_qtiles, div_H, div_group;   // by qtiles, H and H / Hk
   int tail_cap, vt_pitch;            // LDS tail geometry (keys, elements per V^T row)
+  // positional table geometry (elements): between consecutive rows, between the two 32-dim
+  // halves of a row, and between heads. Row-major [.., P, H, D]: H D, 32, D. In 32-dim column
+  // blocks [.., H, D / 32, P, 32]: 32, 32 P, D P - a 16-row fragment half is then one contiguous
+  // kilobyte, whole 128-byte lines, where row-major rows give each load half-lines.
+  int band_rs, band_hs, band_hd;
   int off_bt, off_kt, off_vt;        // byte offsets of the LDS regions
   float scale_log2;
 };
@@ -202,8 +207,9 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const int rlo = R0 - (a.C - 1);
   const int rhi = R0 + T_len - 1;
   const int qlast = qt * 16 + 15;
-  const size_t prow = (size_t)a.H * kD;
-  const T* ptab = a.pos + (a.per_row ? (size_t)b * a.pos_len * prow : 0) + (size_t)h * kD;
+  const T* ptab = a.pos + (a.per_row ? (size_t)b * a.pos_len * a.H * kD : 0) + (size_t)h * a.band_hd;
+  const size_t prow = (size_t)a.band_rs;
+  const int phalf = a.band_hs;
   auto band_row = [&](int r) { return ptab + (size_t)(uint32_t)clampi(r, rlo, rhi) * prow; };
   // per-key tables (WeNet's convention, no shift): row j is key j's own embedding; keys past the
   // last one read its row (they are masked)
@@ -215,7 +221,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     for (int tt = 0; tt < 2; ++tt) {
       const T* row = key_row(j0 + 8 * (m16 >> 2) + 4 * tt + (m16 & 3)) + 8 * grp;
       p[tt][0] = load8(row);
-      p[tt][1] = load8(row + 32);
+      p[tt][1] = load8(row + phalf);
     }
   };
 
@@ -253,7 +259,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       for (int t = 0; t < 2; ++t) {
         const T* row = band_row(rb + 16 * (t + 1) + m16) + 8 * grp;
         r.p[t][0] = load8(row);
-        r.p[t][1] = load8(row + 32);
+        r.p[t][1] = load8(row + phalf);
       }
     }
   };
@@ -272,7 +278,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       for (int t = 0; t < 3; ++t) {
         const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
         tb[t][0] = load8(row);
-        tb[t][1] = load8(row + 32);
+        tb[t][1] = load8(row + phalf);
       }
     }
   }
@@ -285,7 +291,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
     if (!kPerKey) {
       const T* row = band_row(R0 + 32 * min(s_begin, s_last) - qlast + m16) + 8 * grp;
       p0[0] = load8(row);
-      p0[1] = load8(row + 32);
+      p0[1] = load8(row + phalf);
     }
     load_step(ra, min(s_begin, s_last));
     load_step(rb2, min(s_begin + 1, s_last));
@@ -409,7 +415,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
         for (int t = 0; t < 3; ++t) {
           const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
           pb[t][0] = load8(row);
-          pb[t][1] = load8(row + 32);
+          pb[t][1] = load8(row + phalf);
         }
       }
       floatx4 g[3];
@@ -550,14 +556,11 @@ template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false, 
 void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
   auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey, kGen>;
   if (smem > 64 * 1024) {
-    // beyond the default dynamic LDS size (long chunks): opt in once; MI355X allows 160 KB per
+    // beyond the default dynamic LDS size (long chunks): opt in on every such call, so that no
+    // state is kept between calls (a host-side attribute, no GPU work); MI355X allows 160 KB per
     // workgroup
-    static bool opted = false;
-    if (!opted) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynamicLds);
-      opted = true;
-    }
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   }
   hipLaunchKernelGGL(fn, grid, dim3(waves_of<T>() * 64), smem, stream, a);
 }
@@ -631,6 +634,10 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   a.pos_len = p.pos_len;
   a.per_row = p.pos_layout & PKC_POS_PER_ROW;
   a.per_key = (p.pos_layout & PKC_POS_PER_KEY) != 0;
+  const bool blocked = (p.pos_layout & PKC_POS_COL_BLOCKED) != 0;
+  a.band_rs = blocked ? 32 : p.n_head * kD;
+  a.band_hs = blocked ? 32 * p.pos_len : 32;
+  a.band_hd = blocked ? kD * p.pos_len : kD;
   a.qtiles = (p.chunk + 15) / 16;
   a.div_qtiles = make_fastdiv(a.qtiles);
   a.div_H = make_fastdiv(a.H);

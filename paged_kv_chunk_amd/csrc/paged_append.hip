@@ -86,11 +86,13 @@ commit_kernel(int32_t* __restrict__ cache_seqlens, const int32_t* __restrict__ c
   if (b >= batch) return;
   int cache = cache_seqlens[b] + (chunk_lens ? clampi(chunk_lens[b], 0, chunk) : chunk);
   if (window_start && cache > max_cached) {
-    const int drop = (cache - max_cached + block_size - 1) / block_size;
+    // only whole filled blocks leave: the next chunk is written right after the cached frames,
+    // so a partly filled block stays (with a cap below one block, cache then stays above it)
+    const int drop = min((cache - max_cached + block_size - 1) / block_size, max(cache, 0) / block_size);
     window_start[b] += drop * block_size;
     cache -= drop * block_size;
   }
-  cache_seqlens[b] = cache;
+  cache_seqlens[b] = max(cache, 0);
 }
 
 }  // namespace

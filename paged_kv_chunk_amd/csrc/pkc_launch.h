@@ -91,6 +91,23 @@ struct PosProjParams {
   int pos_first, pos_step, n_tables, rows, d_model, out_features;
 };
 
+// The memory-path ceiling of a fused launch (gather_read.hip): the same bytes, no arithmetic
+struct GatherParams {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* cache_seqlens;
+  const void* pos;
+  const void* pos_bias_u;
+  const void* pos_bias_v;
+  void* out;
+  int batch, chunk, n_head, n_kv_head, block_size, num_blocks, max_blocks, max_cache;
+  int pos_len, pos_layout, waves, split;
+};
+
 hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream);
 hipError_t launch_linear(pkc_dtype dtype, const GemmParams& p, hipStream_t stream);
 hipError_t launch_qkv_append(pkc_dtype dtype, const QkvParams& p, hipStream_t stream);
@@ -99,9 +116,8 @@ hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int3
                          int max_cached, int block_size, int batch, int chunk, hipStream_t stream);
 hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream);
 hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_t stream);
+hipError_t launch_gather_read(const GatherParams& p, hipStream_t stream);
 
-// Largest number of pages per stream the attention kernel stages in LDS.
-constexpr int kMaxStagedBlocks = 4096;
 
 // Dynamic LDS of one chunk-attention workgroup, and the budget it must fit.
 size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int max_cache, int block_size, bool fused);
@@ -111,5 +127,6 @@ constexpr size_t kMaxDynamicLds = 160 * 1024;
 // multiply-shift divisions, so a launch must stay below 2^31 workgroups.
 int64_t chunk_attn_workgroups(int batch, int n_head, int chunk);
 int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen);
+int64_t gather_read_workgroups(int batch, int n_head, int split);
 
 }  // namespace pkc

@@ -17,6 +17,8 @@ from .cohorts import (  # noqa: F401
     embed_distances,
     descending_table,
     column_blocked,
+    column_blocked_table,
+    add_blocked_table,
     key_position_tables,
     use_key_position_tables,
     linear_weights,

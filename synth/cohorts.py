@@ -70,6 +70,24 @@ def column_blocked(k_pool):
     return k_pool.reshape(n, hk, s, d // 32, 32).permute(0, 1, 3, 2, 4).contiguous()
 
 
+def column_blocked_table(pos, per_row):
+    """A positional table stored in 32-dim column blocks per head (a layout change only):
+    [P, H, D] -> [H, D / 32, P, 32], or per row [B, P, H, D] -> [B, H, D / 32, P, 32]. Element
+    (r, h, d) lands at (h, d // 32, r, d % 32)."""
+    if per_row:
+        B, P, H, D = pos.shape
+        return pos.reshape(B, P, H, D // 32, 32).permute(0, 2, 3, 1, 4).contiguous()
+    P, H, D = pos.shape
+    return pos.reshape(P, H, D // 32, 32).permute(1, 2, 0, 3).contiguous()
+
+
+def add_blocked_table(co):
+    """Give a cohort the column-blocked copy of its positional table (co.pos stays row-major,
+    as the oracle reads it)."""
+    co.pos_cb = column_blocked_table(co.pos, co.per_row_pos)
+    return co
+
+
 def key_position_tables(proj, starts, width, n_head, head_dim):
     """Per-key tables (WeNet's convention): row j of table b is the projected sinusoid of the
     absolute position starts[b] + j; float64 [len(starts), width, n_head, head_dim]."""
@@ -87,6 +105,7 @@ def use_key_position_tables(co, starts, per_row=True):
     co.pos = (tabs if per_row else tabs[0]).to(co.q.dtype).to(co.q.device)
     co.per_row_pos = per_row
     co.per_key_pos = True
+    co.pos_cb = None
     return co
 
 
@@ -132,6 +151,7 @@ class ChunkCohort:
     max_cache_seqlen: int
     meta: dict = field(default_factory=dict)
     per_key_pos: bool = False     # pos rows are keys (WeNet), not distances
+    pos_cb: torch.Tensor = None   # the same table in 32-dim column blocks (add_blocked_table)
 
     @property
     def shape(self):

@@ -109,7 +109,7 @@ def test_append_validation(lib, kw, status):
     (dict(pos_len=158), SHAPE),                      # even shared table
     (dict(pos_len=157), SHAPE),                      # (157 - 1) / 2 < 64 + 16 - 1
     (dict(per_row=1, pos_len=158), SHAPE),           # per-row needs 2 * 80 - 1
-    (dict(per_row=4), SHAPE), (dict(per_row=-1), SHAPE),
+    (dict(per_row=8), SHAPE), (dict(per_row=12), SHAPE), (dict(per_row=-1), SHAPE),
     (dict(per_row=2, pos_len=79), SHAPE),            # per-key table needs 64 + 16 rows
     (dict(per_row=3, pos_len=79), SHAPE),
     (dict(D=128), UNSUP), (dict(S=12, M=12), UNSUP), (dict(S=24, M=12), UNSUP),
@@ -252,3 +252,96 @@ def pos_call(lib, dtype=1, w=P, start=None, first=80, step=-1, n_tables=1, rows=
 ])
 def test_rel_pos_projection_validation(lib, kw, status):
     assert pos_call(lib, **kw) == status
+
+
+# --------------------------------------------------------------------------------------------
+# The binding checks every size the kernels index by, before calling into the library
+# --------------------------------------------------------------------------------------------
+
+def _chunk_args(B=2, C=16, H=4, Hk=4, D=64, S=16, N=32, M=8, P=159, per_row=False, blocked=False):
+    import torch
+    z = lambda *s: torch.zeros(*s)
+    if blocked:
+        pos = z(B, H, D // 32, P, 32) if per_row else z(H, D // 32, P, 32)
+    else:
+        pos = z(B, P, H, D) if per_row else z(P, H, D)
+    return dict(q=z(B, C, H, D), k_new=z(B, C, Hk, D), v_new=z(B, C, Hk, D),
+                k_pool=z(N, Hk, D // 32, S, 32), v_pool=z(N, Hk, D, S),
+                block_tables=torch.zeros(B, M, dtype=torch.int32),
+                cache_seqlens=torch.zeros(B, dtype=torch.int32), pos=pos, pos_bias_u=z(H, D),
+                pos_bias_v=z(H, D), out=z(B, C, H, D))
+
+
+def _fused(a, **kw):
+    return pkc.paged_kv_append_relpos_attn(a["q"], a["k_new"], a["v_new"], a["k_pool"],
+                                           a["v_pool"], a["block_tables"], a["cache_seqlens"],
+                                           a["pos"], a["pos_bias_u"], a["pos_bias_v"], 64,
+                                           out=a["out"], **kw)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(out=(2, 16, 4, 32)), dict(out=(1, 16, 4, 64)), dict(pos_bias_u=(4, 32)),
+    dict(pos_bias_v=(2, 64)), dict(k_new=(2, 8, 4, 64)), dict(v_new=(2, 16, 2, 64)),
+    dict(pos=(159, 2, 64)), dict(pos=(159, 4, 32)), dict(block_tables=(1, 8)),
+    dict(cache_seqlens=(1,)), dict(v_pool=(32, 4, 64, 8)),
+])
+def test_binding_rejects_mis_shaped_tensors(lib, bad):
+    """Any size disagreeing with q / the pools raises ValueError in Python (no kernel could be
+    launched with it: the C ABI sees only pointers)."""
+    import torch
+    a = _chunk_args()
+    for k, shape in bad.items():
+        a[k] = torch.zeros(*shape, dtype=a[k].dtype)
+    with pytest.raises(ValueError):
+        _fused(a)
+
+
+def test_binding_checks_lengths_windows_and_table_layouts(lib):
+    import torch
+    a = _chunk_args()
+    with pytest.raises(ValueError, match="chunk_lens"):
+        _fused(a, chunk_lens=torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="window_start"):
+        _fused(a, window_start=torch.zeros(1, dtype=torch.int32))
+    # per-row tables need one table per stream, in the layout the flags name
+    with pytest.raises(ValueError, match="pos"):
+        _fused(_chunk_args(per_row=False), per_row_pos=True)
+    pr = _chunk_args(per_row=True)
+    pr["pos"] = pr["pos"][:1]
+    with pytest.raises(ValueError, match="pos"):
+        _fused(pr, per_row_pos=True)
+    with pytest.raises(ValueError, match="pos"):
+        _fused(_chunk_args(blocked=False), pos_blocked=True)
+    with pytest.raises(ValueError, match="pos"):
+        _fused(_chunk_args(blocked=True), pos_blocked=False)
+    # correctly shaped host tensors pass every shape check and stop at the device check
+    for per_row in (False, True):
+        for blocked in (False, True):
+            with pytest.raises(ValueError, match="GPU"):
+                _fused(_chunk_args(per_row=per_row, blocked=blocked), per_row_pos=per_row,
+                       pos_blocked=blocked)
+
+
+def test_binding_checks_varlen_and_commit_shapes(lib):
+    import torch
+    H, D, total = 2, 64, 40
+    q = torch.zeros(total, H, D)
+    k = torch.zeros(total, H, D)
+    cu = torch.tensor([0, 15, 40], dtype=torch.int32)
+    u = torch.zeros(H, D)
+    good_pos = torch.zeros(2 * total, H, D)
+    with pytest.raises(ValueError, match="pos"):
+        pkc.varlen_packed_relpos_attn(q, k, k, cu, torch.zeros(2 * total - 1, H, D), u, u, 25)
+    with pytest.raises(ValueError, match="k must"):
+        pkc.varlen_packed_relpos_attn(q, k[:-1], k, cu, good_pos, u, u, 25)
+    with pytest.raises(ValueError, match="v must"):
+        pkc.varlen_packed_relpos_attn(q, k, k[:, :1], cu, good_pos, u, u, 25)
+    with pytest.raises(ValueError, match="out"):
+        pkc.varlen_packed_relpos_attn(q, k, k, cu, good_pos, u, u, 25, out=q[:-1])
+    with pytest.raises(ValueError, match="GPU"):
+        pkc.varlen_packed_relpos_attn(q, k, k, cu, good_pos, u, u, 25)
+    cs = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="max_cached_frames"):
+        pkc.paged_kv_commit(cs, 16, window_start=torch.zeros(4, dtype=torch.int32), block_size=8)
+    with pytest.raises(ValueError, match="chunk_lens"):
+        pkc.paged_kv_commit(cs, 16, chunk_lens=torch.zeros(3, dtype=torch.int32))

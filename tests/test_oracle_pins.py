@@ -605,6 +605,17 @@ def test_commit_keeps_the_window_at_the_cap_by_whole_blocks():
     assert cache.tolist() == [19] and start is None
 
 
+def test_commit_drops_only_filled_blocks():
+    """A cap below one block: 0 + 13 frames with 8-frame blocks and cap 0 drops the one filled
+    block and keeps the 5 frames of the partly filled one (the next chunk continues it); dropping
+    two blocks would have left -3 frames and a window start past the next write position."""
+    cache, start = oracle.commit_chunk(np.array([0, 0, 2]), 16, chunk_lens=np.array([13, 16, 5]),
+                                       window_start=np.array([0, 8, 16]), max_cached_frames=0,
+                                       block_size=8)
+    assert cache.tolist() == [5, 0, 7] and start.tolist() == [8, 24, 16]
+    assert (cache >= 0).all()
+
+
 # --------------------------------------------------------------------------------------------
 # Other conventions: WeNet's per-key table (no shift) and the chunked_limited mask
 # --------------------------------------------------------------------------------------------
