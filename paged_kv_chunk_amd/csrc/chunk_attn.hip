@@ -265,11 +265,11 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   };
   // table rows of this wave's first tail step (band tiles 0, 1, 2, or the 32 keys' rows of a
   // per-key table in tb[0..1]): requested first, so that waiting for them waits for nothing
-  // else; the tail step then runs while the body's data is still on its way. A wave without a
-  // tail step requests wave 0's rows (the same lines: cache hits).
+  // else; the tail step then runs while the body's data is still on its way. Only the waves
+  // that have a tail step request them (the branch is uniform over each wave).
   F tb[3][2];
-  {
-    const int k0 = wave < ntail ? wave : 0;
+  if (wave < ntail) {
+    const int k0 = wave;
     if constexpr (kPerKey) {
       load_key_rows(*reinterpret_cast<F(*)[2][2]>(&tb[0]), cache + 32 * k0);
     } else {
