@@ -364,9 +364,11 @@ pkc_status rel_pos_projection(pkc_dtype dtype, const void* w_pos, const int32_t*
  * what it read) into out. It does no arithmetic, so its launch time is what the access pattern
  * costs at a launch shape: waves (4 or 8) wavefronts per workgroup and split (1, 2 or 4)
  * workgroups per (stream, head); split > 1 omits the merge a split attention would need.
+ * reads = 0 runs the same grid but only writes out (reads nothing, appends nothing): the floor
+ * that launching and retiring the grid costs.
  * Arguments are those of paged_kv_append_relpos_attn (no chunk lengths or window starts).
- * Errors: as paged_kv_append_relpos_attn; waves or split outside those sets -> PKC_ERR_SHAPE;
- * fp32, chunk_size > 16 or PKC_POS_PER_KEY -> PKC_ERR_UNSUPPORTED.
+ * Errors: as paged_kv_append_relpos_attn; waves, split or reads outside those sets ->
+ * PKC_ERR_SHAPE; fp32, chunk_size > 16 or PKC_POS_PER_KEY -> PKC_ERR_UNSUPPORTED.
  */
 pkc_status pkc_gather_read(pkc_dtype dtype, const void* q, const void* k_new, const void* v_new,
                            void* k_pool, void* v_pool, const int32_t* block_tables,
@@ -376,7 +378,7 @@ pkc_status pkc_gather_read(pkc_dtype dtype, const void* q, const void* k_new, co
                            int32_t n_kv_head, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_cache_seqlen, int32_t waves, int32_t split,
-                           hipStream_t stream);
+                           int32_t reads, hipStream_t stream);
 
 #ifdef __cplusplus
 }

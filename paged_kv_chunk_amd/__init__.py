@@ -40,7 +40,7 @@ SIGNATURES = {
     "pkc_linear": ([ctypes.c_int] + [_ptr] * 4 + [_i32] * 3 + [_ptr], ctypes.c_int),
     "paged_kv_qkv_append": ([ctypes.c_int] + [_ptr] * 10 + [_i32] * 10 + [_ptr], ctypes.c_int),
     "rel_pos_projection": ([ctypes.c_int, _ptr, _ptr] + [_i32] * 6 + [_ptr, _ptr], ctypes.c_int),
-    "pkc_gather_read": ([ctypes.c_int] + [_ptr] * 8 + [_i32, _i32] + [_ptr] * 3 + [_i32] * 11
+    "pkc_gather_read": ([ctypes.c_int] + [_ptr] * 8 + [_i32, _i32] + [_ptr] * 3 + [_i32] * 12
                         + [_ptr], ctypes.c_int),
 }
 
@@ -419,9 +419,10 @@ def rel_pos_projection(w_pos, rows, pos_start=None, pos_first=0, pos_step=-1, n_
 
 def gather_read(q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u,
                 pos_bias_v, max_cache_seqlen, out, per_row_pos=False, pos_blocked=False, waves=4,
-                split=1, stream=None):
+                split=1, reads=True, stream=None):
     """Measurement only: one launch that moves the bytes of paged_kv_append_relpos_attn with no
-    arithmetic (the pools get the chunk's K/V; ``out`` gets unspecified values)."""
+    arithmetic (the pools get the chunk's K/V; ``out`` gets unspecified values). reads=False:
+    the same grid only writes ``out`` (the launch floor)."""
     B, C, H, D, N, Hk, S, P = _chunk_common(q, k_pool, v_pool, block_tables, cache_seqlens, pos,
                                             pos_bias_u, pos_bias_v, out, None, None, per_row_pos,
                                             pos_blocked)
@@ -431,5 +432,5 @@ def gather_read(q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, po
         _p(k_new), _p(v_new), _p(k_pool), _p(v_pool), _table(block_tables), _table(cache_seqlens),
         _p(pos), P, _layout(per_row_pos, False, pos_blocked), _p(pos_bias_u),
         _p(pos_bias_v), _p(out), B, C, H, Hk, D, S, N, block_tables.shape[1],
-        int(max_cache_seqlen), int(waves), int(split), _stream(stream))
+        int(max_cache_seqlen), int(waves), int(split), int(bool(reads)), _stream(stream))
     _check(st, "pkc_gather_read")

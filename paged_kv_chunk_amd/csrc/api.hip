@@ -240,7 +240,7 @@ pkc_status pkc_gather_read(pkc_dtype dtype, const void* q, const void* k_new, co
                            int32_t n_kv_head, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, int32_t max_blocks_per_seq,
                            int32_t max_cache_seqlen, int32_t waves, int32_t split,
-                           hipStream_t stream) {
+                           int32_t reads, hipStream_t stream) {
   if (!k_new || !v_new) return PKC_ERR_NULL;
   pkc_status st = attn_common(dtype, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool,
                               block_tables, cache_seqlens, nullptr, nullptr, pos, pos_len,
@@ -248,13 +248,15 @@ pkc_status pkc_gather_read(pkc_dtype dtype, const void* q, const void* k_new, co
                               n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq,
                               max_cache_seqlen, 0.f, stream, false);
   if (st != PKC_OK) return st;
-  if ((waves != 4 && waves != 8) || (split != 1 && split != 2 && split != 4)) return PKC_ERR_SHAPE;
+  if ((waves != 4 && waves != 8) || (split != 1 && split != 2 && split != 4) ||
+      (reads != 0 && reads != 1))
+    return PKC_ERR_SHAPE;
   if (dtype != PKC_BF16 || chunk_size > 16 || (pos_layout & PKC_POS_PER_KEY))
     return PKC_ERR_UNSUPPORTED;
   if (gather_read_workgroups(batch, n_head, split) >= (int64_t)1 << 31) return PKC_ERR_UNSUPPORTED;
   GatherParams p{q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u,
                  pos_bias_v, out, batch, chunk_size, n_head, n_kv_head, block_size, num_blocks,
-                 max_blocks_per_seq, max_cache_seqlen, pos_len, pos_layout, waves, split};
+                 max_blocks_per_seq, max_cache_seqlen, pos_len, pos_layout, waves, split, reads};
   return from_hip(launch_gather_read(p, stream));
 }
 

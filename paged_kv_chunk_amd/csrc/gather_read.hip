@@ -18,7 +18,8 @@
 //           what the unit read: garbage, never an attention result).
 // Every load of a wave's step group is issued before the first wait: the block IDs, then the
 // pages. Split variants (split > 1) omit the cross-workgroup merge a split attention would need,
-// so they bound such a design from below.
+// so they bound such a design from below. With reads = 0 the same grid only writes its output
+// rows: the floor that launching, dispatching and retiring this grid costs.
 #include "pkc_device.h"
 #include "pkc_launch.h"
 
@@ -38,7 +39,7 @@ struct GatherArgs {
   const int32_t* cs;
   const bf16* pos;
   bf16* out;
-  int C, H, Hk, S, logS, N, M, max_cache, pos_len, per_row, split;
+  int C, H, Hk, S, logS, N, M, max_cache, pos_len, per_row, split, reads;
   int band_rs, band_hs, band_hd;   // positional table strides: row, 32-dim half, head
   FastDiv div_split, div_H, div_group;
 };
@@ -65,6 +66,14 @@ gather_read_kernel(GatherArgs a) {
   const int b = fdiv(unit, a.div_H);
   const int h = unit - b * a.H;
   const int hk = fdiv(h, a.div_group);
+  if (!a.reads) {
+    // the launch floor: the same grid writing its output rows, reading nothing
+    const int ft = tid >> 3;
+    if (part == 0 && ft < a.C)
+      *reinterpret_cast<u32x4*>(a.out + (((size_t)b * a.C + ft) * a.H + h) * kD + (tid & 7) * 8) =
+          u32x4{(uint32_t)id, 0u, 0u, 0u};
+    return;
+  }
   const int cs_raw = a.cs[b];
   __builtin_amdgcn_sched_barrier(0);
   const int32_t* bt = a.bt + (size_t)b * a.M;
@@ -246,6 +255,7 @@ hipError_t launch_gather_read(const GatherParams& p, hipStream_t stream) {
   a.band_hs = blocked ? 32 * p.pos_len : 32;
   a.band_hd = blocked ? kD * p.pos_len : kD;
   a.split = p.split;
+  a.reads = p.reads;
   a.div_split = make_fastdiv(p.split);
   a.div_H = make_fastdiv(p.n_head);
   a.div_group = make_fastdiv(p.n_head / p.n_kv_head);

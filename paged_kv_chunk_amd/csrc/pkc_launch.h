@@ -105,7 +105,7 @@ struct GatherParams {
   const void* pos_bias_v;
   void* out;
   int batch, chunk, n_head, n_kv_head, block_size, num_blocks, max_blocks, max_cache;
-  int pos_len, pos_layout, waves, split;
+  int pos_len, pos_layout, waves, split, reads;
 };
 
 hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream);

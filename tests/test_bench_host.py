@@ -78,3 +78,37 @@ def test_kernel_hash_ignores_comments_and_sees_code(tmp_path, monkeypatch):
     changed = {k: bench.kernel_source_hash(k) for k in bench.KERNEL_SOURCES}
     assert changed["chunk"] != base["chunk"] and changed["varlen"] != base["varlen"]
     assert changed["gemm"] == base["gemm"]   # the GEMM does not include the step header
+
+
+def test_host_sample_gives_the_oracle_the_same_streams():
+    """The CPU baseline's host copies of a few streams (only their pages, block IDs renumbered)
+    give the oracle exactly the result it gives on the whole cohort for those streams."""
+    import numpy as np
+    import torch
+    import bench
+    import oracle
+    from synth import make_chunk_cohort
+    bench.torch = torch
+    co = make_chunk_cohort(4, 2, 64, 16, 16, [0, 40, 129, 7], dtype=torch.float32, seed=5)
+    h = lambda t: t.detach().double().numpy()
+    bt, cs = co.block_tables.numpy(), co.cache_seqlens.numpy()
+    kp, vp = oracle.paged_kv_append(h(co.k_pool), h(co.v_pool), h(co.k_new), h(co.v_new), bt, cs)
+    full = oracle.chunk_relpos_attn(h(co.q), kp, vp, bt, cs, h(co.pos), h(co.pos_bias_u),
+                                    h(co.pos_bias_v))
+    x = bench.host_sample(co, [2, 0])
+    assert x["k_pool"].shape[0] == (129 + 16 + 15) // 16 + 1
+    kp2, vp2 = oracle.paged_kv_append(x["k_pool"], x["v_pool"], x["k_new"], x["v_new"], x["bt"],
+                                      x["cs"])
+    part = oracle.chunk_relpos_attn(x["q"], kp2, vp2, x["bt"], x["cs"], x["pos"], x["u"], x["w"])
+    np.testing.assert_array_equal(part, full[[2, 0]])
+
+
+def test_cpu_baseline_records_its_sample_and_library():
+    import torch
+    import bench
+    from synth import make_chunk_cohort
+    bench.torch = torch
+    co = make_chunk_cohort(3, 2, 64, 16, 16, [0, 16, 32], dtype=torch.float32, seed=6)
+    r = bench.cpu_baseline(co, 0.05, name="tiny")
+    assert r["value"] > 0 and r["cores"] == 1 and r["threads"] == 1 and r["kind"] == "oracle"
+    assert "blas" in r and r["sample"].startswith("tiny: 3 of 3 streams")
