@@ -293,7 +293,8 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
   if ((int64_t)2 * max_seqlen * (n_head > n_kv_head ? n_head : n_kv_head) * head_dim *
           (dtype == PKC_BF16 ? 2 : 4) >= (int64_t)1 << 31)
     return PKC_ERR_UNSUPPORTED;
-  if (varlen_attn_workgroups(num_seqs, n_head, max_seqlen) >= (int64_t)1 << 31)
+  if (varlen_attn_workgroups(num_seqs, n_head, max_seqlen, dtype == PKC_BF16 ? 2 : 4) >=
+      (int64_t)1 << 31)
     return PKC_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pos) ||
       !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))

@@ -126,7 +126,7 @@ constexpr size_t kMaxDynamicLds = 160 * 1024;
 // Workgroups of one attention launch. The kernels split the workgroup index with 31-bit
 // multiply-shift divisions, so a launch must stay below 2^31 workgroups.
 int64_t chunk_attn_workgroups(int batch, int n_head, int chunk);
-int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen);
+int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen, int dtype_bytes);
 int64_t gather_read_workgroups(int batch, int n_head, int split);
 
 }  // namespace pkc

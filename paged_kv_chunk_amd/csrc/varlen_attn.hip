@@ -6,15 +6,22 @@
 // utterance of length L is the chunk case with no cache and C = L: query i and key j read table
 // row L - 1 + j - i of the utterance's 2 L - 1 rows.
 //
-// Work decomposition. One workgroup of 4 waves per (utterance, 64-query tile, head), the head
-// varying fastest over the grid so that all tiles of one head share an XCD; wave w owns
-// queries [64 t + 16 w, + 16) outright (its own online softmax, no merge). The workgroup walks the
-// utterance's keys in 32-key steps: every step's K rows and V rows are staged once in
-// double-buffered LDS and read by all four waves. The band rows (the table rows the queries
-// touch) go through an LDS ring of 128 rows: the four waves' windows overlap, so a step brings in
-// only the 32 rows that enter the workgroup's window, instead of 32 rows per wave. Every global
-// read is issued two steps ahead. The per-step math is the shared step engine of pkc_step.h.
-// MFMA-bound in principle (6 L^2 D FLOP per utterance and head).
+// Work decomposition. One workgroup of 4 waves per (utterance, query tile, head), the head
+// varying fastest over the grid so that all tiles of one head share an XCD. For bf16 a wave owns
+// 32 queries as two 16-query MFMA tiles (a workgroup 128), for fp32 one tile (64): every K, V and
+// band fragment a wave reads from LDS then feeds both tiles, which halves the LDS reads per MFMA
+// (the CU's LDS bandwidth, shared by its four SIMDs, bounded the step). Each tile keeps its own
+// online softmax; no merge. The workgroup walks the utterance's keys in 32-key steps: every
+// step's K rows and V rows are staged once in double-buffered LDS and read by all four waves. The
+// band rows (the table rows the queries touch) go through an LDS ring of 256 rows: the waves'
+// windows overlap, so a step brings in only the 32 rows that enter the workgroup's window. Every
+// global read is issued two steps ahead. The per-step math is the shared step engine of
+// pkc_step.h. MFMA-bound in principle (6 L^2 D FLOP per utterance and head).
+//
+// Band tiles of a wave at a step: T_m = rows [xb + 16 m, xb + 16 m + 16), m = 0 .. kQT + 1, where
+// query tile k (first query q0 + 16 k) reads T_{kQT-1-k}, T_{kQT-k} and T_{kQT+1-k}. The next step's
+// T_0 and T_1 are this step's T_2 and T_3: the first band product of every tile, and (two tiles) the
+// fragments of T_1, carry over in registers, so a step reads two new band tiles from LDS.
 //
 // V staging. For bf16, V rows stay in their natural [key][head_dim] order in LDS (one 16-byte
 // write per thread) and the PV operand - 8 consecutive keys of one dimension per lane - comes
@@ -41,7 +48,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQTile = 16 * kWaves;     // queries per workgroup
+template <typename T> constexpr int kQT = sizeof(T) == 2 ? 2 : 1;   // 16-query tiles per wave
+template <typename T> constexpr int kQTile = 16 * kQT<T> * kWaves;  // queries per workgroup
 
 template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // band / fp32 K row pitch
 template <typename T> constexpr bool kSwK = sizeof(T) == 2;            // swizzled bf16 K rows
@@ -51,7 +59,10 @@ template <typename T> constexpr bool kSwK = sizeof(T) == 2;            // swizzl
 template <typename T> constexpr int kBP = sizeof(T) == 2 ? kD + 16 : kKP<T>;
 template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch (fp32)
 template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
-constexpr int kRing = 128;   // rows of the band ring (a step reads 80 and stages the next 32)
+// rows of the band ring: it spans the lowest row a step reads to the highest it stages, 64 QT + 64
+// rows, rounded up to a power of two
+template <typename T> constexpr int kRing = kQT<T> == 2 ? 256 : 128;
+constexpr int kSortMax = 64;   // utterances a wave ranks by length (one per lane)
 // Lane group g holds the keys of key_group<true>(g) (groups 1 and 2 swapped): the shifted
 // position values are then read conflict-free.
 constexpr bool kPerm = true;
@@ -77,27 +88,34 @@ struct VarlenArgs {
   const T* u;
   const T* w;
   T* out;
-  int H, Hk, qtiles, total, maxlen;
+  int H, Hk, qtiles, total, maxlen, num_seqs;
   FastDiv div_H, div_qtiles, div_group;   // by H, qtiles and H / Hk
   int chunk, left;            // chunked_limited mask (kLimited)
   float scale_log2;
 };
 
-// (three workgroups per CU: the register budget of 3 waves per SIMD)
+// (bf16: two workgroups per CU, the register budget of 2 waves per SIMD for two query tiles per
+// wave; fp32, one tile per wave: 3)
 template <typename T, bool kLimited>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 3, sizeof(T) == 2 ? 2 : 3)))
 varlen_attn_kernel(VarlenArgs<T> a) {
   typedef typename Frag<T>::type F;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int NV = kD / VEC;
   constexpr int KP = kKP<T>;
   constexpr int VP = kVP<T>;
+  constexpr int QT = kQT<T>;                                       // query tiles per wave
+  constexpr int QTILE = kQTile<T>;                                 // queries per workgroup
   constexpr int KT = kSwK<T> ? kD : KP;                            // K tile row pitch
   constexpr int TILE = 32 * KT + (kTrV<T> ? 32 * kD : kD * VP);   // elements of one K + V stage
 
   __shared__ __align__(16) T s_kv[2 * TILE];
   constexpr int BP = kBP<T>;
-  __shared__ __align__(16) T s_band[kRing * BP];   // row x of the table in slot x % 128
+  constexpr int RING = kRing<T>;
+  __shared__ __align__(16) T s_band[RING * BP];   // row x of the table in slot x % RING
+  // one shift tile per wave, used by its query tiles in turn (LDS executes a wave's accesses in
+  // order, so a tile's writes never overtake the previous tile's reads)
   __shared__ __align__(16) float s_skew[kWaves * kSkewFloats];
 
   const int tid = threadIdx.x;
@@ -109,15 +127,39 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   // head fastest: workgroups go to the 8 XCDs round-robin, so with H a multiple of 8 every tile
   // of one head lands on the same XCD and that head's tables and K/V rows stay in its L2
   const int id = blockIdx.x;
-  const int sq = fdiv(id, a.div_H);
-  const int h = id - sq * a.H;
-  const int s = fdiv(sq, a.div_qtiles);
-  const int qt = sq - s * a.qtiles;
+  const int tix = fdiv(id, a.div_H);   // query tile of the launch
+  const int h = id - tix * a.H;
+  // Longest utterances first. Workgroups start roughly in index order and every tile of an
+  // utterance walks its whole length, so a long utterance reached last sets the launch's tail.
+  // With at most 64 utterances each wave ranks them by length (descending, ties by index), lays
+  // their query tiles out in that order and takes tile tix of it; more keep the natural order.
+  int s, qt;
+  if (a.num_seqs <= kSortMax) {
+    int Lu = -1, nq = 0;   // lane u: utterance u's length and query tiles
+    if (lane < a.num_seqs) {
+      const int lo_u = clampi(a.cu[lane], 0, a.total);
+      Lu = min(clampi(a.cu[lane + 1], lo_u, a.total) - lo_u, a.maxlen);
+      nq = (Lu + QTILE - 1) / QTILE;
+    }
+    int first = 0;         // tiles of the utterances ranked before lane u's
+    for (int t = 0; t < a.num_seqs; ++t) {
+      const int Lt = __builtin_amdgcn_readlane(Lu, t);
+      const int nt = __builtin_amdgcn_readlane(nq, t);
+      first += (Lt > Lu || (Lt == Lu && t < lane)) ? nt : 0;
+    }
+    const uint64_t own = __ballot(lane < a.num_seqs && tix >= first && tix < first + nq);
+    if (own == 0) return;  // past the last tile (uniform over the workgroup)
+    s = (int)__builtin_ctzll(own);
+    qt = tix - __builtin_amdgcn_readlane(first, s);
+  } else {
+    s = fdiv(tix, a.div_qtiles);
+    qt = tix - s * a.qtiles;
+  }
   const int lo = clampi(a.cu[s], 0, a.total);
   // (an utterance longer than max_seqlen is cut to max_seqlen frames: the host bounds every byte
   // offset from an utterance's first row by 2 max_seqlen rows, so 32-bit offsets hold)
   const int L = min(clampi(a.cu[s + 1], lo, a.total) - lo, a.maxlen);
-  if (qt * kQTile >= L) return;  // uniform over the workgroup
+  if (qt * QTILE >= L) return;  // uniform over the workgroup
   const int hk = fdiv(h, a.div_group);
   const size_t krow = (size_t)a.Hk * kD;      // elements between consecutive frames of k / v
   const size_t prow = (size_t)a.H * kD;
@@ -127,38 +169,82 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   const char* ptab = reinterpret_cast<const char*>(a.pos + (size_t)(2 * lo) * prow + (size_t)h * kD);
   const uint32_t krow_b = (uint32_t)(krow * sizeof(T));
   const uint32_t prow_b = (uint32_t)(prow * sizeof(T));
-  const int q0 = qt * kQTile + 16 * wave;       // this wave's first query
+  const int q0 = qt * QTILE + 16 * QT * wave;   // this wave's first query
   const int R0 = L - 1;                         // table row of (i, j) is R0 + j - i
   const int rlo = 0, rhi = 2 * L - 2;
+  // a wave whose queries all lie past the utterance stages rows and meets the barriers, but
+  // computes nothing (uniform over the wave)
+  const int ntile = min(QT, max(0, (L - q0 + 15) >> 4));
 
   // the queries and the biases, requested first; q + u and q + v (pre-scaled into log2 units) are
   // formed after the first steps' rows are requested, so that waiting for them does not hold up
   // those requests
-  F qq[2], uu[2], ww[2];
-  {
-    const T* qrow = a.q + ((size_t)(lo + min(q0 + m16, L - 1)) * a.H + h) * kD;
+  F qq[QT][2], uu[2], ww[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int d0 = 32 * half + 8 * grp;
-      qq[half] = load8(qrow + d0);
-      uu[half] = load8(a.u + h * kD + d0);
-      ww[half] = load8(a.w + h * kD + d0);
-    }
+  for (int k = 0; k < QT; ++k) {
+    const T* qrow = a.q + ((size_t)(lo + min(q0 + 16 * k + m16, L - 1)) * a.H + h) * kD;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) qq[k][half] = load8(qrow + 32 * half + 8 * grp);
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int d0 = 32 * half + 8 * grp;
+    uu[half] = load8(a.u + h * kD + d0);
+    ww[half] = load8(a.w + h * kD + d0);
   }
 
-  // Band window. At the step whose first key is j0 the workgroup's waves read table rows
-  // [xw + j0 + 16, xw + j0 + 96), xw = R0 - (64 t + 63) for query tile t (wave w: tiles 1 and 2 of
-  // its step at xw + j0 + 64 - 16 w; tile 0 is the previous step's tile 2), and the rows
-  // [xw + j0 + 64, xw + j0 + 96) enter the window. Slots x % 128 of the rows staged at the end
-  // of a step never hold a row that step still reads, and a row is overwritten only after the
-  // barrier that ends its last use.
-  const int xw = R0 - (qt * kQTile + kQTile - 1);
+  // Band window. With C0 = R0 - (qt QTILE + 16 QT - 1), wave w's band tile T_m at the step whose
+  // first key is j0 starts at row C0 + j0 - 16 QT w + 16 m (tile k's rows R0 + j0 - i for its
+  // queries i begin at T_{QT-1-k}). Step 0 reads T_0 .. T_{QT+1} of every wave, rows
+  // [C0 + J - 48 QT, C0 + J + 16 QT + 32); a later step T_2 .. T_{QT+1} (QT = 2) or T_1, T_2 (QT = 1),
+  // the 64 QT rows below the window top C0 + j0 + 16 QT + 32. The 32 rows above that top enter for
+  // the next step: they are fetched with the K/V rows of that step, rows [xw + j0', xw + j0' + 32)
+  // for its first key j0', and staged during this one. The ring spans the lowest row a step reads
+  // to the highest it stages (at most 64 QT + 64 rows), so the rows staged during a step never take a
+  // slot that step reads, and a row is overwritten only after the barrier that ends its last use.
+  const int C0 = R0 - (qt * QTILE + 16 * QT - 1);
   // (the row and column offsets are summed in 32 bits first: one offset from the uniform base)
   auto band_src = [&](int x, uint32_t col_b) {
     return ptab + ((uint32_t)clampi(x, rlo, rhi) * prow_b + col_b);
   };
-  auto band_slot = [&](int x) { return s_band + (x & (kRing - 1)) * BP; };
+  auto band_slot = [&](int x) { return s_band + (x & (RING - 1)) * BP; };
 
+  Softmax st[QT];
+#pragma unroll
+  for (int k = 0; k < QT; ++k) {
+    st[k].m = -INFINITY;
+    st[k].l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st[k].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  float* s_g = s_skew + wave * kSkewFloats;
+
+  // the keys this workgroup's queries can see: all of the utterance, or with the chunked_limited
+  // mask the first visible key of its first query to the last of its last query; and per query
+  // column (this lane's query of each tile, clamped into the utterance) its own range
+  int j_first = 0, j_end = L, k_lo_q[QT], k_hi_q[QT];
+#pragma unroll
+  for (int k = 0; k < QT; ++k) {
+    k_lo_q[k] = 0;
+    k_hi_q[k] = L;
+  }
+  if constexpr (kLimited) {
+    const int left = min(a.left, L);   // more chunks than frames sees everything anyway
+    const int tq0 = qt * QTILE;
+    const int tq1 = min(tq0 + QTILE, L) - 1;
+    j_first = max(0, (tq0 / a.chunk - left) * a.chunk);
+    j_end = min(L, (tq1 / a.chunk + 1) * a.chunk);
+#pragma unroll
+    for (int k = 0; k < QT; ++k) {
+      const int iq = min(q0 + 16 * k + m16, L - 1);
+      k_lo_q[k] = max(0, (iq / a.chunk - left) * a.chunk);
+      k_hi_q[k] = min(L, (iq / a.chunk + 1) * a.chunk);
+    }
+  }
+  const int s_first = j_first >> 5;
+  const int nsteps = ((j_end + 31) >> 5) - s_first;
+  const int J = 32 * s_first;
+  const int xw = C0 + 16 * QT;   // band rows fetched with the step at key j0: [xw + j0, + 32)
   // cooperative staging of one 32-key step: 32 K rows, the same 32 V rows and the 32 band rows
   // entering the window. Rows past the utterance read its last frame instead: every staged value
   // is finite, so a masked key (probability exactly 0) adds nothing, and every load is
@@ -174,20 +260,20 @@ varlen_attn_kernel(VarlenArgs<T> a) {
       const uint32_t off = (uint32_t)min(j0 + idx / NV, L - 1) * krow_b + (idx % NV) * 16u;
       rr.k[it] = *reinterpret_cast<const u32x4*>(kseg + off);
       rr.v[it] = *reinterpret_cast<const u32x4*>(vseg + off);
-      rr.b[it] = *reinterpret_cast<const u32x4*>(band_src(xw + j0 + 64 + idx / NV, (idx % NV) * 16u));
+      rr.b[it] = *reinterpret_cast<const u32x4*>(band_src(xw + j0 + idx / NV, (idx % NV) * 16u));
     }
   };
-  auto stash = [&](const Rows& rr, T* st, int j0) {
+  auto stash = [&](const Rows& rr, T* stg, int j0) {
     const u32x4* kr = rr.k;
     const u32x4* vr = rr.v;
-    T* sk = st;
-    T* sv = st + 32 * KT;
+    T* sk = stg;
+    T* sv = stg + 32 * KT;
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
       const int r = idx / NV;
       const int dv = (idx % NV) * VEC;
-      *reinterpret_cast<u32x4*>(band_slot(xw + j0 + 64 + r) + dv) = rr.b[it];
+      *reinterpret_cast<u32x4*>(band_slot(xw + j0 + r) + dv) = rr.b[it];
       if constexpr (kSwK<T>)
         *reinterpret_cast<u32x4*>(sk + r * kD + 8 * ((dv >> 3) ^ k_swz(r))) = kr[it];
       else
@@ -202,76 +288,65 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     }
   };
 
-  Softmax st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float* s_g = s_skew + wave * kSkewFloats;
-
-  // the keys this workgroup's queries can see: all of the utterance, or with the chunked_limited
-  // mask the first visible key of its first query to the last of its last query; and per query
-  // column (this lane's query, clamped into the utterance) its own range [k_lo_q, k_hi_q)
-  int j_first = 0, j_end = L, k_lo_q = 0, k_hi_q = L;
-  if constexpr (kLimited) {
-    const int left = min(a.left, L);   // more chunks than frames sees everything anyway
-    const int tq0 = qt * kQTile;
-    const int tq1 = min(tq0 + kQTile, L) - 1;
-    j_first = max(0, (tq0 / a.chunk - left) * a.chunk);
-    j_end = min(L, (tq1 / a.chunk + 1) * a.chunk);
-    const int iq = min(q0 + m16, L - 1);
-    k_lo_q = max(0, (iq / a.chunk - left) * a.chunk);
-    k_hi_q = min(L, (iq / a.chunk + 1) * a.chunk);
-  }
-  const int s_first = j_first >> 5;
-  const int nsteps = ((j_end + 31) >> 5) - s_first;
   // band tile (16 rows from x, this lane's row x + m16) from the ring
-  const int xl = xw + 64 - 16 * wave + m16;   // + j0 + 16 t: this lane's row of tile t + 1
+  const int xl = C0 - 16 * QT * wave + m16;   // + j0 + 16 m: this lane's row of T_m
   auto band_tile = [&](int x, F& p_lo, F& p_hi) {
     const T* row = band_slot(x) + 8 * grp;
     p_lo = load8(row);
     p_hi = load8(row + 32);
   };
-  const int J = 32 * s_first;
-  // requests in the order they are needed: step 0's rows and the window's first 64 band rows
-  // (staged directly, once), then step 1's rows, which the prologue's waits then leave in flight
+  // requests in the order they are needed: step 0's rows and the window's first rows (staged
+  // directly, once), then step 1's rows, which the prologue's waits then leave in flight. Step 0's
+  // window is 16 QT kWaves + 32 rows: its top 32 come with step 0's fetch, the NPRE chunks of 32
+  // below them here.
+  constexpr int NPRE = QT * kWaves / 2;
+  static_assert(32 * NPRE == 16 * QT * kWaves, "the window below its top chunk is whole chunks");
   fetch(ra, J);
-  u32x4 pre[2][NLD];
+  u32x4 pre[NPRE][NLD];
 #pragma unroll
-  for (int part = 0; part < 2; ++part)
+  for (int part = 0; part < NPRE; ++part)
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
-      const int x = xw + J + 32 * part + idx / NV;
+      const int x = xw + J - 32 * (NPRE - part) + idx / NV;
       pre[part][it] = *reinterpret_cast<const u32x4*>(band_src(x, (idx % NV) * 16u));
     }
   __builtin_amdgcn_sched_barrier(0);
   fetch(rb, J + 32);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int part = 0; part < 2; ++part)
+  for (int part = 0; part < NPRE; ++part)
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
-      const int x = xw + J + 32 * part + idx / NV;
+      const int x = xw + J - 32 * (NPRE - part) + idx / NV;
       *reinterpret_cast<u32x4*>(band_slot(x) + (idx % NV) * VEC) = pre[part][it];
     }
-  F qu[2], qv[2];
+  F qu[QT][2], qv[QT][2];
 #pragma unroll
-  for (int half = 0; half < 2; ++half)
+  for (int k = 0; k < QT; ++k)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      set(qu[half], e, (get(qq[half], e) + get(uu[half], e)) * a.scale_log2);
-      set(qv[half], e, (get(qq[half], e) + get(ww[half], e)) * a.scale_log2);
-    }
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        set(qu[k][half], e, (get(qq[k][half], e) + get(uu[half], e)) * a.scale_log2);
+        set(qv[k][half], e, (get(qq[k][half], e) + get(ww[half], e)) * a.scale_log2);
+      }
   stash(ra, s_kv, J);
   __syncthreads();
-  floatx4 g_prev;
+  // carried band state: the first band product of each tile (tile k: over T_{QT-1-k}), and with
+  // two tiles the fragments of T_1
+  floatx4 g_prev[QT];
+  F c1[2];
   {
     F p_lo, p_hi;
-    band_tile(xl + J - 16, p_lo, p_hi);
-    g_prev = mma(p_lo, qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-    g_prev = mma(p_hi, qv[1], g_prev);
+#pragma unroll
+    for (int k = 0; k < QT; ++k) {
+      band_tile(xl + J + 16 * (QT - 1 - k), p_lo, p_hi);
+      g_prev[k] = mma(p_lo, qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
+      g_prev[k] = mma(p_hi, qv[k][1], g_prev[k]);
+    }
+    if constexpr (QT == 2) band_tile(xl + J + 16, c1[0], c1[1]);
   }
   // one step (index `step` from the first visible one): registers `nxt` already hold step + 1,
   // `fre` receives step + 2
@@ -279,56 +354,74 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     const int j0 = J + 32 * step;
     const T* cur = s_kv + (step & 1) * TILE;
     fetch(fre, j0 + 64);   // (past the last step: harmless re-reads of the last frame)
-    F kf[2][2], vf[4];
-    if constexpr (kSwK<T>) {
-      const int r = 8 * key_group<kPerm>(m16 >> 2) + (m16 & 3);   // tile tt reads row r + 4 tt
-      const int sw = k_swz(r);
+    if (ntile > 0) {
+      F kf[2][2], vf[4];
+      if constexpr (kSwK<T>) {
+        const int r = 8 * key_group<kPerm>(m16 >> 2) + (m16 & 3);   // tile tt reads row r + 4 tt
+        const int sw = k_swz(r);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const T* row = cur + (r + 4 * tt) * kD;
-        kf[tt][0] = load8(row + 8 * (grp ^ sw));
-        kf[tt][1] = load8(row + 8 * ((grp + 4) ^ sw));
+        for (int tt = 0; tt < 2; ++tt) {
+          const T* row = cur + (r + 4 * tt) * kD;
+          kf[tt][0] = load8(row + 8 * (grp ^ sw));
+          kf[tt][1] = load8(row + 8 * ((grp + 4) ^ sw));
+        }
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const T* row = cur + (8 * key_group<kPerm>(m16 >> 2) + 4 * tt + (m16 & 3)) * KP + 8 * grp;
+          kf[tt][0] = load8(row);
+          kf[tt][1] = load8(row + 32);
+        }
       }
-    } else {
+      if constexpr (kTrV<T>) {
+        // lane m16 of the group addresses row 8 kg + m16 / 4 (+ 4), dimensions 16 dt + 4 (m16 % 4)
+        const int r = 8 * key_group<kPerm>(grp) + (m16 >> 2);
+        const T* vlo = cur + 32 * KT + r * kD;
+        const int sw = v_swz(r);   // the same for row r + 4
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const T* row = cur + (8 * key_group<kPerm>(m16 >> 2) + 4 * tt + (m16 & 3)) * KP + 8 * grp;
-        kf[tt][0] = load8(row);
-        kf[tt][1] = load8(row + 32);
+        for (int dt = 0; dt < 4; ++dt) {
+          const int c = 4 * (((4 * dt) + (m16 & 3)) ^ sw);
+          vf[dt] = load8_tr(vlo + c, vlo + 4 * kD + c);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          vf[dt] = load8(cur + 32 * KT + (16 * dt + m16) * VP + 8 * key_group<kPerm>(grp));
+      }
+      // the new band tiles T_2 .. T_{QT+1} (with one tile per wave: T_1 and T_2)
+      F pb[QT + 1][2];
+      if constexpr (QT == 2) {
+        pb[0][0] = c1[0];
+        pb[0][1] = c1[1];
+      }
+#pragma unroll
+      for (int m = (QT == 2 ? 1 : 0); m < QT + 1; ++m)
+        band_tile(xl + j0 + 16 * (m + 1), pb[m][0], pb[m][1]);
+      // tile k reads T_{QT-1-k} (carried product) and T_{QT-k}, T_{QT+1-k}: pb[QT-1-k], pb[QT-k]
+#pragma unroll
+      for (int k = 0; k < QT; ++k) {
+        if (k < ntile) {
+          floatx4 g1 = mma(pb[QT - 1 - k][0], qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
+          g1 = mma(pb[QT - 1 - k][1], qv[k][1], g1);
+          floatx4 g2 = mma(pb[QT - k][0], qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
+          g2 = mma(pb[QT - k][1], qv[k][1], g2);
+          if constexpr (kLimited) {
+            float x[2][4];
+            skew_scores<T, kPerm>(kf, qu[k], g_prev[k], g1, g2, s_g, x);
+            softmax_pv<T, true, kPerm>(st[k], x, vf, k_lo_q[k] - j0, k_hi_q[k] - j0);
+          } else if (j0 + 32 <= L) {
+            step_compute<T, false, true, kPerm>(st[k], kf, vf, qu[k], g_prev[k], g1, g2, s_g, 32);
+          } else {
+            step_compute<T, true, true, kPerm>(st[k], kf, vf, qu[k], g_prev[k], g1, g2, s_g, L - j0);
+          }
+          g_prev[k] = g2;
+        }
+      }
+      if constexpr (QT == 2) {
+        c1[0] = pb[QT][0];
+        c1[1] = pb[QT][1];
       }
     }
-    if constexpr (kTrV<T>) {
-      // lane m16 of the group addresses row 8 kg + m16 / 4 (+ 4), dimensions 16 dt + 4 (m16 % 4)
-      const int r = 8 * key_group<kPerm>(grp) + (m16 >> 2);
-      const T* lo = cur + 32 * KT + r * kD;
-      const int sw = v_swz(r);   // the same for row r + 4
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int c = 4 * (((4 * dt) + (m16 & 3)) ^ sw);
-        vf[dt] = load8_tr(lo + c, lo + 4 * kD + c);
-      }
-    } else {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        vf[dt] = load8(cur + 32 * KT + (16 * dt + m16) * VP + 8 * key_group<kPerm>(grp));
-    }
-    F pb[2][2];
-    band_tile(xl + j0, pb[0][0], pb[0][1]);
-    band_tile(xl + j0 + 16, pb[1][0], pb[1][1]);
-    floatx4 g1 = mma(pb[0][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-    g1 = mma(pb[0][1], qv[1], g1);
-    floatx4 g2 = mma(pb[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
-    g2 = mma(pb[1][1], qv[1], g2);
-    if constexpr (kLimited) {
-      float x[2][4];
-      skew_scores<T, kPerm>(kf, qu, g_prev, g1, g2, s_g, x);
-      softmax_pv<T, true, kPerm>(st, x, vf, k_lo_q - j0, k_hi_q - j0);
-    } else if (j0 + 32 <= L) {
-      step_compute<T, false, true, kPerm>(st, kf, vf, qu, g_prev, g1, g2, s_g, 32);
-    } else {
-      step_compute<T, true, true, kPerm>(st, kf, vf, qu, g_prev, g1, g2, s_g, L - j0);
-    }
-    g_prev = g2;
     // (unconditional, also after the last step: the rows are clamped re-reads going to a buffer
     // and ring slots no later read uses, and every path back to the loop head then has the same
     // loads in flight - a path with one more pending load made the compiler drain them all at
@@ -345,16 +438,19 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   }
   if (step < nsteps) do_step(step, rb, ra);
 
-  // finish: every wave owns its 16 queries
-  st.l = column_sum(st.l);
-  const float inv = 1.f / st.l;
-  const int i = q0 + m16;
-  if (i < L) {
-    T* dst = a.out + ((size_t)(lo + i) * a.H + h) * kD;
+  // finish: every tile of every wave owns its 16 queries
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int k = 0; k < QT; ++k) {
+    const float l = column_sum(st[k].l);
+    const float inv = 1.f / l;
+    const int i = q0 + 16 * k + m16;
+    if (i < L) {
+      T* dst = a.out + ((size_t)(lo + i) * a.H + h) * kD;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[16 * dt + 4 * grp + e] = from_f<T>(st.o[dt][e] * inv);
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[16 * dt + 4 * grp + e] = from_f<T>(st[k].o[dt][e] * inv);
+    }
   }
 }
 
@@ -371,17 +467,19 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
   a.out = (T*)p.out;
   a.H = p.n_head;
   a.Hk = p.n_kv_head;
-  a.qtiles = (p.max_seqlen + kQTile - 1) / kQTile;
+  a.qtiles = (p.max_seqlen + kQTile<T> - 1) / kQTile<T>;
   a.div_H = make_fastdiv(a.H);
   a.div_qtiles = make_fastdiv(a.qtiles);
   a.div_group = make_fastdiv(a.H / a.Hk);
   a.total = p.total;
   a.maxlen = p.max_seqlen;
+  a.num_seqs = p.num_seqs;
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.chunk = p.mask_chunk;
   a.left = p.mask_left_chunks;
-  const dim3 grid((unsigned)varlen_attn_workgroups(p.num_seqs, p.n_head, p.max_seqlen));
+  const dim3 grid((unsigned)varlen_attn_workgroups(p.num_seqs, p.n_head, p.max_seqlen,
+                                                   (int)sizeof(T)));
   if (p.mask_chunk > 0)
     hipLaunchKernelGGL((varlen_attn_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
   else
@@ -391,8 +489,9 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen) {
-  return (int64_t)num_seqs * n_head * ((max_seqlen + kQTile - 1) / kQTile);
+int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen, int dtype_bytes) {
+  const int qtile = dtype_bytes == 2 ? kQTile<bf16> : kQTile<float>;
+  return (int64_t)num_seqs * n_head * ((max_seqlen + qtile - 1) / qtile);
 }
 
 hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_t stream) {

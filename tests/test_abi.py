@@ -146,9 +146,11 @@ def test_fused_validation(lib):
     # must stay under 2^31 bytes
     (dict(total=2_000_000, max_len=2_000_000), UNSUP),
     (dict(dtype=0, total=1_100_000, max_len=1_100_000, H=4, Hk=4), UNSUP),
-    # one workgroup per 64 queries of an utterance and head: 2^31 of them are refused
+    # one workgroup per 128 queries (bf16; 64 for fp32) of an utterance and head: 2^31 of them
+    # are refused
     (dict(S=1 << 20, total=100, max_len=64, H=2048, Hk=2048), UNSUP),
-    (dict(S=1 << 19, total=200, max_len=128, H=2048, Hk=1024), UNSUP),
+    (dict(S=1 << 19, total=300, max_len=256, H=2048, Hk=1024), UNSUP),
+    (dict(dtype=0, S=1 << 19, total=200, max_len=128, H=2048, Hk=1024), UNSUP),
 ])
 def test_varlen_validation(lib, kw, status):
     assert varlen(lib, **kw) == status
