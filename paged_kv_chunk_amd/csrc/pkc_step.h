@@ -35,11 +35,22 @@ __device__ __forceinline__ int key_group(int g) {
   return kPermGrp ? (((g & 1) << 1) | (g >> 1)) : g;
 }
 
-// Running softmax state of one lane (one query column, 8 keys of each step).
+// Running softmax state of one lane (one query column, 8 keys of each step). With the row sum on
+// the MFMA (kSumMfma below), ls holds it instead of l: the product of an all-ones operand with the
+// step's probabilities, the same value in every register (the column's sum of the bf16-rounded
+// probabilities that also weight the values).
 struct Softmax {
   float m, l;
   floatx4 o[4];
+  floatx4 ls;
 };
+
+template <typename T> __device__ __forceinline__ typename Frag<T>::type ones8() {
+  typename Frag<T>::type v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) set(v, e, 1.f);
+  return v;
+}
 
 // Scores of one 32-key step, Transformer-XL convention: S^T = K (q+u)^T from the two key tiles,
 // plus the band product shifted into place through the per-wave LDS tile (scores already in log2
@@ -95,7 +106,7 @@ __device__ __forceinline__ void per_key_scores(const typename Frag<T>::type (&kf
 // Online softmax and PV of one step from its scores. kMask: only keys k_lo <= key < k_hi of the
 // step count for this lane's query column (bounds may differ between columns); a column with no
 // key seen yet contributes nothing.
-template <typename T, bool kMask, bool kPermGrp = false>
+template <typename T, bool kMask, bool kPermGrp = false, bool kSumMfma = false>
 __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
                                            const typename Frag<T>::type (&vf)[4], int k_lo,
                                            int k_hi) {
@@ -117,7 +128,8 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
     // (a column that does not move keeps its scale; computing it as exp2(m - m) would give NaN
     // for a column that has seen no key yet, m = -inf)
     const float alpha = move ? fast_exp2(st.m - m_new) : 1.f;
-    st.l *= alpha;
+    if constexpr (kSumMfma) st.ls *= alpha;
+    else st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
     st.m = m_new;
@@ -131,11 +143,12 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float pe = fast_exp2(x[tt][e] - m_ref);
-      st.l += pe;
+      if constexpr (!kSumMfma) st.l += pe;
       set(pf, 4 * tt + e, pe);
     }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
+  if constexpr (kSumMfma) st.ls = mma(ones8<T>(), pf, st.ls);
 }
 
 // One whole 32-key Transformer-XL step given its operand fragments and the three band product
@@ -143,7 +156,8 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
 // stay between the two wave barriers of the shift, which keeps the register live ranges of the
 // hot loop short. kMask: keys at or past valid_keys are excluded (the same keys for every query
 // column, and never all of a step's keys).
-template <typename T, bool kMask, bool kShiftFirst = false, bool kPermGrp = false>
+template <typename T, bool kMask, bool kShiftFirst = false, bool kPermGrp = false,
+          bool kSumMfma = false>
 __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>::type (&kf)[2][2],
                                              const typename Frag<T>::type (&vf)[4],
                                              const typename Frag<T>::type (&qu)[2],
@@ -197,7 +211,8 @@ __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>
   if (__ballot(move) != 0) {
     const float m_new = move ? mx : st.m;
     const float alpha = fast_exp2(st.m - m_new);
-    st.l *= alpha;
+    if constexpr (kSumMfma) st.ls *= alpha;
+    else st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
     st.m = m_new;
@@ -208,11 +223,12 @@ __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float pe = fast_exp2(x[tt][e] - st.m);
-      st.l += pe;
+      if constexpr (!kSumMfma) st.l += pe;
       set(pf, 4 * tt + e, pe);
     }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
+  if constexpr (kSumMfma) st.ls = mma(ones8<T>(), pf, st.ls);
 }
 
 

@@ -63,6 +63,10 @@ template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natura
 // rows, rounded up to a power of two
 template <typename T> constexpr int kRing = kQT<T> == 2 ? 256 : 128;
 constexpr int kSortMax = 64;   // utterances a wave ranks by length (one per lane)
+// the softmax row sums on the MFMA (a ones operand against the probabilities) instead of eight
+// adds per lane and step; the sums are then those of the bf16-rounded probabilities the values are
+// weighted with
+constexpr bool kSumMfma = true;
 // Lane group g holds the keys of key_group<true>(g) (groups 1 and 2 swapped): the shifted
 // position values are then read conflict-free.
 constexpr bool kPerm = true;
@@ -214,6 +218,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   for (int k = 0; k < QT; ++k) {
     st[k].m = -INFINITY;
     st[k].l = 0.f;
+    st[k].ls = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st[k].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -408,11 +413,13 @@ varlen_attn_kernel(VarlenArgs<T> a) {
           if constexpr (kLimited) {
             float x[2][4];
             skew_scores<T, kPerm>(kf, qu[k], g_prev[k], g1, g2, s_g, x);
-            softmax_pv<T, true, kPerm>(st[k], x, vf, k_lo_q[k] - j0, k_hi_q[k] - j0);
+            softmax_pv<T, true, kPerm, kSumMfma>(st[k], x, vf, k_lo_q[k] - j0, k_hi_q[k] - j0);
           } else if (j0 + 32 <= L) {
-            step_compute<T, false, true, kPerm>(st[k], kf, vf, qu[k], g_prev[k], g1, g2, s_g, 32);
+            step_compute<T, false, true, kPerm, kSumMfma>(st[k], kf, vf, qu[k], g_prev[k], g1, g2,
+                                                          s_g, 32);
           } else {
-            step_compute<T, true, true, kPerm>(st[k], kf, vf, qu[k], g_prev[k], g1, g2, s_g, L - j0);
+            step_compute<T, true, true, kPerm, kSumMfma>(st[k], kf, vf, qu[k], g_prev[k], g1, g2,
+                                                         s_g, L - j0);
           }
           g_prev[k] = g2;
         }
@@ -441,7 +448,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   // finish: every tile of every wave owns its 16 queries
 #pragma unroll
   for (int k = 0; k < QT; ++k) {
-    const float l = column_sum(st[k].l);
+    const float l = kSumMfma ? st[k].ls[0] : column_sum(st[k].l);
     const float inv = 1.f / l;
     const int i = q0 + 16 * k + m16;
     if (i < L) {
