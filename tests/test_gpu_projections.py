@@ -205,15 +205,14 @@ def test_qkv_append_then_attention_equals_append_of_projected_rows():
 
 def _pos_bound(w64, pos, dtype, d_model, ref):
     """Per-element tolerance of a projected sinusoid table [n, rows, N]."""
-    i = np.arange(d_model // 2)
-    f = np.power(10000.0, -2.0 * i / d_model)
     emb = oracle.sinusoid(pos.reshape(-1), d_model)
     absprod = np.abs(emb) @ np.abs(w64).T
     if dtype == BF16:
         extra = 2.0 ** -8 * absprod
     else:
-        phase = np.repeat(np.abs(pos.reshape(-1, 1)) * f[None, :] + 4.0, 2, axis=1) * 2.0 ** -23
-        extra = phase @ np.abs(w64).T
+        # the phase is reduced exactly (fp64) before fp32 sees it, so its error, about 2^-25
+        # turns, and the fp32 sine's own few ulps do not grow with |p|
+        extra = np.broadcast_to(2.0 ** -21 * np.abs(w64).sum(axis=1), absprod.shape)
     return bound(ref, absprod.reshape(ref.shape), dtype, d_model) + extra.reshape(ref.shape)
 
 
@@ -249,6 +248,24 @@ def test_rel_pos_projection_parity(case, dtype):
     pos = oracle.table_positions(starts, step, rows)
     assert got.shape == ref.shape
     assert_within(host64(got), ref, _pos_bound(w64, pos, dtype, dm, ref), case)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("step", [-1, 1])
+def test_rel_pos_projection_at_large_positions(dtype, step):
+    """Positions far from zero (10^5 .. 2^24, the largest the entry accepts): the phase p f_j is
+    reduced exactly, so the error bound is the one small positions get."""
+    dm, rows = 256, 70
+    w, _ = linear_weights(dm, dm, seed=14, dtype=dtype, device=DEV, bias=False)
+    starts = np.array([100003, -524287, 999999, -1000000, 2 ** 24 - rows, -(2 ** 24) + rows])
+    st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    got = pkc.rel_pos_projection(w, rows, pos_start=st, pos_step=step)
+    torch.cuda.synchronize()
+    w64 = host64(w)
+    ref = oracle.rel_pos_projection(w64, starts, step, rows)
+    pos = oracle.table_positions(starts, step, rows)
+    assert np.abs(pos).max() <= 2 ** 24
+    assert_within(host64(got), ref, _pos_bound(w64, pos, dtype, dm, ref), f"large_{step}")
 
 
 # --------------------------------------------------------------------------------------------
