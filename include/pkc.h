@@ -95,6 +95,12 @@
  *   reads the frames past them: through the row's next entry, which may name another stream's
  *   page (or hold any value, clamped into [0, N)). Those frames are masked and their V zeroed
  *   before use, so such reads never change a result; they only touch valid pool memory.
+ *   With window_start, w_b + max_cache_seqlen + C stays below 2^31 (positions are 32-bit).
+ *
+ * Launch limits, common to every entry point: HIP launches fewer than 2^32 work-items along a
+ * grid dimension, so a call whose grid (workgroups x threads per workgroup, stated per entry point
+ * below) would reach 2^32 is refused with PKC_ERR_UNSUPPORTED before anything is launched. Sizes
+ * are combined in 64-bit (saturating) arithmetic on the host, so no int32 argument can wrap a check.
  */
 #ifndef PKC_H
 #define PKC_H
@@ -107,7 +113,16 @@
 extern "C" {
 #endif
 
-typedef enum pkc_status {
+/* The enums below are 32-bit ints on both sides of the ABI. A C caller may pass any int where an
+ * enum is expected (the entry points reject values they do not know), so in C++ they get int32_t
+ * as a fixed underlying type, which makes every int32 value a valid value of the type. */
+#ifdef __cplusplus
+#define PKC_ENUM_BASE : int32_t
+#else
+#define PKC_ENUM_BASE
+#endif
+
+typedef enum pkc_status PKC_ENUM_BASE {
   PKC_OK = 0,
   PKC_ERR_NULL = 1,        /* a required pointer is NULL                                    */
   PKC_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree                      */
@@ -118,10 +133,10 @@ typedef enum pkc_status {
   PKC_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned                       */
 } pkc_status;
 
-typedef enum pkc_dtype { PKC_F32 = 0, PKC_BF16 = 1 } pkc_dtype;
+typedef enum pkc_dtype PKC_ENUM_BASE { PKC_F32 = 0, PKC_BF16 = 1 } pkc_dtype;
 
 /* Layout of the positional tables (flags of the pos_layout argument). */
-typedef enum pkc_pos_layout {
+typedef enum pkc_pos_layout PKC_ENUM_BASE {
   PKC_POS_SHARED = 0,   /* one table by distance for the cohort                         */
   PKC_POS_PER_ROW = 1,  /* one table per stream                                          */
   PKC_POS_PER_KEY = 2,  /* rows are keys, not distances (WeNet's convention, no shift)   */
@@ -143,9 +158,12 @@ const char* pkc_status_string(int status);
  *     v_pool[block_tables[b][L / S]][g][:][L % S] = v_new[b][t][g][:]
  * for every kv head g. No other pool element is touched; the copy is bit-exact. The caller then
  * runs the attention and afterwards advances cache_seqlens by n_b itself.
+ * Grid: batch x n_kv_head workgroups of 256 threads; a workgroup stages 64 frames of V in LDS,
+ * 64 (head_dim + 16 / element bytes) element bytes, which must fit the default 64 KiB
+ * (head_dim <= 504 in bf16, <= 252 in fp32).
  * Errors: NULL pointers -> PKC_ERR_NULL; non-positive sizes or head_dim not a multiple of 8 ->
- * PKC_ERR_SHAPE; head_dim not a multiple of 32 -> PKC_ERR_UNSUPPORTED;
- * max_cache_seqlen + chunk_size > max_blocks_per_seq * block_size ->
+ * PKC_ERR_SHAPE; head_dim not a multiple of 32, the V staging beyond 64 KiB or the launch limits
+ * -> PKC_ERR_UNSUPPORTED; max_cache_seqlen + chunk_size > max_blocks_per_seq * block_size ->
  * PKC_ERR_CAPACITY (the analogue of the pool/table ceiling errors of [ENG 6]).
  */
 pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new, void* k_pool,
@@ -180,8 +198,8 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  * softmax_scale <= 0 selects 1 / sqrt(head_dim).
  * Errors: as paged_kv_append; n_head % n_kv_head != 0 or a table too short -> PKC_ERR_SHAPE;
  * head_dim != 64, block_size not a power of two >= 8, a chunk too long for the kernel's LDS
- * staging, or batch n_head ceil(chunk_size / 16) at or past 2^31 (one workgroup per 16 queries of
- * a stream and head) -> PKC_ERR_UNSUPPORTED. The kernel stages the chunk's chunk_size frames in LDS (the
+ * staging, pos_len >= 2^25, or the launch limits (batch n_head ceil(chunk_size / 16) workgroups
+ * of 256 threads: one per 16 queries of a stream and head) -> PKC_ERR_UNSUPPORTED. The kernel stages the chunk's chunk_size frames in LDS (the
  * cached frames stream from the pages), which allows chunk_size <= 512 in bf16 and <= 256 in
  * fp32.
  */
@@ -284,8 +302,9 @@ pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,
  * its frames can see (its own frames plus the trained history). mask_chunk = 0: full context.
  * Errors: as above; a negative mask_chunk or mask_left_chunks -> PKC_ERR_SHAPE; head_dim != 64,
  * 2 max_seqlen max(H, Hk) head_dim element bytes at or past 2^31 (an utterance's rows are
- * addressed by 32-bit byte offsets), or num_seqs n_head ceil(max_seqlen / 64) at or past 2^31
- * (one workgroup per 64 queries of an utterance and head) -> PKC_ERR_UNSUPPORTED.
+ * addressed by 32-bit byte offsets), or the launch limits (num_seqs n_head ceil(max_seqlen / Q)
+ * workgroups of 256 threads, one per Q = 128 queries in bf16, 64 in fp32, of an utterance and
+ * head) -> PKC_ERR_UNSUPPORTED.
  */
 pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,
                                      const int32_t* cu_seqlens, int32_t num_seqs,
@@ -301,9 +320,10 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
  *
  * x [M, K], w [N, K] (out_features x in_features, the nn.Linear storage), bias [N] or NULL,
  * y [M, N]; all row-major, one dtype. y is written in full; nothing else is touched.
- * Errors: NULL x, w or y -> PKC_ERR_NULL; a non-positive size -> PKC_ERR_SHAPE; K not a multiple
- * of 32 or N not a multiple of 16 -> PKC_ERR_UNSUPPORTED; a pointer not 16-byte aligned ->
- * PKC_ERR_ALIGN.
+ * Grid: one 256-thread workgroup per output tile (128 x 128, 128 x 64 or 64 x 64, picked by size).
+ * Errors: NULL x, w or y -> PKC_ERR_NULL; a non-positive size, or M, N or K at or past 2^30 ->
+ * PKC_ERR_SHAPE; K not a multiple of 32, N not a multiple of 16 or the launch limits ->
+ * PKC_ERR_UNSUPPORTED; a pointer not 16-byte aligned -> PKC_ERR_ALIGN.
  */
 pkc_status pkc_linear(pkc_dtype dtype, const void* x, const void* w, const void* bias, void* y,
                       int32_t M, int32_t N, int32_t K, hipStream_t stream);
@@ -343,12 +363,15 @@ pkc_status paged_kv_qkv_append(pkc_dtype dtype, const void* x, const void* w_qkv
  * pos_out [n_tables, rows, out_features]. A Transformer-XL table by distance centred at c
  * (row r holds distance c - r, the layout chunk_paged_relpos_attn reads) is pos_first = c,
  * pos_step = -1, rows = 2 c + 1; WeNet's per-key table of stream b [MOD nem] is
- * pos_start[b] = offset_b - cache_seqlens[b], pos_step = +1. The sinusoid is computed in fp32
- * and rounded to the dtype before the product.
+ * pos_start[b] = offset_b - cache_seqlens[b], pos_step = +1. The phase p f_i is formed and
+ * reduced to a fraction of a turn in fp64, so its error (about 2^-25 turns) does not grow with
+ * |p|; the sine and cosine are taken in fp32 and rounded to the dtype before the product. The
+ * GEMM's grid and limits are those of pkc_linear with M = n_tables x rows.
  * Errors: NULL w_pos or pos_out -> PKC_ERR_NULL; non-positive n_tables or rows, or positions
- * beyond +-2^24 (fp32-exact integers; checked for pos_first, the caller's precondition for
- * pos_start) -> PKC_ERR_SHAPE; d_model not a multiple of 32 or out_features not a multiple of
- * 16 -> PKC_ERR_UNSUPPORTED; a pointer not 16-byte aligned -> PKC_ERR_ALIGN.
+ * beyond +-2^24 (the range the phase accuracy is stated for; checked for pos_first, the caller's
+ * precondition for pos_start) -> PKC_ERR_SHAPE; d_model not a multiple of 32, out_features not a
+ * multiple of 16 or the launch limits -> PKC_ERR_UNSUPPORTED; a pointer not 16-byte aligned ->
+ * PKC_ERR_ALIGN.
  */
 pkc_status rel_pos_projection(pkc_dtype dtype, const void* w_pos, const int32_t* pos_start,
                               int32_t pos_first, int32_t pos_step, int32_t n_tables, int32_t rows,

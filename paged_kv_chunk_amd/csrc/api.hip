@@ -11,6 +11,8 @@ namespace {
 
 constexpr int kVersion = 400;  // 0.4.0: the projections either side of the attention
 
+constexpr int32_t kMaxPosRows = (int32_t)1 << 25;   // rows of one positional table
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 pkc_status check_dtype(pkc_dtype dtype) {
@@ -50,16 +52,20 @@ pkc_status check_attn(int32_t chunk, int32_t n_head, int32_t n_kv_head, int32_t 
   }
   if (head_dim != 64) return PKC_ERR_UNSUPPORTED;
   if (block_size < 8 || (block_size & (block_size - 1)) != 0) return PKC_ERR_UNSUPPORTED;
+  // the kernels step through one head's column-blocked table with 32-bit strides of 64 rows
+  if (pos_len >= kMaxPosRows) return PKC_ERR_UNSUPPORTED;
   return PKC_OK;
 }
 
 pkc_status from_hip(hipError_t e) { return e == hipSuccess ? PKC_OK : PKC_ERR_HIP; }
 
-// GEMM shapes the kernel is built for: whole 32-deep contraction stages, 16-feature output tiles
+// GEMM shapes the kernel is built for: whole 32-deep contraction stages, 16-feature output tiles,
+// and a tile grid one launch holds
 pkc_status check_gemm(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return PKC_ERR_SHAPE;
-  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 30)) return PKC_ERR_SHAPE;
+  if (M >= ((int64_t)1 << 30) || N >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 30)) return PKC_ERR_SHAPE;
   if (K % 32 != 0 || N % 16 != 0) return PKC_ERR_UNSUPPORTED;
+  if (!gemm_grid(M, N).fits()) return PKC_ERR_UNSUPPORTED;
   return PKC_OK;
 }
 
@@ -97,6 +103,9 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
   if (st != PKC_OK) return st;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
     return PKC_ERR_ALIGN;
+  if (!paged_append_grid(batch, n_kv_head).fits() ||
+      paged_append_lds_bytes(dtype == PKC_BF16 ? 2 : 4, head_dim) > kDefaultDynamicLds)
+    return PKC_ERR_UNSUPPORTED;
   AppendParams p{k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, chunk_lens,
                  window_start, batch, chunk_size,
                  n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq, max_cache_seqlen};
@@ -132,7 +141,7 @@ static pkc_status attn_common(pkc_dtype dtype, const void* q, const void* k_new,
   if (chunk_attn_lds_bytes(dtype == PKC_BF16 ? 2 : 4, chunk_size, max_cache_seqlen, block_size,
                            k_new != nullptr) > kMaxDynamicLds)
     return PKC_ERR_UNSUPPORTED;
-  if (chunk_attn_workgroups(batch, n_head, chunk_size) >= (int64_t)1 << 31)
+  if (!chunk_attn_grid(dtype == PKC_BF16 ? 2 : 4, batch, n_head, chunk_size).fits())
     return PKC_ERR_UNSUPPORTED;
   AttnParams p{};
   p.q = q;
@@ -253,7 +262,7 @@ pkc_status pkc_gather_read(pkc_dtype dtype, const void* q, const void* k_new, co
     return PKC_ERR_SHAPE;
   if (dtype != PKC_BF16 || chunk_size > 16 || (pos_layout & PKC_POS_PER_KEY))
     return PKC_ERR_UNSUPPORTED;
-  if (gather_read_workgroups(batch, n_head, split) >= (int64_t)1 << 31) return PKC_ERR_UNSUPPORTED;
+  if (!gather_read_grid(batch, n_head, split, waves).fits()) return PKC_ERR_UNSUPPORTED;
   GatherParams p{q, k_new, v_new, k_pool, v_pool, block_tables, cache_seqlens, pos, pos_bias_u,
                  pos_bias_v, out, batch, chunk_size, n_head, n_kv_head, block_size, num_blocks,
                  max_blocks_per_seq, max_cache_seqlen, pos_len, pos_layout, waves, split, reads};
@@ -266,6 +275,7 @@ pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,
   if (!cache_seqlens) return PKC_ERR_NULL;
   if (batch <= 0 || chunk_size <= 0) return PKC_ERR_SHAPE;
   if (window_start && (block_size <= 0 || max_cached_frames < 0)) return PKC_ERR_SHAPE;
+  if (!commit_grid(batch).fits()) return PKC_ERR_UNSUPPORTED;
   return from_hip(launch_commit(cache_seqlens, chunk_lens, window_start, max_cached_frames,
                                 block_size, batch, chunk_size, stream));
 }
@@ -290,11 +300,10 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
   if (head_dim != 64) return PKC_ERR_UNSUPPORTED;
   // (the kernel addresses an utterance's rows by 32-bit byte offsets from its first row; its
   // table spans 2 max_seqlen rows)
-  if ((int64_t)2 * max_seqlen * (n_head > n_kv_head ? n_head : n_kv_head) * head_dim *
-          (dtype == PKC_BF16 ? 2 : 4) >= (int64_t)1 << 31)
+  if (mul_sat(mul_sat((int64_t)2 * max_seqlen, n_head > n_kv_head ? n_head : n_kv_head),
+              (int64_t)head_dim * (dtype == PKC_BF16 ? 2 : 4)) >= (int64_t)1 << 31)
     return PKC_ERR_UNSUPPORTED;
-  if (varlen_attn_workgroups(num_seqs, n_head, max_seqlen, dtype == PKC_BF16 ? 2 : 4) >=
-      (int64_t)1 << 31)
+  if (!varlen_attn_grid(dtype == PKC_BF16 ? 2 : 4, num_seqs, n_head, max_seqlen).fits())
     return PKC_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pos) ||
       !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))
@@ -335,7 +344,8 @@ pkc_status paged_kv_qkv_append(pkc_dtype dtype, const void* x, const void* w_qkv
                   max_blocks_per_seq, max_cache_seqlen);
   if (st != PKC_OK) return st;
   if (n_head <= 0 || n_head % n_kv_head != 0) return PKC_ERR_SHAPE;
-  st = check_gemm((int64_t)batch * chunk_size, (int64_t)(n_head + 2 * n_kv_head) * head_dim, d_model);
+  st = check_gemm((int64_t)batch * chunk_size, ((int64_t)n_head + 2 * (int64_t)n_kv_head) * head_dim,
+                  d_model);
   if (st != PKC_OK) return st;
   if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q_out) || !aligned16(k_pool) ||
       !aligned16(v_pool) || (b_qkv && !aligned16(b_qkv)))
@@ -356,7 +366,7 @@ pkc_status rel_pos_projection(pkc_dtype dtype, const void* w_pos, const int32_t*
   if (n_tables <= 0 || rows <= 0) return PKC_ERR_SHAPE;
   st = check_gemm((int64_t)n_tables * rows, out_features, d_model);
   if (st != PKC_OK) return st;
-  // positions are carried in fp32: they must be integers it holds exactly
+  // positions stay within +-2^24, the range the kernel's phase accuracy is stated for
   const int64_t last = (int64_t)pos_first + (int64_t)pos_step * (rows - 1);
   const int64_t span = (int64_t)1 << 24;
   if (!pos_start && (pos_first > span || pos_first < -span || last > span || last < -span))

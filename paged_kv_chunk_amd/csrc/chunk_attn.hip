@@ -554,15 +554,17 @@ template <typename T> constexpr int waves_of() { return 4; }
 
 template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false, bool kGen = true>
 void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
-  auto fn = chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey, kGen>;
   if (smem > 64 * 1024) {
     // beyond the default dynamic LDS size (long chunks): opt in on every such call, so that no
     // state is kept between calls (a host-side attribute, no GPU work); MI355X allows 160 KB per
     // workgroup
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(
+            &chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey, kGen>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   }
-  hipLaunchKernelGGL(fn, grid, dim3(waves_of<T>() * 64), smem, stream, a);
+  hipLaunchKernelGGL((chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey, kGen>),
+                     grid, dim3(waves_of<T>() * 64), smem, stream, a);
 }
 
 // Instantiation for a call: the block sizes of the streaming workloads get constant page
@@ -654,7 +656,7 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   off += (size_t)kD * a.vt_pitch * sizeof(T);
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)chunk_attn_workgroups(p.batch, p.n_head, p.chunk));
+  const dim3 grid((unsigned)chunk_attn_grid((int)sizeof(T), p.batch, p.n_head, p.chunk).workgroups);
   if (p.k_new) launch_s<T, true>(a, grid, off, stream);
   else launch_s<T, false>(a, grid, off, stream);
   return hipGetLastError();
@@ -670,8 +672,9 @@ size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int, int, bool) {
          (size_t)tail_cap * (kD + vec) * dtype_bytes + (size_t)kD * (tail_cap + vec) * dtype_bytes;
 }
 
-int64_t chunk_attn_workgroups(int batch, int n_head, int chunk) {
-  return (int64_t)batch * n_head * ((chunk + 15) / 16);
+LaunchGrid chunk_attn_grid(int dtype_bytes, int batch, int n_head, int chunk) {
+  const int waves = dtype_bytes == 2 ? waves_of<bf16>() : waves_of<float>();
+  return {mul_sat(mul_sat(batch, n_head), ((int64_t)chunk + 15) / 16), waves * 64};
 }
 
 hipError_t launch_chunk_attn(pkc_dtype dtype, const AttnParams& p, hipStream_t stream) {

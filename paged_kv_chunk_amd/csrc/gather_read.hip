@@ -222,8 +222,8 @@ gather_read_kernel(GatherArgs a) {
 
 }  // namespace
 
-int64_t gather_read_workgroups(int batch, int n_head, int split) {
-  return (int64_t)batch * n_head * split;
+LaunchGrid gather_read_grid(int batch, int n_head, int split, int waves) {
+  return {mul_sat(mul_sat(batch, n_head), split), waves * 64};
 }
 
 hipError_t launch_gather_read(const GatherParams& p, hipStream_t stream) {
@@ -259,7 +259,7 @@ hipError_t launch_gather_read(const GatherParams& p, hipStream_t stream) {
   a.div_split = make_fastdiv(p.split);
   a.div_H = make_fastdiv(p.n_head);
   a.div_group = make_fastdiv(p.n_head / p.n_kv_head);
-  const dim3 grid((unsigned)gather_read_workgroups(p.batch, p.n_head, p.split));
+  const dim3 grid((unsigned)gather_read_grid(p.batch, p.n_head, p.split, p.waves).workgroups);
   if (p.waves == 8) hipLaunchKernelGGL(gather_read_kernel<8>, grid, dim3(512), 0, stream, a);
   else hipLaunchKernelGGL(gather_read_kernel<4>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -97,26 +97,36 @@ commit_kernel(int32_t* __restrict__ cache_seqlens, const int32_t* __restrict__ c
 
 }  // namespace
 
+LaunchGrid commit_grid(int batch) { return {((int64_t)batch + kThreads - 1) / kThreads, kThreads}; }
+
+LaunchGrid paged_append_grid(int batch, int n_kv_head) {
+  return {mul_sat(batch, n_kv_head), kThreads};
+}
+
+size_t paged_append_lds_bytes(int dtype_bytes, int head_dim) {
+  return (size_t)kTileFrames * ((size_t)head_dim + 16 / dtype_bytes) * dtype_bytes;
+}
+
 hipError_t launch_commit(int32_t* cache_seqlens, const int32_t* chunk_lens, int32_t* window_start,
                          int max_cached, int block_size, int batch, int chunk, hipStream_t stream) {
-  hipLaunchKernelGGL(commit_kernel, dim3((batch + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, cache_seqlens, chunk_lens, window_start, max_cached, block_size, batch,
-                     chunk);
+  const LaunchGrid g = commit_grid(batch);
+  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)g.workgroups), dim3(g.threads), 0, stream,
+                     cache_seqlens, chunk_lens, window_start, max_cached, block_size, batch, chunk);
   return hipGetLastError();
 }
 
 hipError_t launch_paged_append(pkc_dtype dtype, const AppendParams& p, hipStream_t stream) {
-  const dim3 grid(p.batch * p.n_kv_head);
+  const LaunchGrid g = paged_append_grid(p.batch, p.n_kv_head);
+  const dim3 grid((unsigned)g.workgroups), block(g.threads);
+  const size_t smem = paged_append_lds_bytes(dtype == PKC_BF16 ? 2 : 4, p.head_dim);
   if (dtype == PKC_BF16) {
-    const size_t smem = (size_t)kTileFrames * (p.head_dim + 8) * sizeof(bf16);
-    hipLaunchKernelGGL(paged_append_kernel<bf16>, grid, dim3(kThreads), smem, stream,
+    hipLaunchKernelGGL(paged_append_kernel<bf16>, grid, block, smem, stream,
                        (const bf16*)p.k_new, (const bf16*)p.v_new, (bf16*)p.k_pool, (bf16*)p.v_pool,
                        p.block_tables, p.cache_seqlens, p.chunk_lens, p.window_start, p.chunk,
                        p.n_kv_head, p.head_dim,
                        p.block_size, p.num_blocks, p.max_blocks, p.max_cache);
   } else {
-    const size_t smem = (size_t)kTileFrames * (p.head_dim + 4) * sizeof(float);
-    hipLaunchKernelGGL(paged_append_kernel<float>, grid, dim3(kThreads), smem, stream,
+    hipLaunchKernelGGL(paged_append_kernel<float>, grid, block, smem, stream,
                        (const float*)p.k_new, (const float*)p.v_new, (float*)p.k_pool,
                        (float*)p.v_pool, p.block_tables, p.cache_seqlens, p.chunk_lens,
                        p.window_start, p.chunk,

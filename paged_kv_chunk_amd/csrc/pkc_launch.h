@@ -119,14 +119,35 @@ hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_
 hipError_t launch_gather_read(const GatherParams& p, hipStream_t stream);
 
 
-// Dynamic LDS of one chunk-attention workgroup, and the budget it must fit.
+// Dynamic LDS of one chunk-attention workgroup, and the budget it must fit (the launcher opts in
+// above the default 64 KiB).
 size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int max_cache, int block_size, bool fused);
 constexpr size_t kMaxDynamicLds = 160 * 1024;
+// Dynamic LDS of one append workgroup (staged frames x head_dim); at most the default 64 KiB.
+size_t paged_append_lds_bytes(int dtype_bytes, int head_dim);
+constexpr size_t kDefaultDynamicLds = 64 * 1024;
 
-// Workgroups of one attention launch. The kernels split the workgroup index with 31-bit
-// multiply-shift divisions, so a launch must stay below 2^31 workgroups.
-int64_t chunk_attn_workgroups(int batch, int n_head, int chunk);
-int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen, int dtype_bytes);
-int64_t gather_read_workgroups(int batch, int n_head, int split);
+// Product of non-negative sizes, saturating at 2^62 (no int64 overflow for any int32 inputs).
+inline int64_t mul_sat(int64_t a, int64_t b) {
+  constexpr int64_t kCap = (int64_t)1 << 62;
+  if (a <= 0 || b <= 0) return 0;
+  return a > kCap / b ? kCap : a * b;
+}
+
+// Geometry of one launch: workgroups along x and threads per workgroup. HIP launches fewer than
+// 2^32 work-items along a grid dimension (the dispatch packet's grid size is 32-bit), which also
+// keeps the workgroup index below 2^31 for the kernels' multiply-shift divisions. The launchers
+// take their grid from these functions, and the entry points refuse a launch that does not fit.
+struct LaunchGrid {
+  int64_t workgroups;
+  int threads;
+  bool fits() const { return workgroups <= ((((int64_t)1) << 32) - 1) / threads; }
+};
+LaunchGrid paged_append_grid(int batch, int n_kv_head);
+LaunchGrid commit_grid(int batch);
+LaunchGrid chunk_attn_grid(int dtype_bytes, int batch, int n_head, int chunk);
+LaunchGrid varlen_attn_grid(int dtype_bytes, int num_seqs, int n_head, int max_seqlen);
+LaunchGrid gather_read_grid(int batch, int n_head, int split, int waves);
+LaunchGrid gemm_grid(int64_t M, int64_t N);   // the tile shape the GEMM launchers pick for M x N
 
 }  // namespace pkc

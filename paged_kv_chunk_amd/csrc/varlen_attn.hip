@@ -485,8 +485,8 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
   a.scale_log2 = scale * 1.4426950408889634f;
   a.chunk = p.mask_chunk;
   a.left = p.mask_left_chunks;
-  const dim3 grid((unsigned)varlen_attn_workgroups(p.num_seqs, p.n_head, p.max_seqlen,
-                                                   (int)sizeof(T)));
+  const dim3 grid(
+      (unsigned)varlen_attn_grid((int)sizeof(T), p.num_seqs, p.n_head, p.max_seqlen).workgroups);
   if (p.mask_chunk > 0)
     hipLaunchKernelGGL((varlen_attn_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
   else
@@ -496,9 +496,9 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int64_t varlen_attn_workgroups(int num_seqs, int n_head, int max_seqlen, int dtype_bytes) {
+LaunchGrid varlen_attn_grid(int dtype_bytes, int num_seqs, int n_head, int max_seqlen) {
   const int qtile = dtype_bytes == 2 ? kQTile<bf16> : kQTile<float>;
-  return (int64_t)num_seqs * n_head * ((max_seqlen + qtile - 1) / qtile);
+  return {mul_sat(mul_sat(num_seqs, n_head), ((int64_t)max_seqlen + qtile - 1) / qtile), kThreads};
 }
 
 hipError_t launch_varlen_attn(pkc_dtype dtype, const VarlenParams& p, hipStream_t stream) {

@@ -97,6 +97,10 @@ def varlen(lib, dtype=1, q=P, k=P, v=P, cu=P, S=4, total=100, max_len=40, pos=P,
     (dict(max_cache=113), CAP),                      # 113 + 16 > 8 * 16
     (dict(M=4, max_cache=64), CAP),
     (dict(k_pool=BAD), ALIGN), (dict(k_new=BAD), ALIGN),
+    # one workgroup of 256 threads per stream and kv head: 2^32 work-items or more are refused
+    (dict(B=1 << 20, Hk=16), UNSUP), (dict(B=1 << 24, Hk=1), UNSUP),
+    # the V staging tile (64 frames x head_dim) must fit the default 64 KiB of LDS
+    (dict(D=512), UNSUP), (dict(dtype=0, D=256), UNSUP),
 ])
 def test_append_validation(lib, kw, status):
     assert append(lib, **kw) == status
@@ -114,9 +118,12 @@ def test_append_validation(lib, kw, status):
     (dict(per_row=3, pos_len=79), SHAPE),
     (dict(D=128), UNSUP), (dict(S=12, M=12), UNSUP), (dict(S=24, M=12), UNSUP),
     (dict(S=4, M=40), UNSUP),
-    # one workgroup per 16 queries of a stream and head: 2^31 of them are refused
+    # one 256-thread workgroup per 16 queries of a stream and head: 2^32 work-items are refused
     (dict(B=1 << 24, H=128, Hk=128), UNSUP),
     (dict(B=1 << 23, H=128, Hk=64, C=32, pos_len=2 * (64 + 32) - 1), UNSUP),
+    (dict(B=1 << 20, H=16, Hk=16), UNSUP),
+    # positional tables of 2^25 rows or more (32-bit strides of column-blocked tables)
+    (dict(pos_len=(1 << 25) + 1), UNSUP),
     (dict(max_cache=120), CAP),
     (dict(q=BAD), ALIGN), (dict(pos=BAD), ALIGN), (dict(out=BAD), ALIGN),
 ])
@@ -146,11 +153,12 @@ def test_fused_validation(lib):
     # must stay under 2^31 bytes
     (dict(total=2_000_000, max_len=2_000_000), UNSUP),
     (dict(dtype=0, total=1_100_000, max_len=1_100_000, H=4, Hk=4), UNSUP),
-    # one workgroup per 128 queries (bf16; 64 for fp32) of an utterance and head: 2^31 of them
-    # are refused
+    # one 256-thread workgroup per 128 queries (bf16; 64 for fp32) of an utterance and head:
+    # 2^32 work-items are refused
     (dict(S=1 << 20, total=100, max_len=64, H=2048, Hk=2048), UNSUP),
     (dict(S=1 << 19, total=300, max_len=256, H=2048, Hk=1024), UNSUP),
     (dict(dtype=0, S=1 << 19, total=200, max_len=128, H=2048, Hk=1024), UNSUP),
+    (dict(S=1 << 16, total=300, max_len=256, H=128, Hk=128), UNSUP),
 ])
 def test_varlen_validation(lib, kw, status):
     assert varlen(lib, **kw) == status
@@ -216,6 +224,9 @@ def linear_call(lib, dtype=1, x=P, w=P, bias=None, y=P, M=100, N=64, K=256):
     (dict(dtype=2), DTYPE), (dict(x=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL),
     (dict(M=0), SHAPE), (dict(N=0), SHAPE), (dict(K=-32), SHAPE),
     (dict(K=48), UNSUP), (dict(N=40), UNSUP),
+    (dict(M=1 << 30), SHAPE),
+    # 256-thread workgroups over 128 x 128 .. 64 x 64 output tiles: 2^32 work-items are refused
+    (dict(M=(1 << 30) - 1, N=1 << 13), UNSUP),
     (dict(x=BAD), ALIGN), (dict(y=BAD), ALIGN), (dict(bias=BAD), ALIGN),
 ])
 def test_linear_validation(lib, kw, status):
@@ -234,6 +245,9 @@ def qkv_call(lib, dtype=1, x=P, w=P, b=P, q=P, k_pool=P, v_pool=P, bt=P, cs=P, B
     (dict(B=0), SHAPE), (dict(H=6, Hk=4), SHAPE), (dict(H=0), SHAPE), (dict(dm=0), SHAPE),
     (dict(dm=100), UNSUP), (dict(D=48), UNSUP),
     (dict(max_cache=113), CAP),
+    # (H + 2 Hk) D output features: formed without int32 overflow, then refused by size
+    (dict(H=(1 << 31) - 1, Hk=1), SHAPE),
+    (dict(H=1 << 30, Hk=1 << 30), SHAPE),
     (dict(x=BAD), ALIGN), (dict(b=BAD), ALIGN), (dict(v_pool=BAD), ALIGN),
 ])
 def test_qkv_append_validation(lib, kw, status):
