@@ -38,6 +38,8 @@
 // keys of its own chunk of `chunk` frames and of the `left` chunks before it. A workgroup then
 // walks only the keys its 64 queries can see - its own frames plus the trained history, as one
 // streaming step per query block - and each query column masks to its own range.
+#include <type_traits>
+
 #include "pkc_device.h"
 #include "pkc_launch.h"
 #include "pkc_step.h"
@@ -63,10 +65,6 @@ template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natura
 // rows, rounded up to a power of two
 template <typename T> constexpr int kRing = kQT<T> == 2 ? 256 : 128;
 constexpr int kSortMax = 64;   // utterances a wave ranks by length (one per lane)
-// the softmax row sums on the MFMA (a ones operand against the probabilities) instead of eight
-// adds per lane and step; the sums are then those of the bf16-rounded probabilities the values are
-// weighted with
-constexpr bool kSumMfma = true;
 // Lane group g holds the keys of key_group<true>(g) (groups 1 and 2 swapped): the shifted
 // position values are then read conflict-free.
 constexpr bool kPerm = true;
@@ -80,6 +78,108 @@ __device__ __forceinline__ int v_swz(int r) { return 4 * ((r & 3) ^ ((r >> 4) & 
 // permutation.
 __device__ __forceinline__ int k_swz(int r) {
   return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r ^ (r >> 4)) & 1) << 2);
+}
+
+// One 32-key step of a wave's QT query tiles, written in phases so that the tiles' independent
+// work sits in one basic block and interleaves: the band products of every tile; the relative
+// shift of each tile through the wave's skew tile, tile after tile (LDS executes a wave's accesses
+// in order, so tile k + 1's writes land after tile k's reads), each shifted column starting the
+// accumulation of that tile's content product (S^T = K (q + u)^T); one running-max test for all
+// tiles (a single uniform branch, rarely taken); then the probabilities, the PV products and the
+// row sums on the MFMA (an all-ones operand against the probabilities: the sums are those of the
+// bf16-rounded probabilities the values are weighted with). Tile k's band tiles are pb[QT-1-k]
+// and pb[QT-k] (g1, g2) after the carried product g_prev[k]. kMask: only keys lo[k] <= key < hi[k]
+// of the step count for tile k (relative to the step's first key); a column that has seen no key
+// yet contributes nothing.
+template <typename T, int QT, bool kMask>
+__device__ __forceinline__ void step_tiles(Softmax (&st)[QT],
+                                           const typename Frag<T>::type (&kf)[2][2],
+                                           const typename Frag<T>::type (&vf)[4],
+                                           const typename Frag<T>::type (&qu)[QT][2],
+                                           const typename Frag<T>::type (&qv)[QT][2],
+                                           const typename Frag<T>::type (&pb)[QT + 1][2],
+                                           floatx4 (&g_prev)[QT], float* s_g,
+                                           const int (&lo)[QT], const int (&hi)[QT]) {
+  typedef typename Frag<T>::type F;
+  const int lane = threadIdx.x & 63;
+  const int m16 = lane & 15;
+  const int grp = lane >> 4;
+  const int kg = key_group<kPerm>(grp);
+  floatx4 g1[QT], g2[QT];
+#pragma unroll
+  for (int k = 0; k < QT; ++k) {
+    g1[k] = mma(pb[QT - 1 - k][0], qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
+    g1[k] = mma(pb[QT - 1 - k][1], qv[k][1], g1[k]);
+    g2[k] = mma(pb[QT - k][0], qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
+    g2[k] = mma(pb[QT - k][1], qv[k][1], g2[k]);
+  }
+  // shift: G^T[row][query] -> s_g[query * kSkewPitch + row]; the lane reads its 8 keys' values
+  // from its own query column, shifted by 15 - query
+  float* colw = s_g + m16 * kSkewPitch + 4 * grp;
+  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * kg;
+  floatx4 sc[QT][2];
+#pragma unroll
+  for (int k = 0; k < QT; ++k) {
+    *reinterpret_cast<floatx4*>(colw) = g_prev[k];
+    *reinterpret_cast<floatx4*>(colw + 16) = g1[k];
+    *reinterpret_cast<floatx4*>(colw + 32) = g2[k];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+      sc[k][tt] = floatx4{colr[4 * tt], colr[4 * tt + 1], colr[4 * tt + 2], colr[4 * tt + 3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[k][tt] = mma(kf[tt][0], qu[k][0], sc[k][tt]);
+      sc[k][tt] = mma(kf[tt][1], qu[k][1], sc[k][tt]);
+    }
+    g_prev[k] = g2[k];
+  }
+  float mx[QT];
+  bool move = false;
+#pragma unroll
+  for (int k = 0; k < QT; ++k) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (kMask) {
+          const int key = 8 * kg + 4 * tt + e;
+          sc[k][tt][e] = (key >= lo[k] && key < hi[k]) ? sc[k][tt][e] : -INFINITY;
+        }
+        m = fmaxf(m, sc[k][tt][e]);
+      }
+    mx[k] = column_max(m);
+    move = move || mx[k] > st[k].m + kRescaleLog2;
+  }
+  if (__ballot(move) != 0) {
+#pragma unroll
+    for (int k = 0; k < QT; ++k) {
+      const bool mv = mx[k] > st[k].m + kRescaleLog2;
+      // (a column that does not move keeps its scale; exp2(m - m) would be NaN for a column that
+      // has seen no key yet, m = -inf)
+      const float alpha = mv ? fast_exp2(st[k].m - mx[k]) : 1.f;
+      st[k].ls *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) st[k].o[dt] *= alpha;
+      st[k].m = mv ? mx[k] : st[k].m;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < QT; ++k) {
+    // (masked, a column may still have seen nothing: its probabilities must be 0, not
+    // exp2(-inf - -inf))
+    const float m_ref = (kMask && st[k].m == -INFINITY) ? 0.f : st[k].m;
+    F pf;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) set(pf, 4 * tt + e, fast_exp2(sc[k][tt][e] - m_ref));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st[k].o[dt] = mma(vf[dt], pf, st[k].o[dt]);
+    st[k].ls = mma(ones8<T>(), pf, st[k].ls);
+  }
 }
 
 template <typename T>
@@ -124,7 +224,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -354,12 +454,16 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     if constexpr (QT == 2) band_tile(xl + J + 16, c1[0], c1[1]);
   }
   // one step (index `step` from the first visible one): registers `nxt` already hold step + 1,
-  // `fre` receives step + 2
-  auto do_step = [&](int step, Rows& nxt, Rows& fre) {
+  // `fre` receives step + 2. kM: the step masks keys (every step with the chunked_limited mask,
+  // else only a last step that runs past the utterance). A wave's tiles past the utterance compute
+  // on clamped, finite rows and are never stored; a wave with none inside skips the arithmetic.
+  const bool active = ntile > 0;   // uniform over the wave
+  auto do_step = [&](int step, Rows& nxt, Rows& fre, auto masked) {
+    constexpr bool kM = decltype(masked)::value;
     const int j0 = J + 32 * step;
     const T* cur = s_kv + (step & 1) * TILE;
     fetch(fre, j0 + 64);   // (past the last step: harmless re-reads of the last frame)
-    if (ntile > 0) {
+    if (active) {
       F kf[2][2], vf[4];
       if constexpr (kSwK<T>) {
         const int r = 8 * key_group<kPerm>(m16 >> 2) + (m16 & 3);   // tile tt reads row r + 4 tt
@@ -402,28 +506,13 @@ varlen_attn_kernel(VarlenArgs<T> a) {
 #pragma unroll
       for (int m = (QT == 2 ? 1 : 0); m < QT + 1; ++m)
         band_tile(xl + j0 + 16 * (m + 1), pb[m][0], pb[m][1]);
-      // tile k reads T_{QT-1-k} (carried product) and T_{QT-k}, T_{QT+1-k}: pb[QT-1-k], pb[QT-k]
+      int lo_k[QT], hi_k[QT];
 #pragma unroll
       for (int k = 0; k < QT; ++k) {
-        if (k < ntile) {
-          floatx4 g1 = mma(pb[QT - 1 - k][0], qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
-          g1 = mma(pb[QT - 1 - k][1], qv[k][1], g1);
-          floatx4 g2 = mma(pb[QT - k][0], qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
-          g2 = mma(pb[QT - k][1], qv[k][1], g2);
-          if constexpr (kLimited) {
-            float x[2][4];
-            skew_scores<T, kPerm>(kf, qu[k], g_prev[k], g1, g2, s_g, x);
-            softmax_pv<T, true, kPerm, kSumMfma>(st[k], x, vf, k_lo_q[k] - j0, k_hi_q[k] - j0);
-          } else if (j0 + 32 <= L) {
-            step_compute<T, false, true, kPerm, kSumMfma>(st[k], kf, vf, qu[k], g_prev[k], g1, g2,
-                                                          s_g, 32);
-          } else {
-            step_compute<T, true, true, kPerm, kSumMfma>(st[k], kf, vf, qu[k], g_prev[k], g1, g2,
-                                                         s_g, L - j0);
-          }
-          g_prev[k] = g2;
-        }
+        lo_k[k] = kLimited ? k_lo_q[k] - j0 : 0;
+        hi_k[k] = kLimited ? k_hi_q[k] - j0 : L - j0;
       }
+      step_tiles<T, QT, kM>(st, kf, vf, qu, qv, pb, g_prev, s_g, lo_k, hi_k);
       if constexpr (QT == 2) {
         c1[0] = pb[QT][0];
         c1[1] = pb[QT][1];
@@ -437,18 +526,36 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     __syncthreads();
   };
   // steps in pairs (the two register sets swap roles), an odd last step after the loop: the
-  // loop has one exit, so no path reaches its head with the other set's loads still pending
+  // loop has one exit, so no path reaches its head with the other set's loads still pending.
+  // Without the mask the steps that lie wholly inside the utterance run unmasked, and a last
+  // partial step, masked, after them.
+  const std::integral_constant<bool, true> mask_on;
+  const std::integral_constant<bool, false> mask_off;
+  const int nplain = kLimited ? 0 : (j_end - J) >> 5;   // whole steps that need no mask
   int step = 0;
-  for (; step + 1 < nsteps; step += 2) {
-    do_step(step, rb, ra);
-    do_step(step + 1, ra, rb);
+  for (; step + 1 < nplain; step += 2) {
+    do_step(step, rb, ra, mask_off);
+    do_step(step + 1, ra, rb, mask_off);
   }
-  if (step < nsteps) do_step(step, rb, ra);
+  if (step < nplain) {
+    do_step(step, rb, ra, mask_off);
+    ++step;
+  }
+  if constexpr (kLimited) {
+    for (; step + 1 < nsteps; step += 2) {
+      do_step(step, rb, ra, mask_on);
+      do_step(step + 1, ra, rb, mask_on);
+    }
+  }
+  if (step < nsteps) {
+    if (step & 1) do_step(step, ra, rb, mask_on);
+    else do_step(step, rb, ra, mask_on);
+  }
 
   // finish: every tile of every wave owns its 16 queries
 #pragma unroll
   for (int k = 0; k < QT; ++k) {
-    const float l = kSumMfma ? st[k].ls[0] : column_sum(st[k].l);
+    const float l = st[k].ls[0];
     const float inv = 1.f / l;
     const int i = q0 + 16 * k + m16;
     if (i < L) {
