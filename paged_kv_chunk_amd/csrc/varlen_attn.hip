@@ -80,19 +80,32 @@ __device__ __forceinline__ int k_swz(int r) {
   return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r ^ (r >> 4)) & 1) << 2);
 }
 
+// Running-max reference of a tile column in the folded form the step uses. m is the running
+// maximum (log2 units, -inf before the column's first visible key); the scores are formed
+// relative to r = m, or 0 while m = -inf: -r starts the accumulation of every band product, and
+// each score reads exactly one band value, so a score leaves the MFMA as x - r. thr is the score
+// (relative to r) past which the lazy rescale must run: kRescaleLog2, or -inf while m = -inf (the
+// first visible key must set m).
+struct RunRef {
+  float m, r, thr;
+  floatx4 nr;   // {-r, -r, -r, -r}: the band products' accumulator start
+};
+
 // One 32-key step of a wave's QT query tiles, written in phases so that the tiles' independent
-// work sits in one basic block and interleaves: the band products of every tile; the relative
-// shift of each tile through the wave's skew tile, tile after tile (LDS executes a wave's accesses
-// in order, so tile k + 1's writes land after tile k's reads), each shifted column starting the
-// accumulation of that tile's content product (S^T = K (q + u)^T); one running-max test for all
-// tiles (a single uniform branch, rarely taken); then the probabilities, the PV products and the
-// row sums on the MFMA (an all-ones operand against the probabilities: the sums are those of the
-// bf16-rounded probabilities the values are weighted with). Tile k's band tiles are pb[QT-1-k]
-// and pb[QT-k] (g1, g2) after the carried product g_prev[k]. kMask: only keys lo[k] <= key < hi[k]
-// of the step count for tile k (relative to the step's first key); a column that has seen no key
-// yet contributes nothing.
+// work sits in one basic block and interleaves: the band products of every tile (accumulated onto
+// -r); the relative shift of each tile through the wave's skew tile, tile after tile (LDS executes
+// a wave's accesses in order, so tile k + 1's writes land after tile k's reads), each shifted
+// column starting the accumulation of that tile's content product (S^T = K (q + u)^T), so the
+// scores are x - r; a per-lane test of the scores against thr and one ballot for all tiles (a
+// single uniform branch, rarely taken: the column maxima, the new running maxima, the rescale of
+// the accumulators and the re-basing of the scores and the carried band product are done only
+// there); then the probabilities exp2(x - r), the PV products and the row sums on the MFMA (an
+// all-ones operand against the probabilities: the sums are those of the bf16-rounded
+// probabilities the values are weighted with). Tile k's band tiles are pb[QT-1-k] and pb[QT-k]
+// (g1, g2) after the carried product g_prev[k]. kMask: only keys lo[k] <= key < hi[k] of the step
+// count for tile k (relative to the step's first key).
 template <typename T, int QT, bool kMask>
-__device__ __forceinline__ void step_tiles(Softmax (&st)[QT],
+__device__ __forceinline__ void step_tiles(Softmax (&st)[QT], RunRef (&rr)[QT],
                                            const typename Frag<T>::type (&kf)[2][2],
                                            const typename Frag<T>::type (&vf)[4],
                                            const typename Frag<T>::type (&qu)[QT][2],
@@ -108,9 +121,9 @@ __device__ __forceinline__ void step_tiles(Softmax (&st)[QT],
   floatx4 g1[QT], g2[QT];
 #pragma unroll
   for (int k = 0; k < QT; ++k) {
-    g1[k] = mma(pb[QT - 1 - k][0], qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
+    g1[k] = mma(pb[QT - 1 - k][0], qv[k][0], rr[k].nr);
     g1[k] = mma(pb[QT - 1 - k][1], qv[k][1], g1[k]);
-    g2[k] = mma(pb[QT - k][0], qv[k][0], floatx4{0.f, 0.f, 0.f, 0.f});
+    g2[k] = mma(pb[QT - k][0], qv[k][0], rr[k].nr);
     g2[k] = mma(pb[QT - k][1], qv[k][1], g2[k]);
   }
   // shift: G^T[row][query] -> s_g[query * kSkewPitch + row]; the lane reads its 8 keys' values
@@ -135,8 +148,8 @@ __device__ __forceinline__ void step_tiles(Softmax (&st)[QT],
     }
     g_prev[k] = g2[k];
   }
-  float mx[QT];
-  bool move = false;
+  float lm[QT];   // this lane's maximum over its 8 keys, relative to r
+  bool over = false;
 #pragma unroll
   for (int k = 0; k < QT; ++k) {
     float m = -INFINITY;
@@ -150,32 +163,39 @@ __device__ __forceinline__ void step_tiles(Softmax (&st)[QT],
         }
         m = fmaxf(m, sc[k][tt][e]);
       }
-    mx[k] = column_max(m);
-    move = move || mx[k] > st[k].m + kRescaleLog2;
+    lm[k] = m;
+    over = over || m > rr[k].thr;
   }
-  if (__ballot(move) != 0) {
+  if (__ballot(over) != 0) {
 #pragma unroll
     for (int k = 0; k < QT; ++k) {
-      const bool mv = mx[k] > st[k].m + kRescaleLog2;
-      // (a column that does not move keeps its scale; exp2(m - m) would be NaN for a column that
-      // has seen no key yet, m = -inf)
-      const float alpha = mv ? fast_exp2(st[k].m - mx[k]) : 1.f;
+      const float mx = column_max(lm[k]) + rr[k].r;   // the column's maximum
+      const bool mv = mx > rr[k].m + kRescaleLog2;
+      const float m_new = mv ? mx : rr[k].m;
+      // (a column that does not move keeps its scale; a column that moves for the first time has
+      // nothing accumulated yet, exp2(-inf) = 0)
+      const float alpha = mv ? fast_exp2(rr[k].m - m_new) : 1.f;
       st[k].ls *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) st[k].o[dt] *= alpha;
-      st[k].m = mv ? mx[k] : st[k].m;
+      const float r_new = m_new == -INFINITY ? 0.f : m_new;
+      const float d = r_new - rr[k].r;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) sc[k][tt] -= d;
+      g_prev[k] -= d;
+      rr[k].m = m_new;
+      rr[k].r = r_new;
+      rr[k].thr = m_new == -INFINITY ? -INFINITY : kRescaleLog2;
+      rr[k].nr = floatx4{-r_new, -r_new, -r_new, -r_new};
     }
   }
 #pragma unroll
   for (int k = 0; k < QT; ++k) {
-    // (masked, a column may still have seen nothing: its probabilities must be 0, not
-    // exp2(-inf - -inf))
-    const float m_ref = (kMask && st[k].m == -INFINITY) ? 0.f : st[k].m;
     F pf;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) set(pf, 4 * tt + e, fast_exp2(sc[k][tt][e] - m_ref));
+      for (int e = 0; e < 4; ++e) set(pf, 4 * tt + e, fast_exp2(sc[k][tt][e]));
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st[k].o[dt] = mma(vf[dt], pf, st[k].o[dt]);
     st[k].ls = mma(ones8<T>(), pf, st[k].ls);
@@ -314,13 +334,16 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   auto band_slot = [&](int x) { return s_band + (x & (RING - 1)) * BP; };
 
   Softmax st[QT];
+  RunRef rr[QT];
 #pragma unroll
   for (int k = 0; k < QT; ++k) {
-    st[k].m = -INFINITY;
-    st[k].l = 0.f;
     st[k].ls = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st[k].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    rr[k].m = -INFINITY;
+    rr[k].r = 0.f;
+    rr[k].thr = -INFINITY;
+    rr[k].nr = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   float* s_g = s_skew + wave * kSkewFloats;
 
@@ -512,7 +535,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
         lo_k[k] = kLimited ? k_lo_q[k] - j0 : 0;
         hi_k[k] = kLimited ? k_hi_q[k] - j0 : L - j0;
       }
-      step_tiles<T, QT, kM>(st, kf, vf, qu, qv, pb, g_prev, s_g, lo_k, hi_k);
+      step_tiles<T, QT, kM>(st, rr, kf, vf, qu, qv, pb, g_prev, s_g, lo_k, hi_k);
       if constexpr (QT == 2) {
         c1[0] = pb[QT][0];
         c1[1] = pb[QT][1];
