@@ -303,8 +303,8 @@ pkc_status paged_kv_commit(int32_t* cache_seqlens, const int32_t* chunk_lens,
  * Errors: as above; a negative mask_chunk or mask_left_chunks -> PKC_ERR_SHAPE; head_dim != 64,
  * 2 max_seqlen max(H, Hk) head_dim element bytes at or past 2^31 (an utterance's rows are
  * addressed by 32-bit byte offsets), or the launch limits (num_seqs n_head ceil(max_seqlen / Q)
- * workgroups of 256 threads, one per Q = 128 queries in bf16, 64 in fp32, of an utterance and
- * head) -> PKC_ERR_UNSUPPORTED.
+ * workgroups of 256 threads, one per Q queries of an utterance and head: Q = 128 in bf16, 64 in
+ * fp32 and with the chunked_limited mask) -> PKC_ERR_UNSUPPORTED.
  */
 pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void* k, const void* v,
                                      const int32_t* cu_seqlens, int32_t num_seqs,

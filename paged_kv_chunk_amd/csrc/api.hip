@@ -303,7 +303,8 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
   if (mul_sat(mul_sat((int64_t)2 * max_seqlen, n_head > n_kv_head ? n_head : n_kv_head),
               (int64_t)head_dim * (dtype == PKC_BF16 ? 2 : 4)) >= (int64_t)1 << 31)
     return PKC_ERR_UNSUPPORTED;
-  if (!varlen_attn_grid(dtype == PKC_BF16 ? 2 : 4, num_seqs, n_head, max_seqlen).fits())
+  if (!varlen_attn_grid(dtype == PKC_BF16 ? 2 : 4, num_seqs, n_head, max_seqlen, mask_chunk > 0)
+           .fits())
     return PKC_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pos) ||
       !aligned16(pos_bias_u) || !aligned16(pos_bias_v) || !aligned16(out))

@@ -146,7 +146,8 @@ struct LaunchGrid {
 LaunchGrid paged_append_grid(int batch, int n_kv_head);
 LaunchGrid commit_grid(int batch);
 LaunchGrid chunk_attn_grid(int dtype_bytes, int batch, int n_head, int chunk);
-LaunchGrid varlen_attn_grid(int dtype_bytes, int num_seqs, int n_head, int max_seqlen);
+LaunchGrid varlen_attn_grid(int dtype_bytes, int num_seqs, int n_head, int max_seqlen,
+                            bool limited);   // with the chunked_limited mask
 LaunchGrid gather_read_grid(int batch, int n_head, int split, int waves);
 LaunchGrid gemm_grid(int64_t M, int64_t N);   // the tile shape the GEMM launchers pick for M x N
 

@@ -50,8 +50,11 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-template <typename T> constexpr int kQT = sizeof(T) == 2 ? 2 : 1;   // 16-query tiles per wave
-template <typename T> constexpr int kQTile = 16 * kQT<T> * kWaves;  // queries per workgroup
+// 16-query tiles per wave: two for bf16 over the full context, one for fp32 and for the
+// chunked_limited mask (a workgroup walks the union of its queries' visible keys, so smaller
+// query tiles waste fewer masked steps)
+template <typename T, bool kLim> constexpr int kQT = (sizeof(T) == 2 && !kLim) ? 2 : 1;
+template <typename T, bool kLim> constexpr int kQTile = 16 * kQT<T, kLim> * kWaves;  // per workgroup
 
 template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // band / fp32 K row pitch
 template <typename T> constexpr bool kSwK = sizeof(T) == 2;            // swizzled bf16 K rows
@@ -63,7 +66,11 @@ template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T til
 template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
 // rows of the band ring: it spans the lowest row a step reads to the highest it stages, 64 QT + 64
 // rows, rounded up to a power of two
-template <typename T> constexpr int kRing = kQT<T> == 2 ? 256 : 128;
+template <typename T, bool kLim> constexpr int kRing = kQT<T, kLim> == 2 ? 256 : 128;
+// waves per SIMD the register budget targets: bf16 two-tile waves 2, bf16 one-tile waves 3; fp32
+// (one workgroup per CU by its LDS) 1
+template <typename T, bool kLim> constexpr int kWavesPerSimd =
+    sizeof(T) == 4 ? 1 : (kQT<T, kLim> == 2 ? 2 : 3);
 constexpr int kSortMax = 64;   // utterances a wave ranks by length (one per lane)
 // Lane group g holds the keys of key_group<true>(g) (groups 1 and 2 swapped): the shifted
 // position values are then read conflict-free.
@@ -218,25 +225,24 @@ struct VarlenArgs {
   float scale_log2;
 };
 
-// (bf16: two workgroups per CU, the register budget of 2 waves per SIMD for two query tiles per
-// wave; fp32, one tile per wave: 3)
+// (register budget: kWavesPerSimd waves per SIMD)
 template <typename T, bool kLimited>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 3, sizeof(T) == 2 ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<T, kLimited>, kWavesPerSimd<T, kLimited>)))
 varlen_attn_kernel(VarlenArgs<T> a) {
   typedef typename Frag<T>::type F;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int NV = kD / VEC;
   constexpr int KP = kKP<T>;
   constexpr int VP = kVP<T>;
-  constexpr int QT = kQT<T>;                                       // query tiles per wave
-  constexpr int QTILE = kQTile<T>;                                 // queries per workgroup
+  constexpr int QT = kQT<T, kLimited>;                             // query tiles per wave
+  constexpr int QTILE = kQTile<T, kLimited>;                       // queries per workgroup
   constexpr int KT = kSwK<T> ? kD : KP;                            // K tile row pitch
   constexpr int TILE = 32 * KT + (kTrV<T> ? 32 * kD : kD * VP);   // elements of one K + V stage
 
   __shared__ __align__(16) T s_kv[2 * TILE];
   constexpr int BP = kBP<T>;
-  constexpr int RING = kRing<T>;
+  constexpr int RING = kRing<T, kLimited>;
   __shared__ __align__(16) T s_band[RING * BP];   // row x of the table in slot x % RING
   // one shift tile per wave, used by its query tiles in turn (LDS executes a wave's accesses in
   // order, so a tile's writes never overtake the previous tile's reads)
@@ -604,7 +610,9 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
   a.out = (T*)p.out;
   a.H = p.n_head;
   a.Hk = p.n_kv_head;
-  a.qtiles = (p.max_seqlen + kQTile<T> - 1) / kQTile<T>;
+  const bool limited = p.mask_chunk > 0;
+  const int qtile = limited ? kQTile<T, true> : kQTile<T, false>;
+  a.qtiles = (p.max_seqlen + qtile - 1) / qtile;
   a.div_H = make_fastdiv(a.H);
   a.div_qtiles = make_fastdiv(a.qtiles);
   a.div_group = make_fastdiv(a.H / a.Hk);
@@ -615,9 +623,9 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
   a.scale_log2 = scale * 1.4426950408889634f;
   a.chunk = p.mask_chunk;
   a.left = p.mask_left_chunks;
-  const dim3 grid(
-      (unsigned)varlen_attn_grid((int)sizeof(T), p.num_seqs, p.n_head, p.max_seqlen).workgroups);
-  if (p.mask_chunk > 0)
+  const dim3 grid((unsigned)varlen_attn_grid((int)sizeof(T), p.num_seqs, p.n_head, p.max_seqlen,
+                                             limited).workgroups);
+  if (limited)
     hipLaunchKernelGGL((varlen_attn_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((varlen_attn_kernel<T, false>), grid, dim3(kThreads), 0, stream, a);
@@ -626,8 +634,10 @@ hipError_t launch_varlen_t(const VarlenParams& p, hipStream_t stream) {
 
 }  // namespace
 
-LaunchGrid varlen_attn_grid(int dtype_bytes, int num_seqs, int n_head, int max_seqlen) {
-  const int qtile = dtype_bytes == 2 ? kQTile<bf16> : kQTile<float>;
+LaunchGrid varlen_attn_grid(int dtype_bytes, int num_seqs, int n_head, int max_seqlen,
+                            bool limited) {
+  const int qtile = dtype_bytes == 2 ? (limited ? kQTile<bf16, true> : kQTile<bf16, false>)
+                                     : (limited ? kQTile<float, true> : kQTile<float, false>);
   return {mul_sat(mul_sat(num_seqs, n_head), ((int64_t)max_seqlen + qtile - 1) / qtile), kThreads};
 }
 
