@@ -373,6 +373,10 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   st.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Transformer-XL steps keep the running maximum in the folded form (step_fold): the band
+  // products start their accumulation at rr.nr, so the scores need no subtraction
+  RunRef rr;
+  runref_init(rr);
 
   // ---- 4. tail steps over the chunk's frames, from LDS, first (the one workgroup barrier: the
   // tail was staged by all threads; the body below uses only the wave's own registers and LDS).
@@ -421,10 +425,10 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       floatx4 g[3];
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
-        g[t] = mma(pb[t][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        g[t] = mma(pb[t][0], qv[0], rr.nr);
         g[t] = mma(pb[t][1], qv[1], g[t]);
       }
-      step_compute<T, true>(st, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
+      step_fold<T, true>(st, rr, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
     }
   }
 
@@ -432,7 +436,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   if (nmine > 0) {
     floatx4 g_prev;
     if (!kPerKey) {
-      g_prev = mma(p0[0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      g_prev = mma(p0[0], qv[0], rr.nr);
       g_prev = mma(p0[1], qv[1], g_prev);
     }
     auto run = [&](StepRegs<T>& r, int s) {
@@ -446,12 +450,12 @@ chunk_attn_kernel(ChunkArgs<T> a) {
         if (part) softmax_pv<T, true>(st, x, r.v, 0, cache - 32 * s);
         else softmax_pv<T, false>(st, x, r.v, 0, 32);
       } else {
-        floatx4 g1 = mma(r.p[0][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        floatx4 g1 = mma(r.p[0][0], qv[0], rr.nr);
         g1 = mma(r.p[0][1], qv[1], g1);
-        floatx4 g2 = mma(r.p[1][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        floatx4 g2 = mma(r.p[1][0], qv[0], rr.nr);
         g2 = mma(r.p[1][1], qv[1], g2);
-        if (part) step_compute<T, true>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, cache - 32 * s);
-        else step_compute<T, false>(st, r.k, r.v, qu, g_prev, g1, g2, s_g, 32);
+        if (part) step_fold<T, true>(st, rr, r.k, r.v, qu, g_prev, g1, g2, s_g, cache - 32 * s);
+        else step_fold<T, false>(st, rr, r.k, r.v, qu, g_prev, g1, g2, s_g, 32);
         g_prev = g2;
       }
       if (s + 2 < s_end) load_step(r, s + 2);
@@ -507,6 +511,7 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   }
   // ---- 7. merge the waves' partial states in a fixed order -------------------------------------
   st.l = column_sum(st.l);
+  if constexpr (!kPerKey) st.m = rr.m;   // (the folded steps keep the running maximum in rr)
   float* s_o = s_wave + wave * kWaveLds;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)

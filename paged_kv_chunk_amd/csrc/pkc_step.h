@@ -232,4 +232,111 @@ __device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>
 }
 
 
+// Running-max reference of a query column in the folded form (step_fold, and the packed kernel's
+// multi-tile step). m is the running maximum (log2 units, -inf before the column's first visible
+// key); scores are formed relative to r = m, or 0 while m = -inf: -r starts the accumulation of
+// every band product, and each score reads exactly one band value, so a score is x - r without a
+// subtraction. thr is the score (relative to r) past which the lazy rescale must run:
+// kRescaleLog2, or -inf while m = -inf (the first visible key must set m).
+struct RunRef {
+  float m, r, thr;
+  floatx4 nr;   // {-r, -r, -r, -r}: the band products' accumulator start
+};
+
+__device__ __forceinline__ void runref_init(RunRef& rr) {
+  rr.m = -INFINITY;
+  rr.r = 0.f;
+  rr.thr = -INFINITY;
+  rr.nr = floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+// A new running maximum for the column from this lane's maximum lm over its keys (relative to
+// r): the rescale of the accumulators when the column moves, and the shift d = r_new - r that
+// every value still relative to the old reference must drop. Call from a branch uniform over the
+// wave (the column maximum is a cross-lane reduction).
+// (l: the row sum, per-lane partial or the MFMA's floatx4)
+template <typename L>
+__device__ __forceinline__ float runref_move(RunRef& rr, float lm, floatx4 (&o)[4], L& l) {
+  const float mx = column_max(lm) + rr.r;   // the column's maximum
+  const bool mv = mx > rr.m + kRescaleLog2;
+  const float m_new = mv ? mx : rr.m;
+  // (a column that does not move keeps its scale; one that moves for the first time has nothing
+  // accumulated yet, exp2(-inf) = 0)
+  const float alpha = mv ? fast_exp2(rr.m - m_new) : 1.f;
+  l *= alpha;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+  const float r_new = m_new == -INFINITY ? 0.f : m_new;
+  const float d = r_new - rr.r;
+  rr.m = m_new;
+  rr.r = r_new;
+  rr.thr = m_new == -INFINITY ? -INFINITY : kRescaleLog2;
+  rr.nr = floatx4{-r_new, -r_new, -r_new, -r_new};
+  return d;
+}
+
+// One whole 32-key Transformer-XL step with the running-max reference folded in: g0, g1 and g2
+// were accumulated onto rr.nr, so the shifted band values, and the scores with them, come out
+// relative to r, and the probabilities are exp2 of the scores. The lazy-rescale decision is a
+// per-lane test against rr.thr and one ballot; the column maxima, the rescale and the re-basing
+// of the scores and of g2 (the carried band product of the next step) run only in that rare
+// branch. The decisions are those of step_compute. kMask: keys at or past valid_keys are excluded
+// (never all of a step's keys). The row sums stay per-lane in st.l (column_sum at the end).
+template <typename T, bool kMask, bool kPermGrp = false>
+__device__ __forceinline__ void step_fold(Softmax& st, RunRef& rr,
+                                          const typename Frag<T>::type (&kf)[2][2],
+                                          const typename Frag<T>::type (&vf)[4],
+                                          const typename Frag<T>::type (&qu)[2],
+                                          const floatx4& g0, const floatx4& g1, floatx4& g2,
+                                          float* s_g, int valid_keys) {
+  typedef typename Frag<T>::type F;
+  const int lane = threadIdx.x & 63;
+  const int m16 = lane & 15;
+  const int grp = lane >> 4;
+  floatx4 sc[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    sc[tt] = mma(kf[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
+    sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
+  }
+  float* colw = s_g + m16 * kSkewPitch + 4 * grp;
+  *reinterpret_cast<floatx4*>(colw) = g0;
+  *reinterpret_cast<floatx4*>(colw + 16) = g1;
+  *reinterpret_cast<floatx4*>(colw + 32) = g2;
+  __builtin_amdgcn_wave_barrier();
+  const int kg = key_group<kPermGrp>(grp);
+  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * kg;
+  float x[2][4];
+  float lm = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = sc[tt][e] + colr[4 * tt + e];
+      if (kMask) v = (8 * kg + 4 * tt + e < valid_keys) ? v : -INFINITY;
+      x[tt][e] = v;
+      lm = fmaxf(lm, v);
+    }
+  __builtin_amdgcn_wave_barrier();
+  if (__ballot(lm > rr.thr) != 0) {
+    const float d = runref_move(rr, lm, st.o, st.l);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[tt][e] -= d;
+    g2 -= d;
+  }
+  F pf;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = fast_exp2(x[tt][e]);
+      st.l += pe;
+      set(pf, 4 * tt + e, pe);
+    }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
+}
+
 }  // namespace pkc

@@ -87,17 +87,6 @@ __device__ __forceinline__ int k_swz(int r) {
   return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r ^ (r >> 4)) & 1) << 2);
 }
 
-// Running-max reference of a tile column in the folded form the step uses. m is the running
-// maximum (log2 units, -inf before the column's first visible key); the scores are formed
-// relative to r = m, or 0 while m = -inf: -r starts the accumulation of every band product, and
-// each score reads exactly one band value, so a score leaves the MFMA as x - r. thr is the score
-// (relative to r) past which the lazy rescale must run: kRescaleLog2, or -inf while m = -inf (the
-// first visible key must set m).
-struct RunRef {
-  float m, r, thr;
-  floatx4 nr;   // {-r, -r, -r, -r}: the band products' accumulator start
-};
-
 // One 32-key step of a wave's QT query tiles, written in phases so that the tiles' independent
 // work sits in one basic block and interleaves: the band products of every tile (accumulated onto
 // -r); the relative shift of each tile through the wave's skew tile, tile after tile (LDS executes
@@ -176,24 +165,10 @@ __device__ __forceinline__ void step_tiles(Softmax (&st)[QT], RunRef (&rr)[QT],
   if (__ballot(over) != 0) {
 #pragma unroll
     for (int k = 0; k < QT; ++k) {
-      const float mx = column_max(lm[k]) + rr[k].r;   // the column's maximum
-      const bool mv = mx > rr[k].m + kRescaleLog2;
-      const float m_new = mv ? mx : rr[k].m;
-      // (a column that does not move keeps its scale; a column that moves for the first time has
-      // nothing accumulated yet, exp2(-inf) = 0)
-      const float alpha = mv ? fast_exp2(rr[k].m - m_new) : 1.f;
-      st[k].ls *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) st[k].o[dt] *= alpha;
-      const float r_new = m_new == -INFINITY ? 0.f : m_new;
-      const float d = r_new - rr[k].r;
+      const float d = runref_move(rr[k], lm[k], st[k].o, st[k].ls);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) sc[k][tt] -= d;
       g_prev[k] -= d;
-      rr[k].m = m_new;
-      rr[k].r = r_new;
-      rr[k].thr = m_new == -INFINITY ? -INFINITY : kRescaleLog2;
-      rr[k].nr = floatx4{-r_new, -r_new, -r_new, -r_new};
     }
   }
 #pragma unroll
@@ -346,10 +321,7 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     st[k].ls = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st[k].o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    rr[k].m = -INFINITY;
-    rr[k].r = 0.f;
-    rr[k].thr = -INFINITY;
-    rr[k].nr = floatx4{0.f, 0.f, 0.f, 0.f};
+    runref_init(rr[k]);
   }
   float* s_g = s_skew + wave * kSkewFloats;
 
