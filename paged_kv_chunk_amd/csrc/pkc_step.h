@@ -35,10 +35,11 @@ __device__ __forceinline__ int key_group(int g) {
   return kPermGrp ? (((g & 1) << 1) | (g >> 1)) : g;
 }
 
-// Running softmax state of one lane (one query column, 8 keys of each step). With the row sum on
-// the MFMA (kSumMfma below), ls holds it instead of l: the product of an all-ones operand with the
-// step's probabilities, the same value in every register (the column's sum of the bf16-rounded
-// probabilities that also weight the values).
+// Running softmax state of one lane (one query column, 8 keys of each step): m the running
+// maximum (the per-key steps; the folded steps keep theirs in RunRef), l this lane's part of the
+// row sum, o the output accumulators. The packed kernel keeps the row sum in ls instead: the
+// product of an all-ones operand with the step's probabilities on the MFMA, the same value in
+// every register (the column's sum of the bf16-rounded probabilities that also weight the values).
 struct Softmax {
   float m, l;
   floatx4 o[4];
@@ -50,38 +51,6 @@ template <typename T> __device__ __forceinline__ typename Frag<T>::type ones8() 
 #pragma unroll
   for (int e = 0; e < 8; ++e) set(v, e, 1.f);
   return v;
-}
-
-// Scores of one 32-key step, Transformer-XL convention: S^T = K (q+u)^T from the two key tiles,
-// plus the band product shifted into place through the per-wave LDS tile (scores already in log2
-// units). x[tt][e] is key 8 grp + 4 tt + e of the step for this lane's query column.
-template <typename T, bool kPermGrp = false>
-__device__ __forceinline__ void skew_scores(const typename Frag<T>::type (&kf)[2][2],
-                                            const typename Frag<T>::type (&qu)[2],
-                                            const floatx4& g0, const floatx4& g1, const floatx4& g2,
-                                            float* s_g, float (&x)[2][4]) {
-  const int lane = threadIdx.x & 63;
-  const int m16 = lane & 15;
-  const int grp = lane >> 4;
-  floatx4 sc[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    sc[tt] = mma(kf[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
-    sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
-  }
-  // Relative shift through LDS: G^T[row][query] -> s_g[query * kSkewPitch + row]; the lane then
-  // reads its 8 keys' values from its own query column, shifted by 15 - query.
-  float* colw = s_g + m16 * kSkewPitch + 4 * grp;
-  *reinterpret_cast<floatx4*>(colw) = g0;
-  *reinterpret_cast<floatx4*>(colw + 16) = g1;
-  *reinterpret_cast<floatx4*>(colw + 32) = g2;
-  __builtin_amdgcn_wave_barrier();
-  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * key_group<kPermGrp>(grp);
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[tt][e] = sc[tt][e] + colr[4 * tt + e];
-  __builtin_amdgcn_wave_barrier();
 }
 
 // Scores of one 32-key step, WeNet convention (no shift): the table has one row per key, in the
@@ -106,7 +75,7 @@ __device__ __forceinline__ void per_key_scores(const typename Frag<T>::type (&kf
 // Online softmax and PV of one step from its scores. kMask: only keys k_lo <= key < k_hi of the
 // step count for this lane's query column (bounds may differ between columns); a column with no
 // key seen yet contributes nothing.
-template <typename T, bool kMask, bool kPermGrp = false, bool kSumMfma = false>
+template <typename T, bool kMask, bool kPermGrp = false>
 __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
                                            const typename Frag<T>::type (&vf)[4], int k_lo,
                                            int k_hi) {
@@ -128,8 +97,7 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
     // (a column that does not move keeps its scale; computing it as exp2(m - m) would give NaN
     // for a column that has seen no key yet, m = -inf)
     const float alpha = move ? fast_exp2(st.m - m_new) : 1.f;
-    if constexpr (kSumMfma) st.ls *= alpha;
-    else st.l *= alpha;
+    st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
     st.m = m_new;
@@ -143,94 +111,12 @@ __device__ __forceinline__ void softmax_pv(Softmax& st, float (&x)[2][4],
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float pe = fast_exp2(x[tt][e] - m_ref);
-      if constexpr (!kSumMfma) st.l += pe;
+      st.l += pe;
       set(pf, 4 * tt + e, pe);
     }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
-  if constexpr (kSumMfma) st.ls = mma(ones8<T>(), pf, st.ls);
 }
-
-// One whole 32-key Transformer-XL step given its operand fragments and the three band product
-// tiles (scores already in log2 units), in one piece: the scores, the mask and the running max
-// stay between the two wave barriers of the shift, which keeps the register live ranges of the
-// hot loop short. kMask: keys at or past valid_keys are excluded (the same keys for every query
-// column, and never all of a step's keys).
-template <typename T, bool kMask, bool kShiftFirst = false, bool kPermGrp = false,
-          bool kSumMfma = false>
-__device__ __forceinline__ void step_compute(Softmax& st, const typename Frag<T>::type (&kf)[2][2],
-                                             const typename Frag<T>::type (&vf)[4],
-                                             const typename Frag<T>::type (&qu)[2],
-                                             const floatx4& g0, const floatx4& g1,
-                                             const floatx4& g2, float* s_g, int valid_keys) {
-  typedef typename Frag<T>::type F;
-  const int lane = threadIdx.x & 63;
-  const int m16 = lane & 15;
-  const int grp = lane >> 4;
-  // Relative shift through LDS: G^T[row][query] -> s_g[query * kSkewPitch + row]; the lane then
-  // reads its 8 keys' values from its own query column, shifted by 15 - query. kShiftFirst: the
-  // shift comes first and its values start the content products' accumulation (no separate
-  // add, a longer dependency chain); otherwise the products overlap the LDS round trip.
-  floatx4 sc[2];
-  if constexpr (!kShiftFirst) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sc[tt] = mma(kf[tt][0], qu[0], floatx4{0.f, 0.f, 0.f, 0.f});
-      sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
-    }
-  }
-  float* colw = s_g + m16 * kSkewPitch + 4 * grp;
-  *reinterpret_cast<floatx4*>(colw) = g0;
-  *reinterpret_cast<floatx4*>(colw + 16) = g1;
-  *reinterpret_cast<floatx4*>(colw + 32) = g2;
-  __builtin_amdgcn_wave_barrier();
-  const int kg = key_group<kPermGrp>(grp);
-  const float* colr = s_g + m16 * kSkewPitch + 15 - m16 + 8 * kg;
-  if constexpr (kShiftFirst) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sc[tt] = mma(kf[tt][0], qu[0],
-                   floatx4{colr[4 * tt], colr[4 * tt + 1], colr[4 * tt + 2], colr[4 * tt + 3]});
-      sc[tt] = mma(kf[tt][1], qu[1], sc[tt]);
-    }
-  }
-  float x[2][4];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float v = kShiftFirst ? sc[tt][e] : sc[tt][e] + colr[4 * tt + e];
-      if (kMask) v = (8 * kg + 4 * tt + e < valid_keys) ? v : -INFINITY;
-      x[tt][e] = v;
-      mx = fmaxf(mx, v);
-    }
-  __builtin_amdgcn_wave_barrier();
-  mx = column_max(mx);
-  const bool move = mx > st.m + kRescaleLog2;
-  if (__ballot(move) != 0) {
-    const float m_new = move ? mx : st.m;
-    const float alpha = fast_exp2(st.m - m_new);
-    if constexpr (kSumMfma) st.ls *= alpha;
-    else st.l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
-    st.m = m_new;
-  }
-  F pf;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pe = fast_exp2(x[tt][e] - st.m);
-      if constexpr (!kSumMfma) st.l += pe;
-      set(pf, 4 * tt + e, pe);
-    }
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) st.o[dt] = mma(vf[dt], pf, st.o[dt]);
-  if constexpr (kSumMfma) st.ls = mma(ones8<T>(), pf, st.ls);
-}
-
 
 // Running-max reference of a query column in the folded form (step_fold, and the packed kernel's
 // multi-tile step). m is the running maximum (log2 units, -inf before the column's first visible
@@ -280,7 +166,8 @@ __device__ __forceinline__ float runref_move(RunRef& rr, float lm, floatx4 (&o)[
 // relative to r, and the probabilities are exp2 of the scores. The lazy-rescale decision is a
 // per-lane test against rr.thr and one ballot; the column maxima, the rescale and the re-basing
 // of the scores and of g2 (the carried band product of the next step) run only in that rare
-// branch. The decisions are those of step_compute. kMask: keys at or past valid_keys are excluded
+// branch. The decisions are those of the plain form (rescale when a column maximum passes m by
+// kRescaleLog2). kMask: keys at or past valid_keys are excluded
 // (never all of a step's keys). The row sums stay per-lane in st.l (column_sum at the end).
 template <typename T, bool kMask, bool kPermGrp = false>
 __device__ __forceinline__ void step_fold(Softmax& st, RunRef& rr,

@@ -8,15 +8,17 @@
 //
 // Work decomposition. One workgroup of 4 waves per (utterance, query tile, head), the head
 // varying fastest over the grid so that all tiles of one head share an XCD. For bf16 a wave owns
-// 32 queries as two 16-query MFMA tiles (a workgroup 128), for fp32 one tile (64): every K, V and
-// band fragment a wave reads from LDS then feeds both tiles, which halves the LDS reads per MFMA
-// (the CU's LDS bandwidth, shared by its four SIMDs, bounded the step). Each tile keeps its own
-// online softmax; no merge. The workgroup walks the utterance's keys in 32-key steps: every
-// step's K rows and V rows are staged once in double-buffered LDS and read by all four waves. The
-// band rows (the table rows the queries touch) go through an LDS ring of 256 rows: the waves'
-// windows overlap, so a step brings in only the 32 rows that enter the workgroup's window. Every
-// global read is issued two steps ahead. The per-step math is the shared step engine of
-// pkc_step.h. MFMA-bound in principle (6 L^2 D FLOP per utterance and head).
+// 32 queries as two 16-query MFMA tiles (a workgroup 128); fp32, and the chunked_limited mask,
+// keep one tile (64): every K, V and band fragment a wave reads from LDS then feeds both tiles,
+// which halves the LDS reads per MFMA (the CU's LDS bandwidth, shared by its four SIMDs, bounded
+// the step). Each tile keeps its own online softmax; no merge. The workgroup walks the
+// utterance's keys in 32-key steps: every step's K rows and V rows are staged once in
+// double-buffered LDS and read by all four waves. The band rows (the table rows the queries
+// touch) go through an LDS ring of 256 rows (128 with one tile per wave): the waves' windows
+// overlap, so a step brings in only the 32 rows that enter the workgroup's window. Every global
+// read is issued two steps ahead. The step's arithmetic is step_tiles below, with the folded
+// running-max reference of pkc_step.h. MFMA-bound in principle (6 L^2 D FLOP per utterance and
+// head).
 //
 // Band tiles of a wave at a step: T_m = rows [xb + 16 m, xb + 16 m + 16), m = 0 .. kQT + 1, where
 // query tile k (first query q0 + 16 k) reads T_{kQT-1-k}, T_{kQT-k} and T_{kQT+1-k}. The next step's
