@@ -12,13 +12,14 @@
 // keep one tile (64): every K, V and band fragment a wave reads from LDS then feeds both tiles,
 // which halves the LDS reads per MFMA (the CU's LDS bandwidth, shared by its four SIMDs, bounded
 // the step). Each tile keeps its own online softmax; no merge. The workgroup walks the
-// utterance's keys in 32-key steps: every step's K rows and V rows are staged once in
-// double-buffered LDS and read by all four waves. The band rows (the table rows the queries
-// touch) go through an LDS ring of 256 rows (128 with one tile per wave): the waves' windows
-// overlap, so a step brings in only the 32 rows that enter the workgroup's window. Every global
-// read is issued two steps ahead. The step's arithmetic is step_tiles below, with the folded
-// running-max reference of pkc_step.h. MFMA-bound in principle (6 L^2 D FLOP per utterance and
-// head).
+// utterance's keys in stages of two 32-key steps (one with one tile per wave): every stage's K
+// rows and V rows are staged once in double-buffered LDS and read by all four waves, with one
+// barrier per stage. The band rows (the table rows the queries touch) go through an LDS ring of
+// 256 rows (128 with one tile per wave): the waves' windows overlap, so a stage brings in only
+// the rows that enter the workgroup's window. Every global read is issued at least two steps
+// before its rows are used: two-step stages request a stage's rows one stage ahead, one-step
+// stages two. The step's arithmetic is step_tiles below, with the folded running-max reference
+// of pkc_step.h. MFMA-bound in principle (6 L^2 D FLOP per utterance and head).
 //
 // Band tiles of a wave at a step: T_m = rows [xb + 16 m, xb + 16 m + 16), m = 0 .. kQT + 1, where
 // query tile k (first query q0 + 16 k) reads T_{kQT-1-k}, T_{kQT-k} and T_{kQT+1-k}. The next step's
@@ -58,17 +59,27 @@ constexpr int kThreads = kWaves * 64;
 template <typename T, bool kLim> constexpr int kQT = (sizeof(T) == 2 && !kLim) ? 2 : 1;
 template <typename T, bool kLim> constexpr int kQTile = 16 * kQT<T, kLim> * kWaves;  // per workgroup
 
+// 32-key steps per staging stage (one barrier, one K/V buffer): two with two query tiles per wave,
+// so that a workgroup meets half as many barriers per key and its global reads run 128 keys
+// ahead; one elsewhere
+template <typename T, bool kLim> constexpr int kSubs = kQT<T, kLim> == 2 ? 2 : 1;
 template <typename T> constexpr int kKP = kD + 16 / (int)sizeof(T);   // band / fp32 K row pitch
 template <typename T> constexpr bool kSwK = sizeof(T) == 2;            // swizzled bf16 K rows
-// band ring row pitch: 160 bytes for bf16 (a read of 16 consecutive rows, one 16-byte column per
-// lane group, measured conflict-free on gfx950 at any starting row; 144, 176 and 208 bytes cost
-// 4 extra cycles per read)
-template <typename T> constexpr int kBP = sizeof(T) == 2 ? kD + 16 : kKP<T>;
+// Band ring rows. With two-step stages (bf16, two tiles): 128 bytes, unpadded, so that the two
+// stages of K and V and the ring fit two workgroups per CU, the eight 16-byte chunks of slot x
+// permuted by chunk ^ (x & 7). A band-tile read (16 consecutive slots, one chunk per lane group)
+// and a staging write (8 lanes per slot) measured conflict-free on gfx950 at every starting slot;
+// chunk ^ ((x >> 1) & 7) cost 3.2 extra cycles per read at most starting slots. Otherwise 160
+// bytes for bf16 (a read of 16 consecutive rows measured conflict-free at any starting row; 144,
+// 176 and 208 bytes cost 4 extra cycles per read).
+template <typename T, bool kLim> constexpr bool kBandSwz = kSubs<T, kLim> == 2;
+template <typename T, bool kLim> constexpr int kBP =
+    kBandSwz<T, kLim> ? kD : (sizeof(T) == 2 ? kD + 16 : kKP<T>);
 template <typename T> constexpr int kVP = 32 + 16 / (int)sizeof(T);   // V^T tile row pitch (fp32)
 template <typename T> constexpr bool kTrV = sizeof(T) == 2;            // natural V rows + tr reads
-// rows of the band ring: it spans the lowest row a step reads to the highest it stages, 64 QT + 64
-// rows, rounded up to a power of two
-template <typename T, bool kLim> constexpr int kRing = kQT<T, kLim> == 2 ? 256 : 128;
+// rows of the band ring: it spans the lowest row a stage reads to the highest it stages,
+// 16 QT kWaves + 64 kSubs rows (256 with two tiles and two-step stages, 128 with one and one)
+template <typename T, bool kLim> constexpr int kRing = 16 * kQT<T, kLim> * kWaves + 64 * kSubs<T, kLim>;
 // waves per SIMD the register budget targets: bf16 two-tile waves 2, bf16 one-tile waves 3; fp32
 // (one workgroup per CU by its LDS) 1
 template <typename T, bool kLim> constexpr int kWavesPerSimd =
@@ -214,12 +225,18 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   constexpr int VP = kVP<T>;
   constexpr int QT = kQT<T, kLimited>;                             // query tiles per wave
   constexpr int QTILE = kQTile<T, kLimited>;                       // queries per workgroup
+  constexpr int SUBS = kSubs<T, kLimited>;                         // 32-key steps per stage
+  constexpr int SK = 32 * SUBS;                                    // keys per stage
   constexpr int KT = kSwK<T> ? kD : KP;                            // K tile row pitch
-  constexpr int TILE = 32 * KT + (kTrV<T> ? 32 * kD : kD * VP);   // elements of one K + V stage
+  constexpr int TILE = SK * KT + (kTrV<T> ? SK * kD : kD * VP);   // elements of one K + V stage
+  static_assert(kTrV<T> || SUBS == 1, "the transposed V tile holds one 32-key step");
 
   __shared__ __align__(16) T s_kv[2 * TILE];
-  constexpr int BP = kBP<T>;
+  constexpr bool BSW = kBandSwz<T, kLimited>;
+  constexpr int BP = kBP<T, kLimited>;
   constexpr int RING = kRing<T, kLimited>;
+  static_assert((RING & (RING - 1)) == 0, "ring slots are row & (RING - 1)");
+  static_assert(!BSW || sizeof(T) == 2, "the ring swizzle permutes 16-byte chunks of bf16 rows");
   __shared__ __align__(16) T s_band[RING * BP];   // row x of the table in slot x % RING
   // one shift tile per wave, used by its query tiles in turn (LDS executes a wave's accesses in
   // order, so a tile's writes never overtake the previous tile's reads)
@@ -304,16 +321,21 @@ varlen_attn_kernel(VarlenArgs<T> a) {
   // first key is j0 starts at row C0 + j0 - 16 QT w + 16 m (tile k's rows R0 + j0 - i for its
   // queries i begin at T_{QT-1-k}). Step 0 reads T_0 .. T_{QT+1} of every wave, rows
   // [C0 + J - 48 QT, C0 + J + 16 QT + 32); a later step T_2 .. T_{QT+1} (QT = 2) or T_1, T_2 (QT = 1),
-  // the 64 QT rows below the window top C0 + j0 + 16 QT + 32. The 32 rows above that top enter for
-  // the next step: they are fetched with the K/V rows of that step, rows [xw + j0', xw + j0' + 32)
-  // for its first key j0', and staged during this one. The ring spans the lowest row a step reads
-  // to the highest it stages (at most 64 QT + 64 rows), so the rows staged during a step never take a
-  // slot that step reads, and a row is overwritten only after the barrier that ends its last use.
+  // the 64 QT rows below the window top C0 + j0 + 16 QT + 32. A stage of SK keys at j0 reads up to
+  // the top xw + j0 + SK; the SK rows above it enter for the next stage: they are fetched with that
+  // stage's K/V rows, rows [xw + j0', xw + j0' + SK) for its first key j0', and staged during this
+  // one. The ring spans the lowest row a stage reads to the highest it stages (at most
+  // 16 QT kWaves + 2 SK rows), so the rows staged during a stage never take a slot that stage
+  // reads, and a row is overwritten only after the barrier that ends its last use.
   const int C0 = R0 - (qt * QTILE + 16 * QT - 1);
+  const int xw = C0 + 16 * QT;   // band rows fetched with the stage at key j0: [xw + j0, + SK)
   // (the row and column offsets are summed in 32 bits first: one offset from the uniform base)
   auto band_src = [&](int x, uint32_t col_b) {
     return ptab + ((uint32_t)clampi(x, rlo, rhi) * prow_b + col_b);
   };
+  // Slot of a staged 16-byte chunk. Every row this thread stages is xw + (tid / NV) plus a multiple
+  // of 16, and the swizzle (slot bits 0 .. 2) depends on no higher bit: one column per thread.
+  const int st_col = BSW ? 8 * ((tid % NV) ^ ((xw + tid / NV) & 7)) : (tid % NV) * VEC;
   auto band_slot = [&](int x) { return s_band + (x & (RING - 1)) * BP; };
 
   Softmax st[QT];
@@ -350,17 +372,23 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     }
   }
   const int s_first = j_first >> 5;
-  const int nsteps = ((j_end + 31) >> 5) - s_first;
+  const int nsteps = ((j_end + 31) >> 5) - s_first;   // 32-key steps
   const int J = 32 * s_first;
-  const int xw = C0 + 16 * QT;   // band rows fetched with the step at key j0: [xw + j0, + 32)
-  // cooperative staging of one 32-key step: 32 K rows, the same 32 V rows and the 32 band rows
-  // entering the window. Rows past the utterance read its last frame instead: every staged value
-  // is finite, so a masked key (probability exactly 0) adds nothing, and every load is
-  // unconditional - a wait never has to drain loads requested for a later step.
-  constexpr int NLD = 32 * NV / kThreads;   // 16-byte vectors per thread per tensor
-  static_assert(NLD * kThreads == 32 * NV, "the staging threads cover the 32 rows exactly");
+  // cooperative staging of one stage: SK K rows, the same SK V rows and the SK band rows entering
+  // the window. Rows past the utterance read its last frame instead: every staged value is
+  // finite, so a masked key (probability exactly 0) adds nothing, and every load is
+  // unconditional - a wait never has to drain loads requested for a later stage.
+  constexpr int NLD = SK * NV / kThreads;   // 16-byte vectors per thread per tensor
+  static_assert(NLD * kThreads == SK * NV, "the staging threads cover the stage's rows exactly");
+  static_assert(kThreads % NV == 0 && (kThreads / NV) % 16 == 0,
+                "a thread's staged rows differ by multiples of 16");
   struct Rows { u32x4 k[NLD], v[NLD], b[NLD]; };
-  Rows ra, rb;   // two steps in flight
+  // Two-step stages hold one stage's rows in registers: a stage stashes the next stage's rows as
+  // it starts and reuses their registers for the stage after (ra; rb only in the prologue and the
+  // first stage). One-step stages keep two register sets in flight and stash as they end, so
+  // that a load has two steps to arrive either way.
+  constexpr bool ONE = SUBS == 2;
+  Rows ra, rb;
   auto fetch = [&](Rows& rr, int j0) {
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
@@ -375,13 +403,15 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     const u32x4* kr = rr.k;
     const u32x4* vr = rr.v;
     T* sk = stg;
-    T* sv = stg + 32 * KT;
+    T* sv = stg + SK * KT;
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
       const int r = idx / NV;
       const int dv = (idx % NV) * VEC;
-      *reinterpret_cast<u32x4*>(band_slot(xw + j0 + r) + dv) = rr.b[it];
+      *reinterpret_cast<u32x4*>(band_slot(xw + j0 + r) + st_col) = rr.b[it];
+      // (k_swz and v_swz read no bit of r above bit 4: row r of a stage and row r % 32 of its
+      // step share a permutation)
       if constexpr (kSwK<T>)
         *reinterpret_cast<u32x4*>(sk + r * kD + 8 * ((dv >> 3) ^ k_swz(r))) = kr[it];
       else
@@ -396,19 +426,22 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     }
   };
 
-  // band tile (16 rows from x, this lane's row x + m16) from the ring
+  // band tile (16 rows from x, this lane's row x + m16) from the ring. Every row a lane reads is
+  // xl plus a multiple of 16, so its two chunk columns are fixed.
   const int xl = C0 - 16 * QT * wave + m16;   // + j0 + 16 m: this lane's row of T_m
+  const int bsw = BSW ? xl & 7 : 0;
+  const int bcol_lo = 8 * (grp ^ bsw), bcol_hi = 8 * ((grp + 4) ^ bsw);
   auto band_tile = [&](int x, F& p_lo, F& p_hi) {
-    const T* row = band_slot(x) + 8 * grp;
-    p_lo = load8(row);
-    p_hi = load8(row + 32);
+    const T* row = band_slot(x);
+    p_lo = load8(row + bcol_lo);
+    p_hi = load8(row + bcol_hi);
   };
-  // requests in the order they are needed: step 0's rows and the window's first rows (staged
-  // directly, once), then step 1's rows, which the prologue's waits then leave in flight. Step 0's
-  // window is 16 QT kWaves + 32 rows: its top 32 come with step 0's fetch, the NPRE chunks of 32
-  // below them here.
-  constexpr int NPRE = QT * kWaves / 2;
-  static_assert(32 * NPRE == 16 * QT * kWaves, "the window below its top chunk is whole chunks");
+  // requests in the order they are needed: stage 0's rows and the window's first rows (staged
+  // directly, once), then stage 1's rows, which the prologue's waits then leave in flight. Stage
+  // 0's window is 16 QT kWaves + SK rows: its top SK come with stage 0's fetch, the NPRE chunks of
+  // SK below them here.
+  constexpr int NPRE = QT * kWaves * 16 / SK;
+  static_assert(SK * NPRE == 16 * QT * kWaves, "the window below its top chunk is whole chunks");
   fetch(ra, J);
   u32x4 pre[NPRE][NLD];
 #pragma unroll
@@ -416,19 +449,19 @@ varlen_attn_kernel(VarlenArgs<T> a) {
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
-      const int x = xw + J - 32 * (NPRE - part) + idx / NV;
+      const int x = xw + J - SK * (NPRE - part) + idx / NV;
       pre[part][it] = *reinterpret_cast<const u32x4*>(band_src(x, (idx % NV) * 16u));
     }
   __builtin_amdgcn_sched_barrier(0);
-  fetch(rb, J + 32);
+  fetch(rb, J + SK);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int part = 0; part < NPRE; ++part)
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
       const int idx = tid + kThreads * it;
-      const int x = xw + J - 32 * (NPRE - part) + idx / NV;
-      *reinterpret_cast<u32x4*>(band_slot(x) + (idx % NV) * VEC) = pre[part][it];
+      const int x = xw + J - SK * (NPRE - part) + idx / NV;
+      *reinterpret_cast<u32x4*>(band_slot(x) + st_col) = pre[part][it];
     }
   F qu[QT][2], qv[QT][2];
 #pragma unroll
@@ -456,103 +489,126 @@ varlen_attn_kernel(VarlenArgs<T> a) {
     }
     if constexpr (QT == 2) band_tile(xl + J + 16, c1[0], c1[1]);
   }
-  // one step (index `step` from the first visible one): registers `nxt` already hold step + 1,
-  // `fre` receives step + 2. kM: the step masks keys (every step with the chunked_limited mask,
-  // else only a last step that runs past the utterance). A wave's tiles past the utterance compute
-  // on clamped, finite rows and are never stored; a wave with none inside skips the arithmetic.
-  const bool active = ntile > 0;   // uniform over the wave
-  auto do_step = [&](int step, Rows& nxt, Rows& fre, auto masked) {
+  // One 32-key step at key j0 whose K and V rows start at `kv` (a stage buffer plus the step's
+  // offset in it). kM: the step masks keys (every step with the chunked_limited mask, else only a
+  // last step that runs past the utterance). A wave's tiles past the utterance compute on
+  // clamped, finite rows and are never stored.
+  auto step = [&](int j0, const T* kv, auto masked) {
     constexpr bool kM = decltype(masked)::value;
-    const int j0 = J + 32 * step;
-    const T* cur = s_kv + (step & 1) * TILE;
-    fetch(fre, j0 + 64);   // (past the last step: harmless re-reads of the last frame)
-    if (active) {
-      F kf[2][2], vf[4];
-      if constexpr (kSwK<T>) {
-        const int r = 8 * key_group<kPerm>(m16 >> 2) + (m16 & 3);   // tile tt reads row r + 4 tt
-        const int sw = k_swz(r);
+    F kf[2][2], vf[4];
+    if constexpr (kSwK<T>) {
+      const int r = 8 * key_group<kPerm>(m16 >> 2) + (m16 & 3);   // tile tt reads row r + 4 tt
+      const int sw = k_swz(r);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const T* row = cur + (r + 4 * tt) * kD;
-          kf[tt][0] = load8(row + 8 * (grp ^ sw));
-          kf[tt][1] = load8(row + 8 * ((grp + 4) ^ sw));
-        }
-      } else {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const T* row = cur + (8 * key_group<kPerm>(m16 >> 2) + 4 * tt + (m16 & 3)) * KP + 8 * grp;
-          kf[tt][0] = load8(row);
-          kf[tt][1] = load8(row + 32);
-        }
+      for (int tt = 0; tt < 2; ++tt) {
+        const T* row = kv + (r + 4 * tt) * kD;
+        kf[tt][0] = load8(row + 8 * (grp ^ sw));
+        kf[tt][1] = load8(row + 8 * ((grp + 4) ^ sw));
       }
-      if constexpr (kTrV<T>) {
-        // lane m16 of the group addresses row 8 kg + m16 / 4 (+ 4), dimensions 16 dt + 4 (m16 % 4)
-        const int r = 8 * key_group<kPerm>(grp) + (m16 >> 2);
-        const T* vlo = cur + 32 * KT + r * kD;
-        const int sw = v_swz(r);   // the same for row r + 4
+    } else {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int c = 4 * (((4 * dt) + (m16 & 3)) ^ sw);
-          vf[dt] = load8_tr(vlo + c, vlo + 4 * kD + c);
-        }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          vf[dt] = load8(cur + 32 * KT + (16 * dt + m16) * VP + 8 * key_group<kPerm>(grp));
-      }
-      // the new band tiles T_2 .. T_{QT+1} (with one tile per wave: T_1 and T_2)
-      F pb[QT + 1][2];
-      if constexpr (QT == 2) {
-        pb[0][0] = c1[0];
-        pb[0][1] = c1[1];
-      }
-#pragma unroll
-      for (int m = (QT == 2 ? 1 : 0); m < QT + 1; ++m)
-        band_tile(xl + j0 + 16 * (m + 1), pb[m][0], pb[m][1]);
-      int lo_k[QT], hi_k[QT];
-#pragma unroll
-      for (int k = 0; k < QT; ++k) {
-        lo_k[k] = kLimited ? k_lo_q[k] - j0 : 0;
-        hi_k[k] = kLimited ? k_hi_q[k] - j0 : L - j0;
-      }
-      step_tiles<T, QT, kM>(st, rr, kf, vf, qu, qv, pb, g_prev, s_g, lo_k, hi_k);
-      if constexpr (QT == 2) {
-        c1[0] = pb[QT][0];
-        c1[1] = pb[QT][1];
+      for (int tt = 0; tt < 2; ++tt) {
+        const T* row = kv + (8 * key_group<kPerm>(m16 >> 2) + 4 * tt + (m16 & 3)) * KP + 8 * grp;
+        kf[tt][0] = load8(row);
+        kf[tt][1] = load8(row + 32);
       }
     }
-    // (unconditional, also after the last step: the rows are clamped re-reads going to a buffer
+    if constexpr (kTrV<T>) {
+      // lane m16 of the group addresses row 8 kg + m16 / 4 (+ 4), dimensions 16 dt + 4 (m16 % 4)
+      const int r = 8 * key_group<kPerm>(grp) + (m16 >> 2);
+      const T* vlo = kv + SK * KT + r * kD;
+      const int sw = v_swz(r);   // the same for row r + 4
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int c = 4 * (((4 * dt) + (m16 & 3)) ^ sw);
+        vf[dt] = load8_tr(vlo + c, vlo + 4 * kD + c);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        vf[dt] = load8(kv + SK * KT + (16 * dt + m16) * VP + 8 * key_group<kPerm>(grp));
+    }
+    // the new band tiles T_2 .. T_{QT+1} (with one tile per wave: T_1 and T_2)
+    F pb[QT + 1][2];
+    if constexpr (QT == 2) {
+      pb[0][0] = c1[0];
+      pb[0][1] = c1[1];
+    }
+#pragma unroll
+    for (int m = (QT == 2 ? 1 : 0); m < QT + 1; ++m)
+      band_tile(xl + j0 + 16 * (m + 1), pb[m][0], pb[m][1]);
+    int lo_k[QT], hi_k[QT];
+#pragma unroll
+    for (int k = 0; k < QT; ++k) {
+      lo_k[k] = kLimited ? k_lo_q[k] - j0 : 0;
+      hi_k[k] = kLimited ? k_hi_q[k] - j0 : L - j0;
+    }
+    step_tiles<T, QT, kM>(st, rr, kf, vf, qu, qv, pb, g_prev, s_g, lo_k, hi_k);
+    if constexpr (QT == 2) {
+      c1[0] = pb[QT][0];
+      c1[1] = pb[QT][1];
+    }
+  };
+  // one stage (index `stage` from the first visible key): registers `nxt` already hold stage + 1,
+  // `fre` receives stage + 2; a wave with no query inside the utterance skips the arithmetic
+  // (uniform over the wave). A masked stage runs only its steps before the last visible key.
+  // (With one register set, the barrier that ended the previous stage also ended every read of
+  // the buffer and ring slots the stash at the start fills.)
+  const bool active = ntile > 0;
+  auto do_stage = [&](int stage, Rows& nxt, Rows& fre, auto masked) {
+    constexpr bool kM = decltype(masked)::value;
+    const int j0 = J + SK * stage;
+    const T* cur = s_kv + (stage & 1) * TILE;
+    if constexpr (ONE) stash(nxt, s_kv + ((stage + 1) & 1) * TILE, j0 + SK);
+    fetch(fre, j0 + 2 * SK);   // (past the last stage: harmless re-reads of the last frame)
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < SUBS; ++u) {
+        if (!kM || u == 0 || SUBS * stage + u < nsteps) step(j0 + 32 * u, cur + 32 * u * kD, masked);
+      }
+    }
+    // (unconditional, also after the last stage: the rows are clamped re-reads going to a buffer
     // and ring slots no later read uses, and every path back to the loop head then has the same
     // loads in flight - a path with one more pending load made the compiler drain them all at
-    // the head, which cut the look-ahead to one step)
-    stash(nxt, s_kv + ((step + 1) & 1) * TILE, j0 + 32);
+    // the head, which cut the look-ahead to one stage)
+    if constexpr (!ONE) stash(nxt, s_kv + ((stage + 1) & 1) * TILE, j0 + SK);
     __syncthreads();
   };
-  // steps in pairs (the two register sets swap roles), an odd last step after the loop: the
+  // stages in pairs (the two register sets swap roles), an odd last stage after the loop: the
   // loop has one exit, so no path reaches its head with the other set's loads still pending.
-  // Without the mask the steps that lie wholly inside the utterance run unmasked, and a last
-  // partial step, masked, after them.
+  // Without the mask the stages that lie wholly inside the utterance run unmasked, and a last
+  // partial stage, masked, after them.
   const std::integral_constant<bool, true> mask_on;
   const std::integral_constant<bool, false> mask_off;
-  const int nplain = kLimited ? 0 : (j_end - J) >> 5;   // whole steps that need no mask
-  int step = 0;
-  for (; step + 1 < nplain; step += 2) {
-    do_step(step, rb, ra, mask_off);
-    do_step(step + 1, ra, rb, mask_off);
+  // stages whose steps need no mask (whole 32-key steps inside the utterance, SUBS to a stage)
+  const int nplain = kLimited ? 0 : ((j_end - J) >> 5) / SUBS;
+  const int nstages = (nsteps + SUBS - 1) / SUBS;
+  int stage = 0;
+  if constexpr (ONE) {
+    // the first stage stashes the prologue's second set; every later one reuses ra
+    if (nplain > 0) do_stage(0, rb, ra, mask_off);
+    else do_stage(0, rb, ra, mask_on);
+    for (stage = 1; stage < nplain; ++stage) do_stage(stage, ra, ra, mask_off);
+    if (stage < nstages) do_stage(stage, ra, ra, mask_on);
+  } else {
+  for (; stage + 1 < nplain; stage += 2) {
+    do_stage(stage, rb, ra, mask_off);
+    do_stage(stage + 1, ra, rb, mask_off);
   }
-  if (step < nplain) {
-    do_step(step, rb, ra, mask_off);
-    ++step;
+  if (stage < nplain) {
+    do_stage(stage, rb, ra, mask_off);
+    ++stage;
   }
   if constexpr (kLimited) {
-    for (; step + 1 < nsteps; step += 2) {
-      do_step(step, rb, ra, mask_on);
-      do_step(step + 1, ra, rb, mask_on);
+    for (; stage + 1 < nstages; stage += 2) {
+      do_stage(stage, rb, ra, mask_on);
+      do_stage(stage + 1, ra, rb, mask_on);
     }
   }
-  if (step < nsteps) {
-    if (step & 1) do_step(step, ra, rb, mask_on);
-    else do_step(step, rb, ra, mask_on);
+  if (stage < nstages) {
+    if (stage & 1) do_stage(stage, ra, rb, mask_on);
+    else do_stage(stage, rb, ra, mask_on);
+  }
   }
 
   // finish: every tile of every wave owns its 16 queries

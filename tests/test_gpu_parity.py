@@ -222,9 +222,11 @@ def gpu_varlen(co):
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
 def test_varlen_parity_small(dtype):
-    # 1 to 5 key steps: even and odd step counts (an odd last step runs after the paired loop)
-    co = make_varlen_cohort([1, 5, 0, 16, 17, 40, 70, 100, 150], 2, 64, dtype=dtype, seed=2,
-                            device=DEV)
+    # 1 to 9 key steps of 32: even and odd step counts (bf16 stages two steps, fp32 pairs its
+    # one-step stages), every way a length ends - whole stages only, a last stage of one or two
+    # steps, its last step whole or cut - and one to three query tiles
+    co = make_varlen_cohort([1, 5, 0, 16, 17, 32, 40, 64, 70, 96, 100, 128, 150, 257], 2, 64,
+                            dtype=dtype, seed=2, device=DEV)
     ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
                                     co.cu_seqlens.cpu().numpy(), host64(co.pos),
                                     host64(co.pos_bias_u), host64(co.pos_bias_v))
