@@ -574,8 +574,9 @@ def replay_ms(graphs, steps, warmup):
 
 
 # launch shapes of the memory-path ceiling kernel: (waves per workgroup, workgroups per stream
-# and head); the attention kernel's own grid is (4, 1)
-CEILING_SHAPES = ((4, 1), (8, 1), (4, 2))
+# and head); the attention kernel's own grids are (4, 1) and, for cohorts whose grid fills every
+# wave slot with one wave per unit, (1, 1)
+CEILING_SHAPES = ((4, 1), (8, 1), (4, 2), (1, 1))
 
 
 def chains_of(sets):

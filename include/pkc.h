@@ -199,9 +199,14 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  * Errors: as paged_kv_append; n_head % n_kv_head != 0 or a table too short -> PKC_ERR_SHAPE;
  * head_dim != 64, block_size not a power of two >= 8, a chunk too long for the kernel's LDS
  * staging, pos_len >= 2^25, or the launch limits (batch n_head ceil(chunk_size / 16) workgroups
- * of 256 threads: one per 16 queries of a stream and head) -> PKC_ERR_UNSUPPORTED. The kernel stages the chunk's chunk_size frames in LDS (the
- * cached frames stream from the pages), which allows chunk_size <= 512 in bf16 and <= 256 in
- * fp32.
+ * of 256 threads: one per 16 queries of a stream and head) -> PKC_ERR_UNSUPPORTED. The kernel
+ * stages the chunk's chunk_size frames in LDS (the cached frames stream from the pages), which
+ * allows chunk_size <= 512 in bf16 and <= 256 in fp32.
+ * Launch shape: each workgroup runs its keys as four fixed partitions merged in a fixed order, on
+ * 4 wavefronts, or on 1 (64 threads) when the grid fills every wave slot of the GPU with one
+ * wavefront per workgroup (bf16 fused entries, chunk_size <= 32, block_size 16 or 32, no
+ * chunk_lens or window_start); the results are bitwise the same either way. The environment
+ * variable PKC_CHUNK_WAVES = 1, 2 or 4, read at each launch, forces the count for those calls.
  */
 pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_tables,
@@ -385,7 +390,7 @@ pkc_status rel_pos_projection(pkc_dtype dtype, const void* w_pos, const int32_t*
  * of every 32-key step) with the attention kernel's own per-lane addresses, writes the chunk's
  * K/V into the pools exactly as paged_kv_append does, and writes unspecified values (an XOR of
  * what it read) into out. It does no arithmetic, so its launch time is what the access pattern
- * costs at a launch shape: waves (4 or 8) wavefronts per workgroup and split (1, 2 or 4)
+ * costs at a launch shape: waves (1, 4 or 8) wavefronts per workgroup and split (1, 2 or 4)
  * workgroups per (stream, head); split > 1 omits the merge a split attention would need.
  * reads = 0 runs the same grid but only writes out (reads nothing, appends nothing): the floor
  * that launching and retiring the grid costs.

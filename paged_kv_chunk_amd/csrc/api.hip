@@ -257,7 +257,7 @@ pkc_status pkc_gather_read(pkc_dtype dtype, const void* q, const void* k_new, co
                               n_kv_head, head_dim, block_size, num_blocks, max_blocks_per_seq,
                               max_cache_seqlen, 0.f, stream, false);
   if (st != PKC_OK) return st;
-  if ((waves != 4 && waves != 8) || (split != 1 && split != 2 && split != 4) ||
+  if ((waves != 1 && waves != 4 && waves != 8) || (split != 1 && split != 2 && split != 4) ||
       (reads != 0 && reads != 1))
     return PKC_ERR_SHAPE;
   if (dtype != PKC_BF16 || chunk_size > 16 || (pos_layout & PKC_POS_PER_KEY))

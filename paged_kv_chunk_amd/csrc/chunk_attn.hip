@@ -45,6 +45,7 @@
 // Table geometry: the row for (query i, key j) is R0 + j - i with R0 = centre - cache; only rows
 // [R0 - (C - 1), R0 + T - 1] are read.
 #include <math.h>
+#include <stdlib.h>
 
 #include "pkc_device.h"
 #include "pkc_launch.h"
@@ -86,6 +87,7 @@ struct ChunkArgs {
   // kilobyte, whole 128-byte lines, where row-major rows give each load half-lines.
   int band_rs, band_hs, band_hd;
   int off_bt, off_kt, off_vt;        // byte offsets of the LDS regions
+  int phys;                          // physical waves per workgroup (host-side choice)
   float scale_log2;
 };
 
@@ -99,13 +101,25 @@ struct StepRegs {
 
 template <typename T> constexpr int kt_pitch() { return kD + 16 / (int)sizeof(T); }
 
+// The keys of a (stream, head, query tile) unit are split over kWaves = 4 virtual waves, each
+// with its own online softmax, merged in a fixed order: a stream's result bits depend on its own
+// length only. kPhys physical waves run them, kWaves / kPhys each, one after another over a
+// contiguous range of body steps (the loads run ahead across the virtual waves' boundaries):
+// fewer physical waves per unit put more units on a CU at once, with identical results.
 // kGen: per-stream chunk lengths or window starts may be given. Without them (the common case)
 // both are compile-time constants, which keeps the prologue's instruction count down.
-template <typename T, bool kFused, int kWaves, int kS, bool kRegTail, bool kPerKey, bool kGen>
-__global__ void __launch_bounds__(kWaves * 64)
+template <typename T, bool kFused, int kPhys, int kS, bool kRegTail, bool kPerKey, bool kGen>
+__global__ void __launch_bounds__(kPhys * 64)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
 chunk_attn_kernel(ChunkArgs<T> a) {
   typedef typename Frag<T>::type F;
-  constexpr int kThreads = kWaves * 64;
+  constexpr int kWaves = 4;                 // virtual waves of the arithmetic
+  constexpr int kR = kWaves / kPhys;        // virtual waves per physical wave
+  static_assert(kR * kPhys == kWaves, "physical waves divide the virtual ones");
+  // (several virtual waves per physical wave only for chunks held in registers, at most 32
+  // frames: the tail is then one step, the first virtual wave's)
+  static_assert(kR == 1 || kRegTail, "virtual waves after the first have no tail step");
+  constexpr int kThreads = kPhys * 64;
   constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte vector
   constexpr int NV = kD / VEC;          // vectors per row
   constexpr int KTP = kt_pitch<T>();
@@ -169,12 +183,17 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       ww[half] = load8(a.w + h * kD + d0);
     }
   }
-  // the chunk's own frames (fused, short chunks: one 16-byte vector of K and of V per thread)
-  u32x4 nk, nv;
+  // the chunk's own frames (fused, short chunks: kR 16-byte vectors of K and of V per thread,
+  // 32 frames in all)
+  u32x4 nk[kR], nv[kR];
   if constexpr (kRegTail) {
-    const size_t row = ((size_t)(b * a.C + min(tid / NV, a.C - 1)) * a.Hk + hk) * kD + (tid % NV) * VEC;
-    nk = *reinterpret_cast<const u32x4*>(a.k_new + row);
-    nv = *reinterpret_cast<const u32x4*>(a.v_new + row);
+#pragma unroll
+    for (int it = 0; it < kR; ++it) {
+      const int idx = tid + kThreads * it;
+      const size_t row = ((size_t)(b * a.C + min(idx / NV, a.C - 1)) * a.Hk + hk) * kD + (idx % NV) * VEC;
+      nk[it] = *reinterpret_cast<const u32x4*>(a.k_new + row);
+      nv[it] = *reinterpret_cast<const u32x4*>(a.v_new + row);
+    }
   }
   const int cache = clampi(cs_raw, 0, a.max_cache);
   // real frames of this stream's chunk: frames past them do not exist (not appended, not keys;
@@ -197,8 +216,10 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const uint32_t blk_stride = (uint32_t)(a.Hk * S * kD);
   const T* kp = a.k_pool + (size_t)hk * page;
   const T* vp = a.v_pool + (size_t)hk * page;
-  const int s_begin = (wave * nbody) / kWaves;
-  const int s_end = ((wave + 1) * nbody) / kWaves;
+  const int v0 = wave * kR;                                 // this wave's first virtual wave
+  auto vbound = [&](int v) { return (v * nbody) / kWaves; };   // first body step of virtual wave v
+  const int s_begin = vbound(v0);
+  const int s_end = vbound(v0 + kR);
   const int nmine = s_end - s_begin;
 
   // a per-row table is built for the full chunk width: centred at cache + C - 1
@@ -268,8 +289,8 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   // else; the tail step then runs while the body's data is still on its way. Only the waves
   // that have a tail step request them (the branch is uniform over each wave).
   F tb[3][2];
-  if (wave < ntail) {
-    const int k0 = wave;
+  if (v0 < ntail) {
+    const int k0 = v0;
     if constexpr (kPerKey) {
       load_key_rows(*reinterpret_cast<F(*)[2][2]>(&tb[0]), cache + 32 * k0);
     } else {
@@ -301,14 +322,18 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   // after the body steps' loads are requested: waiting for the frames then leaves those loads in
   // flight, and the staging's LDS writes are not on their way
   if constexpr (kRegTail) {
-    if (tid < n_real * NV) {
-      const int t = tid / NV;
-      const int dv = (tid % NV) * VEC;
-      *reinterpret_cast<u32x4*>(s_kt + t * KTP + dv) = nk;
-      const uint32_t wd[4] = {nv[0], nv[1], nv[2], nv[3]};
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        reinterpret_cast<uint16_t*>(s_vt)[(dv + c) * a.vt_pitch + t] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
+    for (int it = 0; it < kR; ++it) {
+      const int idx = tid + kThreads * it;
+      if (idx < n_real * NV) {
+        const int t = idx / NV;
+        const int dv = (idx % NV) * VEC;
+        *reinterpret_cast<u32x4*>(s_kt + t * KTP + dv) = nk[it];
+        const uint32_t wd[4] = {nv[it][0], nv[it][1], nv[it][2], nv[it][3]};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          reinterpret_cast<uint16_t*>(s_vt)[(dv + c) * a.vt_pitch + t] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
+      }
     }
     for (int x = tid; x < (32 * ntail - n_real) * kD; x += kThreads)
       s_vt[(x % kD) * a.vt_pitch + n_real + x / kD] = from_f<T>(0.f);
@@ -367,79 +392,189 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       set(qv[half], e, (get(qq[half], e) + get(ww[half], e)) * a.scale_log2);
     }
 
-  float* s_g = s_wave + wave * kWaveLds;
+  // Merge slot of virtual wave vv: its o^T tile (kD rows of the 16 query columns, pitch SP), then
+  // m and l. With several physical waves each virtual wave has a slot at s_wave and its shift
+  // tile aliases it. With one, the LDS is cut so that eight workgroups fit a CU: one shift tile at
+  // s_wave for every virtual wave, the third wave's slot after it, the first two slots in the
+  // chunk's staging area (free once the append below has read it), and the last wave's state
+  // merged from its registers.
+  constexpr bool kOne = kPhys == 1;
+  constexpr int SP = kOne ? 16 : kOPitch;
+  constexpr int SF = kD * SP + 32;
+  auto slot = [&](int vv) -> float* {
+    if constexpr (kOne) {
+      return vv < 2 ? reinterpret_cast<float*>(smem + a.off_kt) + vv * SF : s_wave + kSkewFloats;
+    }
+    return s_wave + vv * kWaveLds;
+  };
+  auto shift_tile = [&](int vv) -> float* { return kOne ? s_wave : s_wave + vv * kWaveLds; };
+  // the virtual wave being run (uniform over the wave), its shift tile and its online-softmax
+  // state
+  int v = v0;
+  float* s_g = shift_tile(v0);
   Softmax st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   // Transformer-XL steps keep the running maximum in the folded form (step_fold): the band
   // products start their accumulation at rr.nr, so the scores need no subtraction
   RunRef rr;
-  runref_init(rr);
+  auto reset = [&]() {
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    runref_init(rr);
+  };
+  reset();
 
-  // ---- 4. tail steps over the chunk's frames, from LDS, first (the one workgroup barrier: the
-  // tail was staged by all threads; the body below uses only the wave's own registers and LDS).
-  // The wave with a tail step runs it while its body data is still arriving. ----------------
-  __syncthreads();
-  for (int k = wave; k < ntail; k += kWaves) {
-    const int j0 = cache + 32 * k;
-    F kf[2][2], vf[4];
+  // tail steps of virtual wave vv over the chunk's frames, from LDS (its first one, when it is
+  // this wave's first virtual wave, with the table rows requested at the start)
+  auto tail_steps = [&](int vv) {
+    for (int k = vv; k < ntail; k += kWaves) {
+      const int j0 = cache + 32 * k;
+      F kf[2][2], vf[4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const T* row = s_kt + (32 * k + 8 * (m16 >> 2) + 4 * tt + (m16 & 3)) * KTP + 8 * grp;
-      kf[tt][0] = load8(row);
-      kf[tt][1] = load8(row + 32);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(s_vt + (16 * dt + m16) * a.vt_pitch + 32 * k + 8 * grp);
-    if constexpr (kPerKey) {
-      F pk[2][2];
-      if (k == wave) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int half = 0; half < 2; ++half) pk[tt][half] = tb[tt][half];   // prefetched
-      } else {
-        load_key_rows(pk, j0);
+      for (int tt = 0; tt < 2; ++tt) {
+        const T* row = s_kt + (32 * k + 8 * (m16 >> 2) + 4 * tt + (m16 & 3)) * KTP + 8 * grp;
+        kf[tt][0] = load8(row);
+        kf[tt][1] = load8(row + 32);
       }
-      float x[2][4];
-      per_key_scores<T>(kf, pk, qu, qv, x);
-      softmax_pv<T, true>(st, x, vf, 0, T_len - j0);
-    } else {
-      F pb[3][2];
-      if (k == wave) {
 #pragma unroll
-        for (int t = 0; t < 3; ++t)
+      for (int dt = 0; dt < 4; ++dt) vf[dt] = load8(s_vt + (16 * dt + m16) * a.vt_pitch + 32 * k + 8 * grp);
+      if constexpr (kPerKey) {
+        F pk[2][2];
+        if (k == v0) {
 #pragma unroll
-          for (int half = 0; half < 2; ++half) pb[t][half] = tb[t][half];   // prefetched
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) pk[tt][half] = tb[tt][half];   // prefetched
+        } else {
+          load_key_rows(pk, j0);
+        }
+        float x[2][4];
+        per_key_scores<T>(kf, pk, qu, qv, x);
+        softmax_pv<T, true>(st, x, vf, 0, T_len - j0);
       } else {
-        const int rb = R0 + j0 - qlast;
+        F pb[3][2];
+        if (k == v0) {
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) pb[t][half] = tb[t][half];   // prefetched
+        } else {
+          const int rb = R0 + j0 - qlast;
+#pragma unroll
+          for (int t = 0; t < 3; ++t) {
+            const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
+            pb[t][0] = load8(row);
+            pb[t][1] = load8(row + phalf);
+          }
+        }
+        floatx4 g[3];
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
-          const T* row = band_row(rb + 16 * t + m16) + 8 * grp;
-          pb[t][0] = load8(row);
-          pb[t][1] = load8(row + phalf);
+          g[t] = mma(pb[t][0], qv[0], rr.nr);
+          g[t] = mma(pb[t][1], qv[1], g[t]);
+        }
+        step_fold<T, true>(st, rr, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
+      }
+    }
+  };
+  // the state of virtual wave vv into its merge slot (with one physical wave, the last one's
+  // stays in registers)
+  auto flush = [&](int vv) {
+    st.l = column_sum(st.l);
+    if constexpr (!kPerKey) st.m = rr.m;   // (the folded steps keep the running maximum in rr)
+    if (kOne && vv == kWaves - 1) return;
+    float* s_o = slot(vv);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_o[(16 * dt + 4 * grp + e) * SP + m16] = st.o[dt][e];
+    if (grp == 0) {
+      s_o[kD * SP + m16] = st.m;
+      s_o[kD * SP + 16 + m16] = st.l;
+    }
+  };
+
+  // ---- 6. fused append: this tile's chunk frames from LDS into the pool ---------------------
+  // (issued after the wave's last load, so no load wait queues behind these stores, and they
+  // drain while the waves merge; with one physical wave, right after the tail step instead, so
+  // that the staging area is free for the merge slots)
+  auto append = [&]() {
+    if (kFused && h == hk * (a.H / a.Hk)) {
+      const int t_lo = qt * 16;
+      const int t_hi = min(n_real, t_lo + 16);
+      for (int x = tid; x < (t_hi - t_lo) * NV; x += kThreads) {
+        const int t = t_lo + x / NV;
+        const int dv = (x % NV) * VEC;
+        const int key = cache + t;
+        T* dst = a.k_pool_w + (size_t)hk * page + (uint64_t)block_of(key >> logS) * blk_stride +
+                 (uint32_t)(((dv >> 5) * S + (key & (S - 1))) * 32 + (dv & 31));
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s_kt + t * KTP + dv);
+      }
+      // V: 8-frame groups of one dimension, aligned to the page slots (never across a page: block
+      // sizes are powers of two >= 8); one 16-byte store when all 8 frames belong to this tile
+      const int f_lo = cache + t_lo, f_hi = cache + t_hi;
+      const int g0 = (f_lo >> 3) << 3;
+      const int ngroups = (f_hi - g0 + 7) >> 3;
+      for (int x = tid; x < ngroups * kD; x += kThreads) {
+        const int d = x & (kD - 1);
+        const int kg = g0 + 8 * (x >> 6);
+        T* dst = a.v_pool_w + (size_t)hk * page + (uint64_t)block_of(kg >> logS) * blk_stride +
+                 (uint32_t)(d * S + (kg & (S - 1)));
+        const T* row = s_vt + d * a.vt_pitch;
+        if (kg >= f_lo && kg + 8 <= f_hi) {
+          F v8;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) set(v8, c, to_f(row[kg + c - cache]));
+          store8(dst, v8);
+        } else {
+          for (int c = 0; c < 8; ++c)
+            if (kg + c >= f_lo && kg + c < f_hi) dst[c] = row[kg + c - cache];
         }
       }
-      floatx4 g[3];
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        g[t] = mma(pb[t][0], qv[0], rr.nr);
-        g[t] = mma(pb[t][1], qv[1], g[t]);
-      }
-      step_fold<T, true>(st, rr, kf, vf, qu, g[0], g[1], g[2], s_g, T_len - j0);
     }
-  }
+  };
+
+  // ---- 4. tail steps of the first virtual wave over the chunk's frames, from LDS, first (the
+  // one workgroup barrier: the tail was staged by all threads; the body below uses only the
+  // wave's own registers and LDS). The wave with a tail step runs it while its body data is
+  // still arriving. -----------------------------------------------------------------------------
+  __syncthreads();
+  tail_steps(v0);
+  if constexpr (kOne) append();
 
   // ---- 5. body steps, two register sets in turn ------------------------------------------------
+  // With several virtual waves per physical wave, the step that opens a later virtual wave first
+  // moves the finished one's state to its merge slot and starts the next, whose first band
+  // product is computed from the band tile the step before loaded: the same rows and the same
+  // products as a wave of its own would form.
+  int vend = vbound(v0 + 1);
   if (nmine > 0) {
-    floatx4 g_prev;
+    floatx4 g_prev = {0.f, 0.f, 0.f, 0.f};
+    F p_next[2];   // the band tile that opens the next virtual wave (its first step's tile 0)
     if (!kPerKey) {
       g_prev = mma(p0[0], qv[0], rr.nr);
       g_prev = mma(p0[1], qv[1], g_prev);
     }
     auto run = [&](StepRegs<T>& r, int s) {
+      if constexpr (kR > 1) {
+        if (s >= vend) {
+          do {
+            flush(v);
+            ++v;
+            vend = vbound(v + 1);
+            s_g = shift_tile(v);
+            reset();
+          } while (s >= vend);
+          if constexpr (!kPerKey) {
+            // (when the virtual waves before it had no body step, the band tile requested with the
+            // first steps is this step's first)
+            const bool first = s == s_begin;
+            g_prev = mma(first ? p0[0] : p_next[0], qv[0], rr.nr);
+            g_prev = mma(first ? p0[1] : p_next[1], qv[1], g_prev);
+          }
+        }
+      }
       // the last cached page may be partly filled: frames at or past cache are then excluded,
       // and their V is zeroed (the slots may hold anything)
       const bool part = s == s_part;
@@ -454,6 +589,13 @@ chunk_attn_kernel(ChunkArgs<T> a) {
         g1 = mma(r.p[0][1], qv[1], g1);
         floatx4 g2 = mma(r.p[1][0], qv[0], rr.nr);
         g2 = mma(r.p[1][1], qv[1], g2);
+        if constexpr (kR > 1) {
+          // the next step opens another virtual wave: keep its first band tile
+          if (s + 1 == vend && s + 1 < s_end) {
+            p_next[0] = r.p[1][0];
+            p_next[1] = r.p[1][1];
+          }
+        }
         if (part) step_fold<T, true>(st, rr, r.k, r.v, qu, g_prev, g1, g2, s_g, cache - 32 * s);
         else step_fold<T, false>(st, rr, r.k, r.v, qu, g_prev, g1, g2, s_g, 32);
         g_prev = g2;
@@ -472,54 +614,54 @@ chunk_attn_kernel(ChunkArgs<T> a) {
       }
     }
   }
-
-  // ---- 6. fused append: this tile's chunk frames from LDS into the pool ---------------------
-  // (issued after the wave's last load, so no load wait queues behind these stores, and they
-  // drain while the waves merge)
-  if (kFused && h == hk * (a.H / a.Hk)) {
-    const int t_lo = qt * 16;
-    const int t_hi = min(n_real, t_lo + 16);
-    for (int x = tid; x < (t_hi - t_lo) * NV; x += kThreads) {
-      const int t = t_lo + x / NV;
-      const int dv = (x % NV) * VEC;
-      const int key = cache + t;
-      T* dst = a.k_pool_w + (size_t)hk * page + (uint64_t)block_of(key >> logS) * blk_stride +
-               (uint32_t)(((dv >> 5) * S + (key & (S - 1))) * 32 + (dv & 31));
-      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s_kt + t * KTP + dv);
-    }
-    // V: 8-frame groups of one dimension, aligned to the page slots (never across a page: block
-    // sizes are powers of two >= 8); one 16-byte store when all 8 frames belong to this tile
-    const int f_lo = cache + t_lo, f_hi = cache + t_hi;
-    const int g0 = (f_lo >> 3) << 3;
-    const int ngroups = (f_hi - g0 + 7) >> 3;
-    for (int x = tid; x < ngroups * kD; x += kThreads) {
-      const int d = x & (kD - 1);
-      const int kg = g0 + 8 * (x >> 6);
-      T* dst = a.v_pool_w + (size_t)hk * page + (uint64_t)block_of(kg >> logS) * blk_stride +
-               (uint32_t)(d * S + (kg & (S - 1)));
-      const T* row = s_vt + d * a.vt_pitch;
-      if (kg >= f_lo && kg + 8 <= f_hi) {
-        F v8;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) set(v8, c, to_f(row[kg + c - cache]));
-        store8(dst, v8);
-      } else {
-        for (int c = 0; c < 8; ++c)
-          if (kg + c >= f_lo && kg + c < f_hi) dst[c] = row[kg + c - cache];
-      }
-    }
+  // the virtual waves left: the current one, then any after it with no body step (and no tail
+  // step: see above)
+  flush(v);
+  for (int vv = v + 1; vv < v0 + kR; ++vv) {
+    reset();
+    flush(vv);
   }
-  // ---- 7. merge the waves' partial states in a fixed order -------------------------------------
-  st.l = column_sum(st.l);
-  if constexpr (!kPerKey) st.m = rr.m;   // (the folded steps keep the running maximum in rr)
-  float* s_o = s_wave + wave * kWaveLds;
+  if constexpr (!kOne) append();
+
+  // ---- 7. merge the virtual waves' partial states in a fixed order ------------------------------
+  if constexpr (kOne) {
+    // one wave: each lane combines its own query column's dimensions 16 dt + 4 grp + e, the last
+    // virtual wave's from its registers - the same operations, in the same order, as below
+    const int i = qt * 16 + m16;
+    float mw[kWaves], lw[kWaves];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = w < kWaves - 1 ? slot(w)[kD * SP + m16] : st.m;
+      lw[w] = w < kWaves - 1 ? slot(w)[kD * SP + 16 + m16] : st.l;
+    }
+    float mmax = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[(16 * dt + 4 * grp + e) * kOPitch + m16] = st.o[dt][e];
-  if (grp == 0) {
-    s_o[kD * kOPitch + m16] = st.m;
-    s_o[kD * kOPitch + 16 + m16] = st.l;
+    for (int w = 0; w < kWaves; ++w) mmax = fmaxf(mmax, mw[w]);
+    float lsum = 0.f;
+    float acc[4][4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[dt][e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(mw[w] - mmax);
+      lsum += f * lw[w];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[dt][e] += f * (w < kWaves - 1 ? slot(w)[(16 * dt + 4 * grp + e) * SP + m16] : st.o[dt][e]);
+    }
+    const float inv = 1.f / lsum;
+    if (i < a.C) {
+      T* dst = a.out + (((size_t)b * a.C + i) * a.H + h) * kD + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[16 * dt + e] = from_f<T>(acc[dt][e] * inv);
+    }
+    return;
   }
   __syncthreads();
   for (int x = tid; x < 16 * (kD / 4); x += kThreads) {
@@ -553,38 +695,72 @@ chunk_attn_kernel(ChunkArgs<T> a) {
 
 }
 
-// Wavefronts per workgroup. Fixed (never chosen from the cohort size), so a stream's step-to-wave
-// assignment and merge order, and with them its result bits, depend on its own length only.
+// Virtual waves per unit: fixed (never chosen from the cohort size), so a stream's step-to-wave
+// assignment and merge order, and with them its result bits, depend on its own length only. The
+// physical waves per workgroup (launch_chunk_t) change the speed, not the bits.
 template <typename T> constexpr int waves_of() { return 4; }
 
-template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false, bool kGen = true>
-void launch_inst(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
+// LDS layout for kPhys physical waves: merge slots and shift tiles (with one physical wave one
+// shift tile and one slot, the first two slots then reusing the chunk's staging area), block-ID
+// windows, the chunk's K rows and V^T. Returns the bytes.
+template <typename T>
+size_t chunk_lds_layout(ChunkArgs<T>& a, int phys) {
+  size_t off = phys == 1 ? (size_t)(kSkewFloats + kD * 16 + 32) * sizeof(float)
+                         : (size_t)waves_of<T>() * kWaveLds * sizeof(float);
+  a.off_bt = (int)off;
+  off += (size_t)phys * kBtWindow * sizeof(int);
+  a.off_kt = (int)off;
+  off += (size_t)a.tail_cap * kt_pitch<T>() * sizeof(T);
+  a.off_vt = (int)off;
+  off += (size_t)kD * a.vt_pitch * sizeof(T);
+  return off;
+}
+
+template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false, bool kGen = true,
+          int kPhys = 4>
+void launch_inst(const ChunkArgs<T>& a_in, dim3 grid, size_t, hipStream_t stream) {
+  // (the layout follows the variant launched, whatever count the host asked for)
+  ChunkArgs<T> a = a_in;
+  a.phys = kPhys;
+  const size_t smem = chunk_lds_layout(a, kPhys);
   if (smem > 64 * 1024) {
     // beyond the default dynamic LDS size (long chunks): opt in on every such call, so that no
     // state is kept between calls (a host-side attribute, no GPU work); MI355X allows 160 KB per
     // workgroup
     (void)hipFuncSetAttribute(
         reinterpret_cast<const void*>(
-            &chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey, kGen>),
+            &chunk_attn_kernel<T, kFused, kPhys, kS, kRegTail, kPerKey, kGen>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   }
-  hipLaunchKernelGGL((chunk_attn_kernel<T, kFused, waves_of<T>(), kS, kRegTail, kPerKey, kGen>),
-                     grid, dim3(waves_of<T>() * 64), smem, stream, a);
+  hipLaunchKernelGGL((chunk_attn_kernel<T, kFused, kPhys, kS, kRegTail, kPerKey, kGen>),
+                     grid, dim3(kPhys * 64), smem, stream, a);
+}
+
+// the lean variant (no chunk lengths or window starts) at a.phys physical waves per workgroup
+// (register-held chunks only: see the kernel)
+template <typename T, bool kFused, int kS, bool kRegTail>
+void launch_phys(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
+  if constexpr (kRegTail) {
+    if (a.phys == 1) return launch_inst<T, kFused, kS, true, false, false, 1>(a, grid, smem, stream);
+    if (a.phys == 2) return launch_inst<T, kFused, kS, true, false, false, 2>(a, grid, smem, stream);
+  }
+  launch_inst<T, kFused, kS, kRegTail, false, false, 4>(a, grid, smem, stream);
 }
 
 // Instantiation for a call: the block sizes of the streaming workloads get constant page
-// geometry and, without chunk lengths or window starts, the lean kGen = false variant; fp32
-// (used for checking), per-key tables and the rest take the general ones.
+// geometry and, without chunk lengths or window starts, the lean kGen = false variant (at 1, 2
+// or 4 physical waves); fp32 (used for checking), per-key tables and the rest take the general
+// ones, at 4.
 template <typename T, bool kFused, bool kRegTail>
 void launch_lean(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
   const bool gen = a.lens != nullptr || a.ws != nullptr;
   if (a.S == 16) {
     if (gen) return launch_inst<T, kFused, 16, kRegTail, false, true>(a, grid, smem, stream);
-    return launch_inst<T, kFused, 16, kRegTail, false, false>(a, grid, smem, stream);
+    return launch_phys<T, kFused, 16, kRegTail>(a, grid, smem, stream);
   }
   if (a.S == 32) {
     if (gen) return launch_inst<T, kFused, 32, kRegTail, false, true>(a, grid, smem, stream);
-    return launch_inst<T, kFused, 32, kRegTail, false, false>(a, grid, smem, stream);
+    return launch_phys<T, kFused, 32, kRegTail>(a, grid, smem, stream);
   }
   if (gen) return launch_inst<T, kFused, 0, kRegTail, false, true>(a, grid, smem, stream);
   launch_inst<T, kFused, 0, kRegTail, false, false>(a, grid, smem, stream);
@@ -609,6 +785,26 @@ void launch_s(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream)
     return launch_lean<T, kFused, false>(a, grid, smem, stream);
   }
   launch_inst<T, kFused, 0, false>(a, grid, smem, stream);
+}
+
+// Physical waves per workgroup for a grid of `units` workgroups: one when the grid fills every
+// wave slot of the GPU with one wave per unit (eight per CU at the kernel's two waves per SIMD),
+// so that a large cohort runs eight units per CU at once instead of two; else four. (Two waves
+// measured no faster than four on the ragged cohort.) PKC_CHUNK_WAVES = 1, 2 or 4 forces a count;
+// the results are the same at any count.
+int phys_waves(int64_t units) {
+  if (const char* e = getenv("PKC_CHUNK_WAVES")) {
+    const int w = atoi(e);
+    if (w == 1 || w == 2 || w == 4) return w;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();   // (a failed query must not surface as the launch's error)
+    return 4;
+  }
+  return units >= (int64_t)cus * 8 ? 1 : 4;
 }
 
 template <typename T>
@@ -651,17 +847,15 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   a.div_group = make_fastdiv(a.H / a.Hk);
   a.tail_cap = ((p.chunk + 31) / 32) * 32;
   a.vt_pitch = a.tail_cap + 16 / (int)sizeof(T);
-  constexpr int kWaves = waves_of<T>();
-  size_t off = (size_t)kWaves * kWaveLds * sizeof(float);
-  a.off_bt = (int)off;
-  off += (size_t)kWaves * kBtWindow * sizeof(int);
-  a.off_kt = (int)off;
-  off += (size_t)a.tail_cap * kt_pitch<T>() * sizeof(T);
-  a.off_vt = (int)off;
-  off += (size_t)kD * a.vt_pitch * sizeof(T);
+  const LaunchGrid lg = chunk_attn_grid((int)sizeof(T), p.batch, p.n_head, p.chunk);
+  // physical waves: fewer than 4 only for the register-held chunks of the lean bf16 variant
+  const bool lean = sizeof(T) == 2 && p.k_new && p.chunk <= 32 && !p.chunk_lens &&
+                    !p.window_start && !a.per_key && (p.block_size == 16 || p.block_size == 32);
+  a.phys = lean ? phys_waves(lg.workgroups) : 4;
+  const size_t off = chunk_lds_layout(a, 4);   // (launch_inst lays out its own variant's LDS)
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)chunk_attn_grid((int)sizeof(T), p.batch, p.n_head, p.chunk).workgroups);
+  const dim3 grid((unsigned)lg.workgroups);
   if (p.k_new) launch_s<T, true>(a, grid, off, stream);
   else launch_s<T, false>(a, grid, off, stream);
   return hipGetLastError();

@@ -9,7 +9,7 @@
 // fixed_attention_window (the positional rows a chunk touches: distances cache + i - j, one
 // shared table for a uniform cache, one table per row otherwise).
 //
-// Per (stream b, head h) unit, split over `split` workgroups of kWaves waves:
+// Per (stream b, head h) unit, split over `split` workgroups of kWaves (1, 4 or 8) waves:
 //   reads   the 16 queries, u and v, the chunk's K/V (k_new, v_new), the cached K/V pages
 //           [0, cache) in 32-key steps, and the positional band rows of each step, all with the
 //           attention kernel's own per-lane addresses;
@@ -68,9 +68,8 @@ gather_read_kernel(GatherArgs a) {
   const int hk = fdiv(h, a.div_group);
   if (!a.reads) {
     // the launch floor: the same grid writing its output rows, reading nothing
-    const int ft = tid >> 3;
-    if (part == 0 && ft < a.C)
-      *reinterpret_cast<u32x4*>(a.out + (((size_t)b * a.C + ft) * a.H + h) * kD + (tid & 7) * 8) =
+    for (int f = tid >> 3; part == 0 && f < a.C; f += kThreads / 8)
+      *reinterpret_cast<u32x4*>(a.out + (((size_t)b * a.C + f) * a.H + h) * kD + (tid & 7) * 8) =
           u32x4{(uint32_t)id, 0u, 0u, 0u};
     return;
   }
@@ -92,13 +91,20 @@ gather_read_kernel(GatherArgs a) {
     qv[5] = *reinterpret_cast<const u32x4*>(a.w + h * kD + 32 + 8 * grp);
   }
   const bool chunk_owner = part == 0;
-  u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
-  const int ft = tid >> 3;                 // chunk frame of this thread (8 vectors per row)
+  // chunk frames of this thread (8 vectors per row): ft, ft + kThreads / 8, ... (at most 16)
+  constexpr int NF = (16 * 8 + kThreads - 1) / kThreads;
+  u32x4 nk[NF], nv[NF];
+  const int ft = tid >> 3;
   const int fdv = (tid & 7) * 8;
-  if (chunk_owner && ft < a.C) {
-    const size_t row = ((size_t)(b * a.C + ft) * a.Hk + hk) * kD + fdv;
-    nk = *reinterpret_cast<const u32x4*>(a.k_new + row);
-    nv = *reinterpret_cast<const u32x4*>(a.v_new + row);
+#pragma unroll
+  for (int it = 0; it < NF; ++it) {
+    nk[it] = nv[it] = u32x4{0u, 0u, 0u, 0u};
+    const int f = ft + it * (kThreads / 8);
+    if (chunk_owner && f < a.C) {
+      const size_t row = ((size_t)(b * a.C + f) * a.Hk + hk) * kD + fdv;
+      nk[it] = *reinterpret_cast<const u32x4*>(a.k_new + row);
+      nv[it] = *reinterpret_cast<const u32x4*>(a.v_new + row);
+    }
   }
 
   const int cache = clampi(cs_raw, 0, a.max_cache);
@@ -177,16 +183,20 @@ gather_read_kernel(GatherArgs a) {
 
   // the append: the chunk's K rows into their column-blocked slots, V transposed through LDS
   const bool append = chunk_owner && h == hk * (a.H / a.Hk);
-  if (append && ft < a.C) {
-    const int key = cache + ft;
-    bf16* dst = a.k_pool + (size_t)hk * a.S * kD +
-                (uint64_t)clampi(bt[page_id(key >> a.logS)], 0, a.N - 1) * blk_stride +
-                (uint32_t)(((fdv >> 5) * a.S + (key & (a.S - 1))) * 32 + (fdv & 31));
-    *reinterpret_cast<u32x4*>(dst) = nk;
-    const uint32_t wd[4] = {nv[0], nv[1], nv[2], nv[3]};
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      reinterpret_cast<uint16_t*>(&s_vt[fdv + c][0])[ft] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
+  for (int it = 0; it < NF; ++it) {
+    const int f = ft + it * (kThreads / 8);
+    if (append && f < a.C) {
+      const int key = cache + f;
+      bf16* dst = a.k_pool + (size_t)hk * a.S * kD +
+                  (uint64_t)clampi(bt[page_id(key >> a.logS)], 0, a.N - 1) * blk_stride +
+                  (uint32_t)(((fdv >> 5) * a.S + (key & (a.S - 1))) * 32 + (fdv & 31));
+      *reinterpret_cast<u32x4*>(dst) = nk[it];
+      const uint32_t wd[4] = {nv[it][0], nv[it][1], nv[it][2], nv[it][3]};
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        reinterpret_cast<uint16_t*>(&s_vt[fdv + c][0])[f] = (uint16_t)(wd[c >> 1] >> (16 * (c & 1)));
+    }
   }
   s_x[wave][lane] = acc;
   __syncthreads();
@@ -212,11 +222,14 @@ gather_read_kernel(GatherArgs a) {
       }
     }
   }
-  if (chunk_owner && ft < a.C) {
-    u32x4 o = s_x[0][tid & 63];
+  u32x4 o = s_x[0][tid & 63];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) o ^= s_x[w][tid & 63];
-    *reinterpret_cast<u32x4*>(a.out + (((size_t)b * a.C + ft) * a.H + h) * kD + fdv) = o;
+  for (int w = 1; w < kWaves; ++w) o ^= s_x[w][tid & 63];
+#pragma unroll
+  for (int it = 0; it < NF; ++it) {
+    const int f = ft + it * (kThreads / 8);
+    if (chunk_owner && f < a.C)
+      *reinterpret_cast<u32x4*>(a.out + (((size_t)b * a.C + f) * a.H + h) * kD + fdv) = o;
   }
 }
 
@@ -261,6 +274,7 @@ hipError_t launch_gather_read(const GatherParams& p, hipStream_t stream) {
   a.div_group = make_fastdiv(p.n_head / p.n_kv_head);
   const dim3 grid((unsigned)gather_read_grid(p.batch, p.n_head, p.split, p.waves).workgroups);
   if (p.waves == 8) hipLaunchKernelGGL(gather_read_kernel<8>, grid, dim3(512), 0, stream, a);
+  else if (p.waves == 1) hipLaunchKernelGGL(gather_read_kernel<1>, grid, dim3(64), 0, stream, a);
   else hipLaunchKernelGGL(gather_read_kernel<4>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }

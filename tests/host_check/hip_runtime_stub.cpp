@@ -1,6 +1,6 @@
 // Stand-in definitions of the HIP runtime entry points that the library's host code and the
 // compiler-generated kernel stubs call (module registration, launch configuration, launch, function
-// attributes, error query). Each launch is checked against HIP's launch limits and the gfx950
+// attributes, error query, device queries). Each launch is checked against HIP's launch limits and the gfx950
 // LDS budget; a violation prints what it saw and aborts the process.
 #include "hip_runtime_stub.h"
 
@@ -124,6 +124,21 @@ hipError_t hipFuncSetAttribute(const void* function, hipFuncAttribute attr, int 
 
 hipError_t hipGetLastError(void) {
   ++state().calls;
+  return hipSuccess;
+}
+
+// Device queries: one MI355X (256 CUs) as device 0.
+hipError_t hipGetDevice(int* device) {
+  ++state().calls;
+  if (!device) return hipErrorInvalidValue;
+  *device = 0;
+  return hipSuccess;
+}
+
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device) {
+  ++state().calls;
+  if (!value || device != 0) return hipErrorInvalidValue;
+  *value = attr == hipDeviceAttributeMultiprocessorCount ? 256 : 0;
   return hipSuccess;
 }
 

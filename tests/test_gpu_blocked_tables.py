@@ -136,7 +136,7 @@ def test_commit_with_a_cap_below_one_block_matches_the_oracle():
 
 
 @pytest.mark.parametrize("cfg", [1, 3])
-@pytest.mark.parametrize("waves,split", [(4, 1), (8, 1), (4, 2)])
+@pytest.mark.parametrize("waves,split", [(4, 1), (8, 1), (4, 2), (1, 1)])
 def test_gather_read_writes_the_pools_as_the_append(cfg, waves, split):
     """The memory-path ceiling kernel appends the chunk exactly as paged_kv_append does (it
     touches no other pool element); its `out` is unspecified and not checked."""
