@@ -207,6 +207,10 @@ pkc_status paged_kv_append(pkc_dtype dtype, const void* k_new, const void* v_new
  * wavefront per workgroup (bf16 fused entries, chunk_size <= 32, block_size 16 or 32, no
  * chunk_lens or window_start); the results are bitwise the same either way. The environment
  * variable PKC_CHUNK_WAVES = 1, 2 or 4, read at each launch, forces the count for those calls.
+ * For those variants at 4 wavefronts, a grid larger than two workgroups per CU (at most 4096
+ * streams) runs the streams longest cache first (each workgroup ranks the cache lengths itself);
+ * PKC_CHUNK_ORDER = 0 or 1 forces it. The order changes which workgroup runs which stream, not
+ * any result.
  */
 pkc_status chunk_paged_relpos_attn(pkc_dtype dtype, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_tables,

@@ -88,8 +88,56 @@ struct ChunkArgs {
   int band_rs, band_hs, band_hd;
   int off_bt, off_kt, off_vt;        // byte offsets of the LDS regions
   int phys;                          // physical waves per workgroup (host-side choice)
+  int B;                             // streams
+  int rank;                          // run the streams longest cache first (host-side choice)
+  FastDiv div_hq;                    // by H qtiles
   float scale_log2;
 };
+
+// The stream at place r (0-based) when the B streams are ordered longest cache first - by their
+// body step count in 64 buckets, longest bucket first, index order inside a bucket. Each wave
+// works it out on its own: every stream's bucket counted in a wave-private LDS histogram (hist,
+// 64 ints), the counts' prefix over the buckets, the bucket holding place r, then that bucket's
+// streams walked in index order. The order only decides which workgroup runs which stream; the
+// arithmetic, and with it every result bit, is the same in any order.
+__device__ __forceinline__ int stream_by_length(const int32_t* cs, int B, int max_cache, int r,
+                                                int* hist) {
+  const int lane = threadIdx.x & 63;
+  const int kmax = (max_cache + 31) >> 5;
+  auto bucket = [&](int c) {   // 0: the longest caches
+    const int key = (clampi(c, 0, max_cache) + 31) >> 5;
+    return 63 - (int)(((int64_t)key * 64) / (kmax + 1));
+  };
+  hist[lane] = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int s0 = 0; s0 < B; s0 += 64)
+    if (s0 + lane < B) atomicAdd(&hist[bucket(cs[s0 + lane])], 1);
+  __builtin_amdgcn_wave_barrier();
+  const int cnt = hist[lane];
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  const int start = incl - cnt;
+  const uint64_t hit = __ballot(start <= r && r < incl);
+  const int J = hit ? (int)__builtin_ctzll(hit) : 0;
+  int t = r - __shfl(start, J);
+  for (int s0 = 0; s0 < B; s0 += 64) {
+    const bool in = s0 + lane < B && bucket(cs[min(s0 + lane, B - 1)]) == J;
+    const uint64_t m = __ballot(in);
+    const int n = __popcll(m);
+    if (t < n) {
+      // the lane holding the t-th stream of the bucket in this group of 64
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      const uint64_t pick = __ballot(in && below == t);
+      return __builtin_amdgcn_readfirstlane(s0 + (int)__builtin_ctzll(pick));
+    }
+    t -= n;
+  }
+  return min(r, B - 1);   // (not reached: place r < B lies in some bucket)
+}
 
 template <typename T>
 struct StepRegs {
@@ -108,7 +156,8 @@ template <typename T> constexpr int kt_pitch() { return kD + 16 / (int)sizeof(T)
 // fewer physical waves per unit put more units on a CU at once, with identical results.
 // kGen: per-stream chunk lengths or window starts may be given. Without them (the common case)
 // both are compile-time constants, which keeps the prologue's instruction count down.
-template <typename T, bool kFused, int kPhys, int kS, bool kRegTail, bool kPerKey, bool kGen>
+template <typename T, bool kFused, int kPhys, int kS, bool kRegTail, bool kPerKey, bool kGen,
+          bool kRank = false>
 __global__ void __launch_bounds__(kPhys * 64)
 __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
 chunk_attn_kernel(ChunkArgs<T> a) {
@@ -138,14 +187,25 @@ chunk_attn_kernel(ChunkArgs<T> a) {
   const int m16 = lane & 15;
   const int grp = lane >> 4;
 
-  // Grid order (b, h, query tile), tile fastest: consecutive workgroups go round-robin to the
+  // Grid order (stream, h, query tile), tile fastest: consecutive workgroups go round-robin to the
   // XCDs, so for H a multiple of 8 each XCD serves one head and a shared table's band for that
-  // head stays in that XCD's L2.
+  // head stays in that XCD's L2. The streams go in index order, or, when the grid runs in more
+  // than one pass over the CUs (kRank), longest cache first: workgroups start roughly in grid
+  // order, and a long stream reached last would set the launch's tail.
   const int id = blockIdx.x;
-  const int bh = fdiv(id, a.div_qtiles);
-  const int qt = id - bh * a.qtiles;
-  const int b = fdiv(bh, a.div_H);
-  const int h = bh - b * a.H;
+  int b, h, qt;
+  if constexpr (kRank) {
+    const int sr = fdiv(id, a.div_hq);             // the stream's place in that order
+    const int rem = id - sr * (a.H * a.qtiles);
+    h = fdiv(rem, a.div_qtiles);
+    qt = rem - h * a.qtiles;
+    b = stream_by_length(a.cs, a.B, a.max_cache, sr, s_win);
+  } else {
+    const int bh = fdiv(id, a.div_qtiles);
+    qt = id - bh * a.qtiles;
+    b = fdiv(bh, a.div_H);
+    h = bh - b * a.H;
+  }
   const int hk = fdiv(h, a.div_group);
   const int32_t* bt = a.bt + (size_t)b * a.M;
   // the cache length gates every page and table address below: its request goes first (the
@@ -717,7 +777,7 @@ size_t chunk_lds_layout(ChunkArgs<T>& a, int phys) {
 }
 
 template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false, bool kGen = true,
-          int kPhys = 4>
+          int kPhys = 4, bool kRank = false>
 void launch_inst(const ChunkArgs<T>& a_in, dim3 grid, size_t, hipStream_t stream) {
   // (the layout follows the variant launched, whatever count the host asked for)
   ChunkArgs<T> a = a_in;
@@ -729,21 +789,22 @@ void launch_inst(const ChunkArgs<T>& a_in, dim3 grid, size_t, hipStream_t stream
     // workgroup
     (void)hipFuncSetAttribute(
         reinterpret_cast<const void*>(
-            &chunk_attn_kernel<T, kFused, kPhys, kS, kRegTail, kPerKey, kGen>),
+            &chunk_attn_kernel<T, kFused, kPhys, kS, kRegTail, kPerKey, kGen, kRank>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   }
-  hipLaunchKernelGGL((chunk_attn_kernel<T, kFused, kPhys, kS, kRegTail, kPerKey, kGen>),
+  hipLaunchKernelGGL((chunk_attn_kernel<T, kFused, kPhys, kS, kRegTail, kPerKey, kGen, kRank>),
                      grid, dim3(kPhys * 64), smem, stream, a);
 }
 
 // the lean variant (no chunk lengths or window starts) at a.phys physical waves per workgroup
-// (register-held chunks only: see the kernel)
+// (register-held chunks only: see the kernel; longest-first order at four physical waves)
 template <typename T, bool kFused, int kS, bool kRegTail>
 void launch_phys(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
   if constexpr (kRegTail) {
     if (a.phys == 1) return launch_inst<T, kFused, kS, true, false, false, 1>(a, grid, smem, stream);
     if (a.phys == 2) return launch_inst<T, kFused, kS, true, false, false, 2>(a, grid, smem, stream);
   }
+  if (a.rank) return launch_inst<T, kFused, kS, kRegTail, false, false, 4, true>(a, grid, smem, stream);
   launch_inst<T, kFused, kS, kRegTail, false, false, 4>(a, grid, smem, stream);
 }
 
@@ -791,20 +852,38 @@ void launch_s(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream)
 // wave slot of the GPU with one wave per unit (eight per CU at the kernel's two waves per SIMD),
 // so that a large cohort runs eight units per CU at once instead of two; else four. (Two waves
 // measured no faster than four on the ragged cohort.) PKC_CHUNK_WAVES = 1, 2 or 4 forces a count;
-// the results are the same at any count.
-int phys_waves(int64_t units) {
-  if (const char* e = getenv("PKC_CHUNK_WAVES")) {
-    const int w = atoi(e);
-    if (w == 1 || w == 2 || w == 4) return w;
-  }
+// the results are the same at any count. `cus`: the device's CU count, 0 if unknown.
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0) {
     (void)hipGetLastError();   // (a failed query must not surface as the launch's error)
-    return 4;
+    return 0;
   }
+  return cus;
+}
+
+int phys_waves(int64_t units, int cus) {
+  if (const char* e = getenv("PKC_CHUNK_WAVES")) {
+    const int w = atoi(e);
+    if (w == 1 || w == 2 || w == 4) return w;
+  }
+  if (cus <= 0) return 4;
   return units >= (int64_t)cus * 8 ? 1 : 4;
+}
+
+// Longest cache first when the grid takes more than one pass over the CUs at `phys` physical
+// waves per workgroup (two waves per SIMD: 8 / phys workgroups per CU), for at most 4096 streams
+// (each workgroup walks every stream's length twice to find its own). PKC_CHUNK_ORDER = 0 or 1
+// forces the choice; the results are the same either way.
+int rank_streams(int64_t units, int batch, int phys, int cus) {
+  if (const char* e = getenv("PKC_CHUNK_ORDER")) {
+    const int o = atoi(e);
+    if (o == 0 || o == 1) return batch <= 4096 ? o : 0;
+  }
+  if (cus <= 0 || batch > 4096) return 0;
+  return units > (int64_t)cus * (8 / phys) ? 1 : 0;
 }
 
 template <typename T>
@@ -851,7 +930,15 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   // physical waves: fewer than 4 only for the register-held chunks of the lean bf16 variant
   const bool lean = sizeof(T) == 2 && p.k_new && p.chunk <= 32 && !p.chunk_lens &&
                     !p.window_start && !a.per_key && (p.block_size == 16 || p.block_size == 32);
-  a.phys = lean ? phys_waves(lg.workgroups) : 4;
+  const int cus = device_cus();
+  a.phys = lean ? phys_waves(lg.workgroups, cus) : 4;
+  a.B = p.batch;
+  a.div_hq = make_fastdiv(a.H * a.qtiles);
+  // (ranked only in the bf16 variants without chunk lengths or window starts, at four physical
+  // waves: the ones launch_phys dispatches)
+  const bool rankable = sizeof(T) == 2 && !p.chunk_lens && !p.window_start && !a.per_key &&
+                        (p.block_size == 16 || p.block_size == 32) && a.phys == 4;
+  a.rank = rankable ? rank_streams(lg.workgroups, p.batch, a.phys, cus) : 0;
   const size_t off = chunk_lds_layout(a, 4);   // (launch_inst lays out its own variant's LDS)
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;

@@ -1,9 +1,10 @@
-"""GPU: the chunk attention at 1, 2 and 4 physical waves per workgroup.
+"""GPU: the chunk attention's launch choices - physical waves per workgroup and stream order.
 
 The kernel splits a unit's keys over four virtual waves and merges them in a fixed order; a
-large cohort runs them on fewer physical waves (more units per CU at once). The physical count is
-a launch choice only: outputs and pools must be bit-identical at every count, and match the
-oracle. PKC_CHUNK_WAVES forces the count (read by the library at each launch).
+large cohort runs them on fewer physical waves (more units per CU at once). A grid that takes more
+than one pass over the CUs runs its streams longest cache first. Both are launch choices only:
+outputs and pools must be bit-identical under every choice, and match the oracle.
+PKC_CHUNK_WAVES and PKC_CHUNK_ORDER force them (read by the library at each launch).
 """
 
 import os
@@ -44,6 +45,7 @@ def announce(request):
     print(f"\n[gpu] {request.node.nodeid}", flush=True)
     yield
     os.environ.pop("PKC_CHUNK_WAVES", None)
+    os.environ.pop("PKC_CHUNK_ORDER", None)
     torch.cuda.synchronize()
 
 
@@ -129,3 +131,44 @@ def test_one_wave_graph_replays_match_eager():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits(out), bits(eager), err_msg=f"replay {r}")
         _ = (co.q.float() * 2).sum().item()   # unrelated eager work between replays
+
+
+def ordered(co, waves, order):
+    os.environ["PKC_CHUNK_ORDER"] = str(order)
+    return fused(co, waves)
+
+
+@pytest.mark.parametrize("name", sorted(COHORTS))
+def test_longest_first_order_bit_identical(name):
+    """Streams run longest cache first (ranked inside each workgroup, at four physical waves)
+    give the bits of index order, pools included; at one physical wave the order switch is
+    ignored and the bits are the same again."""
+    co = make_chunk_cohort(seed=13, device=DEV, **COHORTS[name])
+    c0 = clone(co)
+    base = ordered(c0, 4, 0)
+    for waves in (4, 1):
+        c = clone(co)
+        out = ordered(c, waves, 1)
+        np.testing.assert_array_equal(bits(out), bits(base), err_msg=f"{waves} waves")
+        np.testing.assert_array_equal(bits(c.k_pool), bits(c0.k_pool))
+        np.testing.assert_array_equal(bits(c.v_pool), bits(c0.v_pool))
+
+
+def test_longest_first_order_many_streams():
+    """More than 64 streams (the ranking walks them in groups of 64), cache lengths with ties
+    and empty caches: every order gives the same bits, and the oracle's values."""
+    rng = np.random.default_rng(5)
+    cache = (rng.integers(0, 40, size=150) * 16).tolist()
+    cache[::7] = [0] * len(cache[::7])
+    co = poison(make_chunk_cohort(150, 2, 64, 16, 16, cache, dtype=BF16, seed=14, device=DEV))
+    ref = oracle_chunk(co)
+    base = ordered(clone(co), 4, 0)
+    assert max_err(base, ref) <= TOL[BF16]
+    np.testing.assert_array_equal(bits(ordered(clone(co), 4, 1)), bits(base))
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_longest_first_order_on_workloads(cfg):
+    co = make_config(cfg, device=DEV)
+    base = ordered(clone(co), 4, 0)
+    np.testing.assert_array_equal(bits(ordered(clone(co), 4, 1)), bits(base))
