@@ -778,7 +778,7 @@ size_t chunk_lds_layout(ChunkArgs<T>& a, int phys) {
 
 template <typename T, bool kFused, int kS, bool kRegTail, bool kPerKey = false, bool kGen = true,
           int kPhys = 4, bool kRank = false>
-void launch_inst(const ChunkArgs<T>& a_in, dim3 grid, size_t, hipStream_t stream) {
+void launch_inst(const ChunkArgs<T>& a_in, dim3 grid, hipStream_t stream) {
   // (the layout follows the variant launched, whatever count the host asked for)
   ChunkArgs<T> a = a_in;
   a.phys = kPhys;
@@ -799,13 +799,13 @@ void launch_inst(const ChunkArgs<T>& a_in, dim3 grid, size_t, hipStream_t stream
 // the lean variant (no chunk lengths or window starts) at a.phys physical waves per workgroup
 // (register-held chunks only: see the kernel; longest-first order at four physical waves)
 template <typename T, bool kFused, int kS, bool kRegTail>
-void launch_phys(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
+void launch_phys(const ChunkArgs<T>& a, dim3 grid, hipStream_t stream) {
   if constexpr (kRegTail) {
-    if (a.phys == 1) return launch_inst<T, kFused, kS, true, false, false, 1>(a, grid, smem, stream);
-    if (a.phys == 2) return launch_inst<T, kFused, kS, true, false, false, 2>(a, grid, smem, stream);
+    if (a.phys == 1) return launch_inst<T, kFused, kS, true, false, false, 1>(a, grid, stream);
+    if (a.phys == 2) return launch_inst<T, kFused, kS, true, false, false, 2>(a, grid, stream);
   }
-  if (a.rank) return launch_inst<T, kFused, kS, kRegTail, false, false, 4, true>(a, grid, smem, stream);
-  launch_inst<T, kFused, kS, kRegTail, false, false, 4>(a, grid, smem, stream);
+  if (a.rank) return launch_inst<T, kFused, kS, kRegTail, false, false, 4, true>(a, grid, stream);
+  launch_inst<T, kFused, kS, kRegTail, false, false, 4>(a, grid, stream);
 }
 
 // Instantiation for a call: the block sizes of the streaming workloads get constant page
@@ -813,39 +813,39 @@ void launch_phys(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stre
 // or 4 physical waves); fp32 (used for checking), per-key tables and the rest take the general
 // ones, at 4.
 template <typename T, bool kFused, bool kRegTail>
-void launch_lean(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
+void launch_lean(const ChunkArgs<T>& a, dim3 grid, hipStream_t stream) {
   const bool gen = a.lens != nullptr || a.ws != nullptr;
   if (a.S == 16) {
-    if (gen) return launch_inst<T, kFused, 16, kRegTail, false, true>(a, grid, smem, stream);
-    return launch_phys<T, kFused, 16, kRegTail>(a, grid, smem, stream);
+    if (gen) return launch_inst<T, kFused, 16, kRegTail, false, true>(a, grid, stream);
+    return launch_phys<T, kFused, 16, kRegTail>(a, grid, stream);
   }
   if (a.S == 32) {
-    if (gen) return launch_inst<T, kFused, 32, kRegTail, false, true>(a, grid, smem, stream);
-    return launch_phys<T, kFused, 32, kRegTail>(a, grid, smem, stream);
+    if (gen) return launch_inst<T, kFused, 32, kRegTail, false, true>(a, grid, stream);
+    return launch_phys<T, kFused, 32, kRegTail>(a, grid, stream);
   }
-  if (gen) return launch_inst<T, kFused, 0, kRegTail, false, true>(a, grid, smem, stream);
-  launch_inst<T, kFused, 0, kRegTail, false, false>(a, grid, smem, stream);
+  if (gen) return launch_inst<T, kFused, 0, kRegTail, false, true>(a, grid, stream);
+  launch_inst<T, kFused, 0, kRegTail, false, false>(a, grid, stream);
 }
 
 template <typename T, bool kFused>
-void launch_s(const ChunkArgs<T>& a, dim3 grid, size_t smem, hipStream_t stream) {
+void launch_s(const ChunkArgs<T>& a, dim3 grid, hipStream_t stream) {
   // register-held chunk for fused bf16 chunks of at most 32 frames (one 16-byte vector of K and
   // one of V per thread, requested at kernel start)
   constexpr bool kRegOk = sizeof(T) == 2 && kFused;
   const bool reg_tail = kRegOk && a.C <= 32;
   if (a.per_key) {
     if constexpr (kRegOk) {
-      if (reg_tail) return launch_inst<T, kFused, 0, true, true>(a, grid, smem, stream);
+      if (reg_tail) return launch_inst<T, kFused, 0, true, true>(a, grid, stream);
     }
-    return launch_inst<T, kFused, 0, false, true>(a, grid, smem, stream);
+    return launch_inst<T, kFused, 0, false, true>(a, grid, stream);
   }
   if constexpr (sizeof(T) == 2) {
     if constexpr (kRegOk) {
-      if (reg_tail) return launch_lean<T, kFused, true>(a, grid, smem, stream);
+      if (reg_tail) return launch_lean<T, kFused, true>(a, grid, stream);
     }
-    return launch_lean<T, kFused, false>(a, grid, smem, stream);
+    return launch_lean<T, kFused, false>(a, grid, stream);
   }
-  launch_inst<T, kFused, 0, false>(a, grid, smem, stream);
+  launch_inst<T, kFused, 0, false>(a, grid, stream);
 }
 
 // Physical waves per workgroup for a grid of `units` workgroups: one when the grid fills every
@@ -939,12 +939,12 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
   const bool rankable = sizeof(T) == 2 && !p.chunk_lens && !p.window_start && !a.per_key &&
                         (p.block_size == 16 || p.block_size == 32) && a.phys == 4;
   a.rank = rankable ? rank_streams(lg.workgroups, p.batch, a.phys, cus) : 0;
-  const size_t off = chunk_lds_layout(a, 4);   // (launch_inst lays out its own variant's LDS)
   const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / sqrtf((float)p.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)lg.workgroups);
-  if (p.k_new) launch_s<T, true>(a, grid, off, stream);
-  else launch_s<T, false>(a, grid, off, stream);
+  // (launch_inst lays out the LDS of the variant it launches)
+  if (p.k_new) launch_s<T, true>(a, grid, stream);
+  else launch_s<T, false>(a, grid, stream);
   return hipGetLastError();
 }
 

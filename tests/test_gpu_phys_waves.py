@@ -165,6 +165,15 @@ def test_longest_first_order_many_streams():
     base = ordered(clone(co), 4, 0)
     assert max_err(base, ref) <= TOL[BF16]
     np.testing.assert_array_equal(bits(ordered(clone(co), 4, 1)), bits(base))
+    # the unfused entry (append, then attention over the pool) ranks the same way
+    c = clone(co)
+    os.environ["PKC_CHUNK_ORDER"] = "1"
+    pkc.paged_kv_append(c.k_new, c.v_new, c.k_pool, c.v_pool, c.block_tables, c.cache_seqlens,
+                        c.max_cache_seqlen)
+    out = pkc.chunk_paged_relpos_attn(c.q, c.k_pool, c.v_pool, c.block_tables, c.cache_seqlens,
+                                      c.pos, c.pos_bias_u, c.pos_bias_v, c.max_cache_seqlen)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out), bits(base))
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
