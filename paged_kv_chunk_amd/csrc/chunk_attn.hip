@@ -853,17 +853,6 @@ void launch_s(const ChunkArgs<T>& a, dim3 grid, hipStream_t stream) {
 // so that a large cohort runs eight units per CU at once instead of two; else four. (Two waves
 // measured no faster than four on the ragged cohort.) PKC_CHUNK_WAVES = 1, 2 or 4 forces a count;
 // the results are the same at any count. `cus`: the device's CU count, 0 if unknown.
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0) {
-    (void)hipGetLastError();   // (a failed query must not surface as the launch's error)
-    return 0;
-  }
-  return cus;
-}
-
 int phys_waves(int64_t units, int cus) {
   if (const char* e = getenv("PKC_CHUNK_WAVES")) {
     const int w = atoi(e);
@@ -949,6 +938,17 @@ hipError_t launch_chunk_t(const AttnParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();   // (a failed query must not surface as the launch's error)
+    return 0;
+  }
+  return cus;
+}
 
 size_t chunk_attn_lds_bytes(int dtype_bytes, int chunk, int, int, bool) {
   const int tail_cap = ((chunk + 31) / 32) * 32;

@@ -149,6 +149,8 @@ LaunchGrid chunk_attn_grid(int dtype_bytes, int batch, int n_head, int chunk);
 LaunchGrid varlen_attn_grid(int dtype_bytes, int num_seqs, int n_head, int max_seqlen,
                             bool limited);   // with the chunked_limited mask
 LaunchGrid gather_read_grid(int batch, int n_head, int split, int waves);
+// compute units of the current device, 0 if the query fails
+int device_cus();
 LaunchGrid gemm_grid(int64_t M, int64_t N);   // the tile shape the GEMM launchers pick for M x N
 
 }  // namespace pkc

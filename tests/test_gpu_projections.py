@@ -67,6 +67,8 @@ LINEAR = {
     # flight at once)
     "direct_k256_ring": (4096, 1536, 256),
     "dmodel512_qkv_shape_large_tiles": (4096, 1536, 512),
+    # the 128 x 192 tile (one per CU, the deep ring) with a ragged last row of tiles
+    "direct_k512_wide_tiles_ragged_rows": (4000, 1536, 512),
     "out_proj_dmodel512": (4096, 512, 512),
 }
 
@@ -182,6 +184,16 @@ def test_qkv_append_window_start_ring():
     _check_qkv(c, co, x, w, b, ws=starts, lens=[16, 9, 16])
 
 
+def test_qkv_append_wide_tiles_chunk_lens_and_window_starts():
+    """The d_model 512 cohort's launch (128 x 192 tiles, one per CU, the deep ring) with
+    per-stream chunk lengths from 0 to C frames and ring-rotated table rows: each row's stream
+    entries, loaded ahead of the contraction, place its K/V in the right page and slot."""
+    c, co, x, w, b = _qkv_case("dmodel512_cohort", seed=9)
+    starts, co.block_tables = ring_tables(co, 17)
+    lens = np.random.default_rng(19).integers(0, c["C"] + 1, size=c["B"]).tolist()
+    _check_qkv(c, co, x, w, b, ws=starts, lens=lens)
+
+
 def test_qkv_append_then_attention_equals_append_of_projected_rows():
     """The epilogue writes exactly what paged_kv_append writes for the same K/V rows: project with
     the plain linear layer, split, append, and compare the pools bit for bit."""
@@ -218,7 +230,9 @@ def _pos_bound(w64, pos, dtype, d_model, ref):
 
 @pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("case", ["txl_shared_dmodel256", "txl_shared_dmodel512", "wenet_per_stream",
-                                  "dmodel1024_ragged_tables"])
+                                  "dmodel1024_ragged_tables",
+                                  # a width whose rows the kernel stages through registers
+                                  "txl_shared_dmodel384"])
 def test_rel_pos_projection_parity(case, dtype):
     if case == "dmodel1024_ragged_tables":
         # tables whose rows do not fill whole 64-row tiles, crossing table boundaries in a tile
@@ -229,8 +243,9 @@ def test_rel_pos_projection_parity(case, dtype):
         got = pkc.rel_pos_projection(w, rows, pos_start=st, pos_step=-1)
         step = -1
     elif case.startswith("txl"):
-        dm = 256 if case.endswith("256") else 512
-        center = 271 if dm == 256 else 527          # max cache + C - 1 of the streaming workloads
+        dm = int(case.rsplit("dmodel", 1)[1])
+        # max cache + C - 1 of the streaming workloads
+        center = {256: 271, 512: 527}.get(dm, 100)
         w, _ = linear_weights(dm, dm, seed=11, dtype=dtype, device=DEV, bias=False)
         rows = 2 * center + 1
         got = pkc.rel_pos_projection(w, rows, pos_first=center, pos_step=-1)
