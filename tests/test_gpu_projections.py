@@ -69,6 +69,8 @@ LINEAR = {
     "dmodel512_qkv_shape_large_tiles": (4096, 1536, 512),
     # the 128 x 192 tile (one per CU, the deep ring) with a ragged last row of tiles
     "direct_k512_wide_tiles_ragged_rows": (4000, 1536, 512),
+    # 128 x 192 tiles on more than one per CU: the three-slot ring
+    "direct_k512_wide_tiles_ring": (8192, 1536, 512),
     "out_proj_dmodel512": (4096, 512, 512),
 }
 
@@ -232,7 +234,9 @@ def _pos_bound(w64, pos, dtype, d_model, ref):
 @pytest.mark.parametrize("case", ["txl_shared_dmodel256", "txl_shared_dmodel512", "wenet_per_stream",
                                   "dmodel1024_ragged_tables",
                                   # a width whose rows the kernel stages through registers
-                                  "txl_shared_dmodel384"])
+                                  "txl_shared_dmodel384",
+                                  # many per-row tables: more tiles than CUs, the three-slot ring
+                                  "many_tables_dmodel512"])
 def test_rel_pos_projection_parity(case, dtype):
     if case == "dmodel1024_ragged_tables":
         # tables whose rows do not fill whole 64-row tiles, crossing table boundaries in a tile
@@ -242,6 +246,13 @@ def test_rel_pos_projection_parity(case, dtype):
         st = torch.tensor(starts, dtype=torch.int32, device=DEV)
         got = pkc.rel_pos_projection(w, rows, pos_start=st, pos_step=-1)
         step = -1
+    elif case == "many_tables_dmodel512":
+        dm, rows = 512, 300
+        w, _ = linear_weights(dm, dm, seed=15, dtype=dtype, device=DEV, bias=False)
+        starts = np.random.default_rng(16).integers(-5000, 5000, size=40)
+        st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+        got = pkc.rel_pos_projection(w, rows, pos_start=st, pos_step=1)
+        step = 1
     elif case.startswith("txl"):
         dm = int(case.rsplit("dmodel", 1)[1])
         # max cache + C - 1 of the streaming workloads
