@@ -501,8 +501,9 @@ def bench_proj(args, cfg, pkc):
     flops_layer = sum(v["flops"] for v in per_kind.values())
     dom = max(kinds, key=lambda k: per_kind[k]["us"])
     d = per_kind[dom]
-    kernel_name = {"qkv": "gemm_kernel<bf16, Q/K/V paged epilogue>",
-                   "pos": "gemm_kernel<bf16, sinusoid source>", "out": "gemm_kernel<bf16, plain>"}
+    kernel_name = {"qkv": "gemm_dma_kernel<bf16, Q/K/V paged epilogue>",
+                   "pos": "gemm_dma_kernel<bf16, generated sinusoid>",
+                   "out": "gemm_dma_kernel<bf16, plain>"}
     result = {
         "metric": "Q/K/V, positional and output projections per layer: tokens/sec + % of bf16 MFMA roofline, 1 GPU",
         "value": B * C * n_layers / (ms_step / 1e3),
