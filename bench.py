@@ -20,8 +20,9 @@ Prints one JSON line. `value` is chunk*heads per second per layer: B * H * layer
 average launch duration is the graph-replay time of the timed region, measured with HIP events on
 the replay stream, divided by the number of kernel launches in it (gaps between the graph's
 kernels count against the kernel). `roofline.ceiling` is the same-run time of a kernel that moves
-the same bytes through the same tables with no arithmetic, and `roofline.launch_floor_us` that of
-the same grid writing only its output. `configs` holds the other workloads of the same run (the
+the same bytes through the same tables with no arithmetic, `roofline.launch_floor_us` that of
+the same grid writing only its output, and `roofline.copy` that of a plain device copy of the
+same bytes (with the kernel's rate as a fraction of it). `configs` holds the other workloads of the same run (the
 d_model 512 cohort, the ragged cohort, the packed offline batch) with their own rooflines.
 `cpu_baseline` times the float64 oracle on a bounded sample on the host; `cpu_baselines` does so
 for every workload.
@@ -574,6 +575,29 @@ def replay_ms(graphs, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def copy_reference(nbytes, steps, warmup):
+    """Same-run time of a plain device copy moving a launch's bytes (half read, half written),
+    rotated over buffer pairs that together exceed the 256 MB last-level cache and replayed from
+    one HIP graph like the kernels: the HBM rate one launch of this size reaches with no gather
+    and no arithmetic. Returns the roofline's `copy` object (without the kernel's share)."""
+    half = -(-max(nbytes // 2, 1 << 20) // 256) * 256
+    pairs = max(2, -(-(512 << 20) // (2 * half)))
+    bufs = []
+    for _ in range(pairs):
+        src = torch.empty(half, dtype=torch.uint8, device="cuda").random_(0, 255)
+        bufs.append((src, torch.empty_like(src)))
+    graphs = capture_graphs([bufs], lambda sd, st: sd[1].copy_(sd[0]))
+    us = replay_ms(graphs, max(steps // 4, 10), max(warmup // 4, 3)) * 1e3 / pairs
+    del graphs, bufs
+    torch.cuda.empty_cache()
+    moved = 2 * half
+    return {"kernel": f"device copy (the runtime's copy kernel, one launch per copy) of "
+                      f"{half / 2**20:.1f} MiB read + {half / 2**20:.1f} MiB written, over {pairs} "
+                      f"buffer pairs ({pairs * moved / 2**20:.0f} MiB) in turn, graph replay",
+            "bytes_per_copy": moved, "us": us, "achieved": moved / (us * 1e-6) / 1e9,
+            "frac": moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 # launch shapes of the memory-path ceiling kernel: (waves per workgroup, workgroups per stream
 # and head); the attention kernel's own grids are (4, 1) and, for cohorts whose grid fills every
 # wave slot with one wave per unit, (1, 1)
@@ -702,6 +726,10 @@ def chunk_workload(cfg_index, args, pkc, measure_ceiling=True, lens_mode=False):
         res["roofline"]["ceiling"] = ceil
         res["roofline"]["kernel_over_ceiling"] = kernel_us / ceil["us"]
         res["roofline"]["launch_floor_us"] = floor_us
+        # the survey's "% of a measured copy bandwidth": the same bytes through a plain copy
+        copy = copy_reference(nbytes, args.steps, args.warmup)
+        copy["kernel_frac_of_copy"] = achieved / copy["achieved"]
+        res["roofline"]["copy"] = copy
         # (the ceiling kernel appended the same K/V again and left garbage in out; restore a
         # clean state for what follows by replaying the attention once more)
         for g in graphs:
