@@ -236,13 +236,22 @@ def _pos_bound(w64, pos, dtype, d_model, ref):
                                   # a width whose rows the kernel stages through registers
                                   "txl_shared_dmodel384",
                                   # many per-row tables: more tiles than CUs, the three-slot ring
-                                  "many_tables_dmodel512"])
+                                  "many_tables_dmodel512",
+                                  # 1536 output features over 4096 rows: 128 x 192 tiles
+                                  "wide_tiles_dmodel512"])
 def test_rel_pos_projection_parity(case, dtype):
     if case == "dmodel1024_ragged_tables":
         # tables whose rows do not fill whole 64-row tiles, crossing table boundaries in a tile
         dm, rows = 1024, 37
         w, _ = linear_weights(512, dm, seed=13, dtype=dtype, device=DEV, bias=False)
         starts = np.array([40, -7, 3000])
+        st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+        got = pkc.rel_pos_projection(w, rows, pos_start=st, pos_step=-1)
+        step = -1
+    elif case == "wide_tiles_dmodel512":
+        dm, rows = 512, 512
+        w, _ = linear_weights(1536, dm, seed=17, dtype=dtype, device=DEV, bias=False)
+        starts = np.random.default_rng(18).integers(-3000, 3000, size=8)
         st = torch.tensor(starts, dtype=torch.int32, device=DEV)
         got = pkc.rel_pos_projection(w, rows, pos_start=st, pos_step=-1)
         step = -1
