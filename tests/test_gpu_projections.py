@@ -113,6 +113,9 @@ QKV = {
                                   dm=256, dtype=BF16),
     # the d_model 512 cohort at full size, in the launch configuration the projection bench times
     "dmodel512_cohort": dict(B=256, H=8, Hk=8, D=64, C=16, S=16, caches=[512] * 256, dm=512, dtype=BF16),
+    # head sizes other than 64 (the append takes any multiple of 32): the pair and page offsets
+    "head_dim32": dict(B=5, H=4, Hk=2, D=32, C=16, S=16, caches=[0, 15, 16, 100, 33], dm=128, dtype=BF16),
+    "head_dim128_gqa": dict(B=3, H=4, Hk=1, D=128, C=16, S=32, caches=[0, 37, 100], dm=256, dtype=BF16),
 }
 
 
