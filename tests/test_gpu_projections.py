@@ -89,6 +89,32 @@ def test_linear_parity(case, with_bias, dtype):
     assert_within(host64(y), ref, bound(ref, np.abs(xh) @ np.abs(wh).T, dtype, K), f"linear {case}")
 
 
+def _random_shapes(seed, n):
+    """Seeded GEMM shapes over the launcher's choices: every tile shape, ring depth and staging
+    path (K of 256, 512 and 1024 load directly in bf16), ragged M and N (N a multiple of 16)."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(n):
+        K = int(rng.choice([32, 96, 256, 512, 1024]))
+        M = int(rng.integers(1, 4200))
+        N = 16 * int(rng.integers(1, 100))
+        shapes.append((M, N, K))
+    return shapes
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "fp32"])
+def test_linear_random_shapes(dtype):
+    for i, (M, N, K) in enumerate(_random_shapes(21, 16)):
+        x = activations((M, K), seed=100 + i, dtype=dtype, device=DEV)
+        w, b = linear_weights(N, K, seed=200 + i, dtype=dtype, device=DEV, bias=i % 2 == 0)
+        y = pkc.linear(x, w, b)
+        torch.cuda.synchronize()
+        xh, wh = host64(x), host64(w)
+        ref = oracle.linear(xh, wh, host64(b) if b is not None else None)
+        assert_within(host64(y), ref, bound(ref, np.abs(xh) @ np.abs(wh).T, dtype, K),
+                      f"linear M={M} N={N} K={K}")
+
+
 def test_linear_batched_leading_dims():
     x = activations((4, 16, 256), seed=3, device=DEV)
     w, b = linear_weights(256, 256, seed=4, device=DEV)
