@@ -225,6 +225,27 @@ def test_qkv_append_wide_tiles_chunk_lens_and_window_starts():
     _check_qkv(c, co, x, w, b, ws=starts, lens=lens)
 
 
+def test_qkv_append_random_cohorts():
+    """A seeded sweep of cohort shapes: streams, chunk size, heads (GQA), head size (32, 64, 128),
+    block size, d_model and ragged cache lengths, with and without chunk lengths."""
+    rng = np.random.default_rng(31)
+    for i in range(10):
+        Hk = int(rng.choice([1, 2, 4]))
+        H = Hk * int(rng.choice([1, 2]))
+        D = int(rng.choice([32, 64, 128]))
+        C = int(rng.integers(1, 33))
+        S = int(rng.choice([8, 16, 32]))
+        B = int(rng.integers(1, 40))
+        dm = 32 * int(rng.integers(2, 17))
+        caches = rng.integers(0, 300, size=B).tolist()
+        c = dict(B=B, H=H, Hk=Hk, D=D, C=C, S=S, caches=caches, dm=dm, dtype=BF16)
+        co = make_chunk_cohort(B, H, D, C, S, caches, Hk=Hk, dtype=BF16, seed=40 + i, device=DEV)
+        x = activations((B, C, dm), seed=50 + i, dtype=BF16, device=DEV)
+        w, b = linear_weights((H + 2 * Hk) * D, dm, seed=60 + i, dtype=BF16, device=DEV)
+        lens = rng.integers(0, C + 1, size=B).tolist() if i % 2 else None
+        _check_qkv(c, co, x, w, b, lens=lens)
+
+
 def test_qkv_append_then_attention_equals_append_of_projected_rows():
     """The epilogue writes exactly what paged_kv_append writes for the same K/V rows: project with
     the plain linear layer, split, append, and compare the pools bit for bit."""
