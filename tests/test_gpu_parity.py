@@ -168,6 +168,36 @@ def test_attention_parity_workloads(cfg, streams):
     np.testing.assert_array_equal(bits(out), bits(out_f))
 
 
+def test_attention_random_cohorts():
+    """A seeded sweep of cohort shapes: streams, heads (GQA), chunk sizes from 1 to 96, block
+    sizes from 8 to 64, ragged cache lengths (empty caches and partial blocks included), shared
+    or per-row tables, bf16 and fp32. Each cohort against the oracle, with the fused entry and
+    the append + attention pair bitwise equal, pools included."""
+    rng = np.random.default_rng(71)
+    for i in range(12):
+        dtype = torch.float32 if i % 4 == 3 else torch.bfloat16
+        Hk = int(rng.choice([1, 2, 4]))
+        H = Hk * int(rng.choice([1, 2]))
+        C = int(rng.choice([1, 5, 16, 17, 32, 48, 96]))
+        S = int(rng.choice([8, 16, 32, 64]))
+        B = int(rng.integers(1, 24))
+        caches = rng.integers(0, 400, size=B).tolist()
+        per_row = bool(rng.integers(0, 2))
+        co = poison(make_chunk_cohort(B, H, 64, C, S, caches, Hk=Hk, dtype=dtype,
+                                      per_row_pos=per_row, pos_noise=0.5 if per_row else 0.0,
+                                      seed=80 + i, device=DEV))
+        what = f"B={B} H={H} Hk={Hk} C={C} S={S} per_row={per_row} {dtype}"
+        ref = oracle_chunk(co)
+        co2 = clone(co)
+        out_a = gpu_chunk(co)
+        out_f = gpu_chunk(co2, fused=True)
+        torch.cuda.synchronize()
+        assert max_err(out_f, ref) <= TOL[dtype], (what, max_err(out_f, ref))
+        np.testing.assert_array_equal(bits(out_a), bits(out_f), err_msg=what)
+        np.testing.assert_array_equal(bits(co.k_pool), bits(co2.k_pool), err_msg=what)
+        np.testing.assert_array_equal(bits(co.v_pool), bits(co2.v_pool), err_msg=what)
+
+
 def test_block_relabelling_is_bitwise_invariant():
     co = small_cohort("bf16_ragged", seed=5)
     N = co.k_pool.shape[0]
@@ -263,6 +293,23 @@ def test_varlen_gqa_parity():
                                     co.cu_seqlens.cpu().numpy(), host64(co.pos),
                                     host64(co.pos_bias_u), host64(co.pos_bias_v))
     assert max_err(gpu_varlen(co), ref) <= TOL[BF16]
+
+
+def test_varlen_random_batches():
+    """A seeded sweep of packed batches: 1 to 10 utterances of 0 to 700 frames, heads with GQA,
+    bf16 and fp32, each against the oracle."""
+    rng = np.random.default_rng(73)
+    for i in range(8):
+        dtype = F32 if i % 4 == 3 else BF16
+        Hk = int(rng.choice([1, 2, 4]))
+        H = Hk * int(rng.choice([1, 2]))
+        lengths = rng.integers(0, 700, size=int(rng.integers(1, 11))).tolist()
+        co = make_varlen_cohort(lengths, H, 64, Hk=Hk, dtype=dtype, seed=90 + i, device=DEV)
+        ref = oracle.varlen_relpos_attn(host64(co.q), host64(co.k), host64(co.v),
+                                        co.cu_seqlens.cpu().numpy(), host64(co.pos),
+                                        host64(co.pos_bias_u), host64(co.pos_bias_v))
+        err = max_err(gpu_varlen(co), ref)
+        assert err <= TOL[dtype], (lengths, H, Hk, dtype, err)
 
 
 def test_varlen_workload_sampled():
