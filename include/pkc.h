@@ -330,8 +330,9 @@ pkc_status varlen_packed_relpos_attn(pkc_dtype dtype, const void* q, const void*
  * x [M, K], w [N, K] (out_features x in_features, the nn.Linear storage), bias [N] or NULL,
  * y [M, N]; all row-major, one dtype. y is written in full; nothing else is touched.
  * Grid: one workgroup per output tile (128 x 128, 128 x 64 or 64 x 64, picked by size; also
- * 128 x 192 for bf16 with K of 256, 512 or 1024, whose stages are loaded straight into LDS), of
- * 256 threads, or 512 for those direct stages with K of 512 or 1024.
+ * 128 x 192 and 32 x 64 for bf16 with K of 256, 512 or 1024, whose stages are loaded straight
+ * into LDS), of 256 threads, or 512 for those direct stages with K of 512 or 1024 on tiles of 64
+ * rows or more.
  * Errors: NULL x, w or y -> PKC_ERR_NULL; a non-positive size, or M, N or K at or past 2^30 ->
  * PKC_ERR_SHAPE; K not a multiple of 32, N not a multiple of 16 or the launch limits ->
  * PKC_ERR_UNSUPPORTED; a pointer not 16-byte aligned -> PKC_ERR_ALIGN.
